@@ -1,0 +1,117 @@
+/*
+ * libbiwkv — Vision-RWKV spatial-mix hot path for AMD Instinct MI355X (gfx950).
+ *
+ * Operations (cited by page title and equation; the pages define what is computed):
+ *   Bi-WKV   — "OpenGVLab&港中文&复旦&南大&清华提出Vision-RWKV Backbone" (Vision-RWKV article),
+ *              section "Linear Complexity Bidirectional Attention", Eq. (5) (summation form) and
+ *              Eq. (6)-(7) (the four-state RNN form the library evaluates as a chunked scan):
+ *                wkv_t = ( sum_{i != t} e^{-((|t-i|-1)/T) w + k_i} v_i + e^{u + k_t} v_t )
+ *                      / ( sum_{i != t} e^{-((|t-i|-1)/T) w + k_i}     + e^{u + k_t}     )
+ *              per batch item and channel; w (decay, any sign) and u (bonus) are per-channel.
+ *              The exponent is divided by T as the article's "Scale Up Stability" section asks.
+ *   Q-Shift  — the q_shift function in "LinXin's Blog" Vision-RWKV notes (and Eq. (9) of the
+ *              article, whose direction order the listing supersedes): on the H x W token grid
+ *              (token n = h*W + w), channel groups [0,g1) shift right, [g1,g2) left, [g2,g3) down,
+ *              [g3,g4) up by `shift` tokens with zero fill; channels >= g4 are copied;
+ *              g_j = int(C * gamma * j) computed in double precision as in the listing.
+ *   Fused    — Bi-WKV applied to Q-Shift(k) and Q-Shift(v), with T = H*W. Zero-filled sources
+ *              enter the attention as k = 0, v = 0 (they are values, not masks).
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers of the current HIP device, except where stated. Arrays are
+ *     contiguous; [B, T, C] means C is the fastest-varying index.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the null stream. Calls are asynchronous:
+ *     they validate on the host, enqueue, and return. No call synchronises.
+ *   - The caller owns every buffer. The library keeps no pointer to caller memory after the
+ *     enqueued work completes. Bi-WKV calls use library-owned scratch (chunk aggregates and a
+ *     small counter block) kept per (device, stream); it is allocated on first use of a stream and
+ *     grown when a larger problem arrives, so the first call on a stream, and a call that needs
+ *     more scratch than before, must not be made under HIP graph capture.
+ *   - All argument validation happens on the host before any HIP call. A problem with zero
+ *     elements returns BIWKV_OK without enqueuing anything. Nothing is printed; no C++ exception
+ *     crosses this interface.
+ *   - Thread safety: calls may come from several host threads. Calls on the same stream are
+ *     serialised by the stream; calls on different streams use different scratch.
+ */
+#ifndef LIBBIWKV_BIWKV_H
+#define LIBBIWKV_BIWKV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage type of k and v. Bi-WKV always accumulates and writes in fp32. */
+#define BIWKV_F32 0   /* IEEE binary32 */
+#define BIWKV_BF16 1  /* bfloat16 (upper half of a binary32) */
+
+/* Status codes. */
+#define BIWKV_OK 0
+#define BIWKV_ERR_NULL (-1)        /* a required pointer is NULL                                 */
+#define BIWKV_ERR_SHAPE (-2)       /* a dimension < 0, too large, or T != H*W                    */
+#define BIWKV_ERR_DTYPE (-3)       /* dtype is neither BIWKV_F32 nor BIWKV_BF16                  */
+#define BIWKV_ERR_PARAM (-4)       /* gamma outside [0, 1/4] or NaN; shift < 0 or > min(H, W)   */
+#define BIWKV_ERR_ALIAS (-5)       /* out overlaps an input                                      */
+#define BIWKV_ERR_ALIGN (-6)       /* a pointer is not aligned to its element size               */
+#define BIWKV_ERR_NO_DEVICE (-7)   /* no usable HIP device                                       */
+#define BIWKV_ERR_HIP (-8)         /* a HIP runtime call or launch failed; see biwkv_last_hip_error */
+#define BIWKV_ERR_UNSUPPORTED (-9) /* T needs more chunks than can be resident at once          */
+
+/*
+ * Bi-WKV forward, Eq. (5) of the Vision-RWKV article.
+ *   k, v : [B, T, C], storage type `dtype` (BIWKV_F32 or BIWKV_BF16), device memory.
+ *   w, u : [C] float32, device memory (decay, divided by T inside; bonus).
+ *   out  : [B, T, C] float32, device memory; must not overlap k, v, w or u.
+ * Errors: BIWKV_ERR_NULL, _SHAPE (B, T, C < 0 or B*T*C*4 bytes overflow), _DTYPE, _ALIAS, _ALIGN,
+ * _NO_DEVICE, _UNSUPPORTED (T beyond the co-resident chunk capacity, about 32k tokens), _HIP.
+ */
+int biwkv_forward(const void* k, const void* v, const float* w, const float* u, float* out,
+                  int64_t B, int64_t T, int64_t C, int dtype, void* stream);
+
+/*
+ * Q-Shift token shift X-dagger of the q_shift listing (LinXin's Blog, Vision-RWKV notes).
+ *   x, out : [B, H*W, C] float32, device memory; values are moved bit for bit (NaN payloads,
+ *            signed zeros and denormals are preserved); out must not overlap x.
+ *   shift  : grid offset in tokens, 0 <= shift <= min(H, W).
+ *   gamma  : channel-group fraction, 0 <= gamma <= 1/4 (the listing asserts gamma <= 1/4).
+ * Errors: BIWKV_ERR_NULL, _SHAPE, _PARAM, _ALIAS, _ALIGN, _NO_DEVICE, _HIP.
+ */
+int qshift(const float* x, float* out, int64_t B, int64_t H, int64_t W, int64_t C, int shift,
+           double gamma, void* stream);
+
+/*
+ * Fused Q-Shift + Bi-WKV: out = Bi-WKV(Q-Shift(k), Q-Shift(v)) with T = H*W. The shift is applied
+ * while k and v are loaded; no shifted copy is written to memory.
+ *   k, v : [B, H*W, C], storage type `dtype`; w, u : [C] float32; out : [B, H*W, C] float32.
+ *   shift, gamma as for qshift().
+ * Errors: as biwkv_forward() plus BIWKV_ERR_PARAM.
+ */
+int biwkv_qshift_forward(const void* k, const void* v, const float* w, const float* u, float* out,
+                         int64_t B, int64_t H, int64_t W, int64_t C, int shift, double gamma,
+                         int dtype, void* stream);
+
+/* Static, NUL-terminated description of a status code. Never NULL. */
+const char* biwkv_status_string(int status);
+
+/* Raw hipError_t value of the most recent BIWKV_ERR_HIP returned on the calling host thread. */
+int biwkv_last_hip_error(void);
+
+/*
+ * Diagnostic: synchronises `stream`, then reports and clears the device-side fault word of that
+ * stream's scratch. *flags receives 0 when every Bi-WKV launch on the stream since the last query
+ * completed its cross-chunk exchange normally; bit 0 set means a chunk stopped waiting for a
+ * neighbour's aggregate after its bounded wait ran out (its output is then invalid). Returns
+ * BIWKV_OK, BIWKV_ERR_NULL (flags NULL), _NO_DEVICE or _HIP. A stream with no scratch yet
+ * reports 0.
+ */
+int biwkv_stream_fault_flags(void* stream, uint32_t* flags);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int biwkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBBIWKV_BIWKV_H */

@@ -1,0 +1,19 @@
+"""Vision-RWKV spatial-mix hot path (Bi-WKV and Q-Shift) for AMD Instinct MI355X.
+
+The computation lives in libbiwkv.so (hand-written HIP for gfx950, C ABI in include/biwkv.h);
+this package only marshals torch tensors to it.
+"""
+from ._lib import (  # noqa: F401
+    BF16,
+    F32,
+    LIB_PATH,
+    BiwkvError,
+    biwkv_forward,
+    biwkv_qshift_forward,
+    header_symbols,
+    load_library,
+    qshift,
+    status_codes,
+    status_string,
+    stream_fault_flags,
+)
