@@ -1,0 +1,277 @@
+"""Benchmark: Bi-WKV forward (+ Q-Shift) throughput and HBM roofline on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--entry fused|biwkv|qshift]
+
+One step = one pass of the whole hot path over one batch: the fused Q-Shift + Bi-WKV entry on the
+high-resolution workload (B=4, 64x64 grid so T=4096, C=1024, bf16 k/v, fp32 accumulate and
+output). Inputs are resident in HBM before timing; R copies of inputs and outputs are rotated so
+each step's buffers were last touched more than 256 MB of traffic ago (the MALL size), i.e. every
+step streams from HBM. Prints ONE JSON line.
+
+Also:
+    python bench.py --calibrate-copy      plain device copy of a known size (for counter scaling)
+    python bench.py --summarize DIR       summarise rocprofv3 output (kernel stats / counters)
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E peak
+MALL_BYTES = 256 * 1024 * 1024
+KERNEL_SRC = os.path.join(ROOT, "linear_complexity_vision_amd", "csrc", "biwkv.hip")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters_biwkv_qshift_B4_T4096_C1024_bf16.json")
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def alg_bytes(entry: str, B: int, H: int, W: int, C: int, kv_bytes: int, shift: int = 1, gamma: float = 0.25) -> int:
+    """Algorithmic HBM bytes of one call: what the method must move.
+
+    biwkv:  read k and v (kv_bytes each), write fp32 out, read w and u.
+    fused:  as biwkv, but the Q-Shift zero-filled sources are never read.
+    qshift: read the in-grid sources, write every output (fp32).
+    """
+    T = H * W
+    n = B * T * C
+    g = [int(C * gamma * j) for j in (1, 2, 3, 4)]
+    zero_per_b = shift * H * g[1] + shift * W * (g[3] - g[1])  # zero-filled outputs per batch item
+    if entry == "biwkv":
+        return 2 * kv_bytes * n + 4 * n + 8 * C
+    if entry == "fused":
+        return 2 * kv_bytes * (n - B * zero_per_b) + 4 * n + 8 * C
+    if entry == "qshift":
+        return 4 * (n - B * zero_per_b) + 4 * n
+    raise ValueError(entry)
+
+
+def _load_counters():
+    """Counter-derived HBM bytes per launch, valid only for the kernel source they were taken on."""
+    try:
+        rec = json.load(open(COUNTERS_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, entry: str) -> dict:
+    """The float64 oracle (four-state RNN form, the method's own O(TC) algorithm) on host cores,
+    over the whole workload; input conversion is outside the timed span."""
+    import numpy as np
+
+    import oracle
+
+    k = wl.k.astype(np.float64)
+    v = wl.v.astype(np.float64)
+    w = wl.w.astype(np.float64)
+    u = wl.u.astype(np.float64)
+    threads = oracle.max_threads()
+    oracle.biwkv_rnn(k[:, :64], v[:, :64], w, u, threads=threads)  # warm the library and threads
+    if entry == "qshift":
+        x32 = wl.k
+        t0 = time.perf_counter()
+        oracle.qshift(x32, wl.H, wl.W, wl.shift, wl.gamma)
+        dt = time.perf_counter() - t0
+        elems = wl.B * wl.T * wl.C
+        return {"value": elems / dt / 1e9, "unit": "Gtoken*ch/s", "cores": 1, "kind": "oracle",
+                "seconds": dt, "cpu": _cpu_model(),
+                "sample": f"whole workload ({wl.B}x{wl.T}x{wl.C}); single-threaded oracle Q-Shift gather"}
+    t0 = time.perf_counter()
+    if entry == "fused":
+        ks = oracle.qshift_f64(k, wl.H, wl.W, wl.shift, wl.gamma)
+        vs = oracle.qshift_f64(v, wl.H, wl.W, wl.shift, wl.gamma)
+        oracle.biwkv_rnn(ks, vs, w, u, threads=threads)
+    else:
+        oracle.biwkv_rnn(k, v, w, u, threads=threads)
+    dt = time.perf_counter() - t0
+    elems = wl.B * wl.T * wl.C
+    return {"value": elems / dt / 1e9, "unit": "Gtoken*ch/s", "cores": threads, "kind": "oracle",
+            "seconds": dt, "cpu": _cpu_model(),
+            "sample": f"whole workload ({wl.B}x{wl.T}x{wl.C}); float64 four-state RNN oracle"
+                      + (" after the oracle Q-Shift of k and v" if entry == "fused" else "")}
+
+
+def _rotation(bytes_per_set: int) -> int:
+    return max(2, -(-2 * MALL_BYTES // bytes_per_set) + 1)
+
+
+def run_bench(args) -> dict:
+    import numpy as np
+    import torch
+
+    import linear_complexity_vision_amd as lib
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = workloads.make(4)
+    B, H, W, C = wl.B, wl.H, wl.W, wl.C
+    T = H * W
+    entry = args.entry
+    ks, vs = wl.kv_storage()
+    kb = torch.from_numpy(np.ascontiguousarray(ks)).view(torch.bfloat16).to(dev)
+    vb = torch.from_numpy(np.ascontiguousarray(vs)).view(torch.bfloat16).to(dev)
+    w = torch.from_numpy(wl.w).to(dev)
+    u = torch.from_numpy(wl.u).to(dev)
+    set_bytes = (kb.numel() + vb.numel()) * 2 + B * T * C * 4
+    R = _rotation(set_bytes)
+    ks_ = [kb] + [kb.clone() for _ in range(R - 1)]
+    vs_ = [vb] + [vb.clone() for _ in range(R - 1)]
+    outs = [torch.empty((B, T, C), dtype=torch.float32, device=dev) for _ in range(R)]
+    if entry == "qshift":
+        xs = [torch.from_numpy(wl.k).to(dev).contiguous() for _ in range(R)]
+
+    def step(i):
+        r = i % R
+        if entry == "fused":
+            lib.biwkv_qshift_forward(ks_[r], vs_[r], w, u, H, W, wl.shift, wl.gamma, out=outs[r])
+        elif entry == "biwkv":
+            lib.biwkv_forward(ks_[r], vs_[r], w, u, out=outs[r])
+        else:
+            lib.qshift(xs[r], H, W, wl.shift, wl.gamma, out=outs[r])
+
+    stream = torch.cuda.current_stream(dev)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    assert lib.stream_fault_flags(dev) == 0
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step(args.warmup + i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    assert lib.stream_fault_flags(dev) == 0
+
+    avg_ms = sum(durs_ms) / len(durs_ms)
+    ms_per_step = wall * 1e3 / args.steps
+    elems = B * T * C
+    kv_bytes = 4 if entry == "qshift" else 2
+    ab = alg_bytes(entry, B, H, W, C, kv_bytes, wl.shift, wl.gamma)
+    achieved = ab / (avg_ms * 1e-3) / 1e9
+    counters = _load_counters()
+    traffic = None
+    if counters is not None and entry in counters.get("entries", {}):
+        traffic = counters["entries"][entry]["hbm_bytes_per_launch"]
+    names = {"fused": "biwkv_qshift_forward", "biwkv": "biwkv_forward", "qshift": "qshift"}
+    return {
+        "metric": "Bi-WKV fwd Gtoken*ch/s + achieved HBM GB/s (% peak) at T=4096 C=1024",
+        "value": elems * args.steps / wall / 1e9,
+        "unit": "Gtoken*ch/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "entry": names[entry], "B": B, "T": T, "H": H, "W": W, "C": C,
+                   "kv_storage": "bf16" if entry != "qshift" else "f32", "shift": wl.shift,
+                   "gamma": wl.gamma, "buffer_sets_rotated": R},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "alg_bytes_per_launch": ab, "avg_launch_ms": avg_ms,
+                     "p10_launch_ms": durs_ms[len(durs_ms) // 10],
+                     "p90_launch_ms": durs_ms[(9 * len(durs_ms)) // 10]},
+        "_wl": wl,
+    }
+
+
+def calibrate_copy(args) -> None:
+    """A plain device copy of a known size, for scaling FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+
+    n_bytes = 512 * 1024 * 1024
+    a = torch.empty(n_bytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(args.steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read": n_bytes, "bytes_written": n_bytes,
+                      "launches": args.steps}))
+
+
+def summarize(path: str) -> None:
+    """Summarise rocprofv3 CSV output under `path`: per-kernel durations or counter values."""
+    stats = glob.glob(os.path.join(path, "**", "*kernel_stats.csv"), recursive=True)
+    for f in stats:
+        print(f"# kernel stats: {os.path.relpath(f, path)}")
+        for row in csv.DictReader(open(f)):
+            print(f"{row.get('Name', '?')[:90]:90s} calls={row.get('Calls')} "
+                  f"avg_ns={float(row.get('AverageNs', 'nan')):.0f} min_ns={row.get('MinNs')} "
+                  f"max_ns={row.get('MaxNs')} pct={row.get('Percentage')}")
+    ctr = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    for f in ctr:
+        print(f"# counters: {os.path.relpath(f, path)}")
+        acc = {}
+        for row in csv.DictReader(open(f)):
+            key = (row.get("Kernel_Name", "?")[:90], row.get("Counter_Name"))
+            acc.setdefault(key, []).append(float(row.get("Counter_Value", "nan")))
+        for (kname, cname), vals in sorted(acc.items()):
+            print(f"{kname:90s} {cname} dispatches={len(vals)} mean={sum(vals) / len(vals):.1f} "
+                  f"min={min(vals):.1f} max={max(vals):.1f}")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--entry", choices=["fused", "biwkv", "qshift"], default="fused")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--summarize", metavar="DIR")
+    args = ap.parse_args()
+
+    if args.summarize:
+        summarize(args.summarize)
+        return 0
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only (the Bi-WKV path shards by batch, channel "
+              "or token rows without changing the per-GPU kernel); run with --gpus 1", file=sys.stderr)
+        return 2
+    if args.calibrate_copy:
+        calibrate_copy(args)
+        return 0
+    res = run_bench(args)
+    wl = res.pop("_wl")
+    res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(wl, args.entry)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
