@@ -1,0 +1,496 @@
+// Bi-WKV whole-row kernel (a row held by one workgroup).
+#pragma once
+
+#include <type_traits>
+
+#include "common.cuh"
+
+namespace {
+
+// ---------------------------------------------------------------------------------------------
+// Bi-WKV whole-row kernel: one workgroup owns every token of a (batch, channel tile) row
+// ---------------------------------------------------------------------------------------------
+//
+// Used when a row fits in one workgroup's registers (T * TILE elements, 64 tokens per lane at
+// most). Lane (c, g) holds channel c of the tile and token group g (L consecutive tokens); the
+// GROUPS = 1024 / TILE groups of a channel are combined by a Hillis-Steele scan in LDS, so no
+// data leaves the workgroup between load and store. Each lane then sweeps its tokens in
+// sub-blocks of 8: forward states (a, c) left to right, keeping (alpha, beta) = (a - c v, c +
+// e^{u+k}) per token in LDS, then backward states (b, d) right to left, writing Eq. (7).
+//
+// Every lane holds exactly L token slots. Slots past the end of the row hold k = -inf, i.e. a
+// weight of exactly 0, so the sweeps need no per-token bounds: a lane's forward sum is anchored
+// at its last slot, and such slots are only ever followed by more empty slots. Loads and stores
+// go through range-checked buffer resources over one batch item, so slots past the row read 0
+// and their stores are dropped by the hardware.
+
+// Per-lane token storage: bf16 k and v packed in one 32-bit register per token (k in the low
+// half, v in the high half); fp32 k and v in two registers. fence() makes the stored words
+// opaque to the compiler (no instruction), so values unpacked in one phase are not kept live
+// into the next one: unpacking again is cheaper than the registers. pad_from(n) sets k = -inf
+// in slots n and later.
+template <int DT, int L>
+struct RowKV;
+
+template <int L>
+struct RowKV<BIWKV_BF16, L> {
+  uint32_t r[L];
+  __device__ __forceinline__ float k(int i) const { return __uint_as_float(r[i] << 16); }
+  __device__ __forceinline__ float v(int i) const { return __uint_as_float(r[i] & 0xffff0000u); }
+  __device__ __forceinline__ void fence() {
+#pragma unroll
+    for (int i = 0; i < L; ++i) asm volatile("" : "+v"(r[i]));
+  }
+  __device__ __forceinline__ void pad_from(int n) {
+#pragma unroll
+    for (int i = 0; i < L; ++i)
+      if (i >= n) r[i] = (r[i] & 0xffff0000u) | 0xff80u;
+  }
+};
+
+template <int L>
+struct RowKV<BIWKV_F32, L> {
+  float kk[L], vv[L];
+  __device__ __forceinline__ float k(int i) const { return kk[i]; }
+  __device__ __forceinline__ float v(int i) const { return vv[i]; }
+  __device__ __forceinline__ void fence() {
+#pragma unroll
+    for (int i = 0; i < L; ++i) asm volatile("" : "+v"(kk[i]), "+v"(vv[i]));
+  }
+  __device__ __forceinline__ void pad_from(int n) {
+#pragma unroll
+    for (int i = 0; i < L; ++i)
+      if (i >= n) kk[i] = kNegInf;
+  }
+};
+
+// bf16 with channel pairs: a lane keeps its channel at two consecutive tokens in each register
+// (k[2m] | k[2m+1] << 16 and likewise v), so 32-bit loads land in the final registers.
+template <int L>
+struct RowKVPair {
+  static_assert(L % 2 == 0, "paired storage needs an even token count");
+  uint32_t kk[L / 2], vv[L / 2];
+  __device__ __forceinline__ float k(int i) const {
+    return __uint_as_float((i & 1) ? (kk[i >> 1] & 0xffff0000u) : (kk[i >> 1] << 16));
+  }
+  __device__ __forceinline__ float v(int i) const {
+    return __uint_as_float((i & 1) ? (vv[i >> 1] & 0xffff0000u) : (vv[i >> 1] << 16));
+  }
+  __device__ __forceinline__ void fence() {
+#pragma unroll
+    for (int m = 0; m < L / 2; ++m) asm volatile("" : "+v"(kk[m]), "+v"(vv[m]));
+  }
+  __device__ __forceinline__ void pad_from(int n) {
+#pragma unroll
+    for (int m = 0; m < L / 2; ++m) {
+      if (2 * m >= n) kk[m] = (kk[m] & 0xffff0000u) | 0xff80u;
+      if (2 * m + 1 >= n) kk[m] = (kk[m] & 0x0000ffffu) | 0xff800000u;
+    }
+  }
+};
+
+// Raw buffer resource over n_bytes at base. The range check covers the whole offset (it is all
+// passed in the vector offset): an offset at or past n_bytes reads 0 and drops a store.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t n_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(n_bytes), 0x00020000);
+}
+// Byte offset of a skipped access: past every resource (the host keeps a batch item's k, v and
+// out below 2^31 bytes), and adding up to 2^31 - 1 more does not wrap.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+struct RowParams {
+  const void* k;
+  const void* v;
+  const float* w;
+  const float* u;
+  float* out;
+  long long T;
+  int C;
+  int n_rows;   // B * tiles
+  int n_tiles;  // channel tiles per batch item
+  int share;    // rows sharing one 128-byte line of k (mapped to one XCD), 1 = identity
+  int H, W, shift, g1, g2, g3, g4;  // Q-Shift (fused entry only)
+};
+
+// Per-lane constants: lane (c, g) holds channel ch = tile * TILE + c at the tokens
+// [s_g, s_g + n_g) of batch item b (n_g < L only in the last groups of a row).
+struct RowLane {
+  long long b, s_g;
+  int c, g, ch, n_g;
+  bool on;
+  float D, lam, U, grow, eU;
+};
+
+template <int TILE, int L>
+__device__ __forceinline__ RowLane row_lane(const RowParams& p) {
+  RowLane ln;
+  const int tid = threadIdx.x;
+  ln.c = tid % TILE;
+  ln.g = tid / TILE;
+  // Rows whose tiles share a cache line of k run on one XCD (workgroup i runs on XCD i % 8), so
+  // the line is fetched into that XCD's L2 once.
+  int row = blockIdx.x;
+  if (p.share > 1) {
+    const int sh = p.share;
+    row = ((row / (8 * sh)) * 8 + row % 8) * sh + (row / 8) % sh;
+  }
+  const int tile = row % p.n_tiles;
+  ln.b = row / p.n_tiles;
+  ln.ch = tile * TILE + ln.c;
+  ln.on = ln.ch < p.C;
+  ln.s_g = static_cast<long long>(ln.g) * L;
+  const long long rem = p.T - ln.s_g;
+  ln.n_g = rem <= 0 ? 0 : (rem < L ? static_cast<int>(rem) : L);
+  const float wc = ln.on ? p.w[ln.ch] : 0.f;
+  const float uc = ln.on ? p.u[ln.ch] : 0.f;
+  ln.D = (wc / static_cast<float>(p.T)) * kLog2e;
+  ln.lam = fast_exp2(-ln.D);
+  ln.U = uc * kLog2e;
+  ln.grow = fmaxf(-ln.D, 0.f);
+  ln.eU = fast_exp2(ln.U);
+  return ln;
+}
+
+// Loads the lane's k and v (Q-Shift applied when FUSED: padded sources read 0), then marks the
+// slots past the row empty.
+template <int DT, int TILE, int L, bool FUSED, bool PAIR, class Store>
+__device__ __forceinline__ void row_load(const RowParams& p, const RowLane& ln, Store& kv) {
+  const long long T = p.T;
+  const int C = p.C;
+  const long long plane = T * C;  // elements of one batch item
+  constexpr int ES = DT == BIWKV_F32 ? 4 : 2;
+  const char* kb = static_cast<const char*>(p.k) + ln.b * plane * ES;
+  const char* vb = static_cast<const char*>(p.v) + ln.b * plane * ES;
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(kb, static_cast<uint32_t>(plane * ES));
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(vb, static_cast<uint32_t>(plane * ES));
+  QShiftLane qs;
+  if constexpr (FUSED) qs.init(ln.ch, p.H, p.W, T, p.shift, p.g1, p.g2, p.g3, p.g4);
+  const uint32_t row_bytes = static_cast<uint32_t>(C) * ES;
+  if constexpr (PAIR) {
+    // Lanes 2j and 2j+1 of a group both read channels (2j, 2j+1) as one 32-bit word: the even
+    // lane at the group's even tokens, the odd lane at its odd tokens. Swapping 16-bit halves
+    // with the neighbour then leaves each lane its own channel at tokens (2m, 2m+1).
+    const int odd = ln.c & 1;
+    const uint32_t lane_byte = static_cast<uint32_t>(ln.ch - odd) * 2u;
+    int col = 0;
+    if constexpr (FUSED) col = static_cast<int>((ln.s_g + odd) % p.W);
+#pragma unroll
+    for (int m = 0; m < L / 2; ++m) {
+      const int i = 2 * m + odd;
+      const long long t = ln.s_g + i;
+      bool ok = ln.on && t < T;
+      long long src = t;
+      if constexpr (FUSED) {
+        ok = ok && qs.valid(t, col);
+        src = t + qs.off;
+        col += 2;
+        if (col >= p.W) col -= p.W;
+        if (col >= p.W) col -= p.W;
+      }
+      const uint32_t off = ok ? static_cast<uint32_t>(src) * row_bytes + lane_byte : kOutOfRange;
+      kv.kk[m] = __builtin_amdgcn_raw_buffer_load_b32(kr, off, 0, 0);
+      kv.vv[m] = __builtin_amdgcn_raw_buffer_load_b32(vr, off, 0, 0);
+    }
+    // even lane: (own low, neighbour low); odd lane: (neighbour high, own high)
+    const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
+#pragma unroll
+    for (int m = 0; m < L / 2; ++m) {
+      const uint32_t nk = __builtin_amdgcn_mov_dpp(kv.kk[m], 0xB1, 0xf, 0xf, false);
+      const uint32_t nv = __builtin_amdgcn_mov_dpp(kv.vv[m], 0xB1, 0xf, 0xf, false);
+      kv.kk[m] = __builtin_amdgcn_perm(nk, kv.kk[m], sel);
+      kv.vv[m] = __builtin_amdgcn_perm(nv, kv.vv[m], sel);
+    }
+  } else {
+    int col = 0;
+    if constexpr (FUSED) col = static_cast<int>(ln.s_g % p.W);
+    const uint32_t lane_byte = static_cast<uint32_t>(ln.ch) * ES;
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const long long t = ln.s_g + i;
+      bool ok = ln.on && t < T;
+      long long src = t;
+      if constexpr (FUSED) {
+        ok = ok && qs.valid(t, col);
+        src = t + qs.off;
+        col = col + 1 == p.W ? 0 : col + 1;
+      }
+      const uint32_t off = ok ? static_cast<uint32_t>(src) * row_bytes + lane_byte : kOutOfRange;
+      if constexpr (DT == BIWKV_F32) {
+        kv.kk[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(kr, off, 0, 0));
+        kv.vv[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vr, off, 0, 0));
+      } else {
+        const uint32_t kx = __builtin_amdgcn_raw_buffer_load_b16(kr, off, 0, 0);
+        const uint32_t vx = __builtin_amdgcn_raw_buffer_load_b16(vr, off, 0, 0);
+        kv.r[i] = kx | (vx << 16);
+      }
+    }
+  }
+  if (ln.n_g < L) kv.pad_from(ln.n_g);
+}
+
+// One whole row: load, lane sums (phase A), scan over the groups, sweeps (phase C). WIDE selects
+// the per-token running-maximum arithmetic; the fast form scales every term of a lane against
+// one exponent.
+template <int DT, int TILE, int L, bool FUSED, bool PAIR, bool WIDE>
+__device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln, float* lds) {
+  constexpr int NT = 1024;
+  constexpr int GROUPS = NT / TILE;
+  constexpr int SB = 8;  // tokens per sub-block of the sweeps
+  constexpr int NSB = L / SB;
+  static_assert(L % SB == 0, "bad row-kernel shape");
+  float (*scan)[6][NT] = reinterpret_cast<float (*)[6][NT]>(lds);
+  float2 (*lds_ab)[NT] = reinterpret_cast<float2 (*)[NT]>(lds);
+  const int tid = threadIdx.x;
+  const int g = ln.g;
+  const long long T = p.T;
+  const int C = p.C;
+  const float D = ln.D, lam = ln.lam, grow = ln.grow;
+  const float span = grow * static_cast<float>(L - 1);  // largest growth inside one lane
+
+  using Store = std::conditional_t<PAIR, RowKVPair<L>, RowKV<DT, L>>;
+  Store kv;
+  row_load<DT, TILE, L, FUSED, PAIR>(p, ln, kv);
+
+  // ---- phase A: lane sums (forward anchored at its last slot, backward at its first) and, per
+  //      sub-block, the backward sum of everything after it inside the lane ----
+  Agg af, ab;
+  float kmax = kNegInf;
+  float capF[WIDE ? 1 : NSB], capG[WIDE ? 1 : NSB];  // fast form: anchored at (q + 1) * SB
+  Agg cap[WIDE ? NSB : 1];                           // wide form
+  if constexpr (!WIDE) {
+#pragma unroll
+    for (int i = 0; i < L; ++i) kmax = fmaxf(kmax, kv.k(i));
+    kmax *= kLog2e;
+    kv.fence();
+    const bool any = kmax != kNegInf;
+    const float mw = any ? kmax + span : 0.f;  // every term <= 1 against mw
+    float fF = 0.f, fG = 0.f;
+    float bF[NSB], bG[NSB];  // backward sum of each sub-block, anchored at its first token
+#pragma unroll
+    for (int q = 0; q < NSB; ++q) {
+      float pp[SB], pv[SB];
+#pragma unroll
+      for (int i = 0; i < SB; ++i) {
+        const int t = q * SB + i;
+        pp[i] = fast_exp2(fmaf(kv.k(t), kLog2e, -mw));
+        pv[i] = pp[i] * kv.v(t);
+        fF = fmaf(fF, lam, pv[i]);
+        fG = fmaf(fG, lam, pp[i]);
+      }
+      bF[q] = pv[SB - 1];
+      bG[q] = pp[SB - 1];
+#pragma unroll
+      for (int i = SB - 2; i >= 0; --i) {
+        bF[q] = fmaf(bF[q], lam, pv[i]);
+        bG[q] = fmaf(bG[q], lam, pp[i]);
+      }
+    }
+    const float lsb = fast_exp2(-static_cast<float>(SB) * D);  // lam^SB
+    float cF = 0.f, cG = 0.f;
+#pragma unroll
+    for (int q = NSB - 1; q >= 0; --q) {
+      capF[q] = cF;
+      capG[q] = cG;
+      cF = fmaf(cF, lsb, bF[q]);
+      cG = fmaf(cG, lsb, bG[q]);
+    }
+    const float m_agg = any ? mw : kNegInf;
+    af = Agg{m_agg, fF, fG};
+    ab = Agg{m_agg, cF, cG};
+  } else {
+    // Wide range: one decay step at a time, each sum against its own running maximum (an empty
+    // slot, k = -inf, adds nothing).
+    af = agg_empty();
+    Agg bs[NSB];
+#pragma unroll
+    for (int q = 0; q < NSB; ++q) {
+      bs[q] = agg_empty();
+#pragma unroll
+      for (int i = (q + 1) * SB - 1; i >= q * SB; --i)
+        bs[q] = agg_add(agg_shift(bs[q], 1.f, D), Agg{kv.k(i) * kLog2e, kv.v(i), 1.f});
+    }
+#pragma unroll
+    for (int i = 0; i < L; ++i)
+      af = agg_add(agg_shift(af, 1.f, D), Agg{kv.k(i) * kLog2e, kv.v(i), 1.f});
+    Agg cs = agg_empty();
+#pragma unroll
+    for (int q = NSB - 1; q >= 0; --q) {
+      cap[q] = cs;
+      cs = agg_add(bs[q], agg_shift(cs, static_cast<float>(SB), D));
+    }
+    ab = cs;
+  }
+  kv.fence();
+
+  // ---- inclusive scans over the groups of each channel (Hillis-Steele, fixed order); group
+  //      sums are L slots apart in both directions ----
+  int cur = 0;
+  scan[0][0][tid] = af.m;
+  scan[0][1][tid] = af.F;
+  scan[0][2][tid] = af.G;
+  scan[0][3][tid] = ab.m;
+  scan[0][4][tid] = ab.F;
+  scan[0][5][tid] = ab.G;
+  __syncthreads();
+#pragma unroll
+  for (int d = 1; d < GROUPS; d *= 2) {
+    Agg f{scan[cur][0][tid], scan[cur][1][tid], scan[cur][2][tid]};
+    Agg bk{scan[cur][3][tid], scan[cur][4][tid], scan[cur][5][tid]};
+    if (g >= d) {
+      const int o = tid - d * TILE;
+      const Agg pf{scan[cur][0][o], scan[cur][1][o], scan[cur][2][o]};
+      f = agg_add(agg_shift(pf, static_cast<float>(d * L), D), f);
+    }
+    if (g + d < GROUPS) {
+      const int o = tid + d * TILE;
+      const Agg pb{scan[cur][3][o], scan[cur][4][o], scan[cur][5][o]};
+      bk = agg_add(bk, agg_shift(pb, static_cast<float>(d * L), D));
+    }
+    cur ^= 1;
+    scan[cur][0][tid] = f.m;
+    scan[cur][1][tid] = f.F;
+    scan[cur][2][tid] = f.G;
+    scan[cur][3][tid] = bk.m;
+    scan[cur][4][tid] = bk.F;
+    scan[cur][5][tid] = bk.G;
+    __syncthreads();
+  }
+  // exclusive carries: forward sum of the earlier groups (anchored just before this lane's first
+  // token), backward sum of the later groups (anchored just after its last slot)
+  Agg X = agg_empty(), Y = agg_empty();
+  if (g > 0) {
+    const int o = tid - TILE;
+    X = Agg{scan[cur][0][o], scan[cur][1][o], scan[cur][2][o]};
+  }
+  if (g + 1 < GROUPS) {
+    const int o = tid + TILE;
+    Y = Agg{scan[cur][3][o], scan[cur][4][o], scan[cur][5][o]};
+  }
+  __syncthreads();  // the scan buffer becomes the (alpha, beta) buffer
+  kv.fence();
+
+  // ---- phase C: sweep each sub-block forward, then backward, writing Eq. (7) ----
+  if (ln.n_g <= 0) return;  // no barrier follows
+  const long long plane = T * C;
+  const __amdgpu_buffer_rsrc_t orr =
+      make_rsrc(p.out + ln.b * plane, static_cast<uint32_t>(plane * 4));
+  const uint32_t row_bytes = static_cast<uint32_t>(C) * 4u;
+  // slots past the row (and masked lanes) store out of range
+  const uint32_t out0 =
+      ln.on ? static_cast<uint32_t>(ln.s_g) * row_bytes + static_cast<uint32_t>(ln.ch) * 4u
+            : kOutOfRange;
+  if constexpr (!WIDE) {
+    // every scaled term is <= 1 against M
+    const float top = fmaxf(fmaxf(kmax, X.m), Y.m);
+    const float M = top + span;
+    const float sig = fast_exp2(kmax - top);  // 2^{mw - M}
+    const float sx = fast_exp2(X.m - M), sy = fast_exp2(Y.m - M);
+    const float eU = ln.eU;
+    float A = X.F * sx, Cs = X.G * sx;
+    const float YF = Y.F * sy, YG = Y.G * sy;
+#pragma unroll
+    for (int q = 0; q < NSB; ++q) {
+      float ph[SB];
+#pragma unroll
+      for (int i = 0; i < SB; ++i) {
+        const int t = q * SB + i;
+        const float kf = kv.k(t), vf = kv.v(t);
+        const float pi = fast_exp2(fmaf(kf, kLog2e, -M));
+        ph[i] = pi;
+        const float al = fmaf(-Cs, vf, A);
+        const float be = fmaf(pi, eU, Cs);
+        lds_ab[i][tid] = make_float2(al, be);
+        A = fmaf(A, lam, pi * vf);
+        Cs = fmaf(Cs, lam, pi);
+      }
+      // backward state entering this sub-block from the right: the later sub-blocks of the lane
+      // plus the later groups
+      const float lr = fast_exp2(-static_cast<float>(L - (q + 1) * SB) * D);
+      float Bs = fmaf(YF, lr, sig * capF[q]);
+      float Ds = fmaf(YG, lr, sig * capG[q]);
+#pragma unroll
+      for (int i = SB - 1; i >= 0; --i) {
+        const int t = q * SB + i;
+        const float vf = kv.v(t);
+        const float2 ab2 = lds_ab[i][tid];
+        const float num = fmaf(-Ds, vf, ab2.x + Bs);
+        const float den = fmaxf(ab2.y + Ds, 1.17549435e-38f);
+        const float y = fmaf(num, fast_rcp(den), vf);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), orr, out0 + t * row_bytes, 0,
+                                              0);
+        Bs = fmaf(Bs, lam, ph[i] * vf);
+        Ds = fmaf(Ds, lam, ph[i]);
+      }
+    }
+  } else {
+    const float U = ln.U;
+    Agg xs = X;
+#pragma unroll
+    for (int q = 0; q < NSB; ++q) {
+#pragma unroll
+      for (int i = 0; i < SB; ++i) {
+        const int t = q * SB + i;
+        const float kf = kv.k(t), vf = kv.v(t);
+        const bool any = xs.m != kNegInf && xs.G > 0.f;
+        const float be = any ? xs.m + fast_log2(xs.G) : kNegInf;
+        const float al = any ? xs.F * fast_rcp(xs.G) - vf : 0.f;
+        lds_ab[i][tid] = make_float2(al, be);
+        xs = agg_add(agg_shift(xs, 1.f, D), Agg{kf * kLog2e, vf, 1.f});
+      }
+      Agg ys = agg_add(cap[q], agg_shift(Y, static_cast<float>(L - (q + 1) * SB), D));
+#pragma unroll
+      for (int i = SB - 1; i >= 0; --i) {
+        const int t = q * SB + i;
+        const float kf = kv.k(t), vf = kv.v(t);
+        const float2 ab2 = lds_ab[i][tid];
+        const float kl = kf * kLog2e;
+        const float ks = kl + U;
+        const float Mt = fmaxf(fmaxf(ab2.y, ys.m), ks);
+        const float sa = fast_exp2(ab2.y - Mt), sb = fast_exp2(ys.m - Mt);
+        const float e = fast_exp2(ks - Mt);
+        const float num = ab2.x * sa + fmaf(-ys.G, vf, ys.F) * sb;
+        const float den = sa + ys.G * sb + e;
+        const float y = fmaf(num, fast_rcp(den), vf);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), orr, out0 + t * row_bytes, 0,
+                                              0);
+        ys = agg_add(agg_shift(ys, 1.f, D), Agg{kl, vf, 1.f});
+      }
+    }
+  }
+}
+
+// The wide form is rare (extreme w or u) and needs more registers than the fast form: keeping it
+// out of line gives it its own register allocation, so its spills never touch the fast form. It
+// reads the parameters from the kernel's argument segment (a pointer, so the kernel keeps them in
+// scalar registers instead of building a private copy).
+template <int DT, int TILE, int L, bool FUSED, bool PAIR>
+__device__ __noinline__ void row_body_wide(const RowParams* args, float* lds) {
+  const RowParams p = *args;
+  const RowLane ln = row_lane<TILE, L>(p);
+  row_body<DT, TILE, L, FUSED, PAIR, true>(p, ln, lds);
+}
+
+template <int DT, int TILE, int L, bool FUSED, bool PAIR>
+__global__ void __launch_bounds__(1024)
+    biwkv_row_kernel(RowParams p) {
+  static_assert(!PAIR || (DT == BIWKV_BF16 && TILE % 2 == 0), "pairs are bf16 channel pairs");
+  static_assert(1024 % TILE == 0, "bad row-kernel tile");
+  constexpr int NT = 1024;
+  constexpr int kScanFloats = 2 * 6 * NT;  // double-buffered (m, F, G) forward + backward
+  constexpr int kSweepFloats = 8 * NT * 2;
+  __shared__ float lds[kScanFloats > kSweepFloats ? kScanFloats : kSweepFloats];
+  const RowLane ln = row_lane<TILE, L>(p);
+  // The whole workgroup takes the wide form when any of its channels needs it.
+  const bool wide_lane = fabsf(ln.D) * static_cast<float>(L - 1) > kFastRange ||
+                         ln.U > kBonusRange || ln.U < -kBonusRange;
+  if (__syncthreads_or(wide_lane)) {
+    // the kernel's only argument is p, at the start of the argument segment
+    const auto* args = (const RowParams*)(__builtin_amdgcn_kernarg_segment_ptr());
+    row_body_wide<DT, TILE, L, FUSED, PAIR>(args, lds);
+  } else {
+    row_body<DT, TILE, L, FUSED, PAIR, false>(p, ln, lds);
+  }
+}
+
+}  // namespace
