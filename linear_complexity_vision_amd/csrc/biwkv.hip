@@ -227,15 +227,26 @@ int launch_biwkv(BiwkvParams prm, int64_t B, int dev, void* stream) {
   return BIWKV_OK;
 }
 
+// Tile kernel launch: rows of TILE channels, chunks of (1024 / TILE) * L tokens. Returns 1 when
+// the shape is outside what the kernel addresses (the caller then uses the chunk-scan kernel).
 template <int DT, int TILE, int L, bool FUSED, bool PAIR>
-int launch_row(const BiwkvParams& bp, int64_t B, void* stream) {
+int launch_row(const BiwkvParams& bp, int64_t B, int dev, void* stream) {
+  constexpr int CT = (1024 / TILE) * L;
+  const long long T = bp.T;
+  // byte offsets into one batch item of out (and so of k, v), including the empty slots past
+  // the row end, must stay below 2^31
+  if ((T + CT) * static_cast<long long>(bp.C) * 4 >= (1ll << 31)) return 1;
+  const int64_t n_tiles = (bp.C + TILE - 1) / TILE;
+  const int64_t n_chunks = (T + CT - 1) / CT;
+  const int64_t total = B * n_tiles * n_chunks;
+  if (total > 0x7FFFFFFFll) return BIWKV_ERR_SHAPE;
   RowParams rp{};
   rp.k = bp.k;
   rp.v = bp.v;
   rp.w = bp.w;
   rp.u = bp.u;
   rp.out = bp.out;
-  rp.T = bp.T;
+  rp.T = T;
   rp.C = bp.C;
   rp.H = bp.H;
   rp.W = bp.W;
@@ -244,42 +255,49 @@ int launch_row(const BiwkvParams& bp, int64_t B, void* stream) {
   rp.g2 = bp.g2;
   rp.g3 = bp.g3;
   rp.g4 = bp.g4;
-  const int64_t n_tiles = (bp.C + TILE - 1) / TILE;
-  const int64_t n_rows = B * n_tiles;
-  if (n_rows > 0x7FFFFFFFll) return BIWKV_ERR_SHAPE;
-  const int elem = DT == BIWKV_F32 ? 4 : 2;
-  int share = 128 / (TILE * elem);
-  if (share < 1 || n_rows % (8 * share) != 0) share = 1;
-  rp.n_rows = static_cast<int>(n_rows);
   rp.n_tiles = static_cast<int>(n_tiles);
-  rp.share = share;
-  hipLaunchKernelGGL((biwkv_row_kernel<DT, TILE, L, FUSED, PAIR>),
-                     dim3(static_cast<unsigned>(n_rows)), dim3(1024), 0,
-                     static_cast<hipStream_t>(stream), rp);
+  rp.n_chunks = static_cast<int>(n_chunks);
+  rp.total = static_cast<unsigned>(total);
+  if (n_chunks > 1) {
+    // The chunks of a row wait for each other: they must all fit on the device at once.
+    const void* kfn = reinterpret_cast<const void*>(&biwkv_row_kernel<DT, TILE, L, FUSED, PAIR>);
+    std::lock_guard<std::mutex> lock(g_mu);
+    int cap = 0;
+    int rc = resident_capacity(dev, kfn, 1024, &cap);
+    if (rc) return rc;
+    if (n_chunks > cap) return 1;
+    StreamScratch* sc = nullptr;
+    rc = get_scratch(dev, stream, total * 2 * TILE * 2, &sc);
+    if (rc) return rc;
+    rp.ctr = sc->ctr;
+    rp.slots = sc->slots;
+    hipLaunchKernelGGL((biwkv_row_kernel<DT, TILE, L, FUSED, PAIR>),
+                       dim3(static_cast<unsigned>(total)), dim3(1024), 0,
+                       static_cast<hipStream_t>(stream), rp);
+  } else {
+    hipLaunchKernelGGL((biwkv_row_kernel<DT, TILE, L, FUSED, PAIR>),
+                       dim3(static_cast<unsigned>(total)), dim3(1024), 0,
+                       static_cast<hipStream_t>(stream), rp);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e);
   return BIWKV_OK;
 }
 
-// Whole-row kernel when the sequence fits one workgroup (64 tokens per lane for bf16 k/v, 32 for
-// fp32), else the chunked kernel with the cross-workgroup exchange. Returns 1 if not handled.
+// Tile shapes: one 128-byte line of channels per tile (64 bf16, 32 fp32), 64 registers of k and v
+// per lane, and chunks no longer than the sequence needs.
 template <int DT, bool FUSED, bool PAIR>
-int try_row_shape(const BiwkvParams& bp, int64_t B, void* stream) {
+int try_row_shape(const BiwkvParams& bp, int64_t B, int dev, void* stream) {
   const long long T = bp.T;
-  // byte offsets into one batch item of out (and so of k, v), including the up to 63 empty
-  // slots past the row end, must stay below 2^31
-  if ((T + 64) * static_cast<long long>(bp.C) * 4 >= (1ll << 31)) return 1;
-  if (T <= 256) return launch_row<DT, 64, 16, FUSED, PAIR>(bp, B, stream);
-  if (T <= 512) return launch_row<DT, 64, 32, FUSED, PAIR>(bp, B, stream);
   if constexpr (DT == BIWKV_BF16) {
-    if (T <= 1024) return launch_row<DT, 64, 64, FUSED, PAIR>(bp, B, stream);
-    if (T <= 2048) return launch_row<DT, 16, 32, FUSED, PAIR>(bp, B, stream);
-    if (T <= 4096) return launch_row<DT, 16, 64, FUSED, PAIR>(bp, B, stream);
+    if (T <= 256) return launch_row<DT, 64, 16, FUSED, PAIR>(bp, B, dev, stream);
+    if (T <= 512) return launch_row<DT, 64, 32, FUSED, PAIR>(bp, B, dev, stream);
+    return launch_row<DT, 64, 64, FUSED, PAIR>(bp, B, dev, stream);
   } else {
-    if (T <= 1024) return launch_row<DT, 16, 16, FUSED, PAIR>(bp, B, stream);
-    if (T <= 2048) return launch_row<DT, 16, 32, FUSED, PAIR>(bp, B, stream);
+    if (T <= 256) return launch_row<DT, 32, 8, FUSED, PAIR>(bp, B, dev, stream);
+    if (T <= 512) return launch_row<DT, 32, 16, FUSED, PAIR>(bp, B, dev, stream);
+    return launch_row<DT, 32, 32, FUSED, PAIR>(bp, B, dev, stream);
   }
-  return 1;
 }
 
 // bf16 rows read channel pairs as 32-bit words when every pair is whole: C even, 4-byte aligned
@@ -291,17 +309,17 @@ bool pairs_ok(const BiwkvParams& bp, bool fused) {
 }
 
 template <int DT, bool FUSED>
-int try_row(const BiwkvParams& bp, int64_t B, void* stream) {
+int try_row(const BiwkvParams& bp, int64_t B, int dev, void* stream) {
   if constexpr (DT == BIWKV_BF16) {
-    if (pairs_ok(bp, FUSED)) return try_row_shape<DT, FUSED, true>(bp, B, stream);
+    if (pairs_ok(bp, FUSED)) return try_row_shape<DT, FUSED, true>(bp, B, dev, stream);
   }
-  return try_row_shape<DT, FUSED, false>(bp, B, stream);
+  return try_row_shape<DT, FUSED, false>(bp, B, dev, stream);
 }
 
 template <bool FUSED>
 int dispatch_biwkv(BiwkvParams prm, int64_t B, int dtype, bool vec2, int dev, void* stream) {
-  const int rrc = dtype == BIWKV_F32 ? try_row<BIWKV_F32, FUSED>(prm, B, stream)
-                                     : try_row<BIWKV_BF16, FUSED>(prm, B, stream);
+  const int rrc = dtype == BIWKV_F32 ? try_row<BIWKV_F32, FUSED>(prm, B, dev, stream)
+                                     : try_row<BIWKV_BF16, FUSED>(prm, B, dev, stream);
   if (rrc != 1) return rrc;
   if (dtype == BIWKV_F32)
     return vec2 ? launch_biwkv<BIWKV_F32, 2, FUSED>(prm, B, dev, stream)

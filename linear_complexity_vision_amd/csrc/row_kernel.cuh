@@ -1,4 +1,5 @@
-// Bi-WKV whole-row kernel (a row held by one workgroup).
+// Bi-WKV tile kernel: a (batch, channel tile) row held by one workgroup, or by a few workgroups
+// (chunks of the row) that exchange their sums.
 #pragma once
 
 #include <type_traits>
@@ -8,13 +9,18 @@
 namespace {
 
 // ---------------------------------------------------------------------------------------------
-// Bi-WKV whole-row kernel: one workgroup owns every token of a (batch, channel tile) row
+// Bi-WKV tile kernel: a workgroup owns one chunk (GROUPS * L tokens) of a (batch, channel tile)
+// row; a tile is one 128-byte line of k (64 bf16 or 32 fp32 channels), so every load and store of
+// a wavefront moves whole lines.
 // ---------------------------------------------------------------------------------------------
 //
-// Used when a row fits in one workgroup's registers (T * TILE elements, 64 tokens per lane at
-// most). Lane (c, g) holds channel c of the tile and token group g (L consecutive tokens); the
-// GROUPS = 1024 / TILE groups of a channel are combined by a Hillis-Steele scan in LDS, so no
-// data leaves the workgroup between load and store. Each lane then sweeps its tokens in
+// Lane (c, g) holds channel c of the tile and token group g (L consecutive tokens) in registers
+// from load to store. The GROUPS = 1024 / TILE groups of a channel are combined by a
+// Hillis-Steele scan in LDS. When a row has several chunks, each workgroup publishes its chunk's
+// forward and backward sums (epoch-tagged slots, see slot_store) and folds the sums of the other
+// chunks of its row, in a fixed order, into its carries; workgroups take tickets in launch order
+// and chunks of a row hold consecutive tickets, so a workgroup only waits for workgroups that
+// have started or will start once earlier rows finish. Each lane then sweeps its tokens in
 // sub-blocks of 8: forward states (a, c) left to right, keeping (alpha, beta) = (a - c v, c +
 // e^{u+k}) per token in LDS, then backward states (b, d) right to left, writing Eq. (7).
 //
@@ -107,39 +113,38 @@ struct RowParams {
   float* out;
   long long T;
   int C;
-  int n_rows;   // B * tiles
-  int n_tiles;  // channel tiles per batch item
-  int share;    // rows sharing one 128-byte line of k (mapped to one XCD), 1 = identity
+  int n_tiles;   // channel tiles per batch item
+  int n_chunks;  // workgroups per row
+  unsigned total;                // workgroups of the launch
+  Counters* ctr;                 // ticket / epoch block (n_chunks > 1)
+  unsigned long long* slots;     // [row][chunk][dir][TILE] (l, mu) slot pairs (n_chunks > 1)
   int H, W, shift, g1, g2, g3, g4;  // Q-Shift (fused entry only)
 };
 
-// Per-lane constants: lane (c, g) holds channel ch = tile * TILE + c at the tokens
-// [s_g, s_g + n_g) of batch item b (n_g < L only in the last groups of a row).
+// Per-lane constants: lane (c, g) of the workgroup for chunk `chunk` of row `row` holds channel
+// ch = tile * TILE + c at the tokens [s_g, s_g + n_g) of batch item b (n_g < L only at the end
+// of a row).
 struct RowLane {
   long long b, s_g;
-  int c, g, ch, n_g;
+  int row, chunk, c, g, ch, n_g;
   bool on;
   float D, lam, U, grow, eU;
 };
 
 template <int TILE, int L>
-__device__ __forceinline__ RowLane row_lane(const RowParams& p) {
+__device__ __forceinline__ RowLane row_lane(const RowParams& p, unsigned unit) {
+  constexpr int CT = (1024 / TILE) * L;  // tokens per chunk
   RowLane ln;
   const int tid = threadIdx.x;
   ln.c = tid % TILE;
   ln.g = tid / TILE;
-  // Rows whose tiles share a cache line of k run on one XCD (workgroup i runs on XCD i % 8), so
-  // the line is fetched into that XCD's L2 once.
-  int row = blockIdx.x;
-  if (p.share > 1) {
-    const int sh = p.share;
-    row = ((row / (8 * sh)) * 8 + row % 8) * sh + (row / 8) % sh;
-  }
-  const int tile = row % p.n_tiles;
-  ln.b = row / p.n_tiles;
+  ln.row = static_cast<int>(unit / static_cast<unsigned>(p.n_chunks));
+  ln.chunk = static_cast<int>(unit % static_cast<unsigned>(p.n_chunks));
+  const int tile = ln.row % p.n_tiles;
+  ln.b = ln.row / p.n_tiles;
   ln.ch = tile * TILE + ln.c;
   ln.on = ln.ch < p.C;
-  ln.s_g = static_cast<long long>(ln.g) * L;
+  ln.s_g = static_cast<long long>(ln.chunk) * CT + static_cast<long long>(ln.g) * L;
   const long long rem = p.T - ln.s_g;
   ln.n_g = rem <= 0 ? 0 : (rem < L ? static_cast<int>(rem) : L);
   const float wc = ln.on ? p.w[ln.ch] : 0.f;
@@ -233,9 +238,11 @@ __device__ __forceinline__ void row_load(const RowParams& p, const RowLane& ln, 
 // the per-token running-maximum arithmetic; the fast form scales every term of a lane against
 // one exponent.
 template <int DT, int TILE, int L, bool FUSED, bool PAIR, bool WIDE>
-__device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln, float* lds) {
+__device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln, float* lds,
+                                         unsigned epoch) {
   constexpr int NT = 1024;
   constexpr int GROUPS = NT / TILE;
+  constexpr int CT = GROUPS * L;  // tokens per chunk
   constexpr int SB = 8;  // tokens per sub-block of the sweeps
   constexpr int NSB = L / SB;
   static_assert(L % SB == 0, "bad row-kernel shape");
@@ -367,6 +374,67 @@ __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln, 
     const int o = tid + TILE;
     Y = Agg{scan[cur][3][o], scan[cur][4][o], scan[cur][5][o]};
   }
+  if (p.n_chunks > 1) {
+    // ---- exchange with the other chunks of the row ----
+    const int nch = p.n_chunks, chunk = ln.chunk, c = ln.c;
+    unsigned long long* rs = p.slots + static_cast<size_t>(ln.row) * nch * 2 * TILE * 2;
+    auto slot = [&](int ck, int dir) { return rs + (static_cast<size_t>(ck * 2 + dir) * TILE + c) * 2; };
+    // the chunk's own sums: forward (inclusive at the last group, anchored at the chunk's last
+    // slot) and backward (inclusive at group 0, anchored at the chunk's first token)
+    if (g == GROUPS - 1)
+      slot_store(slot(chunk, kFwd), Agg{scan[cur][0][tid], scan[cur][1][tid], scan[cur][2][tid]}, epoch);
+    if (g == 0)
+      slot_store(slot(chunk, kBwd), Agg{scan[cur][3][tid], scan[cur][4][tid], scan[cur][5][tid]}, epoch);
+    // Entries: forward sums of chunks 0 .. chunk-1, then backward sums of chunks chunk+1 ..
+    // nch-1. Thread (c, g) folds entries g, g + GROUPS, ... in order; the partials are then
+    // folded in g order, so the result does not depend on arrival order.
+    const int nf = chunk, ne = nch - 1;
+    Agg pf = agg_empty(), pb = agg_empty();
+    bool timed_out = false;
+    for (int e = g; e < ne; e += GROUPS) {
+      const bool fwd = e < nf;
+      const int ck = fwd ? e : e + 1;
+      // distance from the entry's anchor to this chunk's carry anchor (chunks before this one
+      // are full, so slot positions are token positions)
+      const float dist = static_cast<float>(fwd ? (chunk - 1 - ck) : (ck - chunk - 1)) * CT;
+      const unsigned long long* sp = slot(ck, fwd ? kFwd : kBwd);
+      unsigned long long wv[2];
+      slot_load(sp, wv);
+      unsigned spins = 0;
+      while (!slot_ready(wv, epoch)) {
+        if (++spins > kSpinLimit) {
+          timed_out = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+        slot_load(sp, wv);
+      }
+      const Agg a = agg_shift(slot_value(wv), dist, D);
+      if (fwd)
+        pf = agg_add(pf, a);
+      else
+        pb = agg_add(pb, a);
+    }
+    if (timed_out)
+      __hip_atomic_fetch_or(&p.ctr->fault, kFaultSpin, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    float (*part)[6][TILE] = reinterpret_cast<float (*)[6][TILE]>(&scan[cur ^ 1][0][0]);
+    part[g][0][c] = pf.m;
+    part[g][1][c] = pf.F;
+    part[g][2][c] = pf.G;
+    part[g][3][c] = pb.m;
+    part[g][4][c] = pb.F;
+    part[g][5][c] = pb.G;
+    __syncthreads();
+    Agg xc = agg_empty(), yc = agg_empty();
+    const int np = ne < GROUPS ? ne : GROUPS;
+    for (int k = 0; k < np; ++k) {
+      xc = agg_add(xc, Agg{part[k][0][c], part[k][1][c], part[k][2][c]});
+      yc = agg_add(yc, Agg{part[k][3][c], part[k][4][c], part[k][5][c]});
+    }
+    // xc is anchored just before the chunk, yc just after it
+    X = agg_add(agg_shift(xc, static_cast<float>(g * L), D), X);
+    Y = agg_add(Y, agg_shift(yc, static_cast<float>((GROUPS - 1 - g) * L), D));
+  }
   __syncthreads();  // the scan buffer becomes the (alpha, beta) buffer
   kv.fence();
 
@@ -465,10 +533,11 @@ __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln, 
 // reads the parameters from the kernel's argument segment (a pointer, so the kernel keeps them in
 // scalar registers instead of building a private copy).
 template <int DT, int TILE, int L, bool FUSED, bool PAIR>
-__device__ __noinline__ void row_body_wide(const RowParams* args, float* lds) {
+__device__ __noinline__ void row_body_wide(const RowParams* args, float* lds, unsigned unit,
+                                           unsigned epoch) {
   const RowParams p = *args;
-  const RowLane ln = row_lane<TILE, L>(p);
-  row_body<DT, TILE, L, FUSED, PAIR, true>(p, ln, lds);
+  const RowLane ln = row_lane<TILE, L>(p, unit);
+  row_body<DT, TILE, L, FUSED, PAIR, true>(p, ln, lds, epoch);
 }
 
 template <int DT, int TILE, int L, bool FUSED, bool PAIR>
@@ -480,16 +549,50 @@ __global__ void __launch_bounds__(1024)
   constexpr int kScanFloats = 2 * 6 * NT;  // double-buffered (m, F, G) forward + backward
   constexpr int kSweepFloats = 8 * NT * 2;
   __shared__ float lds[kScanFloats > kSweepFloats ? kScanFloats : kSweepFloats];
-  const RowLane ln = row_lane<TILE, L>(p);
-  // The whole workgroup takes the wide form when any of its channels needs it.
-  const bool wide_lane = fabsf(ln.D) * static_cast<float>(L - 1) > kFastRange ||
-                         ln.U > kBonusRange || ln.U < -kBonusRange;
-  if (__syncthreads_or(wide_lane)) {
-    // the kernel's only argument is p, at the start of the argument segment
-    const auto* args = (const RowParams*)(__builtin_amdgcn_kernarg_segment_ptr());
-    row_body_wide<DT, TILE, L, FUSED, PAIR>(args, lds);
-  } else {
-    row_body<DT, TILE, L, FUSED, PAIR, false>(p, ln, lds);
+  __shared__ unsigned sh_ticket, sh_epoch;
+  const int tid = threadIdx.x;
+  const bool chunked = p.n_chunks > 1;
+  unsigned unit = blockIdx.x, epoch = 0u;
+  bool valid = true;
+  if (chunked) {
+    if (tid == 0) {
+      sh_ticket = __hip_atomic_fetch_add(&p.ctr->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      sh_epoch = __hip_atomic_load(&p.ctr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    // A ticket beyond the grid can only come from a counter left non-zero by an earlier launch;
+    // such a workgroup touches no data and only retires.
+    valid = sh_ticket < p.total;
+    if (!valid && tid == 0)
+      __hip_atomic_fetch_or(&p.ctr->fault, kFaultTicket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unit = sh_ticket;
+    epoch = sh_epoch;
+  }
+  if (valid) {  // uniform over the workgroup
+    const RowLane ln = row_lane<TILE, L>(p, unit);
+    // The whole workgroup takes the wide form when any of its channels needs it.
+    const bool wide_lane = fabsf(ln.D) * static_cast<float>(L - 1) > kFastRange ||
+                           ln.U > kBonusRange || ln.U < -kBonusRange;
+    if (__syncthreads_or(wide_lane)) {
+      // the kernel's only argument is p, at the start of the argument segment
+      const auto* args = (const RowParams*)(__builtin_amdgcn_kernarg_segment_ptr());
+      row_body_wide<DT, TILE, L, FUSED, PAIR>(args, lds, unit, epoch);
+    } else {
+      row_body<DT, TILE, L, FUSED, PAIR, false>(p, ln, lds, epoch);
+    }
+  }
+  if (chunked) {
+    // ---- retire: the last workgroup of the launch resets the counters for the next launch ----
+    __syncthreads();
+    if (tid == 0) {
+      const unsigned fin =
+          __hip_atomic_fetch_add(&p.ctr->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (fin + 1u == p.total) {
+        __hip_atomic_store(&p.ctr->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&p.ctr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(&p.ctr->epoch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
   }
 }
 
