@@ -266,6 +266,7 @@ int launch_row(const BiwkvParams& bp, int64_t B, int dev, void* stream) {
     int rc = resident_capacity(dev, kfn, 1024, &cap);
     if (rc) return rc;
     if (n_chunks > cap) return 1;
+    rp.ordered = total > cap ? 1 : 0;
     StreamScratch* sc = nullptr;
     rc = get_scratch(dev, stream, total * 2 * TILE * 2, &sc);
     if (rc) return rc;
