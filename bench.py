@@ -11,6 +11,10 @@ step streams from HBM. Prints ONE JSON line.
 Also:
     python bench.py --calibrate-copy      plain device copy of a known size (for counter scaling)
     python bench.py --summarize DIR       summarise rocprofv3 output (kernel stats / counters)
+    python bench.py --record-counters KF KW CF CW
+        turn four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE of the bench, the same two of
+        --calibrate-copy) into profiles/hbm_counters_*.json: HBM bytes per launch, scaled so that
+        the copy's counters read its known size, stamped with the hash of the kernel sources
 """
 from __future__ import annotations
 
@@ -29,12 +33,21 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E peak
 MALL_BYTES = 256 * 1024 * 1024
-KERNEL_SRC = os.path.join(ROOT, "linear_complexity_vision_amd", "csrc", "biwkv.hip")
+KERNEL_DIR = os.path.join(ROOT, "linear_complexity_vision_amd", "csrc")
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters_biwkv_qshift_B4_T4096_C1024_bf16.json")
+CALIBRATION_BYTES = 512 * 1024 * 1024
+MIN_CPU_SECONDS = 3.0
+COPY_KERNEL = "copy"  # substring of the device copy kernel's name in the counter output
+KERNEL_NAMES = {"fused": "biwkv_row_kernel", "biwkv": "biwkv_row_kernel", "qshift": "qshift_kernel"}
 
 
 def kernel_source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    """Hash of every kernel source file (the counters are only valid for the code they measured)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(KERNEL_DIR)):
+        h.update(name.encode())
+        h.update(open(os.path.join(KERNEL_DIR, name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def alg_bytes(entry: str, B: int, H: int, W: int, C: int, kv_bytes: int, shift: int = 1, gamma: float = 0.25) -> int:
@@ -100,18 +113,24 @@ def cpu_baseline(wl, entry: str) -> dict:
         return {"value": elems / dt / 1e9, "unit": "Gtoken*ch/s", "cores": 1, "kind": "oracle",
                 "seconds": dt, "cpu": _cpu_model(),
                 "sample": f"whole workload ({wl.B}x{wl.T}x{wl.C}); single-threaded oracle Q-Shift gather"}
+    # the whole workload, repeated until at least MIN_CPU_SECONDS have passed
+    reps = 0
     t0 = time.perf_counter()
-    if entry == "fused":
-        ks = oracle.qshift_f64(k, wl.H, wl.W, wl.shift, wl.gamma)
-        vs = oracle.qshift_f64(v, wl.H, wl.W, wl.shift, wl.gamma)
-        oracle.biwkv_rnn(ks, vs, w, u, threads=threads)
-    else:
-        oracle.biwkv_rnn(k, v, w, u, threads=threads)
-    dt = time.perf_counter() - t0
+    while True:
+        if entry == "fused":
+            ks = oracle.qshift_f64(k, wl.H, wl.W, wl.shift, wl.gamma)
+            vs = oracle.qshift_f64(v, wl.H, wl.W, wl.shift, wl.gamma)
+            oracle.biwkv_rnn(ks, vs, w, u, threads=threads)
+        else:
+            oracle.biwkv_rnn(k, v, w, u, threads=threads)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= MIN_CPU_SECONDS:
+            break
     elems = wl.B * wl.T * wl.C
-    return {"value": elems / dt / 1e9, "unit": "Gtoken*ch/s", "cores": threads, "kind": "oracle",
-            "seconds": dt, "cpu": _cpu_model(),
-            "sample": f"whole workload ({wl.B}x{wl.T}x{wl.C}); float64 four-state RNN oracle"
+    return {"value": reps * elems / dt / 1e9, "unit": "Gtoken*ch/s", "cores": threads,
+            "kind": "oracle", "seconds": dt, "repetitions": reps, "cpu": _cpu_model(),
+            "sample": f"whole workload ({wl.B}x{wl.T}x{wl.C}) x{reps}; float64 four-state RNN oracle"
                       + (" after the oracle Q-Shift of k and v" if entry == "fused" else "")}
 
 
@@ -145,35 +164,54 @@ def run_bench(args) -> dict:
     if entry == "qshift":
         xs = [torch.from_numpy(wl.k).to(dev).contiguous() for _ in range(R)]
 
-    def step(i):
-        r = i % R
+    # One checked call per buffer set through the package, then the same C entry point called
+    # with the already marshalled arguments (the timed loop measures the library, not Python).
+    stream = torch.cuda.current_stream(dev)
+    cl = lib.load_library()
+    calls = []
+    for r in range(R):
         if entry == "fused":
             lib.biwkv_qshift_forward(ks_[r], vs_[r], w, u, H, W, wl.shift, wl.gamma, out=outs[r])
+            calls.append((cl.biwkv_qshift_forward,
+                          (ks_[r].data_ptr(), vs_[r].data_ptr(), w.data_ptr(), u.data_ptr(),
+                           outs[r].data_ptr(), B, H, W, C, wl.shift, wl.gamma, lib.BF16,
+                           stream.cuda_stream)))
         elif entry == "biwkv":
             lib.biwkv_forward(ks_[r], vs_[r], w, u, out=outs[r])
+            calls.append((cl.biwkv_forward,
+                          (ks_[r].data_ptr(), vs_[r].data_ptr(), w.data_ptr(), u.data_ptr(),
+                           outs[r].data_ptr(), B, T, C, lib.BF16, stream.cuda_stream)))
         else:
             lib.qshift(xs[r], H, W, wl.shift, wl.gamma, out=outs[r])
+            calls.append((cl.qshift, (xs[r].data_ptr(), outs[r].data_ptr(), B, H, W, C, wl.shift,
+                                      wl.gamma, stream.cuda_stream)))
 
-    stream = torch.cuda.current_stream(dev)
+    def step(i):
+        fn, a = calls[i % R]
+        rc = fn(*a)
+        if rc != 0:
+            raise lib.BiwkvError(rc, lib.status_string(rc))
+
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     assert lib.stream_fault_flags(dev) == 0
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # HIP events on the launch stream bracket the timed region; the launches queue back to back
+    # (host submission is faster than the kernel), so the event span / K is the average launch
+    # duration including the short gaps between kernels.
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    start.record(stream)
     for i in range(args.steps):
-        starts[i].record(stream)
         step(args.warmup + i)
-        ends[i].record(stream)
+    end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    durs_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
     assert lib.stream_fault_flags(dev) == 0
 
-    avg_ms = sum(durs_ms) / len(durs_ms)
+    avg_ms = start.elapsed_time(end) / args.steps
     ms_per_step = wall * 1e3 / args.steps
     elems = B * T * C
     kv_bytes = 4 if entry == "qshift" else 2
@@ -202,25 +240,74 @@ def run_bench(args) -> dict:
                    "gamma": wl.gamma, "buffer_sets_rotated": R},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "alg_bytes_per_launch": ab, "avg_launch_ms": avg_ms,
-                     "p10_launch_ms": durs_ms[len(durs_ms) // 10],
-                     "p90_launch_ms": durs_ms[(9 * len(durs_ms)) // 10]},
+                     "alg_bytes_per_launch": ab, "avg_launch_ms": avg_ms},
         "_wl": wl,
     }
 
 
 def calibrate_copy(args) -> None:
-    """A plain device copy of a known size, for scaling FETCH_SIZE / WRITE_SIZE counters."""
+    """A plain device copy of a known size, for scaling FETCH_SIZE / WRITE_SIZE counters.
+
+    The source is the oldest quarter of a buffer four times larger than the copy, written before
+    the rest of it, so none of it is still held in the memory-side cache when the copy reads it."""
     import torch
 
-    n_bytes = 512 * 1024 * 1024
-    a = torch.empty(n_bytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
-    b = torch.empty_like(a)
+    n = CALIBRATION_BYTES // 4
+    big = torch.empty(4 * n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty(n, dtype=torch.float32, device="cuda:0")
     for _ in range(args.steps):
-        b.copy_(a)
+        for q in range(4):
+            big[q * n:(q + 1) * n].fill_(1.0)
+        dst.copy_(big[:n])  # one read and one write of CALIBRATION_BYTES
     torch.cuda.synchronize()
-    print(json.dumps({"calibration": "device copy", "bytes_read": n_bytes, "bytes_written": n_bytes,
-                      "launches": args.steps}))
+    print(json.dumps({"calibration": "device copy", "bytes_read": CALIBRATION_BYTES,
+                      "bytes_written": CALIBRATION_BYTES, "launches": args.steps}))
+
+
+def _counter_means(path: str, counter: str, kernel: str) -> float:
+    """Mean per-dispatch value of `counter` over the largest-grid dispatches of kernels whose name
+    contains `kernel` (smaller dispatches of the same kernel, e.g. set-up copies, are skipped)."""
+    vals = {}
+    for f in glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True):
+        for row in csv.DictReader(open(f)):
+            if row.get("Counter_Name") != counter or kernel not in row.get("Kernel_Name", ""):
+                continue
+            # one row per dispatch and counter (values of one dispatch's instances are summed)
+            key = (f, row.get("Dispatch_Id", row.get("Correlation_Id")))
+            grid = int(row.get("Grid_Size", "0"))
+            v = vals.setdefault(key, [grid, 0.0])
+            v[1] += float(row["Counter_Value"])
+    if not vals:
+        raise SystemExit(f"no {counter} values for {kernel} under {path}")
+    top = max(g for g, _ in vals.values())
+    sel = [x for g, x in vals.values() if g == top]
+    return sum(sel) / len(sel)
+
+
+def record_counters(kf: str, kw: str, cf: str, cw: str, entry: str) -> None:
+    """HBM traffic per launch of the bench kernel from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
+    each scaled by what it reads for a device copy of CALIBRATION_BYTES."""
+    fetch = _counter_means(kf, "FETCH_SIZE", KERNEL_NAMES[entry])
+    write = _counter_means(kw, "WRITE_SIZE", KERNEL_NAMES[entry])
+    cal_fetch = _counter_means(cf, "FETCH_SIZE", COPY_KERNEL)
+    cal_write = _counter_means(cw, "WRITE_SIZE", COPY_KERNEL)
+    f_scale = CALIBRATION_BYTES / cal_fetch
+    w_scale = CALIBRATION_BYTES / cal_write
+    rec = {}
+    try:
+        rec = json.load(open(COUNTERS_FILE))
+    except (OSError, ValueError):
+        pass
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        rec = {"entries": {}}
+    rec["kernel_source_sha256_16"] = kernel_source_hash()
+    rec["calibration"] = {"bytes": CALIBRATION_BYTES, "fetch_kib": cal_fetch, "write_kib": cal_write,
+                          "fetch_bytes_per_unit": f_scale, "write_bytes_per_unit": w_scale}
+    rec["entries"][entry] = {"fetch_kib_per_launch": fetch, "write_kib_per_launch": write,
+                             "hbm_bytes_per_launch": fetch * f_scale + write * w_scale}
+    os.makedirs(os.path.dirname(COUNTERS_FILE), exist_ok=True)
+    json.dump(rec, open(COUNTERS_FILE, "w"), indent=1, sort_keys=True)
+    print(json.dumps(rec["entries"][entry]))
 
 
 def summarize(path: str) -> None:
@@ -253,10 +340,14 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize", metavar="DIR")
+    ap.add_argument("--record-counters", nargs=4, metavar=("KF", "KW", "CF", "CW"))
     args = ap.parse_args()
 
     if args.summarize:
         summarize(args.summarize)
+        return 0
+    if args.record_counters:
+        record_counters(*args.record_counters, entry=args.entry)
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

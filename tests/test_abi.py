@@ -1,0 +1,114 @@
+"""The C ABI of libbiwkv on the host: it loads, exports what include/biwkv.h declares, and rejects
+bad arguments before any device work. No kernel runs here (no GPU is needed); pointers below are
+never dereferenced because validation only looks at their values."""
+import ctypes
+import math
+
+import pytest
+
+import linear_complexity_vision_amd as lib
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not __import__("os").path.exists(lib.LIB_PATH):
+        pytest.skip("libbiwkv.so is not built (run __graft_entry__.build())")
+    return lib.load_library()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = lib.header_symbols()
+    assert {"biwkv_forward", "qshift", "biwkv_qshift_forward", "biwkv_status_string",
+            "biwkv_last_hip_error", "biwkv_stream_fault_flags", "biwkv_version"} <= set(names)
+    for name in names:
+        assert hasattr(L, name), f"{name} is declared in include/biwkv.h but not exported"
+
+
+def test_status_codes_have_messages(L):
+    codes = lib.status_codes()
+    assert codes["BIWKV_OK"] == 0
+    for name, code in codes.items():
+        if name.startswith("BIWKV_ERR_"):
+            assert code < 0
+            assert lib.status_string(code) != "unknown status", name
+    assert lib.status_string(12345) == "unknown status"
+    assert L.biwkv_version() >= 100
+
+
+# fake device addresses: distinct, 16-byte aligned, never dereferenced on the host
+K, V, WP, UP, OUT = 0x10000000, 0x20000000, 0x30000000, 0x30001000, 0x40000000
+
+
+def _fwd(L, k=K, v=V, w=WP, u=UP, out=OUT, B=2, T=8, C=4, dtype=lib.F32):
+    return L.biwkv_forward(k, v, w, u, out, B, T, C, dtype, None)
+
+
+def _fused(L, k=K, v=V, w=WP, u=UP, out=OUT, B=1, H=2, W=4, C=4, shift=1, gamma=0.25, dtype=lib.BF16):
+    return L.biwkv_qshift_forward(k, v, w, u, out, B, H, W, C, shift, gamma, dtype, None)
+
+
+def _qs(L, x=K, out=OUT, B=1, H=2, W=4, C=4, shift=1, gamma=0.25):
+    return L.qshift(x, out, B, H, W, C, shift, gamma, None)
+
+
+def _code(name):
+    return lib.status_codes()[name]
+
+
+def test_biwkv_forward_validation(L):
+    assert _fwd(L, dtype=7) == _code("BIWKV_ERR_DTYPE")
+    assert _fwd(L, k=None) == _code("BIWKV_ERR_NULL")
+    assert _fwd(L, out=None) == _code("BIWKV_ERR_NULL")
+    assert _fwd(L, w=None) == _code("BIWKV_ERR_NULL")
+    assert _fwd(L, B=-1) == _code("BIWKV_ERR_SHAPE")
+    assert _fwd(L, T=-3) == _code("BIWKV_ERR_SHAPE")
+    assert _fwd(L, B=1 << 40, T=1 << 40, C=1 << 40) == _code("BIWKV_ERR_SHAPE")  # overflow
+    assert _fwd(L, k=K + 1, dtype=lib.BF16) == _code("BIWKV_ERR_ALIGN")
+    assert _fwd(L, k=K + 2, dtype=lib.F32) == _code("BIWKV_ERR_ALIGN")
+    assert _fwd(L, out=K) == _code("BIWKV_ERR_ALIAS")
+    assert _fwd(L, out=V + 8) == _code("BIWKV_ERR_ALIAS")
+    assert _fwd(L, out=WP - 8) == _code("BIWKV_ERR_ALIAS")
+
+
+def test_empty_calls_succeed_without_a_device(L):
+    assert _fwd(L, B=0) == 0
+    assert _fwd(L, T=0, k=None, v=None, out=None) == 0
+    assert _fused(L, H=0, shift=0) == 0  # (a shift larger than an empty grid is rejected)
+    assert _qs(L, C=0, x=None, out=None) == 0
+
+
+def test_qshift_parameter_validation(L):
+    bad = _code("BIWKV_ERR_PARAM")
+    for shift, gamma in [(1, 0.3), (1, -0.1), (1, math.nan), (-1, 0.25), (3, 0.25), (5, 0.0)]:
+        assert _qs(L, shift=shift, gamma=gamma) == bad, (shift, gamma)
+        assert _fused(L, shift=shift, gamma=gamma) == bad, (shift, gamma)
+    assert _qs(L, H=-1) == _code("BIWKV_ERR_SHAPE")
+    assert _qs(L, out=K + 4) == _code("BIWKV_ERR_ALIAS")
+    assert _qs(L, x=K + 2) == _code("BIWKV_ERR_ALIGN")
+    assert _qs(L, x=None) == _code("BIWKV_ERR_NULL")
+    assert _fused(L, dtype=3) == _code("BIWKV_ERR_DTYPE")
+
+
+def test_valid_calls_report_missing_device(L):
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a device is present; covered by the GPU tests")
+    no_dev = _code("BIWKV_ERR_NO_DEVICE")
+    assert _fwd(L) == no_dev
+    assert _fused(L) == no_dev
+    assert _qs(L) == no_dev
+    flags = ctypes.c_uint32(7)
+    assert L.biwkv_stream_fault_flags(None, ctypes.byref(flags)) == no_dev
+    assert L.biwkv_stream_fault_flags(None, None) == _code("BIWKV_ERR_NULL")
+
+
+def test_torch_front_end_refuses_host_tensors():
+    import torch
+
+    k = torch.zeros(1, 4, 2)
+    w = torch.zeros(2)
+    with pytest.raises(ValueError):
+        lib.biwkv_forward(k, k, w, w)
+    with pytest.raises(ValueError):
+        lib.qshift(k, 2, 2)
