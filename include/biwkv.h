@@ -23,10 +23,11 @@
  *   - `stream` is a hipStream_t passed as void*; NULL is the null stream. Calls are asynchronous:
  *     they validate on the host, enqueue, and return. No call synchronises.
  *   - The caller owns every buffer. The library keeps no pointer to caller memory after the
- *     enqueued work completes. Bi-WKV calls use library-owned scratch (chunk aggregates and a
- *     small counter block) kept per (device, stream); it is allocated on first use of a stream and
- *     grown when a larger problem arrives, so the first call on a stream, and a call that needs
- *     more scratch than before, must not be made under HIP graph capture.
+ *     enqueued work completes. Bi-WKV calls whose sequence is split over several workgroups
+ *     (T above 1024) use library-owned scratch (chunk sums and a small counter block) kept per
+ *     (device, stream); it is allocated on the first such call on a stream and grown when a larger
+ *     problem arrives, so those calls must not be made under HIP graph capture. Replaying a
+ *     captured call is safe: launches are told apart by a device-side epoch, not by arguments.
  *   - All argument validation happens on the host before any HIP call. A problem with zero
  *     elements returns BIWKV_OK without enqueuing anything. Nothing is printed; no C++ exception
  *     crosses this interface.
@@ -64,7 +65,9 @@ extern "C" {
  *   w, u : [C] float32, device memory (decay, divided by T inside; bonus).
  *   out  : [B, T, C] float32, device memory; must not overlap k, v, w or u.
  * Errors: BIWKV_ERR_NULL, _SHAPE (B, T, C < 0 or B*T*C*4 bytes overflow), _DTYPE, _ALIAS, _ALIGN,
- * _NO_DEVICE, _UNSUPPORTED (T beyond the co-resident chunk capacity, about 32k tokens), _HIP.
+ * _NO_DEVICE, _HIP, and _UNSUPPORTED when a row needs more chunks than fit on the device at once:
+ * chunks are 1024 tokens while (T + 1024) * C * 4 bytes stay below 2^31 (so T up to 1024 times
+ * the number of resident workgroups, 262144 on MI355X), else 128 tokens (T up to about 32768).
  */
 int biwkv_forward(const void* k, const void* v, const float* w, const float* u, float* out,
                   int64_t B, int64_t T, int64_t C, int dtype, void* stream);
@@ -101,7 +104,8 @@ int biwkv_last_hip_error(void);
  * Diagnostic: synchronises `stream`, then reports and clears the device-side fault word of that
  * stream's scratch. *flags receives 0 when every Bi-WKV launch on the stream since the last query
  * completed its cross-chunk exchange normally; bit 0 set means a chunk stopped waiting for a
- * neighbour's aggregate after its bounded wait ran out (its output is then invalid). Returns
+ * neighbour's aggregate after its bounded wait ran out, bit 1 that a launch found its ticket
+ * counter left non-zero by an earlier, interrupted launch (outputs are then invalid). Returns
  * BIWKV_OK, BIWKV_ERR_NULL (flags NULL), _NO_DEVICE or _HIP. A stream with no scratch yet
  * reports 0.
  */
