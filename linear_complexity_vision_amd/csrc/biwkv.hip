@@ -488,9 +488,13 @@ int biwkv_stream_fault_flags(void* stream, uint32_t* flags) {
   if (e != hipSuccess) return hip_fail(e);
   *flags = c.fault;
   if (c.fault) {
-    const unsigned zero = 0;
-    e = hipMemcpy(reinterpret_cast<char*>(it->second->ctr) + offsetof(Counters, fault), &zero,
-                  sizeof(zero), hipMemcpyHostToDevice);
+    // Clear the fault word, and the ticket and arrival counts that an interrupted launch may
+    // have left behind (the stream is idle here); the epoch keeps counting.
+    Counters fresh = c;
+    fresh.ticket = 0;
+    fresh.done = 0;
+    fresh.fault = 0;
+    e = hipMemcpy(it->second->ctr, &fresh, sizeof(Counters), hipMemcpyHostToDevice);
     if (e != hipSuccess) return hip_fail(e);
   }
   return BIWKV_OK;
