@@ -211,6 +211,39 @@ def test_determinism_and_reuse_across_shapes():
     assert L.stream_fault_flags() == 0
 
 
+def test_graph_replay_matches_eager():
+    """A captured call replays correctly, with eager calls on the same scratch between replays: the
+    chunk exchange tells launches apart by a device-side epoch, not by kernel arguments."""
+    import torch
+    L = _lib()
+    wl = workloads.make_random(21, 2, 3000, 128, dtype="bf16")  # three chunks per row
+    k, v, w, u = to_device_kv(wl)
+    s = torch.cuda.Stream()
+    print("[case] graph replay", flush=True)
+    with torch.cuda.stream(s):
+        ref = L.biwkv_forward(k, v, w, u)  # allocates this stream's scratch outside the capture
+        out = torch.empty_like(ref)
+        L.biwkv_forward(k, v, w, u, out=out)
+    torch.cuda.synchronize()
+    ref_np = ref.cpu().numpy()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        L.biwkv_forward(k, v, w, u, out=out)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(out.cpu().numpy(), ref_np)
+        with torch.cuda.stream(s):
+            eager = L.biwkv_forward(k, v, w, u)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(eager.cpu().numpy(), ref_np)
+    with torch.cuda.stream(s):
+        assert L.stream_fault_flags() == 0
+
+
 def test_side_streams_are_independent():
     import torch
     L = _lib()
