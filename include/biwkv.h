@@ -24,10 +24,11 @@
  *     they validate on the host, enqueue, and return. No call synchronises.
  *   - The caller owns every buffer. The library keeps no pointer to caller memory after the
  *     enqueued work completes. Bi-WKV calls whose sequence is split over several workgroups
- *     (T above 1024) use library-owned scratch (chunk sums and a small counter block) kept per
- *     (device, stream); it is allocated on the first such call on a stream and grown when a larger
- *     problem arrives, so those calls must not be made under HIP graph capture. Replaying a
- *     captured call is safe: launches are told apart by a device-side epoch, not by arguments.
+ *     (T above 1024 for bf16, above 512 for fp32) use library-owned scratch (chunk sums and a
+ *     small counter block) kept per (device, stream); it is allocated on the first such call on
+ *     a stream and grown when a larger problem arrives, so those calls must not be made under
+ *     HIP graph capture. Replaying a captured call is safe: launches are told apart by a
+ *     device-side epoch, not by arguments.
  *   - All argument validation happens on the host before any HIP call. A problem with zero
  *     elements returns BIWKV_OK without enqueuing anything. Nothing is printed; no C++ exception
  *     crosses this interface.
@@ -66,8 +67,10 @@ extern "C" {
  *   out  : [B, T, C] float32, device memory; must not overlap k, v, w or u.
  * Errors: BIWKV_ERR_NULL, _SHAPE (B, T, C < 0 or B*T*C*4 bytes overflow), _DTYPE, _ALIAS, _ALIGN,
  * _NO_DEVICE, _HIP, and _UNSUPPORTED when a row needs more chunks than fit on the device at once:
- * chunks are 1024 tokens while (T + 1024) * C * 4 bytes stay below 2^31 (so T up to 1024 times
- * the number of resident workgroups, 262144 on MI355X), else 128 tokens (T up to about 32768).
+ * while (T + 1024) * C * 4 bytes stay below 2^31, a row that needs several chunks has chunks of
+ * 512 tokens (two workgroups per CU for bf16, one for fp32), so T may reach 512 times the number
+ * of resident workgroups: 262144 (bf16) or 131072 (fp32) on MI355X's 256 CUs; beyond that,
+ * 128-token chunks (T up to about 32768).
  */
 int biwkv_forward(const void* k, const void* v, const float* w, const float* u, float* out,
                   int64_t B, int64_t T, int64_t C, int dtype, void* stream);

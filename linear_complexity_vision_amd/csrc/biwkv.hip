@@ -227,11 +227,11 @@ int launch_biwkv(BiwkvParams prm, int64_t B, int dev, void* stream) {
   return BIWKV_OK;
 }
 
-// Tile kernel launch: rows of TILE channels, chunks of (1024 / TILE) * L tokens. Returns 1 when
+// Tile kernel launch: rows of TILE channels, chunks of (NT / TILE) * L tokens. Returns 1 when
 // the shape is outside what the kernel addresses (the caller then uses the chunk-scan kernel).
-template <int DT, int TILE, int L, bool FUSED, bool PAIR>
+template <int DT, int TILE, int L, int NT, bool FUSED, bool PAIR>
 int launch_row(const BiwkvParams& bp, int64_t B, int dev, void* stream) {
-  constexpr int CT = (1024 / TILE) * L;
+  constexpr int CT = (NT / TILE) * L;
   const long long T = bp.T;
   // byte offsets into one batch item of out (and so of k, v), including the empty slots past
   // the row end, must stay below 2^31
@@ -260,10 +260,10 @@ int launch_row(const BiwkvParams& bp, int64_t B, int dev, void* stream) {
   rp.total = static_cast<unsigned>(total);
   if (n_chunks > 1) {
     // The chunks of a row wait for each other: they must all fit on the device at once.
-    const void* kfn = reinterpret_cast<const void*>(&biwkv_row_kernel<DT, TILE, L, FUSED, PAIR>);
+    const void* kfn = reinterpret_cast<const void*>(&biwkv_row_kernel<DT, TILE, L, NT, FUSED, PAIR>);
     std::lock_guard<std::mutex> lock(g_mu);
     int cap = 0;
-    int rc = resident_capacity(dev, kfn, 1024, &cap);
+    int rc = resident_capacity(dev, kfn, NT, &cap);
     if (rc) return rc;
     if (n_chunks > cap) return 1;
     rp.ordered = total > cap ? 1 : 0;
@@ -272,12 +272,12 @@ int launch_row(const BiwkvParams& bp, int64_t B, int dev, void* stream) {
     if (rc) return rc;
     rp.ctr = sc->ctr;
     rp.slots = sc->slots;
-    hipLaunchKernelGGL((biwkv_row_kernel<DT, TILE, L, FUSED, PAIR>),
-                       dim3(static_cast<unsigned>(total)), dim3(1024), 0,
+    hipLaunchKernelGGL((biwkv_row_kernel<DT, TILE, L, NT, FUSED, PAIR>),
+                       dim3(static_cast<unsigned>(total)), dim3(NT), 0,
                        static_cast<hipStream_t>(stream), rp);
   } else {
-    hipLaunchKernelGGL((biwkv_row_kernel<DT, TILE, L, FUSED, PAIR>),
-                       dim3(static_cast<unsigned>(total)), dim3(1024), 0,
+    hipLaunchKernelGGL((biwkv_row_kernel<DT, TILE, L, NT, FUSED, PAIR>),
+                       dim3(static_cast<unsigned>(total)), dim3(NT), 0,
                        static_cast<hipStream_t>(stream), rp);
   }
   hipError_t e = hipGetLastError();
@@ -285,19 +285,23 @@ int launch_row(const BiwkvParams& bp, int64_t B, int dev, void* stream) {
   return BIWKV_OK;
 }
 
-// Tile shapes: one 128-byte line of channels per tile (64 bf16, 32 fp32), 64 registers of k and v
-// per lane, and chunks no longer than the sequence needs.
+// Tile shapes: 64 channels per tile (one 128-byte line of bf16 k, two of fp32), 64 registers of
+// k and v per lane, and chunks no longer than the sequence needs. Rows longer than one chunk of
+// 1024 tokens use 512-thread workgroups (two per CU): the workgroup a CU received first gets its
+// data first and computes and writes while the other one still reads, so reads and writes
+// overlap. fp32 rows keep 1024 threads: at 32 tokens per lane their 512-thread chunks are short
+// and the exchange between them dominates.
 template <int DT, bool FUSED, bool PAIR>
 int try_row_shape(const BiwkvParams& bp, int64_t B, int dev, void* stream) {
   const long long T = bp.T;
   if constexpr (DT == BIWKV_BF16) {
-    if (T <= 256) return launch_row<DT, 64, 16, FUSED, PAIR>(bp, B, dev, stream);
-    if (T <= 512) return launch_row<DT, 64, 32, FUSED, PAIR>(bp, B, dev, stream);
-    return launch_row<DT, 64, 64, FUSED, PAIR>(bp, B, dev, stream);
+    if (T <= 256) return launch_row<DT, 64, 16, 1024, FUSED, PAIR>(bp, B, dev, stream);
+    if (T <= 512) return launch_row<DT, 64, 32, 1024, FUSED, PAIR>(bp, B, dev, stream);
+    if (T <= 1024) return launch_row<DT, 64, 64, 1024, FUSED, PAIR>(bp, B, dev, stream);
+    return launch_row<DT, 64, 64, 512, FUSED, PAIR>(bp, B, dev, stream);
   } else {
-    if (T <= 256) return launch_row<DT, 32, 8, FUSED, PAIR>(bp, B, dev, stream);
-    if (T <= 512) return launch_row<DT, 32, 16, FUSED, PAIR>(bp, B, dev, stream);
-    return launch_row<DT, 32, 32, FUSED, PAIR>(bp, B, dev, stream);
+    if (T <= 256) return launch_row<DT, 64, 16, 1024, FUSED, PAIR>(bp, B, dev, stream);
+    return launch_row<DT, 64, 32, 1024, FUSED, PAIR>(bp, B, dev, stream);
   }
 }
 

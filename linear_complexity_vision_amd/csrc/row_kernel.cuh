@@ -9,21 +9,22 @@
 namespace {
 
 // ---------------------------------------------------------------------------------------------
-// Bi-WKV tile kernel: a workgroup owns one chunk (GROUPS * L tokens) of a (batch, channel tile)
-// row; a tile is one 128-byte line of k (64 bf16 or 32 fp32 channels), so every load and store of
-// a wavefront moves whole lines.
+// Bi-WKV tile kernel: a workgroup of NT threads owns one chunk (GROUPS * L tokens) of a (batch,
+// channel tile) row; a tile is 64 channels (one 128-byte line of bf16 k, two of fp32), so every
+// load and store of a wavefront moves whole lines.
 // ---------------------------------------------------------------------------------------------
 //
 // Lane (c, g) holds channel c of the tile and token group g (L consecutive tokens) in registers
-// from load to store. The GROUPS = 1024 / TILE groups of a channel are combined by a
-// Hillis-Steele scan in LDS. When a row has several chunks, each workgroup publishes its chunk's
-// forward and backward sums (epoch-tagged slots, see slot_store) and folds the sums of the other
-// chunks of its row, in a fixed order, into its carries. When the whole grid fits on the device
-// the chunks follow the grid order; otherwise workgroups take tickets in launch order and the
-// chunks of a row hold consecutive tickets, so a workgroup only waits for workgroups that have
-// started or will start once earlier rows finish. Each lane then sweeps its tokens in
-// sub-blocks of 8: forward states (a, c) left to right, keeping (alpha, beta) = (a - c v, c +
-// e^{u+k}) per token in LDS, then backward states (b, d) right to left, writing Eq. (7).
+// from load to store. The GROUPS = NT / TILE group sums of a channel are combined by scans on
+// lane shuffles: the sums go through LDS into a transposed layout in which one channel's groups
+// are consecutive lanes of one wavefront. When a row has several chunks, each workgroup
+// publishes its chunk's forward and backward sums (epoch-tagged slots, see slot_store) and folds
+// the sums of the other chunks of its row, in a fixed order, into its carries. When the whole
+// grid fits on the device the chunks follow the grid order; otherwise workgroups take tickets in
+// launch order and the chunks of a row hold consecutive tickets, so a workgroup only waits for
+// workgroups that have started or will start once earlier rows finish. Each lane then sweeps its
+// tokens in sub-blocks of 8: forward states (a, c) left to right, keeping (alpha, beta) = (a - c
+// v, c + e^{u+k}) per token in LDS, then backward states (b, d) right to left, writing Eq. (7).
 //
 // Every lane holds exactly L token slots. Slots past the end of the row hold k = -inf, i.e. a
 // weight of exactly 0, so the sweeps need no per-token bounds: a lane's forward sum is anchored
@@ -151,6 +152,18 @@ struct RowParams {
   int H, W, shift, g1, g2, g3, g4;  // Q-Shift (fused entry only)
 };
 
+// Counts a workgroup out of a chunked launch once none of its wavefronts reads the epoch or a slot
+// again; the last one resets the counters for the next launch on the stream. Nothing else waits
+// for it, so only the calling wavefront sees the round trip.
+__device__ __forceinline__ void row_retire(const RowParams& p) {
+  const unsigned fin = __hip_atomic_fetch_add(&p.ctr->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (fin + 1u == p.total) {
+    __hip_atomic_store(&p.ctr->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&p.ctr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(&p.ctr->epoch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // Whether any thread of the workgroup has pred set (a barrier). The result is read from the first
 // lane so that the compiler sees a uniform value and branches on it without linearising both
 // sides.
@@ -168,9 +181,9 @@ struct RowLane {
   float D, lam, U, grow, eU;
 };
 
-template <int TILE, int L>
+template <int TILE, int L, int NT>
 __device__ __forceinline__ RowLane row_lane(const RowParams& p, unsigned unit) {
-  constexpr int CT = (1024 / TILE) * L;  // tokens per chunk
+  constexpr int CT = (NT / TILE) * L;  // tokens per chunk
   RowLane ln;
   const int tid = threadIdx.x;
   ln.c = tid % TILE;
@@ -199,7 +212,7 @@ __device__ __forceinline__ RowLane row_lane(const RowParams& p, unsigned unit) {
 // Issues every load of the lane's k and v (Q-Shift applied when FUSED: padded sources read 0) and
 // marks the slots past the row empty. Nothing waits here: phase A consumes the words in load
 // order as they arrive.
-template <int DT, int TILE, int L, bool FUSED, bool PAIR, class Store>
+template <int DT, int TILE, int L, int NT, bool FUSED, bool PAIR, class Store>
 __device__ __forceinline__ void row_load(const RowParams& p, const RowLane& ln, Store& kv) {
   const long long T = p.T;
   const int C = p.C;
@@ -221,7 +234,7 @@ __device__ __forceinline__ void row_load(const RowParams& p, const RowLane& ln, 
     // The token offset of word m is uniform, so it moves the resource base (scalar work) and the
     // lane keeps one vector offset. Tokens past the row fall past the shortened resource and
     // read 0, and so does every slot of a masked lane.
-    constexpr int CT = (1024 / TILE) * L;
+    constexpr int CT = (NT / TILE) * L;
     // byte counts below 2^31 (the host checks (T + CT) * C * 4), so 32-bit scalar arithmetic
     const int c0 = ln.chunk * CT * static_cast<int>(row_bytes);  // chunk start
     const int avail = static_cast<int>(plane * ES) - c0;       // bytes from there to the end
@@ -281,20 +294,92 @@ __device__ __forceinline__ void row_load(const RowParams& p, const RowLane& ln, 
 // the other chunks, sweeps (phase C). WIDE selects the per-token running-maximum arithmetic; the fast form scales
 // the terms of a sub-block against one exponent, which keeps every significant term a normal
 // fp32 number while the decay or growth across a lane stays within kFastRange.
+// LDS of the tile kernel: the sweeps' (alpha, beta) buffer (8 tokens x NT lanes of float2),
+// which first holds the lane sums, then the carries and the per-channel D outside it.
+template <int NT>
+constexpr int kRowSweepFloats = 8 * NT * 2;
+template <int TILE, int NT>
+constexpr int kRowLdsFloats = kRowSweepFloats<NT> + 6 * (NT / TILE) * (TILE + 1) + TILE;
+
+// The scans and the exchange use a finite exponent for an empty aggregate (F = G = 0), far below
+// any real one: 2^(empty - m) is then exactly 0 against a real exponent and 1 against another
+// empty one, so adding aggregates needs no branch.
+constexpr float kEmptyM = -1e30f;
+__device__ __forceinline__ Agg row_empty() { return Agg{kEmptyM, 0.f, 0.f}; }
+__device__ __forceinline__ Agg agg_add_f(Agg a, Agg b) {
+  const float m = fmaxf(a.m, b.m);
+  const float sa = fast_exp2(a.m - m), sb = fast_exp2(b.m - m);
+  return Agg{m, fmaf(a.F, sa, b.F * sb), fmaf(a.G, sa, b.G * sb)};
+}
+
+// Aggregates moved between the W consecutive lanes that hold one channel's groups (W is a power
+// of two up to 64). from_below<W, d> gives a lane the value of the lane d below it and
+// from_above<W, d> that of the lane d above; the callers only use results from inside the
+// segment. Segments of up to 16 lanes lie inside one DPP row, so these are row shifts (plain
+// VALU moves); wider segments go through the LDS crossbar (ds_bpermute).
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+template <int W, int d>
+__device__ __forceinline__ Agg agg_from_below(Agg a) {
+  if constexpr (W <= 16)
+    return Agg{dpp_move<0x110 + d>(a.m), dpp_move<0x110 + d>(a.F), dpp_move<0x110 + d>(a.G)};  // row_shr
+  else
+    return Agg{__shfl_up(a.m, d, W), __shfl_up(a.F, d, W), __shfl_up(a.G, d, W)};
+}
+template <int W, int d>
+__device__ __forceinline__ Agg agg_from_above(Agg a) {
+  if constexpr (W <= 16)
+    return Agg{dpp_move<0x100 + d>(a.m), dpp_move<0x100 + d>(a.F), dpp_move<0x100 + d>(a.G)};  // row_shl
+  else
+    return Agg{__shfl_down(a.m, d, W), __shfl_down(a.F, d, W), __shfl_down(a.G, d, W)};
+}
+template <int W>
+__device__ __forceinline__ Agg agg_from_first(Agg a) {
+  return Agg{__shfl(a.m, 0, W), __shfl(a.F, 0, W), __shfl(a.G, 0, W)};
+}
+
+// Inclusive scans over the W groups of a channel (lane tg holds group tg; groups are L slots
+// apart): forward over groups 0..tg, anchored at tg's last slot, and backward over tg..W-1,
+// anchored at tg's first token. Hillis-Steele, fixed order.
+template <int W, int L, int d = 1>
+__device__ __forceinline__ void group_scan(Agg& f, Agg& bk, int tg, float D) {
+  if constexpr (d < W) {
+    const Agg pf = agg_from_below<W, d>(f);
+    const Agg pb = agg_from_above<W, d>(bk);
+    if (tg >= d) f = agg_add_f(agg_shift(pf, static_cast<float>(d * L), D), f);
+    if (tg + d < W) bk = agg_add_f(bk, agg_shift(pb, static_cast<float>(d * L), D));
+    group_scan<W, L, 2 * d>(f, bk, tg, D);
+  }
+}
+
+// Folds the W lanes' sums into the segment's first lane in a fixed tree.
+template <int W, int s = 1>
+__device__ __forceinline__ void group_fold(Agg& a, Agg& b, int tg) {
+  if constexpr (s < W) {
+    const Agg oa = agg_from_above<W, s>(a), ob = agg_from_above<W, s>(b);
+    if ((tg & (2 * s - 1)) == 0) {
+      a = agg_add_f(a, oa);
+      b = agg_add_f(b, ob);
+    }
+    group_fold<W, 2 * s>(a, b, tg);
+  }
+}
+
 template <int DT, int TILE, int L, bool PAIR>
 using RowStore = std::conditional_t<PAIR, RowKVPair<L>, RowKV<DT, L>>;
 
-template <int DT, int TILE, int L, bool FUSED, bool PAIR, bool WIDE>
+template <int DT, int TILE, int L, int NT, bool FUSED, bool PAIR, bool WIDE>
 __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
                                          RowStore<DT, TILE, L, PAIR>& kv, float* lds,
                                          const unsigned* sh_epoch) {
-  constexpr int NT = 1024;
   constexpr int GROUPS = NT / TILE;
   constexpr int CT = GROUPS * L;  // tokens per chunk
   constexpr int SB = 8;  // tokens per sub-block of the sweeps
   constexpr int NSB = L / SB;
   static_assert(L % SB == 0, "bad row-kernel shape");
-  float (*scan)[6][NT] = reinterpret_cast<float (*)[6][NT]>(lds);
+  static_assert((GROUPS & (GROUPS - 1)) == 0 && GROUPS <= 64, "a channel's groups share a wavefront");
   float2 (*lds_ab)[NT] = reinterpret_cast<float2 (*)[NT]>(lds);
   const int tid = threadIdx.x;
   const int g = ln.g;
@@ -365,7 +450,7 @@ __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
       cG = fmaf(cG, lsb, bG[q] * sq);
     }
     // the lane sums and the caps are against 2^{kmax + span}
-    const float m_agg = kmax == kNegInf ? kNegInf : kmax + span;
+    const float m_agg = kmax == kNegInf ? kEmptyM : kmax + span;
     af = Agg{m_agg, fF, fG};
     ab = Agg{m_agg, cF, cG};
   } else {
@@ -395,113 +480,113 @@ __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
   }
   kv.fence();
 
-  // ---- inclusive scans over the groups of each channel (Hillis-Steele, fixed order); group
-  //      sums are L slots apart in both directions ----
-  int cur = 0;
-  scan[0][0][tid] = af.m;
-  scan[0][1][tid] = af.F;
-  scan[0][2][tid] = af.G;
-  scan[0][3][tid] = ab.m;
-  scan[0][4][tid] = ab.F;
-  scan[0][5][tid] = ab.G;
+  // ---- scans over the groups of each channel. The lane sums go to LDS group-major; lane
+  //      (tg, tc) = (tid % GROUPS, tid / GROUPS) then takes group tg of channel tc, so the groups
+  //      of a channel are GROUPS consecutive lanes of one wavefront and the scans (and the
+  //      exchange) run on lane shuffles without barriers. Carries go back the same way. ----
+  constexpr int PAD = TILE + 1;         // row pitch of the group-major buffers (no bank conflicts)
+  constexpr int RS = GROUPS * PAD;      // floats per quantity
+  float* red = lds;                     // [6][RS] lane sums (inside the sweep buffer)
+  float* xy = lds + kRowSweepFloats<NT>;  // [6][RS] carries (outside it: read during the sweeps)
+  float* dch = xy + 6 * RS;             // [TILE] D of each channel
+  const int wi = g * PAD + ln.c;
+  if constexpr (WIDE) {  // the wide sums mark an empty aggregate with -inf
+    af.m = fmaxf(af.m, kEmptyM);
+    ab.m = fmaxf(ab.m, kEmptyM);
+  }
+  red[0 * RS + wi] = af.m;
+  red[1 * RS + wi] = af.F;
+  red[2 * RS + wi] = af.G;
+  red[3 * RS + wi] = ab.m;
+  red[4 * RS + wi] = ab.F;
+  red[5 * RS + wi] = ab.G;
+  if (g == 0) dch[ln.c] = D;
   __syncthreads();
-#pragma unroll
-  for (int d = 1; d < GROUPS; d *= 2) {
-    Agg f{scan[cur][0][tid], scan[cur][1][tid], scan[cur][2][tid]};
-    Agg bk{scan[cur][3][tid], scan[cur][4][tid], scan[cur][5][tid]};
-    if (g >= d) {
-      const int o = tid - d * TILE;
-      const Agg pf{scan[cur][0][o], scan[cur][1][o], scan[cur][2][o]};
-      f = agg_add(agg_shift(pf, static_cast<float>(d * L), D), f);
-    }
-    if (g + d < GROUPS) {
-      const int o = tid + d * TILE;
-      const Agg pb{scan[cur][3][o], scan[cur][4][o], scan[cur][5][o]};
-      bk = agg_add(bk, agg_shift(pb, static_cast<float>(d * L), D));
-    }
-    cur ^= 1;
-    scan[cur][0][tid] = f.m;
-    scan[cur][1][tid] = f.F;
-    scan[cur][2][tid] = f.G;
-    scan[cur][3][tid] = bk.m;
-    scan[cur][4][tid] = bk.F;
-    scan[cur][5][tid] = bk.G;
-    __syncthreads();
-  }
-  // exclusive carries: forward sum of the earlier groups (anchored just before this lane's first
+  const int tg = tid % GROUPS, tc = tid / GROUPS;
+  const int ti = tg * PAD + tc;
+  const float Dt = dch[tc];
+  Agg f{red[0 * RS + ti], red[1 * RS + ti], red[2 * RS + ti]};
+  Agg bk{red[3 * RS + ti], red[4 * RS + ti], red[5 * RS + ti]};
+  group_scan<GROUPS, L>(f, bk, tg, Dt);
+  // exclusive carries: forward sum of the earlier groups (anchored just before the group's first
   // token), backward sum of the later groups (anchored just after its last slot)
-  Agg X = agg_empty(), Y = agg_empty();
-  if (g > 0) {
-    const int o = tid - TILE;
-    X = Agg{scan[cur][0][o], scan[cur][1][o], scan[cur][2][o]};
-  }
-  if (g + 1 < GROUPS) {
-    const int o = tid + TILE;
-    Y = Agg{scan[cur][3][o], scan[cur][4][o], scan[cur][5][o]};
-  }
+  Agg X = agg_from_below<GROUPS, 1>(f), Y = agg_from_above<GROUPS, 1>(bk);
+  if (tg == 0) X = row_empty();
+  if (tg == GROUPS - 1) Y = row_empty();
   if (p.n_chunks > 1) {
     // ---- exchange with the other chunks of the row ----
-    const int nch = p.n_chunks, chunk = ln.chunk, c = ln.c;
-    const unsigned epoch = __builtin_amdgcn_readfirstlane(*sh_epoch);  // set before the scan
+    const int nch = p.n_chunks, chunk = ln.chunk;
+    const unsigned epoch = __builtin_amdgcn_readfirstlane(*sh_epoch);  // set before the barrier
     unsigned long long* rs = p.slots + static_cast<size_t>(ln.row) * nch * 2 * TILE * 2;
-    auto slot = [&](int ck, int dir) { return rs + (static_cast<size_t>(ck * 2 + dir) * TILE + c) * 2; };
+    auto slot = [&](int ck, int dir) { return rs + (static_cast<size_t>(ck * 2 + dir) * TILE + tc) * 2; };
     // the chunk's own sums: forward (inclusive at the last group, anchored at the chunk's last
     // slot) and backward (inclusive at group 0, anchored at the chunk's first token)
-    if (g == GROUPS - 1)
-      slot_store(slot(chunk, kFwd), Agg{scan[cur][0][tid], scan[cur][1][tid], scan[cur][2][tid]}, epoch);
-    if (g == 0)
-      slot_store(slot(chunk, kBwd), Agg{scan[cur][3][tid], scan[cur][4][tid], scan[cur][5][tid]}, epoch);
+    if (tg == GROUPS - 1) slot_store(slot(chunk, kFwd), f, epoch);
+    if (tg == 0) slot_store(slot(chunk, kBwd), bk, epoch);
     // Entries: forward sums of chunks 0 .. chunk-1, then backward sums of chunks chunk+1 ..
-    // nch-1. Thread (c, g) folds entries g, g + GROUPS, ... in order; the partials are then
-    // folded in g order, so the result does not depend on arrival order.
+    // nch-1. Lane tg folds entries tg, tg + GROUPS, ... in order; the lanes' partials are then
+    // folded in a fixed tree, so the result does not depend on arrival order.
     const int nf = chunk, ne = nch - 1;
-    Agg pf = agg_empty(), pb = agg_empty();
+    Agg pf = row_empty(), pb = row_empty();
     bool timed_out = false;
-    for (int e = g; e < ne; e += GROUPS) {
-      const bool fwd = e < nf;
-      const int ck = fwd ? e : e + 1;
-      // distance from the entry's anchor to this chunk's carry anchor (chunks before this one
-      // are full, so slot positions are token positions)
-      const float dist = static_cast<float>(fwd ? (chunk - 1 - ck) : (ck - chunk - 1)) * CT;
-      const unsigned long long* sp = slot(ck, fwd ? kFwd : kBwd);
-      unsigned long long wv[2];
-      slot_load(sp, wv);
-      unsigned spins = 0;
-      while (!slot_ready(wv, epoch)) {
-        if (++spins > kSpinLimit) {
-          timed_out = true;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
-        slot_load(sp, wv);
+    // A lane issues the loads of up to EB entries before it waits for any of them, so a lane
+    // with several entries pays one round trip, not one per entry.
+    constexpr int EB = GROUPS >= 8 ? 1 : 8 / GROUPS;
+    for (int e0 = tg; e0 < ne; e0 += EB * GROUPS) {
+      unsigned long long wv[EB][2];
+#pragma unroll
+      for (int j = 0; j < EB; ++j) {
+        const int e = e0 + j * GROUPS;
+        if (e < ne) slot_load(slot(e < nf ? e : e + 1, e < nf ? kFwd : kBwd), wv[j]);
       }
-      const Agg a = agg_shift(slot_value(wv), dist, D);
-      if (fwd)
-        pf = agg_add(pf, a);
-      else
-        pb = agg_add(pb, a);
+#pragma unroll
+      for (int j = 0; j < EB; ++j) {
+        const int e = e0 + j * GROUPS;
+        if (e >= ne) break;
+        const bool fwd = e < nf;
+        const int ck = fwd ? e : e + 1;
+        // distance from the entry's anchor to this chunk's carry anchor (chunks before this one
+        // are full, so slot positions are token positions)
+        const float dist = static_cast<float>(fwd ? (chunk - 1 - ck) : (ck - chunk - 1)) * CT;
+        const unsigned long long* sp = slot(ck, fwd ? kFwd : kBwd);
+        unsigned spins = 0;
+        while (!slot_ready(wv[j], epoch)) {
+          if (++spins > kSpinLimit) {
+            timed_out = true;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+          slot_load(sp, wv[j]);
+        }
+        Agg a = slot_value(wv[j]);
+        a.m = fmaxf(a.m, kEmptyM);
+        a = agg_shift(a, dist, Dt);
+        if (fwd)
+          pf = agg_add_f(pf, a);
+        else
+          pb = agg_add_f(pb, a);
+      }
     }
     if (timed_out)
       __hip_atomic_fetch_or(&p.ctr->fault, kFaultSpin, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    float (*part)[6][TILE] = reinterpret_cast<float (*)[6][TILE]>(&scan[cur ^ 1][0][0]);
-    part[g][0][c] = pf.m;
-    part[g][1][c] = pf.F;
-    part[g][2][c] = pf.G;
-    part[g][3][c] = pb.m;
-    part[g][4][c] = pb.F;
-    part[g][5][c] = pb.G;
-    __syncthreads();
-    Agg xc = agg_empty(), yc = agg_empty();
-    const int np = ne < GROUPS ? ne : GROUPS;
-    for (int k = 0; k < np; ++k) {
-      xc = agg_add(xc, Agg{part[k][0][c], part[k][1][c], part[k][2][c]});
-      yc = agg_add(yc, Agg{part[k][3][c], part[k][4][c], part[k][5][c]});
-    }
-    // xc is anchored just before the chunk, yc just after it
-    X = agg_add(agg_shift(xc, static_cast<float>(g * L), D), X);
-    Y = agg_add(Y, agg_shift(yc, static_cast<float>((GROUPS - 1 - g) * L), D));
+    group_fold<GROUPS>(pf, pb, tg);
+    // pf (from the first lane of the channel) is anchored just before the chunk, pb just after it
+    pf = agg_from_first<GROUPS>(pf);
+    pb = agg_from_first<GROUPS>(pb);
+    X = agg_add_f(agg_shift(pf, static_cast<float>(tg * L), Dt), X);
+    Y = agg_add_f(Y, agg_shift(pb, static_cast<float>((GROUPS - 1 - tg) * L), Dt));
   }
-  __syncthreads();  // the scan buffer becomes the (alpha, beta) buffer
+  xy[0 * RS + ti] = X.m;
+  xy[1 * RS + ti] = X.F;
+  xy[2 * RS + ti] = X.G;
+  xy[3 * RS + ti] = Y.m;
+  xy[4 * RS + ti] = Y.F;
+  xy[5 * RS + ti] = Y.G;
+  __syncthreads();  // past it, the sum buffer becomes the (alpha, beta) buffer
+  X = Agg{xy[0 * RS + wi], xy[1 * RS + wi], xy[2 * RS + wi]};
+  Y = Agg{xy[3 * RS + wi], xy[4 * RS + wi], xy[5 * RS + wi]};
+  // every wavefront is past its last read of the epoch and of the slots
+  if (p.n_chunks > 1 && tid == 0) row_retire(p);
   kv.fence();
 
   // ---- phase C: sweep each sub-block forward, then backward, writing Eq. (7) ----
@@ -598,26 +683,24 @@ __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
 // out of line gives it its own register allocation, so its spills never touch the fast form. It
 // reads the parameters from the kernel's argument segment (a pointer, so the kernel keeps them in
 // scalar registers instead of building a private copy).
-template <int DT, int TILE, int L, bool FUSED, bool PAIR>
+template <int DT, int TILE, int L, int NT, bool FUSED, bool PAIR>
 __device__ __noinline__ void row_body_wide(const RowParams* args, float* lds, unsigned unit,
                                            const unsigned* sh_epoch) {
   const RowParams p = *args;
-  const RowLane ln = row_lane<TILE, L>(p, unit);
+  const RowLane ln = row_lane<TILE, L, NT>(p, unit);
   RowStore<DT, TILE, L, PAIR> kv;
-  row_load<DT, TILE, L, FUSED, PAIR>(p, ln, kv);
-  row_body<DT, TILE, L, FUSED, PAIR, true>(p, ln, kv, lds, sh_epoch);
+  row_load<DT, TILE, L, NT, FUSED, PAIR>(p, ln, kv);
+  row_body<DT, TILE, L, NT, FUSED, PAIR, true>(p, ln, kv, lds, sh_epoch);
 }
 
-template <int DT, int TILE, int L, bool FUSED, bool PAIR>
-__global__ void __launch_bounds__(1024)
+template <int DT, int TILE, int L, int NT, bool FUSED, bool PAIR>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4)))
     biwkv_row_kernel(RowParams p) {
   static_assert(!PAIR || (DT == BIWKV_BF16 && TILE % 2 == 0), "pairs are bf16 channel pairs");
   static_assert(64 % TILE == 0 || TILE % 64 == 0, "bad row-kernel tile");
   static_assert(TILE <= 64, "a wavefront must hold every channel of the tile");
-  constexpr int NT = 1024;
-  constexpr int kScanFloats = 2 * 6 * NT;  // double-buffered (m, F, G) forward + backward
-  constexpr int kSweepFloats = 8 * NT * 2;
-  __shared__ float lds[kScanFloats > kSweepFloats ? kScanFloats : kSweepFloats];
+  static_assert(NT % 256 == 0 && NT <= 1024 && NT >= 2 * TILE, "bad row-kernel workgroup size");
+  __shared__ float lds[kRowLdsFloats<TILE, NT>];
   __shared__ unsigned sh_ticket, sh_epoch;
   const int tid = threadIdx.x;
   const bool chunked = p.n_chunks > 1;
@@ -643,7 +726,7 @@ __global__ void __launch_bounds__(1024)
     unit = __builtin_amdgcn_readfirstlane(sh_ticket);
   }
   if (valid) {  // uniform over the workgroup
-    const RowLane ln = row_lane<TILE, L>(p, unit);
+    const RowLane ln = row_lane<TILE, L, NT>(p, unit);
     // The whole workgroup takes the wide form when any of its channels needs it. Every
     // wavefront holds all TILE channels, so a wavefront vote is the workgroup's vote.
     const bool wide_lane = fabsf(ln.D) * static_cast<float>(L - 1) > kFastRange ||
@@ -651,26 +734,14 @@ __global__ void __launch_bounds__(1024)
     if (__ballot(wide_lane) != 0ull) {
       // the kernel's only argument is p, at the start of the argument segment
       const auto* args = (const RowParams*)(__builtin_amdgcn_kernarg_segment_ptr());
-      row_body_wide<DT, TILE, L, FUSED, PAIR>(args, lds, unit, &sh_epoch);
+      row_body_wide<DT, TILE, L, NT, FUSED, PAIR>(args, lds, unit, &sh_epoch);
     } else {
       RowStore<DT, TILE, L, PAIR> kv;
-      row_load<DT, TILE, L, FUSED, PAIR>(p, ln, kv);
-      row_body<DT, TILE, L, FUSED, PAIR, false>(p, ln, kv, lds, &sh_epoch);
+      row_load<DT, TILE, L, NT, FUSED, PAIR>(p, ln, kv);
+      row_body<DT, TILE, L, NT, FUSED, PAIR, false>(p, ln, kv, lds, &sh_epoch);
     }
   }
-  if (chunked) {
-    // ---- retire: the last workgroup of the launch resets the counters for the next launch ----
-    __syncthreads();
-    if (tid == 0) {
-      const unsigned fin =
-          __hip_atomic_fetch_add(&p.ctr->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (fin + 1u == p.total) {
-        __hip_atomic_store(&p.ctr->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&p.ctr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_fetch_add(&p.ctr->epoch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-  }
+  if (!valid && tid == 0) row_retire(p);  // (a valid workgroup retires after its exchange)
 }
 
 }  // namespace
