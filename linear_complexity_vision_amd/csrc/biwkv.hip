@@ -235,7 +235,9 @@ int launch_row(const BiwkvParams& bp, int64_t B, int dev, void* stream) {
   const long long T = bp.T;
   // byte offsets into one batch item of out (and so of k, v), including the empty slots past
   // the row end, must stay below 2^31
-  if ((T + CT) * static_cast<long long>(bp.C) * 4 >= (1ll << 31)) return 1;
+  // (the fused loads also start each word's resource s W tokens early and reach s W tokens late)
+  const long long reach = FUSED ? 2ll * bp.shift * bp.W : 0;
+  if ((T + CT + reach) * static_cast<long long>(bp.C) * 4 >= (1ll << 31)) return 1;
   const int64_t n_tiles = (bp.C + TILE - 1) / TILE;
   const int64_t n_chunks = (T + CT - 1) / CT;
   const int64_t total = B * n_tiles * n_chunks;

@@ -209,6 +209,24 @@ __device__ __forceinline__ RowLane row_lane(const RowParams& p, unsigned unit) {
   return ln;
 }
 
+// Loads word m of the lane's k and v (one token, or a channel pair at one token) at byte offset off
+// of the resources km and vm.
+template <int DT, bool PAIR, class Store>
+__device__ __forceinline__ void row_load_word(Store& kv, int m, __amdgpu_buffer_rsrc_t km,
+                                              __amdgpu_buffer_rsrc_t vm, uint32_t off) {
+  if constexpr (PAIR) {
+    kv.kk[m] = __builtin_amdgcn_raw_buffer_load_b32(km, off, 0, kStream);
+    kv.vv[m] = __builtin_amdgcn_raw_buffer_load_b32(vm, off, 0, kStream);
+  } else if constexpr (DT == BIWKV_F32) {
+    kv.kk[m] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(km, off, 0, kStream));
+    kv.vv[m] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vm, off, 0, kStream));
+  } else {
+    const uint32_t kx = __builtin_amdgcn_raw_buffer_load_b16(km, off, 0, kStream);
+    const uint32_t vx = __builtin_amdgcn_raw_buffer_load_b16(vm, off, 0, kStream);
+    kv.r[m] = kx | (vx << 16);
+  }
+}
+
 // Issues every load of the lane's k and v (Q-Shift applied when FUSED: padded sources read 0) and
 // marks the slots past the row empty. Nothing waits here: phase A consumes the words in load
 // order as they arrive.
@@ -222,19 +240,17 @@ __device__ __forceinline__ void row_load(const RowParams& p, const RowLane& ln, 
       uniform_u64(reinterpret_cast<unsigned long long>(p.k) + ln.b * plane * ES));
   const char* vb = reinterpret_cast<const char*>(
       uniform_u64(reinterpret_cast<unsigned long long>(p.v) + ln.b * plane * ES));
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc(kb, static_cast<uint32_t>(plane * ES));
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc(vb, static_cast<uint32_t>(plane * ES));
   const uint32_t row_bytes = static_cast<uint32_t>(C) * ES;
   // PAIR: lane 2j + odd reads channels (2j, 2j + 1) at tokens 2m + odd
   constexpr int STEP = PAIR ? 2 : 1;
   constexpr int NW = L / STEP;  // words per lane and array
   const int odd = PAIR ? (ln.c & 1) : 0;
   const uint32_t lane_byte = static_cast<uint32_t>(ln.ch - odd) * ES;
+  constexpr int CT = (NT / TILE) * L;
   if constexpr (!FUSED) {
     // The token offset of word m is uniform, so it moves the resource base (scalar work) and the
     // lane keeps one vector offset. Tokens past the row fall past the shortened resource and
     // read 0, and so does every slot of a masked lane.
-    constexpr int CT = (NT / TILE) * L;
     // byte counts below 2^31 (the host checks (T + CT) * C * 4), so 32-bit scalar arithmetic
     const int c0 = ln.chunk * CT * static_cast<int>(row_bytes);  // chunk start
     const int avail = static_cast<int>(plane * ES) - c0;       // bytes from there to the end
@@ -247,42 +263,67 @@ __device__ __forceinline__ void row_load(const RowParams& p, const RowLane& ln, 
       const uint32_t n = static_cast<uint32_t>(left > 0 ? left : 0);
       const __amdgpu_buffer_rsrc_t km = make_rsrc(kb + c0 + adv, n);
       const __amdgpu_buffer_rsrc_t vm = make_rsrc(vb + c0 + adv, n);
-      if constexpr (PAIR) {
-        kv.kk[m] = __builtin_amdgcn_raw_buffer_load_b32(km, lane_off, 0, kStream);
-        kv.vv[m] = __builtin_amdgcn_raw_buffer_load_b32(vm, lane_off, 0, kStream);
-      } else if constexpr (DT == BIWKV_F32) {
-        kv.kk[m] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(km, lane_off, 0, kStream));
-        kv.vv[m] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vm, lane_off, 0, kStream));
-      } else {
-        const uint32_t kx = __builtin_amdgcn_raw_buffer_load_b16(km, lane_off, 0, kStream);
-        const uint32_t vx = __builtin_amdgcn_raw_buffer_load_b16(vm, lane_off, 0, kStream);
-        kv.r[m] = kx | (vx << 16);
-      }
+      row_load_word<DT, PAIR>(kv, m, km, vm, lane_off);
     }
   } else {
-    QShiftLane qs;
-    qs.init(ln.ch, p.H, p.W, T, p.shift, p.g1, p.g2, p.g3, p.g4);
-    int col = static_cast<int>((ln.s_g + odd) % p.W);
+    // Q-Shift: the lane reads its own channel at token t + delta, where delta is fixed by the
+    // channel's quarter (right: -s, left: +s, down: -s W, up: +s W, rest: 0). Word m's resource
+    // starts SH = s W tokens before the word's token, so every lane offset is non-negative and
+    // constant; sources past the end of the batch item fall past the resource and read 0. The
+    // other zero-filled sources (a column outside the quarter's band, or a row above the grid for
+    // "down") are cleared words of a per-lane mask, set once.
+    const int Wd = p.W, sh = p.shift, SH = p.shift * p.W;
+    int delta = 0, lo = 0, hi = Wd;  // valid columns [lo, hi)
+    bool down = false;
+    if (ln.ch < p.g1) {
+      delta = -sh;
+      lo = sh;
+    } else if (ln.ch < p.g2) {
+      delta = sh;
+      hi = Wd - sh;
+    } else if (ln.ch < p.g3) {
+      delta = -SH;
+      down = true;
+    } else if (ln.ch < p.g4) {
+      delta = SH;
+    }
+    const int t0 = ln.chunk * CT + ln.g * L + odd;  // token of word 0 (T < 2^31 / (4 C))
+    // bit m: word m (token t0 + STEP m) reads a source inside the grid
+    using Mask = std::conditional_t<(NW > 32), unsigned long long, uint32_t>;
+    constexpr int MB = 8 * sizeof(Mask);
+    auto below = [](int n) { return n >= MB ? ~Mask(0) : (Mask(1) << n) - Mask(1); };  // bits [0, n)
+    Mask valid = ln.on ? below(NW) : Mask(0);
+    // clears the words whose token lies in [a, b)
+    auto clear = [&](int a, int b) {
+      int ma = (a - t0 + STEP - 1) >> (STEP - 1), mb = (b - t0 + STEP - 1) >> (STEP - 1);
+      ma = ma < 0 ? 0 : (ma > NW ? NW : ma);
+      mb = mb < 0 ? 0 : (mb > NW ? NW : mb);
+      valid &= ~(below(mb) & ~below(ma));
+    };
+    if (lo > 0 || hi < Wd) {
+      const int t_last = t0 + STEP * (NW - 1);
+      for (int r = t0 / Wd; r * Wd <= t_last; ++r) {
+        clear(r * Wd, r * Wd + lo);
+        clear(r * Wd + hi, r * Wd + Wd);
+      }
+    }
+    if (down) clear(t0, SH);
+    const uint32_t lane_off = static_cast<uint32_t>(ln.g * L + odd + delta + SH) * row_bytes + lane_byte;
+    // byte counts below 2^31 (the host checks (T + CT + 2 s W) * C * 4), so 32-bit arithmetic
+    const int c0 = (ln.chunk * CT - SH) * static_cast<int>(row_bytes);  // may be negative
+    const int avail = static_cast<int>(plane * ES) - c0;
 #pragma unroll
     for (int m = 0; m < NW; ++m) {
-      const long long t = ln.s_g + m * STEP + odd;
-      const bool ok = ln.on && t < T && qs.valid(t, col);
-      const uint32_t off =
-          ok ? static_cast<uint32_t>(t + qs.off) * row_bytes + lane_byte : kOutOfRange;
-      col += STEP;
-      if (col >= p.W) col -= p.W;
-      if (STEP > 1 && col >= p.W) col -= p.W;
-      if constexpr (PAIR) {
-        kv.kk[m] = __builtin_amdgcn_raw_buffer_load_b32(kr, off, 0, kStream);
-        kv.vv[m] = __builtin_amdgcn_raw_buffer_load_b32(vr, off, 0, kStream);
-      } else if constexpr (DT == BIWKV_F32) {
-        kv.kk[m] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(kr, off, 0, kStream));
-        kv.vv[m] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vr, off, 0, kStream));
-      } else {
-        const uint32_t kx = __builtin_amdgcn_raw_buffer_load_b16(kr, off, 0, kStream);
-        const uint32_t vx = __builtin_amdgcn_raw_buffer_load_b16(vr, off, 0, kStream);
-        kv.r[m] = kx | (vx << 16);
-      }
+      const int adv = m * STEP * static_cast<int>(row_bytes);
+      const int left = avail - adv;
+      const uint32_t n = static_cast<uint32_t>(left > 0 ? left : 0);
+      const __amdgpu_buffer_rsrc_t km = make_rsrc(kb + c0 + adv, n);
+      const __amdgpu_buffer_rsrc_t vm = make_rsrc(vb + c0 + adv, n);
+      // all ones when word m is valid (bit m of the mask, sign-extended)
+      const uint32_t keep =
+          static_cast<uint32_t>(static_cast<std::make_signed_t<Mask>>(valid << (MB - 1 - m)) >> (MB - 1));
+      const uint32_t off = (lane_off & keep) | (kOutOfRange & ~keep);
+      row_load_word<DT, PAIR>(kv, m, km, vm, off);
     }
   }
   // all loads in flight before anything consumes them
