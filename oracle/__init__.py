@@ -14,6 +14,9 @@ Functions follow the pages (cited by title and equation):
 * ``qshift``         — the q_shift function of "LinXin's Blog" Vision-RWKV notes (token shift on
   the H x W grid, groups at int(C*gamma*j), zero fill, remainder copied).
 * ``biwkv_qshift``   — the fused composition Bi-WKV(X†(k), X†(v)).
+* ``biwkv_causal_sum`` / ``biwkv_causal_rnn`` — the causal attention Bi-WKV is derived from (the
+  original RWKV attention, which the same section says stops at the current token): Eq. (5)
+  with the decayed sum over i < t only, and Eq. (6)-(7) with b = d = 0.
 
 All arrays are numpy, [B, T, C] C-contiguous. Floating inputs are widened to float64 (exact for
 fp32 and bf16 values).
@@ -55,7 +58,10 @@ def _load():
         lib.oracle_biwkv_rnn.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, ctypes.c_int]
         lib.oracle_biwkv_rnn_literal.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _P]
         lib.oracle_qshift.argtypes = [_P, _P, _I64, _I64, _I64, _I64, _I64, ctypes.c_double]
-        for f in (lib.oracle_biwkv_sum, lib.oracle_biwkv_rnn, lib.oracle_biwkv_rnn_literal, lib.oracle_qshift):
+        lib.oracle_biwkv_causal_sum.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, ctypes.c_int]
+        lib.oracle_biwkv_causal_rnn.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int]
+        for f in (lib.oracle_biwkv_sum, lib.oracle_biwkv_rnn, lib.oracle_biwkv_rnn_literal, lib.oracle_qshift,
+                  lib.oracle_biwkv_causal_sum, lib.oracle_biwkv_causal_rnn):
             f.restype = ctypes.c_int
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -120,6 +126,28 @@ def biwkv_rnn_literal(k, v, w, u):
     rc = _load().oracle_biwkv_rnn_literal(_ptr(k), _ptr(v), _ptr(w), _ptr(u), B, T, C, _ptr(out))
     if rc != 0:
         raise RuntimeError(f"oracle_biwkv_rnn_literal failed ({rc})")
+    return out
+
+
+def biwkv_causal_sum(k, v, w, u, with_scale=False, threads=0):
+    """Causal attention (sum stops before the current token; same exponent convention as Eq. (5))."""
+    k, v, w, u, B, T, C = _check_bitc(k, v, w, u)
+    out = np.empty((B, T, C), dtype=np.float64)
+    scale = np.empty_like(out) if with_scale else None
+    rc = _load().oracle_biwkv_causal_sum(_ptr(k), _ptr(v), _ptr(w), _ptr(u), B, T, C, _ptr(out),
+                                         _ptr(scale) if scale is not None else None, int(threads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_biwkv_causal_sum failed ({rc})")
+    return (out, scale) if with_scale else out
+
+
+def biwkv_causal_rnn(k, v, w, u, threads=0):
+    """Causal attention in RNN form: prefix states a, c of Eq. (6) and Eq. (7) with b = d = 0."""
+    k, v, w, u, B, T, C = _check_bitc(k, v, w, u)
+    out = np.empty((B, T, C), dtype=np.float64)
+    rc = _load().oracle_biwkv_causal_rnn(_ptr(k), _ptr(v), _ptr(w), _ptr(u), B, T, C, _ptr(out), int(threads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_biwkv_causal_rnn failed ({rc})")
     return out
 
 

@@ -256,6 +256,112 @@ int oracle_biwkv_rnn_literal(const double* k, const double* v, const double* w, 
 }
 
 /*
+ * O1c — the causal attention the pages compare against (the original RWKV attention, whose sum
+ * stops at the token before the current one; [VRWKV] "Linear Complexity Bidirectional
+ * Attention" describes Bi-WKV as raising that upper limit to T-1). Reading: Eq. (5) with the
+ * decayed sum restricted to i < t, same exponent convention, self term exp(u + k_t):
+ *   wkv_t = ( sum_{i < t} exp(-((t-1-i)/T) w + k_i) v_i + exp(u + k_t) v_t )
+ *         / ( sum_{i < t} exp(-((t-1-i)/T) w + k_i)     + exp(u + k_t)     )
+ * The original no-/T convention is the same formula with w replaced by T w. Term by term, with the
+ * largest logit subtracted first (an exact identity); scale as in O1.
+ */
+int oracle_biwkv_causal_sum(const double* k, const double* v, const double* w, const double* u,
+                            int64_t B, int64_t T, int64_t C, double* out, double* scale,
+                            int nthreads) {
+    if (!k || !v || !w || !u || !out || B < 0 || T < 0 || C < 0) return ORC_ERR_ARG;
+    if (B == 0 || T == 0 || C == 0) return ORC_OK;
+    set_threads(nthreads);
+    int failed = 0;
+#pragma omp parallel
+    {
+        double* kc = (double*)malloc(sizeof(double) * (size_t)T);
+        double* vc = (double*)malloc(sizeof(double) * (size_t)T);
+        double* s = (double*)malloc(sizeof(double) * (size_t)T);
+        if (!kc || !vc || !s) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t bc = 0; bc < B * C; ++bc) {
+                const int64_t b = bc / C, c = bc % C;
+                gather_col(k, b, c, T, C, kc);
+                gather_col(v, b, c, T, C, vc);
+                const double wc = w[c], uc = u[c], Td = (double)T;
+                for (int64_t t = 0; t < T; ++t) {
+                    double M = -INFINITY;
+                    for (int64_t i = 0; i <= t; ++i) {
+                        const double si = (i == t) ? uc + kc[i]
+                                                   : -(((double)(t - 1 - i)) / Td) * wc + kc[i];
+                        s[i] = si;
+                        if (si > M) M = si;
+                    }
+                    double num = 0.0, den = 0.0, mag = 0.0;
+                    for (int64_t i = 0; i <= t; ++i) {
+                        const double p = exp(s[i] - M);
+                        num += p * vc[i];
+                        den += p;
+                        mag += p * fabs(vc[i]);
+                    }
+                    const int64_t o = (b * T + t) * C + c;
+                    out[o] = num / den;
+                    if (scale) scale[o] = mag / den;
+                }
+            }
+        }
+        free(kc);
+        free(vc);
+        free(s);
+    }
+    return failed ? ORC_ERR_NOMEM : ORC_OK;
+}
+
+/*
+ * O2c — the causal attention in RNN form: Eq. (6)'s prefix states a, c only (one forward sweep)
+ * and Eq. (7) with b = d = 0:
+ *   A_0 = 0, A_{t+1} = lam*A_t + e_t v_t;  C_0 = 0, C_{t+1} = lam*C_t + e_t
+ *   wkv_t = (A_t + E_t v_t) / (C_t + E_t),  E_t = exp(u + k_t - kappa)
+ * with lam = exp(-w/T), e_i = exp(k_i - kappa), kappa = max_i k_i.
+ */
+int oracle_biwkv_causal_rnn(const double* k, const double* v, const double* w, const double* u,
+                            int64_t B, int64_t T, int64_t C, double* out, int nthreads) {
+    if (!k || !v || !w || !u || !out || B < 0 || T < 0 || C < 0) return ORC_ERR_ARG;
+    if (B == 0 || T == 0 || C == 0) return ORC_OK;
+    set_threads(nthreads);
+    int failed = 0;
+#pragma omp parallel
+    {
+        double* kc = (double*)malloc(sizeof(double) * (size_t)T);
+        double* vc = (double*)malloc(sizeof(double) * (size_t)T);
+        if (!kc || !vc) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t bc = 0; bc < B * C; ++bc) {
+                const int64_t b = bc / C, c = bc % C;
+                gather_col(k, b, c, T, C, kc);
+                gather_col(v, b, c, T, C, vc);
+                double kappa = -INFINITY;
+                for (int64_t t = 0; t < T; ++t)
+                    if (kc[t] > kappa) kappa = kc[t];
+                const double lam = exp(-w[c] / (double)T);
+                double A = 0.0, Cs = 0.0;
+                for (int64_t t = 0; t < T; ++t) {
+                    const double E = exp(u[c] + kc[t] - kappa);
+                    out[(b * T + t) * C + c] = (A + E * vc[t]) / (Cs + E);
+                    const double e = exp(kc[t] - kappa);
+                    A = lam * A + e * vc[t];
+                    Cs = lam * Cs + e;
+                }
+            }
+        }
+        free(kc);
+        free(vc);
+    }
+    return failed ? ORC_ERR_NOMEM : ORC_OK;
+}
+
+/*
  * Channel-group boundaries of the q_shift function in [NOTES]: g_j = int(C * gamma * j),
  * j = 1..4, evaluated as the listing's Python does it: double product, left to right,
  * truncated toward zero.
