@@ -1,6 +1,6 @@
 """Benchmark: Bi-WKV forward (+ Q-Shift) throughput and HBM roofline on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--entry fused|biwkv|qshift]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--entry fused|biwkv|causal|qshift]
 
 One step = one pass of the whole hot path over one batch: the fused Q-Shift + Bi-WKV entry on the
 high-resolution workload (B=4, 64x64 grid so T=4096, C=1024, bf16 k/v, fp32 accumulate and
@@ -38,7 +38,8 @@ COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters_biwkv_qshift_B4_T40
 CALIBRATION_BYTES = 512 * 1024 * 1024
 MIN_CPU_SECONDS = 3.0
 COPY_KERNEL = "copy"  # substring of the device copy kernel's name in the counter output
-KERNEL_NAMES = {"fused": "biwkv_row_kernel", "biwkv": "biwkv_row_kernel", "qshift": "qshift_kernel"}
+KERNEL_NAMES = {"fused": "biwkv_row_kernel", "biwkv": "biwkv_row_kernel", "causal": "biwkv_row_kernel",
+                "qshift": "qshift_kernel"}
 
 
 def kernel_source_hash() -> str:
@@ -53,7 +54,7 @@ def kernel_source_hash() -> str:
 def alg_bytes(entry: str, B: int, H: int, W: int, C: int, kv_bytes: int, shift: int = 1, gamma: float = 0.25) -> int:
     """Algorithmic HBM bytes of one call: what the method must move.
 
-    biwkv:  read k and v (kv_bytes each), write fp32 out, read w and u.
+    biwkv:  read k and v (kv_bytes each), write fp32 out, read w and u (causal: the same).
     fused:  as biwkv, but the Q-Shift zero-filled sources are never read.
     qshift: read the in-grid sources, write every output (fp32).
     """
@@ -61,7 +62,7 @@ def alg_bytes(entry: str, B: int, H: int, W: int, C: int, kv_bytes: int, shift: 
     n = B * T * C
     g = [int(C * gamma * j) for j in (1, 2, 3, 4)]
     zero_per_b = shift * H * g[1] + shift * W * (g[3] - g[1])  # zero-filled outputs per batch item
-    if entry == "biwkv":
+    if entry in ("biwkv", "causal"):
         return 2 * kv_bytes * n + 4 * n + 8 * C
     if entry == "fused":
         return 2 * kv_bytes * (n - B * zero_per_b) + 4 * n + 8 * C
@@ -121,6 +122,8 @@ def cpu_baseline(wl, entry: str) -> dict:
             ks = oracle.qshift_f64(k, wl.H, wl.W, wl.shift, wl.gamma)
             vs = oracle.qshift_f64(v, wl.H, wl.W, wl.shift, wl.gamma)
             oracle.biwkv_rnn(ks, vs, w, u, threads=threads)
+        elif entry == "causal":
+            oracle.biwkv_causal_rnn(k, v, w, u, threads=threads)
         else:
             oracle.biwkv_rnn(k, v, w, u, threads=threads)
         reps += 1
@@ -130,7 +133,8 @@ def cpu_baseline(wl, entry: str) -> dict:
     elems = wl.B * wl.T * wl.C
     return {"value": reps * elems / dt / 1e9, "unit": "Gtoken*ch/s", "cores": threads,
             "kind": "oracle", "seconds": dt, "repetitions": reps, "cpu": _cpu_model(),
-            "sample": f"whole workload ({wl.B}x{wl.T}x{wl.C}) x{reps}; float64 four-state RNN oracle"
+            "sample": f"whole workload ({wl.B}x{wl.T}x{wl.C}) x{reps}; float64 "
+                      + ("two-state causal RNN oracle" if entry == "causal" else "four-state RNN oracle")
                       + (" after the oracle Q-Shift of k and v" if entry == "fused" else "")}
 
 
@@ -181,6 +185,11 @@ def run_bench(args) -> dict:
             calls.append((cl.biwkv_forward,
                           (ks_[r].data_ptr(), vs_[r].data_ptr(), w.data_ptr(), u.data_ptr(),
                            outs[r].data_ptr(), B, T, C, lib.BF16, stream.cuda_stream)))
+        elif entry == "causal":
+            lib.biwkv_causal_forward(ks_[r], vs_[r], w, u, out=outs[r])
+            calls.append((cl.biwkv_causal_forward,
+                          (ks_[r].data_ptr(), vs_[r].data_ptr(), w.data_ptr(), u.data_ptr(),
+                           outs[r].data_ptr(), B, T, C, lib.BF16, stream.cuda_stream)))
         else:
             lib.qshift(xs[r], H, W, wl.shift, wl.gamma, out=outs[r])
             calls.append((cl.qshift, (xs[r].data_ptr(), outs[r].data_ptr(), B, H, W, C, wl.shift,
@@ -221,7 +230,8 @@ def run_bench(args) -> dict:
     traffic = None
     if counters is not None and entry in counters.get("entries", {}):
         traffic = counters["entries"][entry]["hbm_bytes_per_launch"]
-    names = {"fused": "biwkv_qshift_forward", "biwkv": "biwkv_forward", "qshift": "qshift"}
+    names = {"fused": "biwkv_qshift_forward", "biwkv": "biwkv_forward", "causal": "biwkv_causal_forward",
+             "qshift": "qshift"}
     return {
         "metric": "Bi-WKV fwd Gtoken*ch/s + achieved HBM GB/s (% peak) at T=4096 C=1024",
         "value": elems * args.steps / wall / 1e9,
@@ -336,7 +346,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--entry", choices=["fused", "biwkv", "qshift"], default="fused")
+    ap.add_argument("--entry", choices=["fused", "biwkv", "causal", "qshift"], default="fused")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize", metavar="DIR")

@@ -76,6 +76,19 @@ int biwkv_forward(const void* k, const void* v, const float* w, const float* u, 
                   int64_t B, int64_t T, int64_t C, int dtype, void* stream);
 
 /*
+ * Causal attention: the original RWKV attention that the Vision-RWKV article (section "Linear
+ * Complexity Bidirectional Attention") extends to both directions, i.e. Eq. (7) without the
+ * backward states b and d:
+ *   out_t = ( sum_{i<t} e^{-((t-1-i)/T) w + k_i} v_i + e^{u+k_t} v_t )
+ *         / ( sum_{i<t} e^{-((t-1-i)/T) w + k_i}     + e^{u+k_t}     )
+ * w is divided by T as in Eq. (5); the original, undivided decay w0 is w = T * w0.
+ * Arguments, layout, ownership, scratch and errors are those of biwkv_forward, except that there
+ * is no 128-token fallback: a row whose chunks cannot all be resident returns _UNSUPPORTED.
+ */
+int biwkv_causal_forward(const void* k, const void* v, const float* w, const float* u, float* out,
+                         int64_t B, int64_t T, int64_t C, int dtype, void* stream);
+
+/*
  * Q-Shift token shift X-dagger of the q_shift listing (LinXin's Blog, Vision-RWKV notes).
  *   x, out : [B, H*W, C] float32, device memory; values are moved bit for bit (NaN payloads,
  *            signed zeros and denormals are preserved); out must not overlap x.

@@ -8,6 +8,7 @@ from ._lib import (  # noqa: F401
     F32,
     LIB_PATH,
     BiwkvError,
+    biwkv_causal_forward,
     biwkv_forward,
     biwkv_qshift_forward,
     header_symbols,

@@ -49,6 +49,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib = ctypes.CDLL(p)
     lib.biwkv_forward.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P]
     lib.biwkv_forward.restype = ctypes.c_int
+    lib.biwkv_causal_forward.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P]
+    lib.biwkv_causal_forward.restype = ctypes.c_int
     lib.qshift.argtypes = [_P, _P, _I64, _I64, _I64, _I64, ctypes.c_int, ctypes.c_double, _P]
     lib.qshift.restype = ctypes.c_int
     lib.biwkv_qshift_forward.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_int,
@@ -133,6 +135,23 @@ def biwkv_forward(k, v, w, u, out=None):
     with torch.cuda.device(k.device):
         _check(load_library().biwkv_forward(k.data_ptr(), v.data_ptr(), w.data_ptr(), u.data_ptr(),
                                             out.data_ptr(), B, T, C, dt, _stream_handle(k.device)))
+    return out
+
+
+def biwkv_causal_forward(k, v, w, u, out=None):
+    """Causal attention (Eq. (7) with b = d = 0: earlier tokens plus the bonus term); same
+    arguments and exponent convention as biwkv_forward."""
+    torch = _torch()
+    dt = _check_bitc(k, v, w, u)
+    B, T, C = k.shape
+    if out is None:
+        out = torch.empty((B, T, C), dtype=torch.float32, device=k.device)
+    _require(out.shape == k.shape and out.dtype == torch.float32 and out.is_contiguous(),
+             "out must be a contiguous float32 [B, T, C] tensor")
+    with torch.cuda.device(k.device):
+        _check(load_library().biwkv_causal_forward(k.data_ptr(), v.data_ptr(), w.data_ptr(),
+                                                   u.data_ptr(), out.data_ptr(), B, T, C, dt,
+                                                   _stream_handle(k.device)))
     return out
 
 

@@ -229,7 +229,7 @@ int launch_biwkv(BiwkvParams prm, int64_t B, int dev, void* stream) {
 
 // Tile kernel launch: rows of TILE channels, chunks of (NT / TILE) * L tokens. Returns 1 when
 // the shape is outside what the kernel addresses (the caller then uses the chunk-scan kernel).
-template <int DT, int TILE, int L, int NT, bool FUSED, bool PAIR>
+template <int DT, int TILE, int L, int NT, bool FUSED, bool PAIR, bool CAUSAL>
 int launch_row(const BiwkvParams& bp, int64_t B, int dev, void* stream) {
   constexpr int CT = (NT / TILE) * L;
   const long long T = bp.T;
@@ -262,7 +262,7 @@ int launch_row(const BiwkvParams& bp, int64_t B, int dev, void* stream) {
   rp.total = static_cast<unsigned>(total);
   if (n_chunks > 1) {
     // The chunks of a row wait for each other: they must all fit on the device at once.
-    const void* kfn = reinterpret_cast<const void*>(&biwkv_row_kernel<DT, TILE, L, NT, FUSED, PAIR>);
+    const void* kfn = reinterpret_cast<const void*>(&biwkv_row_kernel<DT, TILE, L, NT, FUSED, PAIR, CAUSAL>);
     std::lock_guard<std::mutex> lock(g_mu);
     int cap = 0;
     int rc = resident_capacity(dev, kfn, NT, &cap);
@@ -274,11 +274,11 @@ int launch_row(const BiwkvParams& bp, int64_t B, int dev, void* stream) {
     if (rc) return rc;
     rp.ctr = sc->ctr;
     rp.slots = sc->slots;
-    hipLaunchKernelGGL((biwkv_row_kernel<DT, TILE, L, NT, FUSED, PAIR>),
+    hipLaunchKernelGGL((biwkv_row_kernel<DT, TILE, L, NT, FUSED, PAIR, CAUSAL>),
                        dim3(static_cast<unsigned>(total)), dim3(NT), 0,
                        static_cast<hipStream_t>(stream), rp);
   } else {
-    hipLaunchKernelGGL((biwkv_row_kernel<DT, TILE, L, NT, FUSED, PAIR>),
+    hipLaunchKernelGGL((biwkv_row_kernel<DT, TILE, L, NT, FUSED, PAIR, CAUSAL>),
                        dim3(static_cast<unsigned>(total)), dim3(NT), 0,
                        static_cast<hipStream_t>(stream), rp);
   }
@@ -293,17 +293,17 @@ int launch_row(const BiwkvParams& bp, int64_t B, int dev, void* stream) {
 // data first and computes and writes while the other one still reads, so reads and writes
 // overlap. fp32 rows keep 1024 threads: at 32 tokens per lane their 512-thread chunks are short
 // and the exchange between them dominates.
-template <int DT, bool FUSED, bool PAIR>
+template <int DT, bool FUSED, bool PAIR, bool CAUSAL>
 int try_row_shape(const BiwkvParams& bp, int64_t B, int dev, void* stream) {
   const long long T = bp.T;
   if constexpr (DT == BIWKV_BF16) {
-    if (T <= 256) return launch_row<DT, 64, 16, 1024, FUSED, PAIR>(bp, B, dev, stream);
-    if (T <= 512) return launch_row<DT, 64, 32, 1024, FUSED, PAIR>(bp, B, dev, stream);
-    if (T <= 1024) return launch_row<DT, 64, 64, 1024, FUSED, PAIR>(bp, B, dev, stream);
-    return launch_row<DT, 64, 64, 512, FUSED, PAIR>(bp, B, dev, stream);
+    if (T <= 256) return launch_row<DT, 64, 16, 1024, FUSED, PAIR, CAUSAL>(bp, B, dev, stream);
+    if (T <= 512) return launch_row<DT, 64, 32, 1024, FUSED, PAIR, CAUSAL>(bp, B, dev, stream);
+    if (T <= 1024) return launch_row<DT, 64, 64, 1024, FUSED, PAIR, CAUSAL>(bp, B, dev, stream);
+    return launch_row<DT, 64, 64, 512, FUSED, PAIR, CAUSAL>(bp, B, dev, stream);
   } else {
-    if (T <= 256) return launch_row<DT, 64, 16, 1024, FUSED, PAIR>(bp, B, dev, stream);
-    return launch_row<DT, 64, 32, 1024, FUSED, PAIR>(bp, B, dev, stream);
+    if (T <= 256) return launch_row<DT, 64, 16, 1024, FUSED, PAIR, CAUSAL>(bp, B, dev, stream);
+    return launch_row<DT, 64, 32, 1024, FUSED, PAIR, CAUSAL>(bp, B, dev, stream);
   }
 }
 
@@ -315,12 +315,12 @@ bool pairs_ok(const BiwkvParams& bp, bool fused) {
   return true;
 }
 
-template <int DT, bool FUSED>
+template <int DT, bool FUSED, bool CAUSAL = false>
 int try_row(const BiwkvParams& bp, int64_t B, int dev, void* stream) {
   if constexpr (DT == BIWKV_BF16) {
-    if (pairs_ok(bp, FUSED)) return try_row_shape<DT, FUSED, true>(bp, B, dev, stream);
+    if (pairs_ok(bp, FUSED)) return try_row_shape<DT, FUSED, true, CAUSAL>(bp, B, dev, stream);
   }
-  return try_row_shape<DT, FUSED, false>(bp, B, dev, stream);
+  return try_row_shape<DT, FUSED, false, CAUSAL>(bp, B, dev, stream);
 }
 
 template <bool FUSED>
@@ -380,6 +380,27 @@ int biwkv_forward(const void* k, const void* v, const float* w, const float* u, 
   prm.T = T;
   prm.C = static_cast<int>(C);
   return dispatch_biwkv<false>(prm, B, dtype, vec2, dev, stream);
+}
+
+int biwkv_causal_forward(const void* k, const void* v, const float* w, const float* u, float* out,
+                         int64_t B, int64_t T, int64_t C, int dtype, void* stream) {
+  int rc = validate_biwkv(k, v, w, u, out, B, T, C, dtype);
+  if (rc || !(B && T && C)) return rc;
+  int dev = 0;
+  rc = current_device(&dev);
+  if (rc) return rc;
+  BiwkvParams prm{};
+  prm.k = k;
+  prm.v = v;
+  prm.w = w;
+  prm.u = u;
+  prm.out = out;
+  prm.T = T;
+  prm.C = static_cast<int>(C);
+  // tile kernel only: a shape it does not address has no fallback
+  rc = dtype == BIWKV_F32 ? try_row<BIWKV_F32, false, true>(prm, B, dev, stream)
+                          : try_row<BIWKV_BF16, false, true>(prm, B, dev, stream);
+  return rc == 1 ? BIWKV_ERR_UNSUPPORTED : rc;
 }
 
 int biwkv_qshift_forward(const void* k, const void* v, const float* w, const float* u, float* out,

@@ -382,36 +382,41 @@ __device__ __forceinline__ Agg agg_from_first(Agg a) {
 }
 
 // Inclusive scans over the W groups of a channel (lane tg holds group tg; groups are L slots
-// apart): forward over groups 0..tg, anchored at tg's last slot, and backward over tg..W-1,
-// anchored at tg's first token. Hillis-Steele, fixed order.
-template <int W, int L, int d = 1>
+// apart): forward over groups 0..tg, anchored at tg's last slot, and (BWD) backward over
+// tg..W-1, anchored at tg's first token. Hillis-Steele, fixed order.
+template <int W, int L, bool BWD, int d = 1>
 __device__ __forceinline__ void group_scan(Agg& f, Agg& bk, int tg, float D) {
   if constexpr (d < W) {
     const Agg pf = agg_from_below<W, d>(f);
-    const Agg pb = agg_from_above<W, d>(bk);
     if (tg >= d) f = agg_add_f(agg_shift(pf, static_cast<float>(d * L), D), f);
-    if (tg + d < W) bk = agg_add_f(bk, agg_shift(pb, static_cast<float>(d * L), D));
-    group_scan<W, L, 2 * d>(f, bk, tg, D);
+    if constexpr (BWD) {
+      const Agg pb = agg_from_above<W, d>(bk);
+      if (tg + d < W) bk = agg_add_f(bk, agg_shift(pb, static_cast<float>(d * L), D));
+    }
+    group_scan<W, L, BWD, 2 * d>(f, bk, tg, D);
   }
 }
 
-// Folds the W lanes' sums into the segment's first lane in a fixed tree.
-template <int W, int s = 1>
+// Folds the W lanes' sums (a, and b when BWD) into the segment's first lane in a fixed tree.
+template <int W, bool BWD, int s = 1>
 __device__ __forceinline__ void group_fold(Agg& a, Agg& b, int tg) {
   if constexpr (s < W) {
-    const Agg oa = agg_from_above<W, s>(a), ob = agg_from_above<W, s>(b);
-    if ((tg & (2 * s - 1)) == 0) {
-      a = agg_add_f(a, oa);
-      b = agg_add_f(b, ob);
+    const Agg oa = agg_from_above<W, s>(a);
+    if ((tg & (2 * s - 1)) == 0) a = agg_add_f(a, oa);
+    if constexpr (BWD) {
+      const Agg ob = agg_from_above<W, s>(b);
+      if ((tg & (2 * s - 1)) == 0) b = agg_add_f(b, ob);
     }
-    group_fold<W, 2 * s>(a, b, tg);
+    group_fold<W, BWD, 2 * s>(a, b, tg);
   }
 }
 
 template <int DT, int TILE, int L, bool PAIR>
 using RowStore = std::conditional_t<PAIR, RowKVPair<L>, RowKV<DT, L>>;
 
-template <int DT, int TILE, int L, int NT, bool FUSED, bool PAIR, bool WIDE>
+// CAUSAL: the causal attention (Eq. (7) without the backward states b, d): only forward sums
+// are formed, scanned and exchanged, and the output comes out of the forward sweep.
+template <int DT, int TILE, int L, int NT, bool FUSED, bool PAIR, bool WIDE, bool CAUSAL>
 __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
                                          RowStore<DT, TILE, L, PAIR>& kv, float* lds,
                                          const unsigned* sh_epoch) {
@@ -462,14 +467,16 @@ __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
         qF = fmaf(qF, lam, pv[i]);
         qG = fmaf(qG, lam, pp[i]);
       }
-      bF[q] = pv[SB - 1];
-      bG[q] = pp[SB - 1];
+      if constexpr (!CAUSAL) {
+        bF[q] = pv[SB - 1];
+        bG[q] = pp[SB - 1];
 #pragma unroll
-      for (int i = SB - 2; i >= 0; --i) {
-        bF[q] = fmaf(bF[q], lam, pv[i]);
-        bG[q] = fmaf(bG[q], lam, pp[i]);
+        for (int i = SB - 2; i >= 0; --i) {
+          bF[q] = fmaf(bF[q], lam, pv[i]);
+          bG[q] = fmaf(bG[q], lam, pp[i]);
+        }
+        bm[q] = mq;
       }
-      bm[q] = mq;
       // move the running sums SB tokens on and add this sub-block at the larger exponent
       const float mn = fmaxf(mrun, mq);
       const float mr = mn == kNegInf ? 0.f : mn;
@@ -482,42 +489,45 @@ __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
     kmax = mrun;  // largest key of the lane (-inf when it holds no token)
     const float mr = mrun == kNegInf ? 0.f : mrun;
     float cF = 0.f, cG = 0.f;
+    if constexpr (!CAUSAL) {
 #pragma unroll
-    for (int q = NSB - 1; q >= 0; --q) {
-      capF[q] = cF;
-      capG[q] = cG;
-      const float sq = fast_exp2(bm[q] - mr);
-      cF = fmaf(cF, lsb, bF[q] * sq);
-      cG = fmaf(cG, lsb, bG[q] * sq);
+      for (int q = NSB - 1; q >= 0; --q) {
+        capF[q] = cF;
+        capG[q] = cG;
+        const float sq = fast_exp2(bm[q] - mr);
+        cF = fmaf(cF, lsb, bF[q] * sq);
+        cG = fmaf(cG, lsb, bG[q] * sq);
+      }
     }
     // the lane sums and the caps are against 2^{kmax + span}
     const float m_agg = kmax == kNegInf ? kEmptyM : kmax + span;
     af = Agg{m_agg, fF, fG};
-    ab = Agg{m_agg, cF, cG};
+    ab = CAUSAL ? row_empty() : Agg{m_agg, cF, cG};
   } else {
 #pragma unroll
     for (int q = 0; q < NSB; ++q) kv.prepare(q);
     // Wide range: one decay step at a time, each sum against its own running maximum (an empty
     // slot, k = -inf, adds nothing).
     af = agg_empty();
-    Agg bs[NSB];
-#pragma unroll
-    for (int q = 0; q < NSB; ++q) {
-      bs[q] = agg_empty();
-#pragma unroll
-      for (int i = (q + 1) * SB - 1; i >= q * SB; --i)
-        bs[q] = agg_add(agg_shift(bs[q], 1.f, D), Agg{kv.k(i) * kLog2e, kv.v(i), 1.f});
-    }
 #pragma unroll
     for (int i = 0; i < L; ++i)
       af = agg_add(agg_shift(af, 1.f, D), Agg{kv.k(i) * kLog2e, kv.v(i), 1.f});
-    Agg cs = agg_empty();
+    ab = agg_empty();
+    if constexpr (!CAUSAL) {
+      Agg bs[NSB];
 #pragma unroll
-    for (int q = NSB - 1; q >= 0; --q) {
-      cap[q] = cs;
-      cs = agg_add(bs[q], agg_shift(cs, static_cast<float>(SB), D));
+      for (int q = 0; q < NSB; ++q) {
+        bs[q] = agg_empty();
+#pragma unroll
+        for (int i = (q + 1) * SB - 1; i >= q * SB; --i)
+          bs[q] = agg_add(agg_shift(bs[q], 1.f, D), Agg{kv.k(i) * kLog2e, kv.v(i), 1.f});
+      }
+#pragma unroll
+      for (int q = NSB - 1; q >= 0; --q) {
+        cap[q] = ab;
+        ab = agg_add(bs[q], agg_shift(ab, static_cast<float>(SB), D));
+      }
     }
-    ab = cs;
   }
   kv.fence();
 
@@ -548,12 +558,12 @@ __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
   const float Dt = dch[tc];
   Agg f{red[0 * RS + ti], red[1 * RS + ti], red[2 * RS + ti]};
   Agg bk{red[3 * RS + ti], red[4 * RS + ti], red[5 * RS + ti]};
-  group_scan<GROUPS, L>(f, bk, tg, Dt);
+  group_scan<GROUPS, L, !CAUSAL>(f, bk, tg, Dt);
   // exclusive carries: forward sum of the earlier groups (anchored just before the group's first
   // token), backward sum of the later groups (anchored just after its last slot)
   Agg X = agg_from_below<GROUPS, 1>(f), Y = agg_from_above<GROUPS, 1>(bk);
   if (tg == 0) X = row_empty();
-  if (tg == GROUPS - 1) Y = row_empty();
+  if (CAUSAL || tg == GROUPS - 1) Y = row_empty();
   if (p.n_chunks > 1) {
     // ---- exchange with the other chunks of the row ----
     const int nch = p.n_chunks, chunk = ln.chunk;
@@ -563,11 +573,11 @@ __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
     // the chunk's own sums: forward (inclusive at the last group, anchored at the chunk's last
     // slot) and backward (inclusive at group 0, anchored at the chunk's first token)
     if (tg == GROUPS - 1) slot_store(slot(chunk, kFwd), f, epoch);
-    if (tg == 0) slot_store(slot(chunk, kBwd), bk, epoch);
+    if (!CAUSAL && tg == 0) slot_store(slot(chunk, kBwd), bk, epoch);
     // Entries: forward sums of chunks 0 .. chunk-1, then backward sums of chunks chunk+1 ..
     // nch-1. Lane tg folds entries tg, tg + GROUPS, ... in order; the lanes' partials are then
     // folded in a fixed tree, so the result does not depend on arrival order.
-    const int nf = chunk, ne = nch - 1;
+    const int nf = chunk, ne = CAUSAL ? chunk : nch - 1;
     Agg pf = row_empty(), pb = row_empty();
     bool timed_out = false;
     // A lane issues the loads of up to EB entries before it waits for any of them, so a lane
@@ -610,12 +620,14 @@ __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
     }
     if (timed_out)
       __hip_atomic_fetch_or(&p.ctr->fault, kFaultSpin, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    group_fold<GROUPS>(pf, pb, tg);
+    group_fold<GROUPS, !CAUSAL>(pf, pb, tg);
     // pf (from the first lane of the channel) is anchored just before the chunk, pb just after it
     pf = agg_from_first<GROUPS>(pf);
-    pb = agg_from_first<GROUPS>(pb);
     X = agg_add_f(agg_shift(pf, static_cast<float>(tg * L), Dt), X);
-    Y = agg_add_f(Y, agg_shift(pb, static_cast<float>((GROUPS - 1 - tg) * L), Dt));
+    if constexpr (!CAUSAL) {
+      pb = agg_from_first<GROUPS>(pb);
+      Y = agg_add_f(Y, agg_shift(pb, static_cast<float>((GROUPS - 1 - tg) * L), Dt));
+    }
   }
   xy[0 * RS + ti] = X.m;
   xy[1 * RS + ti] = X.F;
@@ -649,6 +661,21 @@ __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
     const float eU = ln.eU;
     float A = X.F * sx, Cs = X.G * sx;
     const float YF = Y.F * sy, YG = Y.G * sy;
+    if constexpr (CAUSAL) {  // Eq. (7) with b = d = 0, straight out of the forward sweep
+#pragma unroll
+      for (int t = 0; t < L; ++t) {
+        const float kf = kv.k(t), vf = kv.v(t);
+        const float pi = fast_exp2(fmaf(kf, kLog2e, -M));
+        const float al = fmaf(-Cs, vf, A);
+        const float be = fmaf(pi, eU, Cs);  // >= the token's own term, a normal number
+        const float y = fmaf(al, fast_rcp(be), vf);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), orr, out0 + t * row_bytes, 0,
+                                              kStream);
+        A = fmaf(A, lam, pi * vf);
+        Cs = fmaf(Cs, lam, pi);
+      }
+      return;
+    }
 #pragma unroll
     for (int q = 0; q < NSB; ++q) {
       float ph[SB];
@@ -686,6 +713,24 @@ __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
   } else {
     const float U = ln.U;
     Agg xs = X;
+    if constexpr (CAUSAL) {
+#pragma unroll
+      for (int t = 0; t < L; ++t) {
+        const float kf = kv.k(t), vf = kv.v(t);
+        const bool any = xs.m != kNegInf && xs.G > 0.f;
+        const float be = any ? xs.m + fast_log2(xs.G) : kNegInf;  // log2 of the prefix weight
+        const float al = any ? xs.F * fast_rcp(xs.G) - vf : 0.f;  // prefix mean minus v
+        const float kl = kf * kLog2e;
+        const float ks = kl + U;
+        const float Mt = fmaxf(be, ks);
+        const float sa = fast_exp2(be - Mt), e = fast_exp2(ks - Mt);
+        const float y = fmaf(al * sa, fast_rcp(sa + e), vf);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), orr, out0 + t * row_bytes, 0,
+                                              kStream);
+        xs = agg_add(agg_shift(xs, 1.f, D), Agg{kl, vf, 1.f});
+      }
+      return;
+    }
 #pragma unroll
     for (int q = 0; q < NSB; ++q) {
 #pragma unroll
@@ -724,17 +769,17 @@ __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
 // out of line gives it its own register allocation, so its spills never touch the fast form. It
 // reads the parameters from the kernel's argument segment (a pointer, so the kernel keeps them in
 // scalar registers instead of building a private copy).
-template <int DT, int TILE, int L, int NT, bool FUSED, bool PAIR>
+template <int DT, int TILE, int L, int NT, bool FUSED, bool PAIR, bool CAUSAL>
 __device__ __noinline__ void row_body_wide(const RowParams* args, float* lds, unsigned unit,
                                            const unsigned* sh_epoch) {
   const RowParams p = *args;
   const RowLane ln = row_lane<TILE, L, NT>(p, unit);
   RowStore<DT, TILE, L, PAIR> kv;
   row_load<DT, TILE, L, NT, FUSED, PAIR>(p, ln, kv);
-  row_body<DT, TILE, L, NT, FUSED, PAIR, true>(p, ln, kv, lds, sh_epoch);
+  row_body<DT, TILE, L, NT, FUSED, PAIR, true, CAUSAL>(p, ln, kv, lds, sh_epoch);
 }
 
-template <int DT, int TILE, int L, int NT, bool FUSED, bool PAIR>
+template <int DT, int TILE, int L, int NT, bool FUSED, bool PAIR, bool CAUSAL>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4)))
     biwkv_row_kernel(RowParams p) {
   static_assert(!PAIR || (DT == BIWKV_BF16 && TILE % 2 == 0), "pairs are bf16 channel pairs");
@@ -775,11 +820,11 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4)))
     if (__ballot(wide_lane) != 0ull) {
       // the kernel's only argument is p, at the start of the argument segment
       const auto* args = (const RowParams*)(__builtin_amdgcn_kernarg_segment_ptr());
-      row_body_wide<DT, TILE, L, NT, FUSED, PAIR>(args, lds, unit, &sh_epoch);
+      row_body_wide<DT, TILE, L, NT, FUSED, PAIR, CAUSAL>(args, lds, unit, &sh_epoch);
     } else {
       RowStore<DT, TILE, L, PAIR> kv;
       row_load<DT, TILE, L, NT, FUSED, PAIR>(p, ln, kv);
-      row_body<DT, TILE, L, NT, FUSED, PAIR, false>(p, ln, kv, lds, &sh_epoch);
+      row_body<DT, TILE, L, NT, FUSED, PAIR, false, CAUSAL>(p, ln, kv, lds, &sh_epoch);
     }
   }
   if (!valid && tid == 0) row_retire(p);  // (a valid workgroup retires after its exchange)

@@ -59,7 +59,7 @@ def _load():
         lib.oracle_biwkv_rnn_literal.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _P]
         lib.oracle_qshift.argtypes = [_P, _P, _I64, _I64, _I64, _I64, _I64, ctypes.c_double]
         lib.oracle_biwkv_causal_sum.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, ctypes.c_int]
-        lib.oracle_biwkv_causal_rnn.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int]
+        lib.oracle_biwkv_causal_rnn.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, ctypes.c_int]
         for f in (lib.oracle_biwkv_sum, lib.oracle_biwkv_rnn, lib.oracle_biwkv_rnn_literal, lib.oracle_qshift,
                   lib.oracle_biwkv_causal_sum, lib.oracle_biwkv_causal_rnn):
             f.restype = ctypes.c_int
@@ -141,14 +141,16 @@ def biwkv_causal_sum(k, v, w, u, with_scale=False, threads=0):
     return (out, scale) if with_scale else out
 
 
-def biwkv_causal_rnn(k, v, w, u, threads=0):
+def biwkv_causal_rnn(k, v, w, u, with_scale=False, threads=0):
     """Causal attention in RNN form: prefix states a, c of Eq. (6) and Eq. (7) with b = d = 0."""
     k, v, w, u, B, T, C = _check_bitc(k, v, w, u)
     out = np.empty((B, T, C), dtype=np.float64)
-    rc = _load().oracle_biwkv_causal_rnn(_ptr(k), _ptr(v), _ptr(w), _ptr(u), B, T, C, _ptr(out), int(threads))
+    scale = np.empty_like(out) if with_scale else None
+    rc = _load().oracle_biwkv_causal_rnn(_ptr(k), _ptr(v), _ptr(w), _ptr(u), B, T, C, _ptr(out),
+                                         _ptr(scale) if scale is not None else None, int(threads))
     if rc != 0:
         raise RuntimeError(f"oracle_biwkv_causal_rnn failed ({rc})")
-    return out
+    return (out, scale) if with_scale else out
 
 
 class QShiftParamError(ValueError):

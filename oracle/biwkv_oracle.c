@@ -320,10 +320,12 @@ int oracle_biwkv_causal_sum(const double* k, const double* v, const double* w, c
  * and Eq. (7) with b = d = 0:
  *   A_0 = 0, A_{t+1} = lam*A_t + e_t v_t;  C_0 = 0, C_{t+1} = lam*C_t + e_t
  *   wkv_t = (A_t + E_t v_t) / (C_t + E_t),  E_t = exp(u + k_t - kappa)
- * with lam = exp(-w/T), e_i = exp(k_i - kappa), kappa = max_i k_i.
+ * with lam = exp(-w/T), e_i = exp(k_i - kappa), kappa = max_i k_i. Also returns the magnitude
+ * scale (the same recurrence on |v|) when scale is not NULL.
  */
 int oracle_biwkv_causal_rnn(const double* k, const double* v, const double* w, const double* u,
-                            int64_t B, int64_t T, int64_t C, double* out, int nthreads) {
+                            int64_t B, int64_t T, int64_t C, double* out, double* scale,
+                            int nthreads) {
     if (!k || !v || !w || !u || !out || B < 0 || T < 0 || C < 0) return ORC_ERR_ARG;
     if (B == 0 || T == 0 || C == 0) return ORC_OK;
     set_threads(nthreads);
@@ -345,13 +347,15 @@ int oracle_biwkv_causal_rnn(const double* k, const double* v, const double* w, c
                 for (int64_t t = 0; t < T; ++t)
                     if (kc[t] > kappa) kappa = kc[t];
                 const double lam = exp(-w[c] / (double)T);
-                double A = 0.0, Cs = 0.0;
+                double A = 0.0, Cs = 0.0, Am = 0.0;
                 for (int64_t t = 0; t < T; ++t) {
                     const double E = exp(u[c] + kc[t] - kappa);
                     out[(b * T + t) * C + c] = (A + E * vc[t]) / (Cs + E);
+                    if (scale) scale[(b * T + t) * C + c] = (Am + E * fabs(vc[t])) / (Cs + E);
                     const double e = exp(kc[t] - kappa);
                     A = lam * A + e * vc[t];
                     Cs = lam * Cs + e;
+                    Am = lam * Am + e * fabs(vc[t]);
                 }
             }
         }

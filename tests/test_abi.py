@@ -112,3 +112,15 @@ def test_torch_front_end_refuses_host_tensors():
         lib.biwkv_forward(k, k, w, w)
     with pytest.raises(ValueError):
         lib.qshift(k, 2, 2)
+
+
+def test_causal_forward_validation(L):
+    def causal(k=K, v=V, w=WP, u=UP, out=OUT, B=2, T=8, C=4, dtype=lib.F32):
+        return L.biwkv_causal_forward(k, v, w, u, out, B, T, C, dtype, None)
+
+    assert causal(dtype=5) == _code("BIWKV_ERR_DTYPE")
+    assert causal(v=None) == _code("BIWKV_ERR_NULL")
+    assert causal(T=-1) == _code("BIWKV_ERR_SHAPE")
+    assert causal(k=K + 2) == _code("BIWKV_ERR_ALIGN")
+    assert causal(out=V + 4) == _code("BIWKV_ERR_ALIAS")
+    assert causal(B=0) == 0

@@ -27,8 +27,9 @@ def _rand(seed, B, T, C, kstd=1.0, wr=5.0, ustd=1.0):
 def test_causal_sum_equals_rnn(T, C, B):
     k, v, w, u = _rand(T, B, T, C, kstd=3.0, wr=8.0)
     y1, s1 = oracle.biwkv_causal_sum(k, v, w, u, with_scale=True)
-    y2 = oracle.biwkv_causal_rnn(k, v, w, u)
+    y2, s2 = oracle.biwkv_causal_rnn(k, v, w, u, with_scale=True)
     assert r3(y2, y1, s1) <= 1e-12
+    np.testing.assert_allclose(s2, s1, rtol=1e-10)
 
 
 @pytest.mark.parametrize("T", [2, 7, 30])
@@ -98,8 +99,8 @@ CAUSAL_MUTATIONS = {
     "decay_sign_flipped": (": -(((double)(t - 1 - i)) / Td) * wc", ": (((double)(t - 1 - i)) / Td) * wc"),
     "future_included": ("for (int64_t i = 0; i <= t; ++i)", "for (int64_t i = 0; i <= t + (t + 1 < T); ++i)"),
     "bonus_dropped": ("(i == t) ? uc + kc[i]", "(i == t) ? kc[i]"),
-    "rnn_output_after_update": ("out[(b * T + t) * C + c] = (A + E * vc[t]) / (Cs + E);\n                    const double e = exp(kc[t] - kappa);\n                    A = lam * A + e * vc[t];\n                    Cs = lam * Cs + e;",
-                                "const double e = exp(kc[t] - kappa);\n                    A = lam * A + e * vc[t];\n                    Cs = lam * Cs + e;\n                    out[(b * T + t) * C + c] = (A + E * vc[t]) / (Cs + E);"),
+    "rnn_self_term_in_state": ("out[(b * T + t) * C + c] = (A + E * vc[t]) / (Cs + E);",
+                               "out[(b * T + t) * C + c] = (A + exp(kc[t] - kappa) * vc[t] + E * vc[t]) / (Cs + exp(kc[t] - kappa) + E);"),
 }
 
 
@@ -121,7 +122,7 @@ def test_causal_pins_catch_planted_mistakes(tmp_path, name):
     lib = ctypes.CDLL(str(so_path))
     P, I = ctypes.c_void_p, ctypes.c_int64
     lib.oracle_biwkv_causal_sum.argtypes = [P, P, P, P, I, I, I, P, P, ctypes.c_int]
-    lib.oracle_biwkv_causal_rnn.argtypes = [P, P, P, P, I, I, I, P, ctypes.c_int]
+    lib.oracle_biwkv_causal_rnn.argtypes = [P, P, P, P, I, I, I, P, P, ctypes.c_int]
     T, C = 9, 3
     k, v, w, u = _rand(40, 1, T, C, kstd=1.5, wr=6.0)
     ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
@@ -131,7 +132,7 @@ def test_causal_pins_catch_planted_mistakes(tmp_path, name):
         if fn == "sum":
             lib.oracle_biwkv_causal_sum(ptr(k), ptr(v), ptr(w), ptr(u), 1, T, C, ptr(out), None, 1)
         else:
-            lib.oracle_biwkv_causal_rnn(ptr(k), ptr(v), ptr(w), ptr(u), 1, T, C, ptr(out), 1)
+            lib.oracle_biwkv_causal_rnn(ptr(k), ptr(v), ptr(w), ptr(u), 1, T, C, ptr(out), None, 1)
         for t in range(T):
             ref = oracle.biwkv_sum(k[:, : t + 1], v[:, : t + 1], w * (t + 1) / T, u)[:, t]
             if not np.allclose(out[:, t], ref, rtol=1e-9, atol=1e-12):
