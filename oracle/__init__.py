@@ -14,6 +14,9 @@ Functions follow the pages (cited by title and equation):
 * ``qshift``         — the q_shift function of "LinXin's Blog" Vision-RWKV notes (token shift on
   the H x W grid, groups at int(C*gamma*j), zero fill, remainder copied).
 * ``biwkv_qshift``   — the fused composition Bi-WKV(X†(k), X†(v)).
+* ``sigmoid`` / ``biwkv_gated`` — Eq. (2) of the same article: the attention output gated by
+  sigma(R) (elementwise) before the output projection.
+* ``qshift_mix``     — Eq. (9) as printed: X + (1 - mu) X-dagger for each mixing vector mu.
 * ``biwkv_causal_sum`` / ``biwkv_causal_rnn`` — the causal attention Bi-WKV is derived from (the
   original RWKV attention, which the same section says stops at the current token): Eq. (5)
   with the decayed sum over i < t only, and Eq. (6)-(7) with b = d = 0.
@@ -181,6 +184,32 @@ def qshift_f64(x, H, W, shift=1, gamma=0.25):
     if not np.array_equal(x32.astype(np.float64), np.asarray(x, dtype=np.float64), equal_nan=True):
         raise ValueError("qshift_f64 needs values exactly representable in float32")
     return qshift(x32, H, W, shift, gamma).astype(np.float64)
+
+
+def sigmoid(x):
+    """The logistic function of Eq. (2)'s gate (sigma), in float64: 1 / (1 + e^{-x})."""
+    x = np.asarray(x, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-x))
+
+
+def biwkv_gated(k, v, r, w, u, with_scale=False, threads=0):
+    """Eq. (2)'s gated attention output before the output projection: sigma(R) * Bi-WKV(K, V)
+    ("OpenGVLab&港中文&复旦&南大&清华提出Vision-RWKV Backbone", spatial-mix block, Eq. (2))."""
+    y, s = biwkv_rnn(k, v, w, u, with_scale=True, threads=threads)
+    gate = sigmoid(r)
+    return (gate * y, gate * s) if with_scale else gate * y
+
+
+def qshift_mix(x, mu, H, W, shift=1, gamma=0.25):
+    """Eq. (9) as printed, once per mixing vector: out[j] = X + (1 - mu[j]) * X-dagger, with
+    X-dagger the q_shift gather (values must be fp32-exact); float64 result [J, B, N, C]."""
+    x = np.asarray(x, dtype=np.float64)
+    mu = np.asarray(mu, dtype=np.float64)
+    if mu.ndim != 2 or mu.shape[1] != x.shape[2]:
+        raise ValueError("mu must be [J, C]")
+    xd = qshift_f64(x, H, W, shift, gamma)
+    return np.stack([x + (1.0 - mu[j])[None, None, :] * xd for j in range(mu.shape[0])])
 
 
 def biwkv_qshift(k, v, w, u, H, W, shift=1, gamma=0.25, use_rnn=True, with_scale=False, threads=0):
