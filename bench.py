@@ -1,6 +1,6 @@
 """Benchmark: Bi-WKV forward (+ Q-Shift) throughput and HBM roofline on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--entry fused|biwkv|causal|qshift]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--entry fused|biwkv|causal|gated|qshift|mix]
 
 One step = one pass of the whole hot path over one batch: the fused Q-Shift + Bi-WKV entry on the
 high-resolution workload (B=4, 64x64 grid so T=4096, C=1024, bf16 k/v, fp32 accumulate and
@@ -39,7 +39,8 @@ CALIBRATION_BYTES = 512 * 1024 * 1024
 MIN_CPU_SECONDS = 3.0
 COPY_KERNEL = "copy"  # substring of the device copy kernel's name in the counter output
 KERNEL_NAMES = {"fused": "biwkv_row_kernel", "biwkv": "biwkv_row_kernel", "causal": "biwkv_row_kernel",
-                "qshift": "qshift_kernel"}
+                "gated": "biwkv_row_kernel", "qshift": "qshift_kernel", "mix": "qshift_mix_kernel"}
+N_MIX = 3  # mixing vectors of the mix entry (the R, K and V projection inputs)
 
 
 def kernel_source_hash() -> str:
@@ -55,6 +56,7 @@ def alg_bytes(entry: str, B: int, H: int, W: int, C: int, kv_bytes: int, shift: 
     """Algorithmic HBM bytes of one call: what the method must move.
 
     biwkv:  read k and v (kv_bytes each), write fp32 out, read w and u (causal: the same).
+    gated:  as biwkv, plus one read of the gate input r (kv_bytes).
     fused:  as biwkv, but the Q-Shift zero-filled sources are never read.
     qshift: read the in-grid sources, write every output (fp32).
     """
@@ -66,8 +68,12 @@ def alg_bytes(entry: str, B: int, H: int, W: int, C: int, kv_bytes: int, shift: 
         return 2 * kv_bytes * n + 4 * n + 8 * C
     if entry == "fused":
         return 2 * kv_bytes * (n - B * zero_per_b) + 4 * n + 8 * C
+    if entry == "gated":
+        return 3 * kv_bytes * n + 4 * n + 8 * C
     if entry == "qshift":
         return 4 * (n - B * zero_per_b) + 4 * n
+    if entry == "mix":  # x read once (its shifted reads are the same elements), N_MIX outputs
+        return 4 * n + 4 * N_MIX * n + 4 * N_MIX * C
     raise ValueError(entry)
 
 
@@ -105,6 +111,15 @@ def cpu_baseline(wl, entry: str) -> dict:
     u = wl.u.astype(np.float64)
     threads = oracle.max_threads()
     oracle.biwkv_rnn(k[:, :64], v[:, :64], w, u, threads=threads)  # warm the library and threads
+    if entry == "mix":
+        mu = _mix_vectors(wl.C)
+        t0 = time.perf_counter()
+        oracle.qshift_mix(wl.k, mu, wl.H, wl.W, wl.shift, wl.gamma)
+        dt = time.perf_counter() - t0
+        elems = wl.B * wl.T * wl.C
+        return {"value": elems / dt / 1e9, "unit": "Gtoken*ch/s", "cores": 1, "kind": "oracle",
+                "seconds": dt, "cpu": _cpu_model(),
+                "sample": f"whole workload ({wl.B}x{wl.T}x{wl.C}), {N_MIX} mixes; numpy float64 oracle"}
     if entry == "qshift":
         x32 = wl.k
         t0 = time.perf_counter()
@@ -124,6 +139,8 @@ def cpu_baseline(wl, entry: str) -> dict:
             oracle.biwkv_rnn(ks, vs, w, u, threads=threads)
         elif entry == "causal":
             oracle.biwkv_causal_rnn(k, v, w, u, threads=threads)
+        elif entry == "gated":
+            oracle.biwkv_gated(k, v, _gate_input(wl).astype(np.float64), w, u, threads=threads)
         else:
             oracle.biwkv_rnn(k, v, w, u, threads=threads)
         reps += 1
@@ -135,7 +152,25 @@ def cpu_baseline(wl, entry: str) -> dict:
             "kind": "oracle", "seconds": dt, "repetitions": reps, "cpu": _cpu_model(),
             "sample": f"whole workload ({wl.B}x{wl.T}x{wl.C}) x{reps}; float64 "
                       + ("two-state causal RNN oracle" if entry == "causal" else "four-state RNN oracle")
+                      + (" times the sigmoid gate" if entry == "gated" else "")
                       + (" after the oracle Q-Shift of k and v" if entry == "fused" else "")}
+
+
+def _gate_input(wl):
+    """A seeded gate input r for the gated entry: N(0, 3^2) drawn in float64, rounded to the
+    storage type of k (here bf16 values)."""
+    import numpy as np
+
+    import workloads
+    g = np.random.Generator(np.random.PCG64(404))
+    r = (g.standard_normal((wl.B, wl.T, wl.C)) * 3.0).astype(np.float32)
+    return workloads.bf16_bits_to_f32(workloads.round_to_bf16_bits(r)) if wl.dtype == "bf16" else r
+
+
+def _mix_vectors(C: int):
+    """Seeded mixing vectors mu [N_MIX, C] in [0, 1) for the mix entry."""
+    import numpy as np
+    return np.random.Generator(np.random.PCG64(405)).uniform(0, 1, (N_MIX, C)).astype(np.float32)
 
 
 def _rotation(bytes_per_set: int) -> int:
@@ -165,8 +200,15 @@ def run_bench(args) -> dict:
     ks_ = [kb] + [kb.clone() for _ in range(R - 1)]
     vs_ = [vb] + [vb.clone() for _ in range(R - 1)]
     outs = [torch.empty((B, T, C), dtype=torch.float32, device=dev) for _ in range(R)]
-    if entry == "qshift":
+    if entry in ("qshift", "mix"):
         xs = [torch.from_numpy(wl.k).to(dev).contiguous() for _ in range(R)]
+    if entry == "mix":
+        mu = torch.from_numpy(_mix_vectors(C)).to(dev)
+        outs = [torch.empty((N_MIX, B, T, C), dtype=torch.float32, device=dev) for _ in range(R)]
+    if entry == "gated":
+        rb = torch.from_numpy(np.ascontiguousarray(workloads.round_to_bf16_bits(_gate_input(wl)))).view(
+            torch.bfloat16).to(dev)
+        rs_ = [rb] + [rb.clone() for _ in range(R - 1)]
 
     # One checked call per buffer set through the package, then the same C entry point called
     # with the already marshalled arguments (the timed loop measures the library, not Python).
@@ -190,6 +232,15 @@ def run_bench(args) -> dict:
             calls.append((cl.biwkv_causal_forward,
                           (ks_[r].data_ptr(), vs_[r].data_ptr(), w.data_ptr(), u.data_ptr(),
                            outs[r].data_ptr(), B, T, C, lib.BF16, stream.cuda_stream)))
+        elif entry == "gated":
+            lib.biwkv_gated_forward(ks_[r], vs_[r], rs_[r], w, u, out=outs[r])
+            calls.append((cl.biwkv_gated_forward,
+                          (ks_[r].data_ptr(), vs_[r].data_ptr(), rs_[r].data_ptr(), w.data_ptr(),
+                           u.data_ptr(), outs[r].data_ptr(), B, T, C, lib.BF16, stream.cuda_stream)))
+        elif entry == "mix":
+            lib.qshift_mix(xs[r], mu, H, W, wl.shift, wl.gamma, out=outs[r])
+            calls.append((cl.qshift_mix, (xs[r].data_ptr(), mu.data_ptr(), outs[r].data_ptr(), B, H, W,
+                                          C, N_MIX, wl.shift, wl.gamma, stream.cuda_stream)))
         else:
             lib.qshift(xs[r], H, W, wl.shift, wl.gamma, out=outs[r])
             calls.append((cl.qshift, (xs[r].data_ptr(), outs[r].data_ptr(), B, H, W, C, wl.shift,
@@ -223,7 +274,7 @@ def run_bench(args) -> dict:
     avg_ms = start.elapsed_time(end) / args.steps
     ms_per_step = wall * 1e3 / args.steps
     elems = B * T * C
-    kv_bytes = 4 if entry == "qshift" else 2
+    kv_bytes = 4 if entry in ("qshift", "mix") else 2
     ab = alg_bytes(entry, B, H, W, C, kv_bytes, wl.shift, wl.gamma)
     achieved = ab / (avg_ms * 1e-3) / 1e9
     counters = _load_counters()
@@ -231,7 +282,7 @@ def run_bench(args) -> dict:
     if counters is not None and entry in counters.get("entries", {}):
         traffic = counters["entries"][entry]["hbm_bytes_per_launch"]
     names = {"fused": "biwkv_qshift_forward", "biwkv": "biwkv_forward", "causal": "biwkv_causal_forward",
-             "qshift": "qshift"}
+             "gated": "biwkv_gated_forward", "qshift": "qshift", "mix": "qshift_mix"}
     return {
         "metric": "Bi-WKV fwd Gtoken*ch/s + achieved HBM GB/s (% peak) at T=4096 C=1024",
         "value": elems * args.steps / wall / 1e9,
@@ -246,7 +297,7 @@ def run_bench(args) -> dict:
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "entry": names[entry], "B": B, "T": T, "H": H, "W": W, "C": C,
-                   "kv_storage": "bf16" if entry != "qshift" else "f32", "shift": wl.shift,
+                   "kv_storage": "bf16" if entry not in ("qshift", "mix") else "f32", "shift": wl.shift,
                    "gamma": wl.gamma, "buffer_sets_rotated": R},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
@@ -346,7 +397,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--entry", choices=["fused", "biwkv", "causal", "qshift"], default="fused")
+    ap.add_argument("--entry", choices=["fused", "biwkv", "causal", "gated", "qshift", "mix"], default="fused")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize", metavar="DIR")

@@ -89,6 +89,17 @@ int biwkv_causal_forward(const void* k, const void* v, const float* w, const flo
                          int64_t B, int64_t T, int64_t C, int dtype, void* stream);
 
 /*
+ * Gated Bi-WKV, the spatial-mix output of Eq. (2) of the Vision-RWKV article before its output
+ * projection: out = sigmoid(r) * Bi-WKV(k, v), elementwise, with sigmoid(x) = 1 / (1 + e^{-x}).
+ *   r : [B, T, C] gate input (the R projection), storage type `dtype` like k and v, device memory;
+ *       must not overlap out.
+ * Other arguments, layout, ownership, scratch and errors are those of biwkv_forward, except that
+ * there is no 128-token fallback (a row whose chunks cannot all be resident returns _UNSUPPORTED).
+ */
+int biwkv_gated_forward(const void* k, const void* v, const void* r, const float* w, const float* u,
+                        float* out, int64_t B, int64_t T, int64_t C, int dtype, void* stream);
+
+/*
  * Q-Shift token shift X-dagger of the q_shift listing (LinXin's Blog, Vision-RWKV notes).
  *   x, out : [B, H*W, C] float32, device memory; values are moved bit for bit (NaN payloads,
  *            signed zeros and denormals are preserved); out must not overlap x.
@@ -98,6 +109,20 @@ int biwkv_causal_forward(const void* k, const void* v, const float* w, const flo
  */
 int qshift(const float* x, float* out, int64_t B, int64_t H, int64_t W, int64_t C, int shift,
            double gamma, void* stream);
+
+/*
+ * Q-Shift mixing, Eq. (9) of the Vision-RWKV article ("Quad-Directional Token Shift") as printed,
+ * once per mixing vector: out[j] = x + (1 - mu[j]) * X-dagger(x), j = 0 .. n_mix-1 (e.g. the R, K
+ * and V inputs of the spatial-mix projections), with X-dagger the gather of `qshift`.
+ *   x   : [B, H*W, C] float32, device memory.
+ *   mu  : [n_mix, C] float32, device memory.
+ *   out : [n_mix, B, H*W, C] float32, device memory; must not overlap x or mu.
+ *   n_mix : 0 .. 8. shift, gamma: as for qshift.
+ * fp32 arithmetic x + (1 - mu) * xd per element (the compiler may fuse the multiply-add).
+ * Errors: as qshift, plus _SHAPE for n_mix outside 0 .. 8.
+ */
+int qshift_mix(const float* x, const float* mu, float* out, int64_t B, int64_t H, int64_t W,
+               int64_t C, int n_mix, int shift, double gamma, void* stream);
 
 /*
  * Fused Q-Shift + Bi-WKV: out = Bi-WKV(Q-Shift(k), Q-Shift(v)) with T = H*W. The shift is applied

@@ -10,10 +10,12 @@ from ._lib import (  # noqa: F401
     BiwkvError,
     biwkv_causal_forward,
     biwkv_forward,
+    biwkv_gated_forward,
     biwkv_qshift_forward,
     header_symbols,
     load_library,
     qshift,
+    qshift_mix,
     status_codes,
     status_string,
     stream_fault_flags,

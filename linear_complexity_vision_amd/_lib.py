@@ -51,8 +51,13 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.biwkv_forward.restype = ctypes.c_int
     lib.biwkv_causal_forward.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P]
     lib.biwkv_causal_forward.restype = ctypes.c_int
+    lib.biwkv_gated_forward.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P]
+    lib.biwkv_gated_forward.restype = ctypes.c_int
     lib.qshift.argtypes = [_P, _P, _I64, _I64, _I64, _I64, ctypes.c_int, ctypes.c_double, _P]
     lib.qshift.restype = ctypes.c_int
+    lib.qshift_mix.argtypes = [_P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_int, ctypes.c_int,
+                               ctypes.c_double, _P]
+    lib.qshift_mix.restype = ctypes.c_int
     lib.biwkv_qshift_forward.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_int,
                                          ctypes.c_double, ctypes.c_int, _P]
     lib.biwkv_qshift_forward.restype = ctypes.c_int
@@ -155,6 +160,24 @@ def biwkv_causal_forward(k, v, w, u, out=None):
     return out
 
 
+def biwkv_gated_forward(k, v, r, w, u, out=None):
+    """Eq. (2) before the output projection: sigmoid(r) * Bi-WKV(k, v); r like k (same dtype)."""
+    torch = _torch()
+    dt = _check_bitc(k, v, w, u)
+    _require(r.is_cuda and r.shape == k.shape and r.dtype == k.dtype and r.is_contiguous(),
+             "r must be a contiguous tensor shaped and typed like k")
+    B, T, C = k.shape
+    if out is None:
+        out = torch.empty((B, T, C), dtype=torch.float32, device=k.device)
+    _require(out.shape == k.shape and out.dtype == torch.float32 and out.is_contiguous(),
+             "out must be a contiguous float32 [B, T, C] tensor")
+    with torch.cuda.device(k.device):
+        _check(load_library().biwkv_gated_forward(k.data_ptr(), v.data_ptr(), r.data_ptr(), w.data_ptr(),
+                                                  u.data_ptr(), out.data_ptr(), B, T, C, dt,
+                                                  _stream_handle(k.device)))
+    return out
+
+
 def biwkv_qshift_forward(k, v, w, u, H, W, shift=1, gamma=0.25, out=None):
     """Fused Bi-WKV(Q-Shift(k), Q-Shift(v)) on an H x W token grid (T = H * W)."""
     torch = _torch()
@@ -186,6 +209,28 @@ def qshift(x, H, W, shift=1, gamma=0.25, out=None):
     with torch.cuda.device(x.device):
         _check(load_library().qshift(x.data_ptr(), out.data_ptr(), B, H, W, C, int(shift),
                                      float(gamma), _stream_handle(x.device)))
+    return out
+
+
+def qshift_mix(x, mu, H, W, shift=1, gamma=0.25, out=None):
+    """Eq. (9) mixing: out[j] = x + (1 - mu[j]) * X-dagger(x); x [B, H*W, C], mu [J, C] float32
+    -> [J, B, H*W, C] float32."""
+    torch = _torch()
+    _require(x.is_cuda and mu.is_cuda, "x and mu must be on a HIP device")
+    _require(x.dtype == torch.float32 and x.dim() == 3 and x.is_contiguous(),
+             "x must be a contiguous float32 [B, N, C] tensor")
+    B, N, C = x.shape
+    _require(N == H * W, "N must equal H * W")
+    _require(mu.dtype == torch.float32 and mu.dim() == 2 and mu.shape[1] == C and mu.is_contiguous(),
+             "mu must be a contiguous float32 [J, C] tensor")
+    J = mu.shape[0]
+    if out is None:
+        out = torch.empty((J, B, N, C), dtype=torch.float32, device=x.device)
+    _require(out.shape == (J, B, N, C) and out.dtype == torch.float32 and out.is_contiguous(),
+             "out must be a contiguous float32 [J, B, N, C] tensor")
+    with torch.cuda.device(x.device):
+        _check(load_library().qshift_mix(x.data_ptr(), mu.data_ptr(), out.data_ptr(), B, H, W, C, J,
+                                         int(shift), float(gamma), _stream_handle(x.device)))
     return out
 
 

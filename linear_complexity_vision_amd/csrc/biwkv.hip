@@ -169,6 +169,7 @@ int check_qshift_params(int64_t H, int64_t W, int shift, double gamma) {
 }
 
 constexpr int64_t kMaxDim = (1ll << 31) - 1;
+constexpr int kMaxMix = 8;  // mixing vectors per qshift_mix call
 
 int check_bitc_shape(int64_t B, int64_t T, int64_t C) {
   if (B < 0 || T < 0 || C < 0) return BIWKV_ERR_SHAPE;
@@ -229,7 +230,7 @@ int launch_biwkv(BiwkvParams prm, int64_t B, int dev, void* stream) {
 
 // Tile kernel launch: rows of TILE channels, chunks of (NT / TILE) * L tokens. Returns 1 when
 // the shape is outside what the kernel addresses (the caller then uses the chunk-scan kernel).
-template <int DT, int TILE, int L, int NT, bool FUSED, bool PAIR, bool CAUSAL>
+template <int DT, int TILE, int L, int NT, bool FUSED, bool PAIR, bool CAUSAL, bool GATED>
 int launch_row(const BiwkvParams& bp, int64_t B, int dev, void* stream) {
   constexpr int CT = (NT / TILE) * L;
   const long long T = bp.T;
@@ -245,6 +246,7 @@ int launch_row(const BiwkvParams& bp, int64_t B, int dev, void* stream) {
   RowParams rp{};
   rp.k = bp.k;
   rp.v = bp.v;
+  rp.r = bp.r;
   rp.w = bp.w;
   rp.u = bp.u;
   rp.out = bp.out;
@@ -262,7 +264,7 @@ int launch_row(const BiwkvParams& bp, int64_t B, int dev, void* stream) {
   rp.total = static_cast<unsigned>(total);
   if (n_chunks > 1) {
     // The chunks of a row wait for each other: they must all fit on the device at once.
-    const void* kfn = reinterpret_cast<const void*>(&biwkv_row_kernel<DT, TILE, L, NT, FUSED, PAIR, CAUSAL>);
+    const void* kfn = reinterpret_cast<const void*>(&biwkv_row_kernel<DT, TILE, L, NT, FUSED, PAIR, CAUSAL, GATED>);
     std::lock_guard<std::mutex> lock(g_mu);
     int cap = 0;
     int rc = resident_capacity(dev, kfn, NT, &cap);
@@ -274,11 +276,11 @@ int launch_row(const BiwkvParams& bp, int64_t B, int dev, void* stream) {
     if (rc) return rc;
     rp.ctr = sc->ctr;
     rp.slots = sc->slots;
-    hipLaunchKernelGGL((biwkv_row_kernel<DT, TILE, L, NT, FUSED, PAIR, CAUSAL>),
+    hipLaunchKernelGGL((biwkv_row_kernel<DT, TILE, L, NT, FUSED, PAIR, CAUSAL, GATED>),
                        dim3(static_cast<unsigned>(total)), dim3(NT), 0,
                        static_cast<hipStream_t>(stream), rp);
   } else {
-    hipLaunchKernelGGL((biwkv_row_kernel<DT, TILE, L, NT, FUSED, PAIR, CAUSAL>),
+    hipLaunchKernelGGL((biwkv_row_kernel<DT, TILE, L, NT, FUSED, PAIR, CAUSAL, GATED>),
                        dim3(static_cast<unsigned>(total)), dim3(NT), 0,
                        static_cast<hipStream_t>(stream), rp);
   }
@@ -293,17 +295,17 @@ int launch_row(const BiwkvParams& bp, int64_t B, int dev, void* stream) {
 // data first and computes and writes while the other one still reads, so reads and writes
 // overlap. fp32 rows keep 1024 threads: at 32 tokens per lane their 512-thread chunks are short
 // and the exchange between them dominates.
-template <int DT, bool FUSED, bool PAIR, bool CAUSAL>
+template <int DT, bool FUSED, bool PAIR, bool CAUSAL, bool GATED>
 int try_row_shape(const BiwkvParams& bp, int64_t B, int dev, void* stream) {
   const long long T = bp.T;
   if constexpr (DT == BIWKV_BF16) {
-    if (T <= 256) return launch_row<DT, 64, 16, 1024, FUSED, PAIR, CAUSAL>(bp, B, dev, stream);
-    if (T <= 512) return launch_row<DT, 64, 32, 1024, FUSED, PAIR, CAUSAL>(bp, B, dev, stream);
-    if (T <= 1024) return launch_row<DT, 64, 64, 1024, FUSED, PAIR, CAUSAL>(bp, B, dev, stream);
-    return launch_row<DT, 64, 64, 512, FUSED, PAIR, CAUSAL>(bp, B, dev, stream);
+    if (T <= 256) return launch_row<DT, 64, 16, 1024, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream);
+    if (T <= 512) return launch_row<DT, 64, 32, 1024, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream);
+    if (T <= 1024) return launch_row<DT, 64, 64, 1024, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream);
+    return launch_row<DT, 64, 64, 512, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream);
   } else {
-    if (T <= 256) return launch_row<DT, 64, 16, 1024, FUSED, PAIR, CAUSAL>(bp, B, dev, stream);
-    return launch_row<DT, 64, 32, 1024, FUSED, PAIR, CAUSAL>(bp, B, dev, stream);
+    if (T <= 256) return launch_row<DT, 64, 16, 1024, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream);
+    return launch_row<DT, 64, 32, 1024, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream);
   }
 }
 
@@ -315,12 +317,12 @@ bool pairs_ok(const BiwkvParams& bp, bool fused) {
   return true;
 }
 
-template <int DT, bool FUSED, bool CAUSAL = false>
+template <int DT, bool FUSED, bool CAUSAL = false, bool GATED = false>
 int try_row(const BiwkvParams& bp, int64_t B, int dev, void* stream) {
   if constexpr (DT == BIWKV_BF16) {
-    if (pairs_ok(bp, FUSED)) return try_row_shape<DT, FUSED, true, CAUSAL>(bp, B, dev, stream);
+    if (pairs_ok(bp, FUSED)) return try_row_shape<DT, FUSED, true, CAUSAL, GATED>(bp, B, dev, stream);
   }
-  return try_row_shape<DT, FUSED, false, CAUSAL>(bp, B, dev, stream);
+  return try_row_shape<DT, FUSED, false, CAUSAL, GATED>(bp, B, dev, stream);
 }
 
 template <bool FUSED>
@@ -382,6 +384,33 @@ int biwkv_forward(const void* k, const void* v, const float* w, const float* u, 
   return dispatch_biwkv<false>(prm, B, dtype, vec2, dev, stream);
 }
 
+int biwkv_gated_forward(const void* k, const void* v, const void* r, const float* w, const float* u,
+                        float* out, int64_t B, int64_t T, int64_t C, int dtype, void* stream) {
+  int rc = validate_biwkv(k, v, w, u, out, B, T, C, dtype);
+  if (rc || !(B && T && C)) return rc;
+  if (!r) return BIWKV_ERR_NULL;
+  const size_t es = dtype == BIWKV_F32 ? 4 : 2;
+  if (!aligned(r, es)) return BIWKV_ERR_ALIGN;
+  const size_t n = static_cast<size_t>(B) * T * C;
+  if (ranges_overlap(out, n * 4, r, n * es)) return BIWKV_ERR_ALIAS;
+  int dev = 0;
+  rc = current_device(&dev);
+  if (rc) return rc;
+  BiwkvParams prm{};
+  prm.k = k;
+  prm.v = v;
+  prm.r = r;
+  prm.w = w;
+  prm.u = u;
+  prm.out = out;
+  prm.T = T;
+  prm.C = static_cast<int>(C);
+  // tile kernel only: a shape it does not address has no fallback
+  rc = dtype == BIWKV_F32 ? try_row<BIWKV_F32, false, false, true>(prm, B, dev, stream)
+                          : try_row<BIWKV_BF16, false, false, true>(prm, B, dev, stream);
+  return rc == 1 ? BIWKV_ERR_UNSUPPORTED : rc;
+}
+
 int biwkv_causal_forward(const void* k, const void* v, const float* w, const float* u, float* out,
                          int64_t B, int64_t T, int64_t C, int dtype, void* stream) {
   int rc = validate_biwkv(k, v, w, u, out, B, T, C, dtype);
@@ -437,6 +466,48 @@ int biwkv_qshift_forward(const void* k, const void* v, const float* w, const flo
   prm.g3 = static_cast<int>(g[2]);
   prm.g4 = static_cast<int>(g[3]);
   return dispatch_biwkv<true>(prm, B, dtype, vec2, dev, stream);
+}
+
+int qshift_mix(const float* x, const float* mu, float* out, int64_t B, int64_t H, int64_t W,
+               int64_t C, int n_mix, int shift, double gamma, void* stream) {
+  if (H < 0 || W < 0 || H > kMaxDim || W > kMaxDim) return BIWKV_ERR_SHAPE;
+  if (n_mix < 0 || n_mix > kMaxMix) return BIWKV_ERR_SHAPE;
+  int rc = check_bitc_shape(B, H * W, C);
+  if (rc) return rc;
+  const bool nonempty = B && H && W && C && n_mix;
+  if (nonempty && (!x || !mu || !out)) return BIWKV_ERR_NULL;
+  rc = check_qshift_params(H, W, shift, gamma);
+  if (rc || !nonempty) return rc;
+  if (!aligned(x, 4) || !aligned(mu, 4) || !aligned(out, 4)) return BIWKV_ERR_ALIGN;
+  const size_t n = static_cast<size_t>(B) * H * W * C;
+  const size_t out_bytes = n * 4 * static_cast<size_t>(n_mix);
+  if (ranges_overlap(out, out_bytes, x, n * 4) || ranges_overlap(out, out_bytes, mu, C * 4 * n_mix))
+    return BIWKV_ERR_ALIAS;
+  int dev = 0;
+  rc = current_device(&dev);
+  if (rc) return rc;
+  int64_t g[4];
+  group_bounds(C, gamma, g);
+  const bool vec4 = (C % 4 == 0) && (g[0] % 4 == 0) && (g[1] % 4 == 0) && (g[2] % 4 == 0) &&
+                    (g[3] % 4 == 0) && aligned(x, 16) && aligned(mu, 16) && aligned(out, 16);
+  const long long rows = B * H * W;
+  const long long items = rows * (vec4 ? C / 4 : C);
+  long long blocks = (items + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (vec4)
+    hipLaunchKernelGGL(qshift_mix_kernel<4>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
+                       x, mu, out, rows, static_cast<int>(H), static_cast<int>(W),
+                       static_cast<int>(C), n_mix, shift, static_cast<int>(g[0]),
+                       static_cast<int>(g[1]), static_cast<int>(g[2]), static_cast<int>(g[3]));
+  else
+    hipLaunchKernelGGL(qshift_mix_kernel<1>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
+                       x, mu, out, rows, static_cast<int>(H), static_cast<int>(W),
+                       static_cast<int>(C), n_mix, shift, static_cast<int>(g[0]),
+                       static_cast<int>(g[1]), static_cast<int>(g[2]), static_cast<int>(g[3]));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e);
+  return BIWKV_OK;
 }
 
 int qshift(const float* x, float* out, int64_t B, int64_t H, int64_t W, int64_t C, int shift,

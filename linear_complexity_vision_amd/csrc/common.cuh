@@ -32,6 +32,7 @@ struct Counters {
 struct BiwkvParams {
   const void* k;
   const void* v;
+  const void* r;         // gate input (gated entry only)
   const float* w;
   const float* u;
   float* out;

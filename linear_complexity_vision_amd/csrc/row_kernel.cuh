@@ -138,6 +138,7 @@ constexpr uint32_t kOutOfRange = 0x80000000u;
 struct RowParams {
   const void* k;
   const void* v;
+  const void* r;  // gate input of Eq. (2), [B, T, C] like k (gated entry only)
   const float* w;
   const float* u;
   float* out;
@@ -411,12 +412,50 @@ __device__ __forceinline__ void group_fold(Agg& a, Agg& b, int tg) {
   }
 }
 
+// Gate inputs r of Eq. (2) for the SB tokens of a lane's sub-block q (raw bits: an fp32 value, or
+// a bf16 value in the low half), through per-token resources like the unfused k, v loads.
+template <int DT, int TILE, int L, int NT, int SB>
+struct RowGate {
+  const char* base;   // the batch item's r
+  int c0, avail;      // chunk start (bytes) and bytes from there to the item's end
+  uint32_t lane_off;  // this lane's offset from the chunk start (out of range when masked)
+  int row_bytes;
+  __device__ __forceinline__ void init(const RowParams& p, const RowLane& ln) {
+    constexpr int ES = DT == BIWKV_F32 ? 4 : 2;
+    constexpr int CT = (NT / TILE) * L;
+    const long long plane = p.T * p.C;
+    base = reinterpret_cast<const char*>(
+        uniform_u64(reinterpret_cast<unsigned long long>(p.r) + ln.b * plane * ES));
+    row_bytes = p.C * ES;
+    c0 = ln.chunk * CT * row_bytes;
+    avail = static_cast<int>(plane * ES) - c0;
+    lane_off = ln.on ? static_cast<uint32_t>(ln.g * L) * row_bytes + static_cast<uint32_t>(ln.ch) * ES
+                     : kOutOfRange;
+  }
+  __device__ __forceinline__ void load(int q, uint32_t (&dst)[SB]) const {
+#pragma unroll
+    for (int i = 0; i < SB; ++i) {
+      const int adv = (q * SB + i) * row_bytes;
+      const int left = avail - adv;
+      const __amdgpu_buffer_rsrc_t rr =
+          make_rsrc(base + c0 + adv, static_cast<uint32_t>(left > 0 ? left : 0));
+      if constexpr (DT == BIWKV_F32)
+        dst[i] = __builtin_amdgcn_raw_buffer_load_b32(rr, lane_off, 0, kStream);
+      else
+        dst[i] = __builtin_amdgcn_raw_buffer_load_b16(rr, lane_off, 0, kStream);
+    }
+  }
+  __device__ __forceinline__ static float value(uint32_t bits) {
+    return __uint_as_float(DT == BIWKV_F32 ? bits : (bits << 16));
+  }
+};
+
 template <int DT, int TILE, int L, bool PAIR>
 using RowStore = std::conditional_t<PAIR, RowKVPair<L>, RowKV<DT, L>>;
 
 // CAUSAL: the causal attention (Eq. (7) without the backward states b, d): only forward sums
 // are formed, scanned and exchanged, and the output comes out of the forward sweep.
-template <int DT, int TILE, int L, int NT, bool FUSED, bool PAIR, bool WIDE, bool CAUSAL>
+template <int DT, int TILE, int L, int NT, bool FUSED, bool PAIR, bool WIDE, bool CAUSAL, bool GATED>
 __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
                                          RowStore<DT, TILE, L, PAIR>& kv, float* lds,
                                          const unsigned* sh_epoch) {
@@ -530,6 +569,13 @@ __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
     }
   }
   kv.fence();
+  // GATED: the gate inputs of sub-block 0 load during the scan and the exchange
+  RowGate<DT, TILE, L, NT, SB> gate;
+  uint32_t r_next[GATED ? SB : 1];
+  if constexpr (GATED) {
+    gate.init(p, ln);
+    gate.load(0, r_next);
+  }
 
   // ---- scans over the groups of each channel. The lane sums go to LDS group-major; lane
   //      (tg, tc) = (tid % GROUPS, tid / GROUPS) then takes group tg of channel tc, so the groups
@@ -679,6 +725,12 @@ __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
 #pragma unroll
     for (int q = 0; q < NSB; ++q) {
       float ph[SB];
+      uint32_t r_cur[GATED ? SB : 1];
+      if constexpr (GATED) {  // this sub-block's gate inputs; the next one's start loading
+#pragma unroll
+        for (int i = 0; i < SB; ++i) r_cur[i] = r_next[i];
+        if (q + 1 < NSB) gate.load(q + 1, r_next);
+      }
 #pragma unroll
       for (int i = 0; i < SB; ++i) {
         const int t = q * SB + i;
@@ -703,7 +755,14 @@ __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
         const float2 ab2 = lds_ab[i][tid];
         const float num = fmaf(-Ds, vf, ab2.x + Bs);
         const float den = ab2.y + Ds;  // >= the lane's largest term, a normal number
-        const float y = fmaf(num, fast_rcp(den), vf);
+        float y;
+        if constexpr (GATED) {
+          // sigma(r) y = (v den + num) / (den (1 + e^{-r})): one reciprocal for both divisions
+          const float er = fast_exp2(-kLog2e * gate.value(r_cur[i]));
+          y = fmaf(vf, den, num) * fast_rcp(den * (1.f + er));
+        } else {
+          y = fmaf(num, fast_rcp(den), vf);
+        }
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), orr, out0 + t * row_bytes, 0,
                                               kStream);
         Bs = fmaf(Bs, lam, ph[i] * vf);
@@ -744,6 +803,15 @@ __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
         xs = agg_add(agg_shift(xs, 1.f, D), Agg{kf * kLog2e, vf, 1.f});
       }
       Agg ys = agg_add(cap[q], agg_shift(Y, static_cast<float>(L - (q + 1) * SB), D));
+      uint32_t r_cur[GATED ? SB : 1];
+      if constexpr (GATED) {
+        if (q == 0) {
+#pragma unroll
+          for (int i = 0; i < SB; ++i) r_cur[i] = r_next[i];
+        } else {
+          gate.load(q, r_cur);
+        }
+      }
 #pragma unroll
       for (int i = SB - 1; i >= 0; --i) {
         const int t = q * SB + i;
@@ -756,7 +824,13 @@ __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
         const float e = fast_exp2(ks - Mt);
         const float num = ab2.x * sa + fmaf(-ys.G, vf, ys.F) * sb;
         const float den = sa + ys.G * sb + e;
-        const float y = fmaf(num, fast_rcp(den), vf);
+        float y;
+        if constexpr (GATED) {
+          const float er = fast_exp2(-kLog2e * gate.value(r_cur[i]));
+          y = fmaf(vf, den, num) * fast_rcp(den * (1.f + er));
+        } else {
+          y = fmaf(num, fast_rcp(den), vf);
+        }
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), orr, out0 + t * row_bytes, 0,
                                               kStream);
         ys = agg_add(agg_shift(ys, 1.f, D), Agg{kl, vf, 1.f});
@@ -769,20 +843,21 @@ __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
 // out of line gives it its own register allocation, so its spills never touch the fast form. It
 // reads the parameters from the kernel's argument segment (a pointer, so the kernel keeps them in
 // scalar registers instead of building a private copy).
-template <int DT, int TILE, int L, int NT, bool FUSED, bool PAIR, bool CAUSAL>
+template <int DT, int TILE, int L, int NT, bool FUSED, bool PAIR, bool CAUSAL, bool GATED>
 __device__ __noinline__ void row_body_wide(const RowParams* args, float* lds, unsigned unit,
                                            const unsigned* sh_epoch) {
   const RowParams p = *args;
   const RowLane ln = row_lane<TILE, L, NT>(p, unit);
   RowStore<DT, TILE, L, PAIR> kv;
   row_load<DT, TILE, L, NT, FUSED, PAIR>(p, ln, kv);
-  row_body<DT, TILE, L, NT, FUSED, PAIR, true, CAUSAL>(p, ln, kv, lds, sh_epoch);
+  row_body<DT, TILE, L, NT, FUSED, PAIR, true, CAUSAL, GATED>(p, ln, kv, lds, sh_epoch);
 }
 
-template <int DT, int TILE, int L, int NT, bool FUSED, bool PAIR, bool CAUSAL>
+template <int DT, int TILE, int L, int NT, bool FUSED, bool PAIR, bool CAUSAL, bool GATED>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4)))
     biwkv_row_kernel(RowParams p) {
   static_assert(!PAIR || (DT == BIWKV_BF16 && TILE % 2 == 0), "pairs are bf16 channel pairs");
+  static_assert(!(GATED && (CAUSAL || FUSED)), "the gate is built for the bidirectional entry");
   static_assert(64 % TILE == 0 || TILE % 64 == 0, "bad row-kernel tile");
   static_assert(TILE <= 64, "a wavefront must hold every channel of the tile");
   static_assert(NT % 256 == 0 && NT <= 1024 && NT >= 2 * TILE, "bad row-kernel workgroup size");
@@ -820,11 +895,11 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4)))
     if (__ballot(wide_lane) != 0ull) {
       // the kernel's only argument is p, at the start of the argument segment
       const auto* args = (const RowParams*)(__builtin_amdgcn_kernarg_segment_ptr());
-      row_body_wide<DT, TILE, L, NT, FUSED, PAIR, CAUSAL>(args, lds, unit, &sh_epoch);
+      row_body_wide<DT, TILE, L, NT, FUSED, PAIR, CAUSAL, GATED>(args, lds, unit, &sh_epoch);
     } else {
       RowStore<DT, TILE, L, PAIR> kv;
       row_load<DT, TILE, L, NT, FUSED, PAIR>(p, ln, kv);
-      row_body<DT, TILE, L, NT, FUSED, PAIR, false, CAUSAL>(p, ln, kv, lds, &sh_epoch);
+      row_body<DT, TILE, L, NT, FUSED, PAIR, false, CAUSAL, GATED>(p, ln, kv, lds, &sh_epoch);
     }
   }
   if (!valid && tid == 0) row_retire(p);  // (a valid workgroup retires after its exchange)

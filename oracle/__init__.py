@@ -193,10 +193,12 @@ def sigmoid(x):
         return 1.0 / (1.0 + np.exp(-x))
 
 
-def biwkv_gated(k, v, r, w, u, with_scale=False, threads=0):
+def biwkv_gated(k, v, r, w, u, with_scale=False, threads=0, use_sum=False):
     """Eq. (2)'s gated attention output before the output projection: sigma(R) * Bi-WKV(K, V)
-    ("OpenGVLab&港中文&复旦&南大&清华提出Vision-RWKV Backbone", spatial-mix block, Eq. (2))."""
-    y, s = biwkv_rnn(k, v, w, u, with_scale=True, threads=threads)
+    ("OpenGVLab&港中文&复旦&南大&清华提出Vision-RWKV Backbone", spatial-mix block, Eq. (2)).
+    Bi-WKV from the RNN form, or from the summation form (use_sum: any w, small sizes)."""
+    fn = biwkv_sum if use_sum else biwkv_rnn
+    y, s = fn(k, v, w, u, with_scale=True, threads=threads)
     gate = sigmoid(r)
     return (gate * y, gate * s) if with_scale else gate * y
 

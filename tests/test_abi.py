@@ -124,3 +124,31 @@ def test_causal_forward_validation(L):
     assert causal(k=K + 2) == _code("BIWKV_ERR_ALIGN")
     assert causal(out=V + 4) == _code("BIWKV_ERR_ALIAS")
     assert causal(B=0) == 0
+
+
+def test_qshift_mix_validation(L):
+    def mix(x=K, mu=WP, out=OUT, B=1, H=2, W=4, C=4, n_mix=3, shift=1, gamma=0.25):
+        return L.qshift_mix(x, mu, out, B, H, W, C, n_mix, shift, gamma, None)
+
+    assert mix(n_mix=9) == _code("BIWKV_ERR_SHAPE")
+    assert mix(n_mix=-1) == _code("BIWKV_ERR_SHAPE")
+    assert mix(mu=None) == _code("BIWKV_ERR_NULL")
+    assert mix(gamma=0.5) == _code("BIWKV_ERR_PARAM")
+    assert mix(out=K + 64) == _code("BIWKV_ERR_ALIAS")
+    assert mix(mu=OUT + 4 * 8) == _code("BIWKV_ERR_ALIAS")
+    assert mix(x=K + 2) == _code("BIWKV_ERR_ALIGN")
+    assert mix(n_mix=0, mu=None, out=None) == 0
+
+
+def test_gated_forward_validation(L):
+    R = 0x50000000
+
+    def gated(k=K, v=V, r=R, w=WP, u=UP, out=OUT, B=2, T=8, C=4, dtype=lib.F32):
+        return L.biwkv_gated_forward(k, v, r, w, u, out, B, T, C, dtype, None)
+
+    assert gated(r=None) == _code("BIWKV_ERR_NULL")
+    assert gated(r=R + 2) == _code("BIWKV_ERR_ALIGN")
+    assert gated(r=R + 1, dtype=lib.BF16) == _code("BIWKV_ERR_ALIGN")
+    assert gated(out=R) == _code("BIWKV_ERR_ALIAS")
+    assert gated(dtype=9) == _code("BIWKV_ERR_DTYPE")
+    assert gated(B=0, r=None) == 0
