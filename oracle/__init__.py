@@ -14,6 +14,9 @@ Functions follow the pages (cited by title and equation):
 * ``qshift``         — the q_shift function of "LinXin's Blog" Vision-RWKV notes (token shift on
   the H x W grid, groups at int(C*gamma*j), zero fill, remainder copied).
 * ``biwkv_qshift``   — the fused composition Bi-WKV(X†(k), X†(v)).
+* ``biwkv_backward_sum`` / ``biwkv_backward_rnn`` — gradients of Eq. (5) (the article says the
+  backward pass is an O(TC) recurrence; its formulas are not on the pages): the definition written
+  out, and the linear-time form as decayed prefix / suffix sums.
 * ``sigmoid`` / ``biwkv_gated`` — Eq. (2) of the same article: the attention output gated by
   sigma(R) (elementwise) before the output projection.
 * ``qshift_mix``     — Eq. (9) as printed: X + (1 - mu) X-dagger for each mixing vector mu.
@@ -63,8 +66,11 @@ def _load():
         lib.oracle_qshift.argtypes = [_P, _P, _I64, _I64, _I64, _I64, _I64, ctypes.c_double]
         lib.oracle_biwkv_causal_sum.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, ctypes.c_int]
         lib.oracle_biwkv_causal_rnn.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, ctypes.c_int]
+        lib.oracle_biwkv_backward_sum.argtypes = [_P] * 5 + [_I64] * 3 + [_P] * 8 + [ctypes.c_int]
+        lib.oracle_biwkv_backward_rnn.argtypes = [_P] * 5 + [_I64] * 3 + [_P] * 4 + [ctypes.c_int]
         for f in (lib.oracle_biwkv_sum, lib.oracle_biwkv_rnn, lib.oracle_biwkv_rnn_literal, lib.oracle_qshift,
-                  lib.oracle_biwkv_causal_sum, lib.oracle_biwkv_causal_rnn):
+                  lib.oracle_biwkv_causal_sum, lib.oracle_biwkv_causal_rnn, lib.oracle_biwkv_backward_sum,
+                  lib.oracle_biwkv_backward_rnn):
             f.restype = ctypes.c_int
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -184,6 +190,39 @@ def qshift_f64(x, H, W, shift=1, gamma=0.25):
     if not np.array_equal(x32.astype(np.float64), np.asarray(x, dtype=np.float64), equal_nan=True):
         raise ValueError("qshift_f64 needs values exactly representable in float32")
     return qshift(x32, H, W, shift, gamma).astype(np.float64)
+
+
+def biwkv_backward_sum(k, v, w, u, g, with_scale=False, threads=0):
+    """Gradients of Eq. (5) from the definition (quadratic): returns dk, dv [B, T, C] and dw, du [C]
+    (summed over the batch); with_scale also returns the sums of absolute terms of each."""
+    k, v, w, u, B, T, C = _check_bitc(k, v, w, u)
+    g = _f64(g)
+    if g.shape != k.shape:
+        raise ValueError("g must be [B, T, C]")
+    dk, dv = np.empty_like(k), np.empty_like(k)
+    dw, du = np.empty(C), np.empty(C)
+    sc = [np.empty_like(k), np.empty_like(k), np.empty(C), np.empty(C)] if with_scale else [None] * 4
+    rc = _load().oracle_biwkv_backward_sum(_ptr(k), _ptr(v), _ptr(w), _ptr(u), _ptr(g), B, T, C,
+                                           _ptr(dk), _ptr(dv), _ptr(dw), _ptr(du),
+                                           *[(_ptr(a) if a is not None else None) for a in sc], int(threads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_biwkv_backward_sum failed ({rc})")
+    return (dk, dv, dw, du, *sc) if with_scale else (dk, dv, dw, du)
+
+
+def biwkv_backward_rnn(k, v, w, u, g, threads=0):
+    """The same gradients in linear time (decayed prefix / suffix sums): dk, dv, dw, du."""
+    k, v, w, u, B, T, C = _check_bitc(k, v, w, u)
+    g = _f64(g)
+    if g.shape != k.shape:
+        raise ValueError("g must be [B, T, C]")
+    dk, dv = np.empty_like(k), np.empty_like(k)
+    dw, du = np.empty(C), np.empty(C)
+    rc = _load().oracle_biwkv_backward_rnn(_ptr(k), _ptr(v), _ptr(w), _ptr(u), _ptr(g), B, T, C,
+                                           _ptr(dk), _ptr(dv), _ptr(dw), _ptr(du), int(threads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_biwkv_backward_rnn failed ({rc})")
+    return dk, dv, dw, du
 
 
 def sigmoid(x):

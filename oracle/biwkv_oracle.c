@@ -366,6 +366,242 @@ int oracle_biwkv_causal_rnn(const double* k, const double* v, const double* w, c
 }
 
 /*
+ * OB1 — gradients of Eq. (5) of [VRWKV] (the pages state that the backward pass is an O(TC)
+ * recurrence but do not print it), written out from the definition. With the weights
+ * p_ti = exp(s_ti) / sum_j exp(s_tj) of Eq. (5) (s_ti = -((|t-i|-1)/T) w + k_i, s_tt = u + k_t)
+ * and y_t = sum_i p_ti v_i, the upstream gradient g_t = dL/dy_t gives
+ *   dv_i = sum_t g_t p_ti
+ *   dk_i = sum_t g_t p_ti (v_i - y_t)
+ *   du   = sum_t g_t p_tt (v_t - y_t)                                 (summed over b)
+ *   dw   = sum_t sum_{i != t} g_t p_ti (v_i - y_t) * (-(|t-i|-1)/T)    (summed over b)
+ * because dy_t/ds_ti = p_ti (v_i - y_t). Quadratic in T. Also returns magnitude scales (the same
+ * sums of absolute values of each term) for the tests' error metric; any scale pointer may be NULL.
+ */
+int oracle_biwkv_backward_sum(const double* k, const double* v, const double* w, const double* u,
+                              const double* g, int64_t B, int64_t T, int64_t C, double* dk,
+                              double* dv, double* dw, double* du, double* sdk, double* sdv,
+                              double* sdw, double* sdu, int nthreads) {
+    if (!k || !v || !w || !u || !g || !dk || !dv || !dw || !du || B < 0 || T < 0 || C < 0)
+        return ORC_ERR_ARG;
+    for (int64_t c = 0; c < C; ++c) {
+        dw[c] = du[c] = 0.0;
+        if (sdw) sdw[c] = 0.0;
+        if (sdu) sdu[c] = 0.0;
+    }
+    if (B == 0 || T == 0 || C == 0) return ORC_OK;
+    set_threads(nthreads);
+    int failed = 0;
+    /* per (c) accumulation of dw, du over b happens after the parallel loop, in b order */
+    double* pw = (double*)calloc((size_t)(B * C), sizeof(double));
+    double* pu = (double*)calloc((size_t)(B * C), sizeof(double));
+    double* psw = (double*)calloc((size_t)(B * C), sizeof(double));
+    double* psu = (double*)calloc((size_t)(B * C), sizeof(double));
+    if (!pw || !pu || !psw || !psu) {
+        free(pw); free(pu); free(psw); free(psu);
+        return ORC_ERR_NOMEM;
+    }
+#pragma omp parallel
+    {
+        double* kc = (double*)malloc(sizeof(double) * (size_t)T);
+        double* vc = (double*)malloc(sizeof(double) * (size_t)T);
+        double* gc = (double*)malloc(sizeof(double) * (size_t)T);
+        double* p = (double*)malloc(sizeof(double) * (size_t)(T * T));
+        double* y = (double*)malloc(sizeof(double) * (size_t)T);
+        if (!kc || !vc || !gc || !p || !y) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t bc = 0; bc < B * C; ++bc) {
+                const int64_t b = bc / C, c = bc % C;
+                gather_col(k, b, c, T, C, kc);
+                gather_col(v, b, c, T, C, vc);
+                gather_col(g, b, c, T, C, gc);
+                const double wc = w[c], uc = u[c], Td = (double)T;
+                /* the weights p_ti of every output t */
+                for (int64_t t = 0; t < T; ++t) {
+                    double* pt = p + t * T;
+                    double M = -INFINITY;
+                    for (int64_t i = 0; i < T; ++i) {
+                        const int64_t dist = (i > t) ? (i - t) : (t - i);
+                        pt[i] = (i == t) ? uc + kc[i] : -(((double)(dist - 1)) / Td) * wc + kc[i];
+                        if (pt[i] > M) M = pt[i];
+                    }
+                    double den = 0.0, num = 0.0;
+                    for (int64_t i = 0; i < T; ++i) {
+                        pt[i] = exp(pt[i] - M);
+                        den += pt[i];
+                    }
+                    for (int64_t i = 0; i < T; ++i) {
+                        pt[i] /= den;
+                        num += pt[i] * vc[i];
+                    }
+                    y[t] = num;
+                }
+                double dwc = 0.0, duc = 0.0, swc = 0.0, suc = 0.0;
+                for (int64_t i = 0; i < T; ++i) {
+                    double dvi = 0.0, dki = 0.0, svi = 0.0, ski = 0.0;
+                    for (int64_t t = 0; t < T; ++t) {
+                        const double gp = gc[t] * p[t * T + i];
+                        const double term = gp * (vc[i] - y[t]);
+                        dvi += gp;
+                        svi += fabs(gp);
+                        dki += term;
+                        ski += fabs(term);
+                        if (t == i) {
+                            duc += term;
+                            suc += fabs(term);
+                        } else {
+                            const int64_t dist = (i > t) ? (i - t) : (t - i);
+                            const double dterm = term * (-((double)(dist - 1)) / Td);
+                            dwc += dterm;
+                            swc += fabs(dterm);
+                        }
+                    }
+                    const int64_t o = (b * T + i) * C + c;
+                    dv[o] = dvi;
+                    dk[o] = dki;
+                    if (sdv) sdv[o] = svi;
+                    if (sdk) sdk[o] = ski;
+                }
+                pw[b * C + c] = dwc;
+                pu[b * C + c] = duc;
+                psw[b * C + c] = swc;
+                psu[b * C + c] = suc;
+            }
+        }
+        free(kc);
+        free(vc);
+        free(gc);
+        free(p);
+        free(y);
+    }
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t c = 0; c < C; ++c) {
+            dw[c] += pw[b * C + c];
+            du[c] += pu[b * C + c];
+            if (sdw) sdw[c] += psw[b * C + c];
+            if (sdu) sdu[c] += psu[b * C + c];
+        }
+    free(pw);
+    free(pu);
+    free(psw);
+    free(psu);
+    return failed ? ORC_ERR_NOMEM : ORC_OK;
+}
+
+/*
+ * OB2 — the same gradients in linear time, as decayed prefix / suffix sums (float64, valid while
+ * lam^T and exp(u + k - kappa) stay inside float64, like O2). With lam = exp(-w/T),
+ * e_i = exp(k_i - kappa), the forward states of Eq. (6)
+ *   a_j = sum_{i<j} lam^{j-1-i} e_i v_i,  c_j = same with 1,  b_j = sum_{i>j} lam^{i-j-1} e_i v_i,  d_j
+ * and D_j = c_j + d_j + e^{u} e_j, y_j from Eq. (7), put q_t = g_t / D_t and r_t = q_t y_t. Then
+ *   dv_i = e_i (Qpre_i + Qsuf_i + e^{u} q_i),   dk_i = v_i dv_i - e_i (Rpre_i + Rsuf_i + e^{u} r_i)
+ *   du   = sum_t e^{u} e_t (q_t v_t - r_t)
+ * with Qpre_i = sum_{t<i} lam^{i-1-t} q_t and Qsuf_i = sum_{t>i} lam^{t-i-1} q_t (R alike), and,
+ * writing |t-i|-1 as the number of tokens strictly between t and i and splitting lam^{|t-i|-1}
+ * at each such token j,
+ *   dw = -(lam / T) sum_j ( b_j Qpre_j - d_j Rpre_j + a_j Qsuf_j - c_j Rsuf_j ).
+ * (kappa cancels: q carries 1/exp(kappa), the states exp(kappa).)
+ */
+int oracle_biwkv_backward_rnn(const double* k, const double* v, const double* w, const double* u,
+                              const double* g, int64_t B, int64_t T, int64_t C, double* dk,
+                              double* dv, double* dw, double* du, int nthreads) {
+    if (!k || !v || !w || !u || !g || !dk || !dv || !dw || !du || B < 0 || T < 0 || C < 0)
+        return ORC_ERR_ARG;
+    for (int64_t c = 0; c < C; ++c) dw[c] = du[c] = 0.0;
+    if (B == 0 || T == 0 || C == 0) return ORC_OK;
+    set_threads(nthreads);
+    int failed = 0;
+    double* pw = (double*)calloc((size_t)(B * C), sizeof(double));
+    double* pu = (double*)calloc((size_t)(B * C), sizeof(double));
+    if (!pw || !pu) {
+        free(pw);
+        free(pu);
+        return ORC_ERR_NOMEM;
+    }
+#pragma omp parallel
+    {
+        double* buf = (double*)malloc(sizeof(double) * (size_t)T * 14);
+        if (!buf) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+            double *kc = buf, *vc = buf + T, *gc = buf + 2 * T, *e = buf + 3 * T;
+            double *a = buf + 4 * T, *cc = buf + 5 * T, *bb = buf + 6 * T, *d = buf + 7 * T;
+            double *q = buf + 8 * T, *r = buf + 9 * T, *qp = buf + 10 * T, *rp = buf + 11 * T;
+            double *qs = buf + 12 * T, *rs = buf + 13 * T;
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t bc = 0; bc < B * C; ++bc) {
+                const int64_t b = bc / C, c = bc % C;
+                gather_col(k, b, c, T, C, kc);
+                gather_col(v, b, c, T, C, vc);
+                gather_col(g, b, c, T, C, gc);
+                double kappa = -INFINITY;
+                for (int64_t t = 0; t < T; ++t)
+                    if (kc[t] > kappa) kappa = kc[t];
+                const double lam = exp(-w[c] / (double)T), eu = exp(u[c]);
+                for (int64_t t = 0; t < T; ++t) e[t] = exp(kc[t] - kappa);
+                double A = 0.0, Cs = 0.0;
+                for (int64_t t = 0; t < T; ++t) {
+                    a[t] = A;
+                    cc[t] = Cs;
+                    A = lam * A + e[t] * vc[t];
+                    Cs = lam * Cs + e[t];
+                }
+                double Bs = 0.0, D = 0.0;
+                for (int64_t t = T - 1; t >= 0; --t) {
+                    bb[t] = Bs;
+                    d[t] = D;
+                    Bs = lam * Bs + e[t] * vc[t];
+                    D = lam * D + e[t];
+                }
+                for (int64_t t = 0; t < T; ++t) {
+                    const double den = cc[t] + d[t] + eu * e[t];
+                    const double y = (a[t] + bb[t] + eu * e[t] * vc[t]) / den;
+                    q[t] = gc[t] / den;
+                    r[t] = q[t] * y;
+                }
+                double Q = 0.0, R = 0.0;
+                for (int64_t t = 0; t < T; ++t) {
+                    qp[t] = Q;
+                    rp[t] = R;
+                    Q = lam * Q + q[t];
+                    R = lam * R + r[t];
+                }
+                Q = R = 0.0;
+                for (int64_t t = T - 1; t >= 0; --t) {
+                    qs[t] = Q;
+                    rs[t] = R;
+                    Q = lam * Q + q[t];
+                    R = lam * R + r[t];
+                }
+                double dwc = 0.0, duc = 0.0;
+                for (int64_t i = 0; i < T; ++i) {
+                    const double dvi = e[i] * (qp[i] + qs[i] + eu * q[i]);
+                    const int64_t o = (b * T + i) * C + c;
+                    dv[o] = dvi;
+                    dk[o] = vc[i] * dvi - e[i] * (rp[i] + rs[i] + eu * r[i]);
+                    duc += eu * e[i] * (q[i] * vc[i] - r[i]);
+                    dwc += bb[i] * qp[i] - d[i] * rp[i] + a[i] * qs[i] - cc[i] * rs[i];
+                }
+                pw[b * C + c] = -(lam / (double)T) * dwc;
+                pu[b * C + c] = duc;
+            }
+        }
+        free(buf);
+    }
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t c = 0; c < C; ++c) {
+            dw[c] += pw[b * C + c];
+            du[c] += pu[b * C + c];
+        }
+    free(pw);
+    free(pu);
+    return failed ? ORC_ERR_NOMEM : ORC_OK;
+}
+
+/*
  * Channel-group boundaries of the q_shift function in [NOTES]: g_j = int(C * gamma * j),
  * j = 1..4, evaluated as the listing's Python does it: double product, left to right,
  * truncated toward zero.
