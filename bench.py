@@ -1,6 +1,6 @@
 """Benchmark: Bi-WKV forward (+ Q-Shift) throughput and HBM roofline on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--entry fused|biwkv|causal|gated|qshift|mix]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--entry fused|biwkv|causal|gated|qshift|mix|backward]
 
 One step = one pass of the whole hot path over one batch: the fused Q-Shift + Bi-WKV entry on the
 high-resolution workload (B=4, 64x64 grid so T=4096, C=1024, bf16 k/v, fp32 accumulate and
@@ -39,7 +39,11 @@ CALIBRATION_BYTES = 512 * 1024 * 1024
 MIN_CPU_SECONDS = 3.0
 COPY_KERNEL = "copy"  # substring of the device copy kernel's name in the counter output
 KERNEL_NAMES = {"fused": "biwkv_row_kernel", "biwkv": "biwkv_row_kernel", "causal": "biwkv_row_kernel",
-                "gated": "biwkv_row_kernel", "qshift": "qshift_kernel", "mix": "qshift_mix_kernel"}
+                "gated": "biwkv_row_kernel", "qshift": "qshift_kernel", "mix": "qshift_mix_kernel",
+                "backward": "bwd_"}
+# entries made of several kernels: their counters are summed over every kernel of a call, and the
+# calls are counted by a kernel that runs once per call
+CALL_MARKER = {"backward": "bwd_reduce_kernel"}
 N_MIX = 3  # mixing vectors of the mix entry (the R, K and V projection inputs)
 
 
@@ -59,6 +63,9 @@ def alg_bytes(entry: str, B: int, H: int, W: int, C: int, kv_bytes: int, shift: 
     gated:  as biwkv, plus one read of the gate input r (kv_bytes).
     fused:  as biwkv, but the Q-Shift zero-filled sources are never read.
     qshift: read the in-grid sources, write every output (fp32).
+    mix:    read x once (its shifted reads are the same elements), write N_MIX fp32 outputs.
+    backward: read k and v (kv_bytes each) and the fp32 upstream gradient, write fp32 dk and dv,
+            read w and u, write dw and du.
     """
     T = H * W
     n = B * T * C
@@ -74,6 +81,8 @@ def alg_bytes(entry: str, B: int, H: int, W: int, C: int, kv_bytes: int, shift: 
         return 4 * (n - B * zero_per_b) + 4 * n
     if entry == "mix":  # x read once (its shifted reads are the same elements), N_MIX outputs
         return 4 * n + 4 * N_MIX * n + 4 * N_MIX * C
+    if entry == "backward":
+        return 2 * kv_bytes * n + 4 * n + 8 * n + 16 * C
     raise ValueError(entry)
 
 
@@ -141,6 +150,8 @@ def cpu_baseline(wl, entry: str) -> dict:
             oracle.biwkv_causal_rnn(k, v, w, u, threads=threads)
         elif entry == "gated":
             oracle.biwkv_gated(k, v, _gate_input(wl).astype(np.float64), w, u, threads=threads)
+        elif entry == "backward":
+            oracle.biwkv_backward_rnn(k, v, w, u, _upstream_grad(wl).astype(np.float64), threads=threads)
         else:
             oracle.biwkv_rnn(k, v, w, u, threads=threads)
         reps += 1
@@ -151,7 +162,9 @@ def cpu_baseline(wl, entry: str) -> dict:
     return {"value": reps * elems / dt / 1e9, "unit": "Gtoken*ch/s", "cores": threads,
             "kind": "oracle", "seconds": dt, "repetitions": reps, "cpu": _cpu_model(),
             "sample": f"whole workload ({wl.B}x{wl.T}x{wl.C}) x{reps}; float64 "
-                      + ("two-state causal RNN oracle" if entry == "causal" else "four-state RNN oracle")
+                      + ("two-state causal RNN oracle" if entry == "causal" else
+                         "linear-time gradient oracle (prefix and suffix sums)" if entry == "backward"
+                         else "four-state RNN oracle")
                       + (" times the sigmoid gate" if entry == "gated" else "")
                       + (" after the oracle Q-Shift of k and v" if entry == "fused" else "")}
 
@@ -165,6 +178,12 @@ def _gate_input(wl):
     g = np.random.Generator(np.random.PCG64(404))
     r = (g.standard_normal((wl.B, wl.T, wl.C)) * 3.0).astype(np.float32)
     return workloads.bf16_bits_to_f32(workloads.round_to_bf16_bits(r)) if wl.dtype == "bf16" else r
+
+
+def _upstream_grad(wl):
+    """A seeded upstream gradient dL/dy for the backward entry: N(0, 1), float32 [B, T, C]."""
+    import numpy as np
+    return np.random.Generator(np.random.PCG64(406)).standard_normal((wl.B, wl.T, wl.C)).astype(np.float32)
 
 
 def _mix_vectors(C: int):
@@ -195,7 +214,7 @@ def run_bench(args) -> dict:
     vb = torch.from_numpy(np.ascontiguousarray(vs)).view(torch.bfloat16).to(dev)
     w = torch.from_numpy(wl.w).to(dev)
     u = torch.from_numpy(wl.u).to(dev)
-    set_bytes = (kb.numel() + vb.numel()) * 2 + B * T * C * 4
+    set_bytes = (kb.numel() + vb.numel()) * 2 + B * T * C * (16 if entry == "backward" else 4)
     R = _rotation(set_bytes)
     ks_ = [kb] + [kb.clone() for _ in range(R - 1)]
     vs_ = [vb] + [vb.clone() for _ in range(R - 1)]
@@ -205,6 +224,10 @@ def run_bench(args) -> dict:
     if entry == "mix":
         mu = torch.from_numpy(_mix_vectors(C)).to(dev)
         outs = [torch.empty((N_MIX, B, T, C), dtype=torch.float32, device=dev) for _ in range(R)]
+    if entry == "backward":
+        gs_ = [torch.from_numpy(_upstream_grad(wl)).to(dev) for _ in range(R)]
+        dvs = [torch.empty((B, T, C), dtype=torch.float32, device=dev) for _ in range(R)]
+        dws = [torch.empty((2, C), dtype=torch.float32, device=dev) for _ in range(R)]
     if entry == "gated":
         rb = torch.from_numpy(np.ascontiguousarray(workloads.round_to_bf16_bits(_gate_input(wl)))).view(
             torch.bfloat16).to(dev)
@@ -237,6 +260,16 @@ def run_bench(args) -> dict:
             calls.append((cl.biwkv_gated_forward,
                           (ks_[r].data_ptr(), vs_[r].data_ptr(), rs_[r].data_ptr(), w.data_ptr(),
                            u.data_ptr(), outs[r].data_ptr(), B, T, C, lib.BF16, stream.cuda_stream)))
+        elif entry == "backward":
+            dk, dv, dw, du = lib.biwkv_backward(ks_[r], vs_[r], w, u, gs_[r])
+            outs[r].copy_(dk)
+            dvs[r].copy_(dv)
+            dws[r][0].copy_(dw)
+            dws[r][1].copy_(du)
+            calls.append((cl.biwkv_backward,
+                          (ks_[r].data_ptr(), vs_[r].data_ptr(), w.data_ptr(), u.data_ptr(),
+                           gs_[r].data_ptr(), outs[r].data_ptr(), dvs[r].data_ptr(), dws[r][0].data_ptr(),
+                           dws[r][1].data_ptr(), B, T, C, lib.BF16, stream.cuda_stream)))
         elif entry == "mix":
             lib.qshift_mix(xs[r], mu, H, W, wl.shift, wl.gamma, out=outs[r])
             calls.append((cl.qshift_mix, (xs[r].data_ptr(), mu.data_ptr(), outs[r].data_ptr(), B, H, W,
@@ -282,9 +315,11 @@ def run_bench(args) -> dict:
     if counters is not None and entry in counters.get("entries", {}):
         traffic = counters["entries"][entry]["hbm_bytes_per_launch"]
     names = {"fused": "biwkv_qshift_forward", "biwkv": "biwkv_forward", "causal": "biwkv_causal_forward",
-             "gated": "biwkv_gated_forward", "qshift": "qshift", "mix": "qshift_mix"}
+             "gated": "biwkv_gated_forward", "qshift": "qshift", "mix": "qshift_mix",
+             "backward": "biwkv_backward"}
     return {
-        "metric": "Bi-WKV fwd Gtoken*ch/s + achieved HBM GB/s (% peak) at T=4096 C=1024",
+        "metric": ("Bi-WKV bwd" if entry == "backward" else "Bi-WKV fwd")
+                  + " Gtoken*ch/s + achieved HBM GB/s (% peak) at T=4096 C=1024",
         "value": elems * args.steps / wall / 1e9,
         "unit": "Gtoken*ch/s",
         "n_gpus": 1,
@@ -345,11 +380,35 @@ def _counter_means(path: str, counter: str, kernel: str) -> float:
     return sum(sel) / len(sel)
 
 
+def _counter_per_call(path: str, counter: str, kernel: str, marker: str) -> float:
+    """Sum of `counter` over every dispatch of kernels whose name contains `kernel`, divided by the
+    number of dispatches of the once-per-call kernel `marker`: the value per call of an entry point
+    that launches several kernels."""
+    total, calls = 0.0, set()
+    for f in glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True):
+        for row in csv.DictReader(open(f)):
+            if row.get("Counter_Name") != counter:
+                continue
+            name = row.get("Kernel_Name", "")
+            if kernel in name:
+                total += float(row["Counter_Value"])
+            if marker in name:
+                calls.add((f, row.get("Dispatch_Id", row.get("Correlation_Id"))))
+    if not calls:
+        raise SystemExit(f"no {counter} values for {marker} under {path}")
+    return total / len(calls)
+
+
 def record_counters(kf: str, kw: str, cf: str, cw: str, entry: str) -> None:
-    """HBM traffic per launch of the bench kernel from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
-    each scaled by what it reads for a device copy of CALIBRATION_BYTES."""
-    fetch = _counter_means(kf, "FETCH_SIZE", KERNEL_NAMES[entry])
-    write = _counter_means(kw, "WRITE_SIZE", KERNEL_NAMES[entry])
+    """HBM traffic per launch of the bench kernel (per call, for entries of several kernels) from
+    FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by what it reads for a device copy of
+    CALIBRATION_BYTES."""
+    if entry in CALL_MARKER:
+        fetch = _counter_per_call(kf, "FETCH_SIZE", KERNEL_NAMES[entry], CALL_MARKER[entry])
+        write = _counter_per_call(kw, "WRITE_SIZE", KERNEL_NAMES[entry], CALL_MARKER[entry])
+    else:
+        fetch = _counter_means(kf, "FETCH_SIZE", KERNEL_NAMES[entry])
+        write = _counter_means(kw, "WRITE_SIZE", KERNEL_NAMES[entry])
     cal_fetch = _counter_means(cf, "FETCH_SIZE", COPY_KERNEL)
     cal_write = _counter_means(cw, "WRITE_SIZE", COPY_KERNEL)
     f_scale = CALIBRATION_BYTES / cal_fetch
@@ -397,7 +456,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--entry", choices=["fused", "biwkv", "causal", "gated", "qshift", "mix"], default="fused")
+    ap.add_argument("--entry", choices=["fused", "biwkv", "causal", "gated", "qshift", "mix", "backward"],
+                    default="fused")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize", metavar="DIR")

@@ -8,6 +8,7 @@ from ._lib import (  # noqa: F401
     F32,
     LIB_PATH,
     BiwkvError,
+    biwkv_backward,
     biwkv_causal_forward,
     biwkv_forward,
     biwkv_gated_forward,

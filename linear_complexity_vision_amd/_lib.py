@@ -51,6 +51,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.biwkv_forward.restype = ctypes.c_int
     lib.biwkv_causal_forward.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P]
     lib.biwkv_causal_forward.restype = ctypes.c_int
+    lib.biwkv_backward.argtypes = [_P] * 9 + [_I64, _I64, _I64, ctypes.c_int, _P]
+    lib.biwkv_backward.restype = ctypes.c_int
     lib.biwkv_gated_forward.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P]
     lib.biwkv_gated_forward.restype = ctypes.c_int
     lib.qshift.argtypes = [_P, _P, _I64, _I64, _I64, _I64, ctypes.c_int, ctypes.c_double, _P]
@@ -141,6 +143,25 @@ def biwkv_forward(k, v, w, u, out=None):
         _check(load_library().biwkv_forward(k.data_ptr(), v.data_ptr(), w.data_ptr(), u.data_ptr(),
                                             out.data_ptr(), B, T, C, dt, _stream_handle(k.device)))
     return out
+
+
+def biwkv_backward(k, v, w, u, g):
+    """Gradients of a loss through biwkv_forward(k, v, w, u) given g = dL/dy (float32 [B, T, C]):
+    returns dk, dv (float32 [B, T, C]) and dw, du (float32 [C], summed over the batch)."""
+    torch = _torch()
+    dt = _check_bitc(k, v, w, u)
+    _require(g.is_cuda and g.shape == k.shape and g.dtype == torch.float32 and g.is_contiguous(),
+             "g must be a contiguous float32 tensor shaped like k")
+    B, T, C = k.shape
+    dk = torch.empty((B, T, C), dtype=torch.float32, device=k.device)
+    dv = torch.empty_like(dk)
+    dw = torch.empty((C,), dtype=torch.float32, device=k.device)
+    du = torch.empty_like(dw)
+    with torch.cuda.device(k.device):
+        _check(load_library().biwkv_backward(k.data_ptr(), v.data_ptr(), w.data_ptr(), u.data_ptr(),
+                                             g.data_ptr(), dk.data_ptr(), dv.data_ptr(), dw.data_ptr(),
+                                             du.data_ptr(), B, T, C, dt, _stream_handle(k.device)))
+    return dk, dv, dw, du
 
 
 def biwkv_causal_forward(k, v, w, u, out=None):

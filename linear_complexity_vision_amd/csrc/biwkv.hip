@@ -42,6 +42,7 @@
 
 #include "biwkv.h"
 
+#include "backward.cuh"
 #include "chunk_kernel.cuh"
 #include "common.cuh"
 #include "qshift_kernel.cuh"
@@ -64,6 +65,8 @@ struct StreamScratch {
   Counters* ctr = nullptr;
   unsigned long long* slots = nullptr;
   long long slot_words = 0;
+  float* bwd = nullptr;  // backward pass sums, carries and per-chunk terms
+  long long bwd_floats = 0;
   std::vector<void*> retired;  // outgrown buffers; pending launches may still use them
 };
 
@@ -409,6 +412,97 @@ int biwkv_gated_forward(const void* k, const void* v, const void* r, const float
   rc = dtype == BIWKV_F32 ? try_row<BIWKV_F32, false, false, true>(prm, B, dev, stream)
                           : try_row<BIWKV_BF16, false, false, true>(prm, B, dev, stream);
   return rc == 1 ? BIWKV_ERR_UNSUPPORTED : rc;
+}
+
+int biwkv_backward(const void* k, const void* v, const float* w, const float* u, const float* g,
+                   float* dk, float* dv, float* dw, float* du, int64_t B, int64_t T, int64_t C,
+                   int dtype, void* stream) {
+  int rc = check_bitc_shape(B, T, C);
+  if (rc) return rc;
+  if (dtype != BIWKV_F32 && dtype != BIWKV_BF16) return BIWKV_ERR_DTYPE;
+  const bool nonempty = B && T && C;
+  if (nonempty && (!k || !v || !g || !dk || !dv)) return BIWKV_ERR_NULL;
+  if (C && (!w || !u || !dw || !du)) return BIWKV_ERR_NULL;
+  if (!C) return BIWKV_OK;
+  const size_t es = dtype == BIWKV_F32 ? 4 : 2;
+  const size_t n = static_cast<size_t>(B) * T * C;
+  if ((nonempty && (!aligned(k, es) || !aligned(v, es) || !aligned(g, 4) || !aligned(dk, 4) ||
+                    !aligned(dv, 4))) ||
+      !aligned(w, 4) || !aligned(u, 4) || !aligned(dw, 4) || !aligned(du, 4))
+    return BIWKV_ERR_ALIGN;
+  // outputs overlap neither each other nor any input
+  const void* outs[4] = {dk, dv, dw, du};
+  const size_t out_n[4] = {nonempty ? n * 4 : 0, nonempty ? n * 4 : 0, static_cast<size_t>(C) * 4,
+                           static_cast<size_t>(C) * 4};
+  const void* ins[5] = {k, v, g, w, u};
+  const size_t in_n[5] = {nonempty ? n * es : 0, nonempty ? n * es : 0, nonempty ? n * 4 : 0,
+                          static_cast<size_t>(C) * 4, static_cast<size_t>(C) * 4};
+  for (int a = 0; a < 4; ++a) {
+    for (int b2 = 0; b2 < 5; ++b2)
+      if (ranges_overlap(outs[a], out_n[a], ins[b2], in_n[b2])) return BIWKV_ERR_ALIAS;
+    for (int b2 = a + 1; b2 < 4; ++b2)
+      if (ranges_overlap(outs[a], out_n[a], outs[b2], out_n[b2])) return BIWKV_ERR_ALIAS;
+  }
+  int dev = 0;
+  rc = current_device(&dev);
+  if (rc) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const unsigned cb = static_cast<unsigned>((C + 255) / 256);
+  if (!nonempty) {
+    hipLaunchKernelGGL(bwd_zero_kernel, dim3(cb), dim3(256), 0, st, dw, du, static_cast<int>(C));
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? BIWKV_OK : hip_fail(e);
+  }
+  const int64_t n_chunks = (T + BK - 1) / BK;
+  const int64_t n_wg = (n_chunks + kBwdWaves - 1) / kBwdWaves;  // workgroups per row
+  if (B > 65535 || n_wg > 65535) return BIWKV_ERR_UNSUPPORTED;
+  BwdParams bp{};
+  bp.k = k;
+  bp.v = v;
+  bp.w = w;
+  bp.u = u;
+  bp.g = g;
+  bp.dk = dk;
+  bp.dv = dv;
+  bp.dw = dw;
+  bp.du = du;
+  bp.T = T;
+  bp.B = static_cast<int>(B);
+  bp.C = static_cast<int>(C);
+  bp.n_chunks = static_cast<int>(n_chunks);
+  bp.n_wg = static_cast<int>(n_wg);
+  const long long plane = B * n_chunks * C;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    StreamScratch* sc = nullptr;
+    rc = get_scratch(dev, stream, 0, &sc);
+    if (rc) return rc;
+    rc = grow_zeroed(&sc->bwd, &sc->bwd_floats, 26 * plane, 1ll << 20, st, &sc->retired);
+    if (rc) return rc;
+    float* f = sc->bwd;
+    bp.s = BwdScratch{f, f + 6 * plane, f + 12 * plane, f + 18 * plane, f + 24 * plane, f + 25 * plane, plane};
+  }
+  const dim3 tiles(static_cast<unsigned>((C + 63) / 64), static_cast<unsigned>(n_wg), static_cast<unsigned>(B));
+  const dim3 wg(64 * kBwdWaves);
+  const dim3 rows(static_cast<unsigned>((C + 63) / 64), static_cast<unsigned>(B));
+  if (dtype == BIWKV_F32) {
+    hipLaunchKernelGGL(bwd_chunk_sums_kernel<BIWKV_F32>, tiles, wg, 0, st, bp);
+    hipLaunchKernelGGL(bwd_carry_kernel, rows, dim3(64 * kCarryGroups), 0, st, bp, bp.s.a1, bp.s.x1);
+    hipLaunchKernelGGL(bwd_sweep1_kernel<BIWKV_F32>, tiles, wg, 0, st, bp);
+    hipLaunchKernelGGL(bwd_carry_kernel, rows, dim3(64 * kCarryGroups), 0, st, bp, bp.s.a2, bp.s.x2);
+    hipLaunchKernelGGL(bwd_sweep2_kernel<BIWKV_F32>, tiles, wg, 0, st, bp);
+  } else {
+    hipLaunchKernelGGL(bwd_chunk_sums_kernel<BIWKV_BF16>, tiles, wg, 0, st, bp);
+    hipLaunchKernelGGL(bwd_carry_kernel, rows, dim3(64 * kCarryGroups), 0, st, bp, bp.s.a1, bp.s.x1);
+    hipLaunchKernelGGL(bwd_sweep1_kernel<BIWKV_BF16>, tiles, wg, 0, st, bp);
+    hipLaunchKernelGGL(bwd_carry_kernel, rows, dim3(64 * kCarryGroups), 0, st, bp, bp.s.a2, bp.s.x2);
+    hipLaunchKernelGGL(bwd_sweep2_kernel<BIWKV_BF16>, tiles, wg, 0, st, bp);
+  }
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(static_cast<unsigned>((C + 63) / 64)), dim3(64 * kReduceGroups), 0,
+                     st, bp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e);
+  return BIWKV_OK;
 }
 
 int biwkv_causal_forward(const void* k, const void* v, const float* w, const float* u, float* out,

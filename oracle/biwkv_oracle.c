@@ -374,8 +374,11 @@ int oracle_biwkv_causal_rnn(const double* k, const double* v, const double* w, c
  *   dk_i = sum_t g_t p_ti (v_i - y_t)
  *   du   = sum_t g_t p_tt (v_t - y_t)                                 (summed over b)
  *   dw   = sum_t sum_{i != t} g_t p_ti (v_i - y_t) * (-(|t-i|-1)/T)    (summed over b)
- * because dy_t/ds_ti = p_ti (v_i - y_t). Quadratic in T. Also returns magnitude scales (the same
- * sums of absolute values of each term) for the tests' error metric; any scale pointer may be NULL.
+ * because dy_t/ds_ti = p_ti (v_i - y_t). Quadratic in T. Also returns magnitude scales for the
+ * tests' error metric: |g_t| p_ti for dv, and |g_t| p_ti (|v_i| + |y_t|) in place of each term
+ * g_t p_ti (v_i - y_t) (times |t-i|-1 over T for dw), since v_i - y_t of two nearly equal values
+ * (T = 1, a dominant bonus term) is known only to the rounding of y_t, which is relative to
+ * |y_t|; any scale pointer may be NULL.
  */
 int oracle_biwkv_backward_sum(const double* k, const double* v, const double* w, const double* u,
                               const double* g, int64_t B, int64_t T, int64_t C, double* dk,
@@ -444,18 +447,19 @@ int oracle_biwkv_backward_sum(const double* k, const double* v, const double* w,
                     for (int64_t t = 0; t < T; ++t) {
                         const double gp = gc[t] * p[t * T + i];
                         const double term = gp * (vc[i] - y[t]);
+                        const double mag = fabs(gp) * (fabs(vc[i]) + fabs(y[t]));
                         dvi += gp;
                         svi += fabs(gp);
                         dki += term;
-                        ski += fabs(term);
+                        ski += mag;
                         if (t == i) {
                             duc += term;
-                            suc += fabs(term);
+                            suc += mag;
                         } else {
                             const int64_t dist = (i > t) ? (i - t) : (t - i);
                             const double dterm = term * (-((double)(dist - 1)) / Td);
                             dwc += dterm;
-                            swc += fabs(dterm);
+                            swc += mag * (((double)(dist - 1)) / Td);
                         }
                     }
                     const int64_t o = (b * T + i) * C + c;

@@ -152,3 +152,20 @@ def test_gated_forward_validation(L):
     assert gated(out=R) == _code("BIWKV_ERR_ALIAS")
     assert gated(dtype=9) == _code("BIWKV_ERR_DTYPE")
     assert gated(B=0, r=None) == 0
+
+
+def test_backward_validation(L):
+    G, DK, DV, DW, DU = 0x60000000, 0x70000000, 0x80000000, 0x90000000, 0x90001000
+
+    def bwd(k=K, v=V, w=WP, u=UP, g=G, dk=DK, dv=DV, dw=DW, du=DU, B=2, T=8, C=4, dtype=lib.F32):
+        return L.biwkv_backward(k, v, w, u, g, dk, dv, dw, du, B, T, C, dtype, None)
+
+    assert bwd(dtype=4) == _code("BIWKV_ERR_DTYPE")
+    assert bwd(g=None) == _code("BIWKV_ERR_NULL")
+    assert bwd(dw=None) == _code("BIWKV_ERR_NULL")
+    assert bwd(dk=DK + 2) == _code("BIWKV_ERR_ALIGN")
+    assert bwd(dv=DK + 16) == _code("BIWKV_ERR_ALIAS")
+    assert bwd(dk=G) == _code("BIWKV_ERR_ALIAS")
+    assert bwd(du=DW + 8) == _code("BIWKV_ERR_ALIAS")
+    assert bwd(T=-1) == _code("BIWKV_ERR_SHAPE")
+    assert bwd(C=0, w=None, u=None, dw=None, du=None) == 0
