@@ -20,6 +20,9 @@ Functions follow the pages (cited by title and equation):
 * ``sigmoid`` / ``biwkv_gated`` — Eq. (2) of the same article: the attention output gated by
   sigma(R) (elementwise) before the output projection.
 * ``qshift_mix``     — Eq. (9) as printed: X + (1 - mu) X-dagger for each mixing vector mu.
+* ``qshift_bidir``   — the bidirectional shift of the same article's MAE paragraph (Q-Shift on a
+  sparse token sequence): the groups that Q-Shift moves right or down take token n - s, the
+  groups it moves left or up take token n + s; zero fill, remainder copied.
 * ``biwkv_causal_sum`` / ``biwkv_causal_rnn`` — the causal attention Bi-WKV is derived from (the
   original RWKV attention, which the same section says stops at the current token): Eq. (5)
   with the decayed sum over i < t only, and Eq. (6)-(7) with b = d = 0.
@@ -64,11 +67,12 @@ def _load():
         lib.oracle_biwkv_rnn.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, ctypes.c_int]
         lib.oracle_biwkv_rnn_literal.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _P]
         lib.oracle_qshift.argtypes = [_P, _P, _I64, _I64, _I64, _I64, _I64, ctypes.c_double]
+        lib.oracle_qshift_bidir.argtypes = [_P, _P, _I64, _I64, _I64, _I64, ctypes.c_double]
         lib.oracle_biwkv_causal_sum.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, ctypes.c_int]
         lib.oracle_biwkv_causal_rnn.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, ctypes.c_int]
         lib.oracle_biwkv_backward_sum.argtypes = [_P] * 5 + [_I64] * 3 + [_P] * 8 + [ctypes.c_int]
         lib.oracle_biwkv_backward_rnn.argtypes = [_P] * 5 + [_I64] * 3 + [_P] * 4 + [ctypes.c_int]
-        for f in (lib.oracle_biwkv_sum, lib.oracle_biwkv_rnn, lib.oracle_biwkv_rnn_literal, lib.oracle_qshift,
+        for f in (lib.oracle_biwkv_sum, lib.oracle_biwkv_rnn, lib.oracle_biwkv_rnn_literal, lib.oracle_qshift, lib.oracle_qshift_bidir,
                   lib.oracle_biwkv_causal_sum, lib.oracle_biwkv_causal_rnn, lib.oracle_biwkv_backward_sum,
                   lib.oracle_biwkv_backward_rnn):
             f.restype = ctypes.c_int
@@ -190,6 +194,31 @@ def qshift_f64(x, H, W, shift=1, gamma=0.25):
     if not np.array_equal(x32.astype(np.float64), np.asarray(x, dtype=np.float64), equal_nan=True):
         raise ValueError("qshift_f64 needs values exactly representable in float32")
     return qshift(x32, H, W, shift, gamma).astype(np.float64)
+
+
+def qshift_bidir(x, shift=1, gamma=0.25):
+    """Bidirectional shift of a [B, N, C] array of 4-byte elements along the token axis (the
+    MAE form of Q-Shift); returns the same dtype, bit for bit."""
+    x = np.ascontiguousarray(x)
+    if x.ndim != 3 or x.dtype.itemsize != 4:
+        raise ValueError("x must be a [B, N, C] array of 4-byte elements")
+    B, N, C = x.shape
+    bits = x.view(np.uint32)
+    out = np.empty_like(bits)
+    rc = _load().oracle_qshift_bidir(_ptr(bits), _ptr(out), B, N, C, int(shift), float(gamma))
+    if rc == -2:
+        raise QShiftParamError(f"invalid shift={shift} / gamma={gamma} for {N} tokens")
+    if rc != 0:
+        raise RuntimeError(f"oracle_qshift_bidir failed ({rc})")
+    return out.view(x.dtype)
+
+
+def qshift_bidir_f64(x, shift=1, gamma=0.25):
+    """The bidirectional shift of a float64 array, on its float32 bit patterns (fp32-exact values)."""
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    if not np.array_equal(x32.astype(np.float64), np.asarray(x, dtype=np.float64), equal_nan=True):
+        raise ValueError("qshift_bidir_f64 needs values exactly representable in float32")
+    return qshift_bidir(x32, shift, gamma).astype(np.float64)
 
 
 def biwkv_backward_sum(k, v, w, u, g, with_scale=False, threads=0):

@@ -661,3 +661,45 @@ int oracle_qshift(const uint32_t* x, uint32_t* out, int64_t B, int64_t H, int64_
     }
     return ORC_OK;
 }
+
+/*
+ * O3b — the bidirectional shift that the Vision-RWKV article's MAE paragraph puts in place of
+ * Q-Shift for sparse inputs (only the visible tokens of a masked image are present, so there is
+ * no H x W grid). Reading: the token sequence of length N replaces the grid, and each channel
+ * group keeps the sense of its Q-Shift move: the groups that take an earlier raster token (shift
+ * right, shift down) take token n - s, the groups that take a later one (left, up) take token
+ * n + s. Same group bounds g_j, zero fill at the ends, remainder copied, raw 32-bit words:
+ *   c in [0, g1) and [g2, g3):  out[n] = x[n - s]  if n >= s      else 0
+ *   c in [g1, g2) and [g3, g4): out[n] = x[n + s]  if n <  N - s  else 0
+ *   c >= g4:                    out[n] = x[n]
+ * Errors: gamma outside [0, 1/4] or NaN, shift < 0 or shift > N.
+ */
+int oracle_qshift_bidir(const uint32_t* x, uint32_t* out, int64_t B, int64_t N, int64_t C,
+                        int64_t shift, double gamma) {
+    if (!x || !out || B < 0 || N < 0 || C < 0) return ORC_ERR_ARG;
+    if (!(gamma >= 0.0 && gamma <= 0.25)) return ORC_ERR_PARAM;
+    if (shift < 0 || shift > N) return ORC_ERR_PARAM;
+    const int64_t g1 = group_bound(C, gamma, 1), g2 = group_bound(C, gamma, 2);
+    const int64_t g3 = group_bound(C, gamma, 3), g4 = group_bound(C, gamma, 4);
+    const int64_t s = shift;
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t n = 0; n < N; ++n) {
+            for (int64_t c = 0; c < C; ++c) {
+                int64_t src = n;
+                int valid = 1;
+                if (c < g4) {
+                    const int earlier = c < g1 || (c >= g2 && c < g3);
+                    if (earlier) {
+                        src = n - s;
+                        valid = n >= s;
+                    } else {
+                        src = n + s;
+                        valid = n < N - s;
+                    }
+                }
+                out[(b * N + n) * C + c] = valid ? x[(b * N + src) * C + c] : 0u;
+            }
+        }
+    }
+    return ORC_OK;
+}
