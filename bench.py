@@ -1,6 +1,6 @@
 """Benchmark: Bi-WKV forward (+ Q-Shift) throughput and HBM roofline on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--entry fused|biwkv|causal|gated|qshift|mix|backward]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--entry fused|biwkv|causal|gated|qshift|mix|backward|bidir]
 
 One step = one pass of the whole hot path over one batch: the fused Q-Shift + Bi-WKV entry on the
 high-resolution workload (B=4, 64x64 grid so T=4096, C=1024, bf16 k/v, fp32 accumulate and
@@ -40,7 +40,7 @@ MIN_CPU_SECONDS = 3.0
 COPY_KERNEL = "copy"  # substring of the device copy kernel's name in the counter output
 KERNEL_NAMES = {"fused": "biwkv_row_kernel", "biwkv": "biwkv_row_kernel", "causal": "biwkv_row_kernel",
                 "gated": "biwkv_row_kernel", "qshift": "qshift_kernel", "mix": "qshift_mix_kernel",
-                "backward": "bwd_"}
+                "backward": "bwd_", "bidir": "biwkv_row_kernel"}
 # entries made of several kernels: their counters are summed over every kernel of a call, and the
 # calls are counted by a kernel that runs once per call
 CALL_MARKER = {"backward": "bwd_reduce_kernel"}
@@ -66,6 +66,8 @@ def alg_bytes(entry: str, B: int, H: int, W: int, C: int, kv_bytes: int, shift: 
     mix:    read x once (its shifted reads are the same elements), write N_MIX fp32 outputs.
     backward: read k and v (kv_bytes each) and the fp32 upstream gradient, write fp32 dk and dv,
             read w and u, write dw and du.
+    bidir:  as fused, for the sequence shift of a sparse input (H = 1, W = N): each shifted
+            channel has `shift` zero-filled tokens per batch item.
     """
     T = H * W
     n = B * T * C
@@ -83,6 +85,8 @@ def alg_bytes(entry: str, B: int, H: int, W: int, C: int, kv_bytes: int, shift: 
         return 4 * n + 4 * N_MIX * n + 4 * N_MIX * C
     if entry == "backward":
         return 2 * kv_bytes * n + 4 * n + 8 * n + 16 * C
+    if entry == "bidir":
+        return 2 * kv_bytes * (n - B * shift * g[3]) + 4 * n + 8 * C
     raise ValueError(entry)
 
 
@@ -142,7 +146,11 @@ def cpu_baseline(wl, entry: str) -> dict:
     reps = 0
     t0 = time.perf_counter()
     while True:
-        if entry == "fused":
+        if entry == "bidir":
+            ks = oracle.qshift_bidir_f64(k, wl.shift, wl.gamma)
+            vs = oracle.qshift_bidir_f64(v, wl.shift, wl.gamma)
+            oracle.biwkv_rnn(ks, vs, w, u, threads=threads)
+        elif entry == "fused":
             ks = oracle.qshift_f64(k, wl.H, wl.W, wl.shift, wl.gamma)
             vs = oracle.qshift_f64(v, wl.H, wl.W, wl.shift, wl.gamma)
             oracle.biwkv_rnn(ks, vs, w, u, threads=threads)
@@ -166,7 +174,8 @@ def cpu_baseline(wl, entry: str) -> dict:
                          "linear-time gradient oracle (prefix and suffix sums)" if entry == "backward"
                          else "four-state RNN oracle")
                       + (" times the sigmoid gate" if entry == "gated" else "")
-                      + (" after the oracle Q-Shift of k and v" if entry == "fused" else "")}
+                      + (" after the oracle Q-Shift of k and v" if entry == "fused" else "")
+                      + (" after the oracle bidirectional shift of k and v" if entry == "bidir" else "")}
 
 
 def _gate_input(wl):
@@ -205,7 +214,8 @@ def run_bench(args) -> dict:
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    wl = workloads.make(4)
+    # the sparse-input entry runs on the masked-image workload of the same element count
+    wl = workloads.make_mae(2) if args.entry == "bidir" else workloads.make(4)
     B, H, W, C = wl.B, wl.H, wl.W, wl.C
     T = H * W
     entry = args.entry
@@ -245,6 +255,11 @@ def run_bench(args) -> dict:
                           (ks_[r].data_ptr(), vs_[r].data_ptr(), w.data_ptr(), u.data_ptr(),
                            outs[r].data_ptr(), B, H, W, C, wl.shift, wl.gamma, lib.BF16,
                            stream.cuda_stream)))
+        elif entry == "bidir":
+            lib.biwkv_qshift_bidir_forward(ks_[r], vs_[r], w, u, wl.shift, wl.gamma, out=outs[r])
+            calls.append((cl.biwkv_qshift_bidir_forward,
+                          (ks_[r].data_ptr(), vs_[r].data_ptr(), w.data_ptr(), u.data_ptr(),
+                           outs[r].data_ptr(), B, T, C, wl.shift, wl.gamma, lib.BF16, stream.cuda_stream)))
         elif entry == "biwkv":
             lib.biwkv_forward(ks_[r], vs_[r], w, u, out=outs[r])
             calls.append((cl.biwkv_forward,
@@ -316,10 +331,11 @@ def run_bench(args) -> dict:
         traffic = counters["entries"][entry]["hbm_bytes_per_launch"]
     names = {"fused": "biwkv_qshift_forward", "biwkv": "biwkv_forward", "causal": "biwkv_causal_forward",
              "gated": "biwkv_gated_forward", "qshift": "qshift", "mix": "qshift_mix",
-             "backward": "biwkv_backward"}
+             "backward": "biwkv_backward", "bidir": "biwkv_qshift_bidir_forward"}
     return {
         "metric": ("Bi-WKV bwd" if entry == "backward" else "Bi-WKV fwd")
-                  + " Gtoken*ch/s + achieved HBM GB/s (% peak) at T=4096 C=1024",
+                  + " Gtoken*ch/s + achieved HBM GB/s (% peak) at "
+                  + ("N=1024 visible tokens (sparse, MAE) C=1024" if entry == "bidir" else "T=4096 C=1024"),
         "value": elems * args.steps / wall / 1e9,
         "unit": "Gtoken*ch/s",
         "n_gpus": 1,
@@ -456,7 +472,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--entry", choices=["fused", "biwkv", "causal", "gated", "qshift", "mix", "backward"],
+    ap.add_argument("--entry", choices=["fused", "biwkv", "causal", "gated", "qshift", "mix", "backward", "bidir"],
                     default="fused")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")

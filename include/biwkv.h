@@ -155,6 +155,32 @@ int biwkv_qshift_forward(const void* k, const void* v, const float* w, const flo
                          int64_t B, int64_t H, int64_t W, int64_t C, int shift, double gamma,
                          int dtype, void* stream);
 
+/*
+ * Bidirectional token shift for sparse inputs: the form of Q-Shift that the MAE pre-training
+ * paragraph of the Vision-RWKV article uses when only the visible tokens of a masked image are
+ * present (there is no H x W grid). The channel groups of qshift keep the sense of their move
+ * along the token sequence: channels [0, g1) and [g2, g3) (moved right and down by qshift) take
+ * token n - shift, channels [g1, g2) and [g3, g4) (left and up) take token n + shift, with zero
+ * fill past either end; channels >= g4 are copied. g_j = int(C * gamma * j) as for qshift.
+ *   x, out : [B, N, C] float32, device memory; bit copies; out must not overlap x.
+ *   shift  : 0 <= shift <= N.  gamma: 0 <= gamma <= 1/4.
+ * Errors: BIWKV_ERR_NULL, _SHAPE, _PARAM, _ALIAS, _ALIGN, _NO_DEVICE, _HIP.
+ */
+int qshift_bidir(const float* x, float* out, int64_t B, int64_t N, int64_t C, int shift,
+                 double gamma, void* stream);
+
+/*
+ * Fused bidirectional shift + Bi-WKV: out = Bi-WKV(qshift_bidir(k), qshift_bidir(v)) with T = N
+ * (the spatial mix of a sparse, MAE-masked input). The shift is applied while k and v are loaded.
+ *   k, v : [B, N, C], storage type `dtype`; w, u : [C] float32; out : [B, N, C] float32.
+ *   shift, gamma as for qshift_bidir().
+ * Errors: as biwkv_forward() plus BIWKV_ERR_PARAM; no 128-token fallback (a row whose chunks
+ * cannot all be resident returns _UNSUPPORTED).
+ */
+int biwkv_qshift_bidir_forward(const void* k, const void* v, const float* w, const float* u,
+                               float* out, int64_t B, int64_t N, int64_t C, int shift, double gamma,
+                               int dtype, void* stream);
+
 /* Static, NUL-terminated description of a status code. Never NULL. */
 const char* biwkv_status_string(int status);
 

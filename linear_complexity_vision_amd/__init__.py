@@ -12,10 +12,12 @@ from ._lib import (  # noqa: F401
     biwkv_causal_forward,
     biwkv_forward,
     biwkv_gated_forward,
+    biwkv_qshift_bidir_forward,
     biwkv_qshift_forward,
     header_symbols,
     load_library,
     qshift,
+    qshift_bidir,
     qshift_mix,
     status_codes,
     status_string,

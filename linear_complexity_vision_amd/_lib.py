@@ -63,6 +63,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.biwkv_qshift_forward.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_int,
                                          ctypes.c_double, ctypes.c_int, _P]
     lib.biwkv_qshift_forward.restype = ctypes.c_int
+    lib.qshift_bidir.argtypes = [_P, _P, _I64, _I64, _I64, ctypes.c_int, ctypes.c_double, _P]
+    lib.qshift_bidir.restype = ctypes.c_int
+    lib.biwkv_qshift_bidir_forward.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int,
+                                               ctypes.c_double, ctypes.c_int, _P]
+    lib.biwkv_qshift_bidir_forward.restype = ctypes.c_int
     lib.biwkv_status_string.argtypes = [ctypes.c_int]
     lib.biwkv_status_string.restype = ctypes.c_char_p
     lib.biwkv_last_hip_error.argtypes = []
@@ -230,6 +235,39 @@ def qshift(x, H, W, shift=1, gamma=0.25, out=None):
     with torch.cuda.device(x.device):
         _check(load_library().qshift(x.data_ptr(), out.data_ptr(), B, H, W, C, int(shift),
                                      float(gamma), _stream_handle(x.device)))
+    return out
+
+
+def qshift_bidir(x, shift=1, gamma=0.25, out=None):
+    """Bidirectional shift of a [B, N, C] float32 token sequence (the MAE form of Q-Shift: the
+    right/down groups take token n - shift, the left/up groups n + shift); bit-exact gather."""
+    torch = _torch()
+    _require(x.is_cuda and x.dtype == torch.float32 and x.dim() == 3 and x.is_contiguous(),
+             "x must be a contiguous float32 [B, N, C] tensor on a HIP device")
+    B, N, C = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    _require(out.shape == x.shape and out.dtype == torch.float32 and out.is_contiguous(),
+             "out must match x")
+    with torch.cuda.device(x.device):
+        _check(load_library().qshift_bidir(x.data_ptr(), out.data_ptr(), B, N, C, int(shift),
+                                           float(gamma), _stream_handle(x.device)))
+    return out
+
+
+def biwkv_qshift_bidir_forward(k, v, w, u, shift=1, gamma=0.25, out=None):
+    """Fused Bi-WKV(qshift_bidir(k), qshift_bidir(v)) over a sparse token sequence (T = N)."""
+    torch = _torch()
+    dt = _check_bitc(k, v, w, u)
+    B, T, C = k.shape
+    if out is None:
+        out = torch.empty((B, T, C), dtype=torch.float32, device=k.device)
+    _require(out.shape == k.shape and out.dtype == torch.float32 and out.is_contiguous(),
+             "out must be a contiguous float32 [B, T, C] tensor")
+    with torch.cuda.device(k.device):
+        _check(load_library().biwkv_qshift_bidir_forward(
+            k.data_ptr(), v.data_ptr(), w.data_ptr(), u.data_ptr(), out.data_ptr(), B, T, C,
+            int(shift), float(gamma), dt, _stream_handle(k.device)))
     return out
 
 

@@ -171,6 +171,13 @@ int check_qshift_params(int64_t H, int64_t W, int shift, double gamma) {
   return BIWKV_OK;
 }
 
+// The sequence shift of N tokens: the same gamma range, 0 <= shift <= N.
+int check_bidir_params(int64_t N, int shift, double gamma) {
+  if (!(gamma >= 0.0 && gamma <= 0.25)) return BIWKV_ERR_PARAM;
+  if (shift < 0 || shift > N) return BIWKV_ERR_PARAM;
+  return BIWKV_OK;
+}
+
 constexpr int64_t kMaxDim = (1ll << 31) - 1;
 constexpr int kMaxMix = 8;  // mixing vectors per qshift_mix call
 
@@ -262,6 +269,7 @@ int launch_row(const BiwkvParams& bp, int64_t B, int dev, void* stream) {
   rp.g2 = bp.g2;
   rp.g3 = bp.g3;
   rp.g4 = bp.g4;
+  rp.bidir = bp.bidir;
   rp.n_tiles = static_cast<int>(n_tiles);
   rp.n_chunks = static_cast<int>(n_chunks);
   rp.total = static_cast<unsigned>(total);
@@ -357,6 +365,79 @@ int validate_biwkv(const void* k, const void* v, const float* w, const float* u,
       ranges_overlap(out, n * 4, w, C * 4) || ranges_overlap(out, n * 4, u, C * 4))
     return BIWKV_ERR_ALIAS;
   return BIWKV_OK;
+}
+
+// The gather behind qshift and qshift_bidir (parameters already checked, nothing empty). bidir:
+// the sequence shift, given as a 1 x N grid.
+int launch_qshift(const float* x, float* out, int64_t B, int64_t H, int64_t W, int64_t C, int shift,
+                  double gamma, int bidir, void* stream) {
+  if (!aligned(x, 4) || !aligned(out, 4)) return BIWKV_ERR_ALIGN;
+  const size_t n = static_cast<size_t>(B) * H * W * C;
+  if (ranges_overlap(out, n * 4, x, n * 4)) return BIWKV_ERR_ALIAS;
+  int dev = 0;
+  int rc = current_device(&dev);
+  if (rc) return rc;
+  int64_t g[4];
+  group_bounds(C, gamma, g);
+  const bool vec4 = (C % 4 == 0) && (g[0] % 4 == 0) && (g[1] % 4 == 0) && (g[2] % 4 == 0) &&
+                    (g[3] % 4 == 0) && aligned(x, 16) && aligned(out, 16);
+  const long long rows = B * H * W;
+  const long long items = rows * (vec4 ? C / 4 : C);
+  long long blocks = (items + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const uint32_t* xi = reinterpret_cast<const uint32_t*>(x);
+  uint32_t* oi = reinterpret_cast<uint32_t*>(out);
+  if (vec4)
+    hipLaunchKernelGGL(qshift_kernel<4>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, xi,
+                       oi, rows, static_cast<int>(H), static_cast<int>(W), static_cast<int>(C),
+                       shift, static_cast<int>(g[0]), static_cast<int>(g[1]),
+                       static_cast<int>(g[2]), static_cast<int>(g[3]), bidir);
+  else
+    hipLaunchKernelGGL(qshift_kernel<1>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, xi,
+                       oi, rows, static_cast<int>(H), static_cast<int>(W), static_cast<int>(C),
+                       shift, static_cast<int>(g[0]), static_cast<int>(g[1]),
+                       static_cast<int>(g[2]), static_cast<int>(g[3]), bidir);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e);
+  return BIWKV_OK;
+}
+
+// The fused entries' common part: Bi-WKV of the shifted k and v (grid Q-Shift, or with bidir the
+// sequence shift, passed as H = N, W = 1). Parameters already checked, nothing empty.
+int fused_forward(const void* k, const void* v, const float* w, const float* u, float* out,
+                  int64_t B, int64_t H, int64_t W, int64_t C, int shift, double gamma, int dtype,
+                  int bidir, void* stream) {
+  int dev = 0;
+  int rc = current_device(&dev);
+  if (rc) return rc;
+  int64_t g[4];
+  group_bounds(C, gamma, g);
+  const size_t es = dtype == BIWKV_F32 ? 4 : 2;
+  const bool groups_even = (g[0] % 2 == 0) && (g[1] % 2 == 0) && (g[2] % 2 == 0) && (g[3] % 2 == 0);
+  const bool vec2 = (C % 2 == 0) && groups_even && aligned(k, 2 * es) && aligned(v, 2 * es) &&
+                    aligned(out, 8);
+  BiwkvParams prm{};
+  prm.k = k;
+  prm.v = v;
+  prm.w = w;
+  prm.u = u;
+  prm.out = out;
+  prm.T = H * W;
+  prm.C = static_cast<int>(C);
+  prm.H = static_cast<int>(H);
+  prm.W = static_cast<int>(W);
+  prm.shift = shift;
+  prm.g1 = static_cast<int>(g[0]);
+  prm.g2 = static_cast<int>(g[1]);
+  prm.g3 = static_cast<int>(g[2]);
+  prm.g4 = static_cast<int>(g[3]);
+  prm.bidir = bidir;
+  if (!bidir) return dispatch_biwkv<true>(prm, B, dtype, vec2, dev, stream);
+  // the sequence shift exists in the tile kernel only: a shape it does not address has no fallback
+  rc = dtype == BIWKV_F32 ? try_row<BIWKV_F32, true>(prm, B, dev, stream)
+                          : try_row<BIWKV_BF16, true>(prm, B, dev, stream);
+  return rc == 1 ? BIWKV_ERR_UNSUPPORTED : rc;
 }
 
 }  // namespace
@@ -535,31 +616,17 @@ int biwkv_qshift_forward(const void* k, const void* v, const float* w, const flo
   if (rc) return rc;
   rc = check_qshift_params(H, W, shift, gamma);
   if (rc || !(B && T && C)) return rc;
-  int dev = 0;
-  rc = current_device(&dev);
+  return fused_forward(k, v, w, u, out, B, H, W, C, shift, gamma, dtype, 0, stream);
+}
+
+int biwkv_qshift_bidir_forward(const void* k, const void* v, const float* w, const float* u,
+                               float* out, int64_t B, int64_t N, int64_t C, int shift, double gamma,
+                               int dtype, void* stream) {
+  int rc = validate_biwkv(k, v, w, u, out, B, N, C, dtype);
   if (rc) return rc;
-  int64_t g[4];
-  group_bounds(C, gamma, g);
-  const size_t es = dtype == BIWKV_F32 ? 4 : 2;
-  const bool groups_even = (g[0] % 2 == 0) && (g[1] % 2 == 0) && (g[2] % 2 == 0) && (g[3] % 2 == 0);
-  const bool vec2 = (C % 2 == 0) && groups_even && aligned(k, 2 * es) && aligned(v, 2 * es) &&
-                    aligned(out, 8);
-  BiwkvParams prm{};
-  prm.k = k;
-  prm.v = v;
-  prm.w = w;
-  prm.u = u;
-  prm.out = out;
-  prm.T = T;
-  prm.C = static_cast<int>(C);
-  prm.H = static_cast<int>(H);
-  prm.W = static_cast<int>(W);
-  prm.shift = shift;
-  prm.g1 = static_cast<int>(g[0]);
-  prm.g2 = static_cast<int>(g[1]);
-  prm.g3 = static_cast<int>(g[2]);
-  prm.g4 = static_cast<int>(g[3]);
-  return dispatch_biwkv<true>(prm, B, dtype, vec2, dev, stream);
+  rc = check_bidir_params(N, shift, gamma);
+  if (rc || !(B && N && C)) return rc;
+  return fused_forward(k, v, w, u, out, B, N, 1, C, shift, gamma, dtype, 1, stream);
 }
 
 int qshift_mix(const float* x, const float* mu, float* out, int64_t B, int64_t H, int64_t W,
@@ -613,36 +680,18 @@ int qshift(const float* x, float* out, int64_t B, int64_t H, int64_t W, int64_t 
   if (nonempty && (!x || !out)) return BIWKV_ERR_NULL;
   rc = check_qshift_params(H, W, shift, gamma);
   if (rc || !nonempty) return rc;
-  if (!aligned(x, 4) || !aligned(out, 4)) return BIWKV_ERR_ALIGN;
-  const size_t n = static_cast<size_t>(B) * H * W * C;
-  if (ranges_overlap(out, n * 4, x, n * 4)) return BIWKV_ERR_ALIAS;
-  int dev = 0;
-  rc = current_device(&dev);
+  return launch_qshift(x, out, B, H, W, C, shift, gamma, 0, stream);
+}
+
+int qshift_bidir(const float* x, float* out, int64_t B, int64_t N, int64_t C, int shift, double gamma,
+                 void* stream) {
+  int rc = check_bitc_shape(B, N, C);
   if (rc) return rc;
-  int64_t g[4];
-  group_bounds(C, gamma, g);
-  const bool vec4 = (C % 4 == 0) && (g[0] % 4 == 0) && (g[1] % 4 == 0) && (g[2] % 4 == 0) &&
-                    (g[3] % 4 == 0) && aligned(x, 16) && aligned(out, 16);
-  const long long rows = B * H * W;
-  const long long items = rows * (vec4 ? C / 4 : C);
-  long long blocks = (items + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const uint32_t* xi = reinterpret_cast<const uint32_t*>(x);
-  uint32_t* oi = reinterpret_cast<uint32_t*>(out);
-  if (vec4)
-    hipLaunchKernelGGL(qshift_kernel<4>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, xi,
-                       oi, rows, static_cast<int>(H), static_cast<int>(W), static_cast<int>(C),
-                       shift, static_cast<int>(g[0]), static_cast<int>(g[1]),
-                       static_cast<int>(g[2]), static_cast<int>(g[3]));
-  else
-    hipLaunchKernelGGL(qshift_kernel<1>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, xi,
-                       oi, rows, static_cast<int>(H), static_cast<int>(W), static_cast<int>(C),
-                       shift, static_cast<int>(g[0]), static_cast<int>(g[1]),
-                       static_cast<int>(g[2]), static_cast<int>(g[3]));
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return hip_fail(e);
-  return BIWKV_OK;
+  const bool nonempty = B && N && C;
+  if (nonempty && (!x || !out)) return BIWKV_ERR_NULL;
+  rc = check_bidir_params(N, shift, gamma);
+  if (rc || !nonempty) return rc;
+  return launch_qshift(x, out, B, 1, N, C, shift, gamma, 1, stream);
 }
 
 const char* biwkv_status_string(int status) {
@@ -651,7 +700,7 @@ const char* biwkv_status_string(int status) {
     case BIWKV_ERR_NULL: return "a required pointer is NULL";
     case BIWKV_ERR_SHAPE: return "invalid shape (negative, too large, or T != H*W)";
     case BIWKV_ERR_DTYPE: return "unknown dtype (expected BIWKV_F32 or BIWKV_BF16)";
-    case BIWKV_ERR_PARAM: return "invalid Q-Shift parameter (gamma outside [0, 1/4], or shift < 0 or > min(H, W))";
+    case BIWKV_ERR_PARAM: return "invalid shift parameter (gamma outside [0, 1/4], or shift < 0 or beyond the grid (min(H, W)) or the sequence (N))";
     case BIWKV_ERR_ALIAS: return "output overlaps an input";
     case BIWKV_ERR_ALIGN: return "pointer not aligned to its element size";
     case BIWKV_ERR_NO_DEVICE: return "no usable HIP device";

@@ -43,6 +43,7 @@ struct BiwkvParams {
   unsigned int total;    // number of workgroups = B * n_tiles * n_chunks
   int H, W, shift;       // Q-Shift grid (fused entry only)
   int g1, g2, g3, g4;    // Q-Shift channel-group bounds (fused entry only)
+  int bidir;             // fused entry: shift along the token sequence (W = 1), not the grid
   int group;                  // chunks per exchange group
   int n_groups;               // groups per row
   unsigned long long* agg;    // chunk sums: [row][chunk][dir][tile channel][2 tagged words]

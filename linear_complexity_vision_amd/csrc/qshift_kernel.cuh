@@ -6,7 +6,9 @@
 namespace {
 
 // ---------------------------------------------------------------------------------------------
-// Q-Shift gather kernel: out[b, n, c] = X-dagger; bit copies only.
+// Q-Shift gather kernel: out[b, n, c] = X-dagger; bit copies only. With bidir set, the shift along
+// a sparse token sequence (the host passes a 1 x N grid): the down and up groups then move along
+// the sequence too, like the right and left groups.
 // ---------------------------------------------------------------------------------------------
 
 template <int V>
@@ -23,7 +25,7 @@ struct Bits<1> {
 template <int V>
 __global__ void __launch_bounds__(256)
     qshift_kernel(const uint32_t* __restrict__ x, uint32_t* __restrict__ out, long long rows,
-                  int H, int W, int C, int s, int g1, int g2, int g3, int g4) {
+                  int H, int W, int C, int s, int g1, int g2, int g3, int g4, int bidir) {
   using vec_t = typename Bits<V>::t;
   const int CV = C / V;
   const long long n = rows * CV;
@@ -35,6 +37,9 @@ __global__ void __launch_bounds__(256)
     const long long t = r % HW;
     const int h = static_cast<int>(t / W);
     const int w = static_cast<int>(t - static_cast<long long>(h) * W);
+    // the vertical groups' coordinate, extent and token step
+    const int hv = bidir ? w : h, Hv = bidir ? W : H;
+    const long long step = bidir ? 1 : W;
     long long src = r;
     bool ok = true;
     if (c < g1) {
@@ -44,11 +49,11 @@ __global__ void __launch_bounds__(256)
       ok = w < W - s;
       src = r + s;
     } else if (c < g3) {
-      ok = h >= s;
-      src = r - static_cast<long long>(s) * W;
+      ok = hv >= s;
+      src = r - s * step;
     } else if (c < g4) {
-      ok = h < H - s;
-      src = r + static_cast<long long>(s) * W;
+      ok = hv < Hv - s;
+      src = r + s * step;
     }
     vec_t val{};
     if (ok) val = *reinterpret_cast<const vec_t*>(x + src * C + c);

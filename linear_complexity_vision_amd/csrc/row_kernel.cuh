@@ -151,6 +151,7 @@ struct RowParams {
   Counters* ctr;                 // ticket / epoch block (n_chunks > 1)
   unsigned long long* slots;     // [row][chunk][dir][TILE] (l, mu) slot pairs (n_chunks > 1)
   int H, W, shift, g1, g2, g3, g4;  // Q-Shift (fused entry only)
+  int bidir;  // fused: the bidirectional shift along a sparse token sequence (the host sets W = 1)
 };
 
 // Counts a workgroup out of a chunked launch once none of its wavefronts reads the epoch or a slot
@@ -272,11 +273,18 @@ __device__ __forceinline__ void row_load(const RowParams& p, const RowLane& ln, 
     // starts SH = s W tokens before the word's token, so every lane offset is non-negative and
     // constant; sources past the end of the batch item fall past the resource and read 0. The
     // other zero-filled sources (a column outside the quarter's band, or a row above the grid for
-    // "down") are cleared words of a per-lane mask, set once.
+    // "down") are cleared words of a per-lane mask, set once. The bidirectional shift of a sparse
+    // sequence (W = 1) moves the right and down groups by -s and the left and up groups by +s, with
+    // no column bands: only the first s tokens of the -s groups are cleared.
     const int Wd = p.W, sh = p.shift, SH = p.shift * p.W;
     int delta = 0, lo = 0, hi = Wd;  // valid columns [lo, hi)
     bool down = false;
-    if (ln.ch < p.g1) {
+    if (p.bidir) {
+      if (ln.ch < p.g4) {
+        down = ln.ch < p.g1 || (ln.ch >= p.g2 && ln.ch < p.g3);
+        delta = down ? -sh : sh;
+      }
+    } else if (ln.ch < p.g1) {
       delta = -sh;
       lo = sh;
     } else if (ln.ch < p.g2) {

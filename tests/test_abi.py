@@ -169,3 +169,32 @@ def test_backward_validation(L):
     assert bwd(du=DW + 8) == _code("BIWKV_ERR_ALIAS")
     assert bwd(T=-1) == _code("BIWKV_ERR_SHAPE")
     assert bwd(C=0, w=None, u=None, dw=None, du=None) == 0
+
+
+def test_bidir_validation(L):
+    def qb(x=K, out=OUT, B=1, N=8, C=4, shift=1, gamma=0.25):
+        return L.qshift_bidir(x, out, B, N, C, shift, gamma, None)
+
+    def fb(k=K, v=V, w=WP, u=UP, out=OUT, B=1, N=8, C=4, shift=1, gamma=0.25, dtype=lib.BF16):
+        return L.biwkv_qshift_bidir_forward(k, v, w, u, out, B, N, C, shift, gamma, dtype, None)
+
+    bad = _code("BIWKV_ERR_PARAM")
+    for shift, gamma in [(1, 0.3), (1, -0.1), (1, math.nan), (-1, 0.25), (9, 0.25)]:
+        assert qb(shift=shift, gamma=gamma) == bad, (shift, gamma)
+        assert fb(shift=shift, gamma=gamma) == bad, (shift, gamma)
+    # a shift of several tokens is valid on a sequence (a 1 x N grid would refuse it)
+    assert _qs(L, H=1, W=8, shift=3) == bad
+    assert qb(x=None) == _code("BIWKV_ERR_NULL")
+    assert qb(N=-2) == _code("BIWKV_ERR_SHAPE")
+    assert qb(x=K + 2) == _code("BIWKV_ERR_ALIGN")
+    assert qb(out=K + 4) == _code("BIWKV_ERR_ALIAS")
+    assert fb(dtype=9) == _code("BIWKV_ERR_DTYPE")
+    assert fb(out=V + 4) == _code("BIWKV_ERR_ALIAS")
+    assert qb(B=0, x=None, out=None) == 0
+    assert fb(N=0, shift=0) == 0
+    import torch
+
+    if not torch.cuda.is_available():
+        no_dev = _code("BIWKV_ERR_NO_DEVICE")
+        assert qb(shift=3) == no_dev
+        assert fb(shift=8) == no_dev

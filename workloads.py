@@ -116,3 +116,23 @@ def make_random(seed: int, B: int, T: int, C: int, dtype: str = "f32", w_range: 
         k, v = _to_bf16_values(k), _to_bf16_values(v)
     return Workload(f"random_s{seed}_B{B}_T{T}_C{C}_{dtype}", B, H, W, C, dtype, k, v, w, u,
                     notes={"seed": seed})
+
+
+# Sparse (MAE-masked) inputs: the visible tokens of an image with 75% of its patches masked (MAE's
+# usual ratio; the article follows ViT's MAE setting). Only the visible tokens are present, N of
+# them per image; k, v, w, u are drawn as for the dense workloads (iid, so any subset of tokens has
+# the same distribution).
+# name: (seed, B, N, C, dtype, w range)
+MAE_SPECS = {
+    1: ("mae_B64_N49_C384_f32", 6, 64, 49, 384, "f32", 3.0),        # 25% of a 14 x 14 grid
+    2: ("mae_B16_N1024_C1024_bf16", 7, 16, 1024, 1024, "bf16", 5.0),  # 25% of 64 x 64; B * N * C as
+                                                                       # for 4 x 4096 x 1024
+}
+
+
+def make_mae(index: int) -> Workload:
+    """The sparse-input workloads of the bidirectional shift (shift 1, gamma 1/4)."""
+    name, seed, B, N, C, dtype, wr = MAE_SPECS[index]
+    wl = make_random(seed, B, N, C, dtype=dtype, w_range=wr)
+    wl.name = name
+    return wl
