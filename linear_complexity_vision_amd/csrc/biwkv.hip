@@ -43,6 +43,7 @@
 #include "biwkv.h"
 
 #include "backward.cuh"
+#include "bwd_tile.cuh"
 #include "chunk_kernel.cuh"
 #include "common.cuh"
 #include "qshift_kernel.cuh"
@@ -440,6 +441,75 @@ int fused_forward(const void* k, const void* v, const float* w, const float* u, 
   return rc == 1 ? BIWKV_ERR_UNSUPPORTED : rc;
 }
 
+// Backward tile shape: 8 tokens per lane, 512 threads (two workgroups per CU, so one's loads
+// overlap the other's arithmetic), 64-token chunks.
+constexpr int kBwdL = 8;
+constexpr int kBwdNT = 512;
+
+// The backward: bwd_tile_kernel in one launch (a row of one chunk) or three (stages 1, 2, 3),
+// then the dw / du fold. Arguments already checked, nothing empty.
+template <int DT, int L, int NT, int WPE>
+int launch_bwd_tile(const void* k, const void* v, const float* w, const float* u, const float* g,
+                    float* dk, float* dv, float* dw, float* du, int64_t B, int64_t T, int64_t C, int dev,
+                    void* stream) {
+  constexpr int CT = (NT / kBtTile) * L;
+  const int64_t n_tiles = (C + kBtTile - 1) / kBtTile;
+  const int64_t n_chunks = (T + CT - 1) / CT;
+  const int64_t total = B * n_tiles * n_chunks;
+  if (total > 0x7FFFFFFFll) return BIWKV_ERR_SHAPE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  BwdTileParams tp{};
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    StreamScratch* sc = nullptr;
+    int rc = get_scratch(dev, stream, 0, &sc);
+    if (rc) return rc;
+    const long long terms = B * n_chunks * C;                         // dw, du terms
+    const long long sums = n_chunks > 1 ? total * 2 * kBtTile * 3 : 0;  // chunk sums per round
+    rc = grow_zeroed(&sc->bwd, &sc->bwd_floats, 2 * terms + 2 * sums, 1ll << 20, st, &sc->retired);
+    if (rc) return rc;
+    tp.pw = sc->bwd;
+    tp.pu = sc->bwd + terms;
+    tp.sums1 = sc->bwd + 2 * terms;
+    tp.sums2 = sc->bwd + 2 * terms + sums;
+  }
+  tp.k = k;
+  tp.v = v;
+  tp.w = w;
+  tp.u = u;
+  tp.g = g;
+  tp.dk = dk;
+  tp.dv = dv;
+  tp.T = T;
+  tp.C = static_cast<int>(C);
+  tp.n_tiles = static_cast<int>(n_tiles);
+  tp.n_chunks = static_cast<int>(n_chunks);
+  const dim3 grid(static_cast<unsigned>(total)), block(NT);
+  if (n_chunks == 1) {
+    hipLaunchKernelGGL((bwd_tile_kernel<DT, L, NT, WPE, 0>), grid, block, 0, st, tp);
+  } else {
+    hipLaunchKernelGGL((bwd_tile_kernel<DT, L, NT, WPE, 1>), grid, block, 0, st, tp);
+    hipLaunchKernelGGL((bwd_tile_kernel<DT, L, NT, WPE, 2>), grid, block, 0, st, tp);
+    hipLaunchKernelGGL((bwd_tile_kernel<DT, L, NT, WPE, 3>), grid, block, 0, st, tp);
+  }
+  BwdParams rp{};
+  rp.w = w;
+  rp.dw = dw;
+  rp.du = du;
+  rp.T = T;
+  rp.B = static_cast<int>(B);
+  rp.C = static_cast<int>(C);
+  rp.n_chunks = static_cast<int>(n_chunks);
+  rp.n_wg = static_cast<int>(n_chunks);
+  rp.s.pw = tp.pw;
+  rp.s.pu = tp.pu;
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(static_cast<unsigned>((C + 63) / 64)), dim3(64 * kReduceGroups), 0,
+                     st, rp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e);
+  return BIWKV_OK;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------------------------
@@ -534,56 +604,11 @@ int biwkv_backward(const void* k, const void* v, const float* w, const float* u,
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? BIWKV_OK : hip_fail(e);
   }
-  const int64_t n_chunks = (T + BK - 1) / BK;
-  const int64_t n_wg = (n_chunks + kBwdWaves - 1) / kBwdWaves;  // workgroups per row
-  if (B > 65535 || n_wg > 65535) return BIWKV_ERR_UNSUPPORTED;
-  BwdParams bp{};
-  bp.k = k;
-  bp.v = v;
-  bp.w = w;
-  bp.u = u;
-  bp.g = g;
-  bp.dk = dk;
-  bp.dv = dv;
-  bp.dw = dw;
-  bp.du = du;
-  bp.T = T;
-  bp.B = static_cast<int>(B);
-  bp.C = static_cast<int>(C);
-  bp.n_chunks = static_cast<int>(n_chunks);
-  bp.n_wg = static_cast<int>(n_wg);
-  const long long plane = B * n_chunks * C;
-  {
-    std::lock_guard<std::mutex> lock(g_mu);
-    StreamScratch* sc = nullptr;
-    rc = get_scratch(dev, stream, 0, &sc);
-    if (rc) return rc;
-    rc = grow_zeroed(&sc->bwd, &sc->bwd_floats, 26 * plane, 1ll << 20, st, &sc->retired);
-    if (rc) return rc;
-    float* f = sc->bwd;
-    bp.s = BwdScratch{f, f + 6 * plane, f + 12 * plane, f + 18 * plane, f + 24 * plane, f + 25 * plane, plane};
-  }
-  const dim3 tiles(static_cast<unsigned>((C + 63) / 64), static_cast<unsigned>(n_wg), static_cast<unsigned>(B));
-  const dim3 wg(64 * kBwdWaves);
-  const dim3 rows(static_cast<unsigned>((C + 63) / 64), static_cast<unsigned>(B));
-  if (dtype == BIWKV_F32) {
-    hipLaunchKernelGGL(bwd_chunk_sums_kernel<BIWKV_F32>, tiles, wg, 0, st, bp);
-    hipLaunchKernelGGL(bwd_carry_kernel, rows, dim3(64 * kCarryGroups), 0, st, bp, bp.s.a1, bp.s.x1);
-    hipLaunchKernelGGL(bwd_sweep1_kernel<BIWKV_F32>, tiles, wg, 0, st, bp);
-    hipLaunchKernelGGL(bwd_carry_kernel, rows, dim3(64 * kCarryGroups), 0, st, bp, bp.s.a2, bp.s.x2);
-    hipLaunchKernelGGL(bwd_sweep2_kernel<BIWKV_F32>, tiles, wg, 0, st, bp);
-  } else {
-    hipLaunchKernelGGL(bwd_chunk_sums_kernel<BIWKV_BF16>, tiles, wg, 0, st, bp);
-    hipLaunchKernelGGL(bwd_carry_kernel, rows, dim3(64 * kCarryGroups), 0, st, bp, bp.s.a1, bp.s.x1);
-    hipLaunchKernelGGL(bwd_sweep1_kernel<BIWKV_BF16>, tiles, wg, 0, st, bp);
-    hipLaunchKernelGGL(bwd_carry_kernel, rows, dim3(64 * kCarryGroups), 0, st, bp, bp.s.a2, bp.s.x2);
-    hipLaunchKernelGGL(bwd_sweep2_kernel<BIWKV_BF16>, tiles, wg, 0, st, bp);
-  }
-  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(static_cast<unsigned>((C + 63) / 64)), dim3(64 * kReduceGroups), 0,
-                     st, bp);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return hip_fail(e);
-  return BIWKV_OK;
+  // token positions times D must be exact in fp32
+  if (T >= (1ll << 24)) return BIWKV_ERR_UNSUPPORTED;
+  return dtype == BIWKV_F32
+             ? launch_bwd_tile<BIWKV_F32, kBwdL, kBwdNT, 4>(k, v, w, u, g, dk, dv, dw, du, B, T, C, dev, stream)
+             : launch_bwd_tile<BIWKV_BF16, kBwdL, kBwdNT, 4>(k, v, w, u, g, dk, dv, dw, du, B, T, C, dev, stream);
 }
 
 int biwkv_causal_forward(const void* k, const void* v, const float* w, const float* u, float* out,

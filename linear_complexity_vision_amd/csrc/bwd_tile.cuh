@@ -1,0 +1,797 @@
+// Bi-WKV backward in one launch: the gradients of Eq. (5) (see backward.cuh for the formulas) with
+// the tile kernel's work split.
+#pragma once
+
+#include "row_kernel.cuh"
+
+namespace {
+
+// ---------------------------------------------------------------------------------------------
+// A workgroup of NT threads owns one chunk (GROUPS * L tokens) of a (batch, 64-channel tile) row;
+// lane (c, g) holds channel c at L consecutive tokens, and keeps k, v and the upstream gradient g
+// of those tokens in registers from load to store, with the output y and log2 of Eq. (5)'s
+// denominator once they are known. Two rounds of the same three steps:
+//   1. lane sums of (e^k v, e^k) in prefix and suffix form, scanned over the workgroup's groups
+//      and exchanged with the other chunks of the row; a sweep over the lane's tokens gives y and
+//      log2 D at every token;
+//   2. lane sums of (q, r) = (g, g y) / D, scanned and exchanged the same way; a sweep gives dv,
+//      dk and the dw terms at every token (the four states of the first round are formed again
+//      on the way), and the du terms.
+// A row of one chunk runs in one launch. A longer row runs in three launches of the same kernel,
+// each reading the chunk sums the one before wrote, so no workgroup waits for another:
+//   stage 1 writes every chunk's round-1 sums;
+//   stage 2 folds the other chunks' round-1 sums into its carries, sweeps round 1, and writes
+//     every chunk's round-2 sums;
+//   stage 3 does both rounds with the carries of both, and writes dk, dv and the dw, du terms.
+// The dw and du terms of a workgroup are folded per channel in LDS, in a fixed order; a last
+// kernel folds those of the row's chunks.
+//
+// Position-free sums. A prefix sum anchored at token p is 2^{-pD} sum_{t<=p} 2^{x_t + tD} y_t and a
+// suffix sum 2^{pD} sum_{t>=p} 2^{x_t - tD} y_t (D = w log2(e) / T), so a term's exponent is fixed
+// once and sums over any set of tokens are plain sums: the scans and the exchange move no
+// exponent. A sum is an aggregate (m, F, G) = (F, G) 2^m. In the round-1 sweep the running sums
+// of (e^k v, e^k) take each term at their running maximum (two exp2 per term), so their exponent
+// is that of their largest term and the denominator of y is always formed against a term it
+// contains. In the round-2 sweep a running sum keeps one exponent per sub-block of SB tokens (the
+// larger of its own and the sub-block's largest term) and each term costs one exp2. The products
+// b Qpre, d Rpre, a Qsuf, c Rsuf of dw pair a prefix with a suffix sum at the same token, so
+// their position factors cancel and leave 2^{2D}.
+//
+// Precision: lane and sub-block sums form their terms against the largest of them, so a term
+// more than 2^-126 below it is lost; exponents inside a sub-block differ by the keys' spread plus
+// (SB - 1) |D|. The round-2 factors e^{k_i} 2^{exponent of a running sum} are at most
+// 2^{2 (SB - 1) |D|} (a weight p_ti <= 1 times the sub-block's spread of positions), finite for
+// |w| / T below about 20 (every workload has |w| / T < 0.05).
+// ---------------------------------------------------------------------------------------------
+
+constexpr int kBtTile = 64;  // channels per tile (one wavefront)
+constexpr int kBtSB = 4;     // tokens per sub-block of the sweeps
+
+struct BwdTileParams {
+  const void* k;
+  const void* v;
+  const float* w;
+  const float* u;
+  const float* g;
+  float* dk;
+  float* dv;
+  float* pw;  // dw terms per (batch item, chunk, channel), before the factor -lam / T
+  float* pu;  // du terms per (batch item, chunk, channel)
+  float* sums1;  // round-1 chunk sums: [row][chunk][dir][64][3] floats (m, F, G)
+  float* sums2;  // round-2 chunk sums, same layout
+  long long T;
+  int C;
+  int n_tiles;   // channel tiles per batch item
+  int n_chunks;  // chunks per row
+};
+
+// Makes register values opaque to the compiler (no instruction), so that values derived from them
+// in one phase are formed again in the next instead of being kept live in between.
+template <int N>
+__device__ __forceinline__ void bt_fence(float (&x)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(x[i]));
+}
+__device__ __forceinline__ void bt_fence(float& x) { asm volatile("" : "+v"(x)); }
+
+// Per-lane token storage: bf16 k and v packed in one register (k low, v high), fp32 in two; empty
+// slots (past the row, or a masked channel) hold k = -inf, v = 0.
+template <int DT, int L>
+struct BtKV;
+template <int L>
+struct BtKV<BIWKV_BF16, L> {
+  uint32_t r[L];
+  __device__ __forceinline__ float k(int i) const { return __uint_as_float(r[i] << 16); }
+  __device__ __forceinline__ float v(int i) const { return __uint_as_float(r[i] & 0xffff0000u); }
+  __device__ __forceinline__ void fence() {
+#pragma unroll
+    for (int i = 0; i < L; ++i) asm volatile("" : "+v"(r[i]));
+  }
+  __device__ __forceinline__ void load(const void* kp, const void* vp, long long e, bool ok, int i) {
+    const uint32_t kx = ok ? static_cast<const uint16_t*>(kp)[e] : 0xff80u;  // bf16 -inf
+    const uint32_t vx = ok ? static_cast<const uint16_t*>(vp)[e] : 0u;
+    r[i] = kx | (vx << 16);
+  }
+};
+template <int L>
+struct BtKV<BIWKV_F32, L> {
+  float kk[L], vv[L];
+  __device__ __forceinline__ float k(int i) const { return kk[i]; }
+  __device__ __forceinline__ float v(int i) const { return vv[i]; }
+  __device__ __forceinline__ void fence() {
+    bt_fence(kk);
+    bt_fence(vv);
+  }
+  __device__ __forceinline__ void load(const void* kp, const void* vp, long long e, bool ok, int i) {
+    kk[i] = ok ? static_cast<const float*>(kp)[e] : kNegInf;
+    vv[i] = ok ? static_cast<const float*>(vp)[e] : 0.f;
+  }
+};
+
+// The larger of an aggregate's exponent and mx, and the aggregate rescaled to it.
+__device__ __forceinline__ Agg bt_rebase(Agg a, float mx) {
+  const float r = fmaxf(a.m, mx);
+  const float s = fast_exp2(a.m - r);
+  return Agg{r, a.F * s, a.G * s};
+}
+
+// An aggregate of SB terms 2^{x_i} (F_i, G_i) against their largest exponent (empty: kEmptyM).
+template <int SB>
+__device__ __forceinline__ Agg bt_block(const float (&x)[SB], const float (&F)[SB], const float (&G)[SB]) {
+  float mx = kNegInf;
+#pragma unroll
+  for (int i = 0; i < SB; ++i) mx = fmaxf(mx, x[i]);
+  const float ref = mx == kNegInf ? 0.f : mx;
+  Agg a{mx == kNegInf ? kEmptyM : mx, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < SB; ++i) {
+    const float e = fast_exp2(x[i] - ref);
+    a.F = fmaf(e, F[i], a.F);
+    a.G = fmaf(e, G[i], a.G);
+  }
+  return a;
+}
+
+template <int NT>
+constexpr int kBtRedFloats = 6 * (NT / kBtTile) * (kBtTile + 1);
+
+// LDS of the backward tile kernel.
+template <int NT>
+struct BtShared {
+  float sw[4][kBtSB][NT];          // sweep records of one sub-block
+  float red[kBtRedFloats<NT>];     // lane sums (group-major)
+  float xy[kBtRedFloats<NT>];      // carries
+  float dch[kBtTile];              // D of each channel of the tile
+  float fold[2][NT / kBtTile][kBtTile];  // dw and du terms of each lane
+};
+
+// Lane constants: lane (c, g) of the workgroup for chunk `chunk` of row `row` holds channel ch of
+// batch item bi at the tokens [s_g, s_g + L).
+struct BtLane {
+  int row, chunk, bi, ch, c, g;
+  bool on;
+  long long s_g, row0;  // first token; element index of (bi, token 0, ch)
+  float D, U;           // w log2(e) / T and u log2(e) of the channel (0 when masked)
+};
+
+template <int L, int NT>
+__device__ __forceinline__ BtLane bt_lane(const BwdTileParams& p, unsigned unit) {
+  constexpr int CT = (NT / kBtTile) * L;
+  BtLane ln;
+  const int tid = threadIdx.x;
+  ln.c = tid % kBtTile;
+  ln.g = tid / kBtTile;
+  ln.row = __builtin_amdgcn_readfirstlane(unit / static_cast<unsigned>(p.n_chunks));
+  ln.chunk = static_cast<int>(unit) - ln.row * p.n_chunks;
+  ln.bi = __builtin_amdgcn_readfirstlane(ln.row / p.n_tiles);
+  const int tile = ln.row - ln.bi * p.n_tiles;
+  ln.ch = tile * kBtTile + ln.c;
+  ln.on = ln.ch < p.C;
+  ln.s_g = static_cast<long long>(ln.chunk) * CT + static_cast<long long>(ln.g) * L;
+  ln.D = ln.on ? (p.w[ln.ch] / static_cast<float>(p.T)) * kLog2e : 0.f;
+  ln.U = ln.on ? p.u[ln.ch] * kLog2e : 0.f;
+  ln.row0 = static_cast<long long>(ln.bi) * p.T * p.C + ln.ch;
+  return ln;
+}
+
+template <int DT, int L>
+__device__ __forceinline__ void bt_load(const BwdTileParams& p, const BtLane& ln, BtKV<DT, L>& kv, float (&gg)[L]) {
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    const long long t = ln.s_g + i;
+    const bool ok = ln.on && t < p.T;
+    const long long e = ln.row0 + t * p.C;
+    kv.load(p.k, p.v, e, ok, i);
+    gg[i] = ok ? p.g[e] : 0.f;
+  }
+}
+
+enum : int { kBtLocal = 0, kBtProduce = 1, kBtConsume = 2 };
+
+// Scan of the lane sums over the workgroup's groups, and the chunk sums of the row. In: the lane's
+// forward sum f and backward sum b. Out: X, the sum over every token of the row before the lane,
+// and Y, over every token after it. Position-free sums (ANCHORED false) are plain sums in a fixed
+// order; anchored sums (f at the lane's last slot, b at its first token; X anchored just before
+// the lane, Y just after it) move by n tokens with exponent shifts of n D, as in the forward tile
+// kernel. The lane sums go through LDS into the forward tile kernel's transposed layout (a
+// channel's groups on consecutive lanes of one wavefront). MODE:
+//   kBtLocal: the row is one chunk, X and Y come from the scan;
+//   kBtProduce: the chunk's sums (forward at its last slot, backward at its first token) go to
+//     sums for a later launch, and X, Y are not formed;
+//   kBtConsume: the sums of the row's other chunks, written by an earlier launch, are folded in a
+//     fixed order into X and Y (entries in order per lane, then a fixed tree over the lanes).
+template <int NT, int L, bool ANCHORED, int MODE>
+__device__ __forceinline__ void bt_carries(Agg f, Agg b, Agg& X, Agg& Y, BtShared<NT>* sh, float* sums,
+                                           const BwdTileParams& p, const BtLane& ln) {
+  constexpr int GROUPS = NT / kBtTile;
+  constexpr int PAD = kBtTile + 1;
+  constexpr int RS = GROUPS * PAD;
+  constexpr int CT = GROUPS * L;
+  float* red = sh->red;
+  float* xy = sh->xy;
+  const int tid = threadIdx.x;
+  const int wi = ln.g * PAD + ln.c;
+  red[0 * RS + wi] = f.m;
+  red[1 * RS + wi] = f.F;
+  red[2 * RS + wi] = f.G;
+  red[3 * RS + wi] = b.m;
+  red[4 * RS + wi] = b.F;
+  red[5 * RS + wi] = b.G;
+  __syncthreads();
+  const int tg = tid % GROUPS, tc = tid / GROUPS;
+  const int ti = tg * PAD + tc;
+  const float Dt = ANCHORED ? sh->dch[tc] : 0.f;
+  Agg sf{red[0 * RS + ti], red[1 * RS + ti], red[2 * RS + ti]};
+  Agg sb{red[3 * RS + ti], red[4 * RS + ti], red[5 * RS + ti]};
+  group_scan<GROUPS, L, true>(sf, sb, tg, Dt);
+  const int nch = p.n_chunks, chunk = ln.chunk;
+  float* rs = sums + static_cast<size_t>(ln.row) * nch * 2 * kBtTile * 3;
+  auto slot = [&](int ck, int dir) { return rs + (static_cast<size_t>(ck * 2 + dir) * kBtTile + tc) * 3; };
+  if constexpr (MODE == kBtProduce) {
+    if (tg == GROUPS - 1) {
+      float* o = slot(chunk, kFwd);
+      o[0] = sf.m;
+      o[1] = sf.F;
+      o[2] = sf.G;
+    }
+    if (tg == 0) {
+      float* o = slot(chunk, kBwd);
+      o[0] = sb.m;
+      o[1] = sb.F;
+      o[2] = sb.G;
+    }
+  } else {
+    Agg x = agg_from_below<GROUPS, 1>(sf), y = agg_from_above<GROUPS, 1>(sb);
+    if (tg == 0) x = row_empty();
+    if (tg == GROUPS - 1) y = row_empty();
+    if constexpr (MODE == kBtConsume) {
+      // entries: forward sums of chunks 0 .. chunk-1, then backward sums of chunks chunk+1 ..
+      // nch-1; lane tg takes entries tg, tg + GROUPS, ..., EB of them in flight at once
+      const int ne = nch - 1;
+      Agg pf = row_empty(), pb = row_empty();
+      constexpr int EB = 4;
+      for (int e0 = tg; e0 < ne; e0 += EB * GROUPS) {
+        float ev[EB][3];
+#pragma unroll
+        for (int j = 0; j < EB; ++j) {
+          const int e = e0 + j * GROUPS;
+          if (e < ne) {
+            const float* s = slot(e < chunk ? e : e + 1, e < chunk ? kFwd : kBwd);
+            ev[j][0] = s[0];
+            ev[j][1] = s[1];
+            ev[j][2] = s[2];
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < EB; ++j) {
+          const int e = e0 + j * GROUPS;
+          if (e >= ne) break;
+          const bool fwd = e < chunk;
+          Agg a{ev[j][0], ev[j][1], ev[j][2]};
+          if constexpr (ANCHORED)  // from the entry's anchor to this chunk's carry anchor
+            a = agg_shift(a, static_cast<float>(fwd ? (chunk - 1 - e) : (e - chunk)) * CT, Dt);
+          if (fwd)
+            pf = agg_add_f(pf, a);
+          else
+            pb = agg_add_f(pb, a);
+        }
+      }
+      group_fold<GROUPS, true>(pf, pb, tg);
+      pf = agg_from_first<GROUPS>(pf);
+      pb = agg_from_first<GROUPS>(pb);
+      if constexpr (ANCHORED) {  // from just before (after) the chunk to just before (after) group tg
+        pf = agg_shift(pf, static_cast<float>(tg * L), Dt);
+        pb = agg_shift(pb, static_cast<float>((GROUPS - 1 - tg) * L), Dt);
+      }
+      x = agg_add_f(pf, x);
+      y = agg_add_f(y, pb);
+    }
+    xy[0 * RS + ti] = x.m;
+    xy[1 * RS + ti] = x.F;
+    xy[2 * RS + ti] = x.G;
+    xy[3 * RS + ti] = y.m;
+    xy[4 * RS + ti] = y.F;
+    xy[5 * RS + ti] = y.G;
+    __syncthreads();
+    X = Agg{xy[0 * RS + wi], xy[1 * RS + wi], xy[2 * RS + wi]};
+    Y = Agg{xy[3 * RS + wi], xy[4 * RS + wi], xy[5 * RS + wi]};
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Wide form (any w, u): position-free sums, running maxima. Returns the lane's (dw, du) terms.
+// Out of line: it needs more registers than the fast form, and keeping it apart gives it its own
+// allocation. It reads the parameters through the kernel's argument pointer.
+// ---------------------------------------------------------------------------------------------
+template <int DT, int L, int NT, int STAGE>
+__device__ __noinline__ float2 bt_body_wide(const BwdTileParams* args, BtShared<NT>* sh) {
+  constexpr int SB = kBtSB;
+  constexpr int NSB = L / SB;
+  constexpr int MODE = STAGE == 0 ? kBtLocal : kBtConsume;  // when a round's carries are formed
+  const BwdTileParams p = *args;
+  const BtLane lnv = bt_lane<L, NT>(p, blockIdx.x);
+  const int tid = threadIdx.x;
+  const bool on = lnv.on;
+  const long long T = p.T, s_g = lnv.s_g, row0 = lnv.row0;
+  const float D = lnv.D, U = lnv.U;
+  auto& sw = sh->sw;
+  BtKV<DT, L> kv;
+  float gg[L];
+  bt_load<DT, L>(p, lnv, kv, gg);
+  // token position times D, exact for t < 2^24
+  float Dp = D;  // the copy positions are formed from, made opaque between phases
+  auto tD = [&](int i) { return static_cast<float>(s_g + i) * Dp; };
+  auto kl = [&](int i) { return kv.k(i) * kLog2e; };  // -inf in empty slots
+
+  // ---- round 1: lane sums of (e^k v, e^k), prefix form and (per sub-block) suffix form ----
+  Agg lane_f = row_empty();
+  Agg cap1[NSB];  // suffix-form sum of the lane's sub-blocks after q
+  {
+    Agg sbs[NSB];
+#pragma unroll
+    for (int q = 0; q < NSB; ++q) {
+      float xp[SB], xs[SB], vv[SB], one[SB];
+#pragma unroll
+      for (int i = 0; i < SB; ++i) {
+        const int j = q * SB + i;
+        xp[i] = kl(j) + tD(j);
+        xs[i] = kl(j) - tD(j);
+        vv[i] = kv.v(j);
+        one[i] = 1.f;
+      }
+      lane_f = agg_add_f(lane_f, bt_block<SB>(xp, vv, one));
+      sbs[q] = bt_block<SB>(xs, vv, one);
+      __builtin_amdgcn_sched_barrier(0);  // one sub-block at a time (bounded live values)
+    }
+    Agg run = row_empty();
+#pragma unroll
+    for (int q = NSB - 1; q >= 0; --q) {
+      cap1[q] = run;
+      run = agg_add_f(sbs[q], run);
+    }
+    Agg Xc, Yc;
+    if constexpr (STAGE == 1) {
+      bt_carries<NT, L, false, kBtProduce>(lane_f, run, Xc, Yc, sh, p.sums1, p, lnv);
+      return make_float2(0.f, 0.f);
+    }
+    bt_carries<NT, L, false, MODE>(lane_f, run, Xc, Yc, sh, p.sums1, p, lnv);
+    lane_f = Xc;
+    // from here cap1[q] is the suffix-form sum of every token after sub-block q
+#pragma unroll
+    for (int q = 0; q < NSB; ++q) cap1[q] = agg_add_f(Yc, cap1[q]);
+  }
+  const Agg X1 = lane_f;  // prefix-form sum of every token before the lane
+  // values derived from the stored tokens are formed again in each phase, not kept live
+  auto fence_all = [&]() {
+    kv.fence();
+    bt_fence(gg);
+    bt_fence(Dp);
+  };
+  fence_all();
+
+  // ---- round 1 sweep: y and log2 D at every token ----
+  float y[L], nl[L];  // output and -log2 of the denominator (-inf in empty slots)
+  {
+    Agg A = X1;
+#pragma unroll
+    for (int q = 0; q < NSB; ++q) {
+#pragma unroll
+      for (int i = 0; i < SB; ++i) {
+        const int j = q * SB + i;
+        sw[0][i][tid] = A.m;
+        sw[1][i][tid] = A.F;
+        sw[2][i][tid] = A.G;
+        A = agg_add_f(A, Agg{kl(j) + tD(j), kv.v(j), 1.f});
+      }
+      Agg Bs = cap1[q];
+#pragma unroll
+      for (int i = SB - 1; i >= 0; --i) {
+        const int j = q * SB + i;
+        const float t = static_cast<float>(s_g + j);
+        const float am = sw[0][i][tid], aF = sw[1][i][tid], aG = sw[2][i][tid];
+        // Eq. (7): (a + b + e^{u+k} v) / (c + d + e^{u+k}); a, c anchored at t - 1, b, d at t + 1
+        const float xa = am - (t - 1.f) * D, xb = Bs.m + (t + 1.f) * D, xe = kl(j) + U;
+        const float M = fmaxf(fmaxf(xa, xb), xe);
+        const float sa = fast_exp2(xa - M), sb = fast_exp2(xb - M), se = fast_exp2(xe - M);
+        const float vj = kv.v(j);
+        const float num = fmaf(aF, sa, fmaf(Bs.F, sb, se * vj));
+        const float den = fmaf(aG, sa, fmaf(Bs.G, sb, se));  // >= 1: M is a term's exponent
+        const bool live = xe != kNegInf;
+        y[j] = live ? num * fast_rcp(den) : 0.f;
+        nl[j] = live ? -(M + fast_log2(den)) : kNegInf;
+        Bs = agg_add_f(Bs, Agg{kl(j) - tD(j), vj, 1.f});
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  fence_all();
+  bt_fence(y);
+  bt_fence(nl);
+
+  // ---- round 2: lane sums of (q, r) = (g, g y) 2^{-log2 D}; du terms ----
+  Agg X2;
+  Agg cap2[NSB];
+  float du = 0.f;
+  {
+    Agg lane2 = row_empty();
+    Agg sbs[NSB];
+#pragma unroll
+    for (int q = 0; q < NSB; ++q) {
+      float xp[SB], xs[SB], qq[SB], rr[SB];
+#pragma unroll
+      for (int i = 0; i < SB; ++i) {
+        const int j = q * SB + i;
+        xp[i] = nl[j] + tD(j);
+        xs[i] = nl[j] - tD(j);
+        qq[i] = gg[j];
+        rr[i] = gg[j] * y[j];
+        // e^{u+k} (q v - r) = p_tt g (v - y)
+        du = fmaf(fast_exp2(U + kl(j) + nl[j]) * gg[j], kv.v(j) - y[j], du);
+      }
+      lane2 = agg_add_f(lane2, bt_block<SB>(xp, qq, rr));
+      sbs[q] = bt_block<SB>(xs, qq, rr);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    Agg run = row_empty();
+#pragma unroll
+    for (int q = NSB - 1; q >= 0; --q) {
+      cap2[q] = run;
+      run = agg_add_f(sbs[q], run);
+    }
+    Agg Y2;
+    if constexpr (STAGE == 2) {
+      bt_carries<NT, L, false, kBtProduce>(lane2, run, X2, Y2, sh, p.sums2, p, lnv);
+      return make_float2(0.f, 0.f);
+    }
+    bt_carries<NT, L, false, MODE>(lane2, run, X2, Y2, sh, p.sums2, p, lnv);
+#pragma unroll
+    for (int q = 0; q < NSB; ++q) cap2[q] = agg_add_f(Y2, cap2[q]);
+  }
+
+  fence_all();
+  bt_fence(y);
+  bt_fence(nl);
+
+  // ---- round 2 sweep: dv, dk and the dw terms ----
+  float dw1 = 0.f, dw2 = 0.f;  // sum b Qpre - d Rpre (against 2^e1), sum a Qsuf - c Rsuf (2^e2)
+  float e1 = kEmptyM, e2 = kEmptyM;
+  {
+    Agg A = X1, QA = X2;
+#pragma unroll
+    for (int q = 0; q < NSB; ++q) {
+      float mx = kNegInf, mq = kNegInf;
+#pragma unroll
+      for (int i = 0; i < SB; ++i) {
+        mx = fmaxf(mx, kl(q * SB + i) + tD(q * SB + i));
+        mq = fmaxf(mq, nl[q * SB + i] + tD(q * SB + i));
+      }
+      // one exponent per running sum for the whole sub-block
+      A = bt_rebase(A, mx);
+      QA = bt_rebase(QA, mq);
+#pragma unroll
+      for (int i = 0; i < SB; ++i) {
+        const int j = q * SB + i;
+        sw[0][i][tid] = A.F;
+        sw[1][i][tid] = A.G;
+        sw[2][i][tid] = QA.F;
+        sw[3][i][tid] = QA.G;
+        const float e = fast_exp2(kl(j) + tD(j) - A.m);
+        A.F = fmaf(e, kv.v(j), A.F);
+        A.G += e;
+        const float eq = fast_exp2(nl[j] + tD(j) - QA.m);
+        QA.F = fmaf(eq, gg[j], QA.F);
+        QA.G = fmaf(eq, gg[j] * y[j], QA.G);
+      }
+      float ms = kNegInf, mqs = kNegInf;
+#pragma unroll
+      for (int i = 0; i < SB; ++i) {
+        ms = fmaxf(ms, kl(q * SB + i) - tD(q * SB + i));
+        mqs = fmaxf(mqs, nl[q * SB + i] - tD(q * SB + i));
+      }
+      Agg Bs = bt_rebase(cap1[q], ms), QB = bt_rebase(cap2[q], mqs);
+      float s1 = 0.f, s2 = 0.f;  // against 2^{Bs.m + QA.m} and 2^{A.m + QB.m}
+#pragma unroll
+      for (int i = SB - 1; i >= 0; --i) {
+        const int j = q * SB + i;
+        const long long tt = s_g + j;
+        const float t = static_cast<float>(tt);
+        const float aF = sw[0][i][tid], aG = sw[1][i][tid];
+        const float qF = sw[2][i][tid], qG = sw[3][i][tid];
+        // b Qpre - d Rpre and a Qsuf - c Rsuf at this token (their position factors cancel)
+        s1 = fmaf(Bs.F, qF, fmaf(-Bs.G, qG, s1));
+        s2 = fmaf(aF, QB.F, fmaf(-aG, QB.G, s2));
+        // e^{k} (Qpre + Qsuf + e^u q) and the same over r
+        const float k2 = kl(j);
+        const float c1 = qF != 0.f || qG != 0.f ? fast_exp2(QA.m - (t - 1.f) * D + k2) : 0.f;
+        const float c2 = QB.F != 0.f || QB.G != 0.f ? fast_exp2(QB.m + (t + 1.f) * D + k2) : 0.f;
+        const float c3 = fast_exp2(U + nl[j] + k2);
+        const float dvj = fmaf(qF, c1, fmaf(QB.F, c2, gg[j] * c3));
+        const float rj = fmaf(qG, c1, fmaf(QB.G, c2, gg[j] * y[j] * c3));
+        const float dkj = fmaf(kv.v(j), dvj, -rj);
+        if (on && tt < T) {
+          const long long e = row0 + tt * p.C;
+          p.dv[e] = dvj;
+          p.dk[e] = dkj;
+        }
+        const float e = fast_exp2(k2 - tD(j) - Bs.m);
+        Bs.F = fmaf(e, kv.v(j), Bs.F);
+        Bs.G += e;
+        const float eq = fast_exp2(nl[j] - tD(j) - QB.m);
+        QB.F = fmaf(eq, gg[j], QB.F);
+        QB.G = fmaf(eq, gg[j] * y[j], QB.G);
+      }
+      // fold the sub-block's dw sums into the lane's, at the larger exponent
+      const float f1 = Bs.m + QA.m, f2 = A.m + QB.m;
+      const float m1 = fmaxf(e1, f1), m2 = fmaxf(e2, f2);
+      dw1 = fmaf(dw1, fast_exp2(e1 - m1), s1 * fast_exp2(f1 - m1));
+      dw2 = fmaf(dw2, fast_exp2(e2 - m2), s2 * fast_exp2(f2 - m2));
+      e1 = m1;
+      e2 = m2;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // the lane's dw terms: (sum1 2^{e1} + sum2 2^{e2}) 2^{2D}
+  float dw = 0.f;
+  if (e1 > kEmptyM) dw += dw1 * fast_exp2(e1 + 2.f * D);
+  if (e2 > kEmptyM) dw += dw2 * fast_exp2(e2 + 2.f * D);
+
+  return make_float2(dw, du);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Fast form: the lane's terms are formed against one reference per lane and the states of Eq. (6)
+// move one token with a multiply by lam = 2^{-D}, as in the forward tile kernel's fast form.
+// Round 1 keys k, values (v, 1); round 2 keys -log2 D_t, values (g, g y). Lane sums are anchored
+// (forward at the lane's last slot, backward at its first token) and the scan and exchange move
+// them with exponent shifts. Valid while the growth across a lane, |D| (L - 1), stays within
+// kBtFastRange: every state is then at least 2^{-2 span} of its largest term, so the products of
+// a round-1 and a round-2 state in dw stay normal numbers; and while |u| log2(e) <= kBonusRange.
+// ---------------------------------------------------------------------------------------------
+constexpr float kBtFastRange = 24.f;
+
+template <int DT, int L, int NT, int STAGE>
+__device__ __forceinline__ float2 bt_body_fast(const BwdTileParams& p, const BtLane& ln, BtShared<NT>* sh) {
+  constexpr int SB = kBtSB;
+  constexpr int NSB = L / SB;
+  constexpr int MODE = STAGE == 0 ? kBtLocal : kBtConsume;  // when a round's carries are formed
+  const int tid = threadIdx.x;
+  const float D = ln.D, U = ln.U;
+  const float lam = fast_exp2(-D);
+  const float span = fmaxf(-D, 0.f) * static_cast<float>(L - 1);  // largest growth inside a lane
+  const float eU = fast_exp2(U);
+  auto& sw = sh->sw;
+  BtKV<DT, L> kv;
+  float gg[L];
+  bt_load<DT, L>(p, ln, kv, gg);
+  auto kl = [&](int i) { return kv.k(i) * kLog2e; };  // -inf in empty slots
+
+  // ---- round 1 lane sums (against 2^{kmax + span}) and the caps: backward sums of the lane's
+  //      sub-blocks after q, anchored at the first token after sub-block q ----
+  float kmax = kNegInf;
+#pragma unroll
+  for (int i = 0; i < L; ++i) kmax = fmaxf(kmax, kl(i));
+  float capF[NSB], capG[NSB];
+  Agg X, Y;
+  {
+    const float ref = kmax == kNegInf ? 0.f : kmax + span;
+    float pp[L];
+#pragma unroll
+    for (int i = 0; i < L; ++i) pp[i] = fast_exp2(kl(i) - ref);
+    float fF = 0.f, fG = 0.f, cF = 0.f, cG = 0.f;
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      fF = fmaf(fF, lam, pp[i] * kv.v(i));
+      fG = fmaf(fG, lam, pp[i]);
+    }
+#pragma unroll
+    for (int q = NSB - 1; q >= 0; --q) {
+      capF[q] = cF;
+      capG[q] = cG;
+#pragma unroll
+      for (int i = (q + 1) * SB - 1; i >= q * SB; --i) {
+        cF = fmaf(cF, lam, pp[i] * kv.v(i));
+        cG = fmaf(cG, lam, pp[i]);
+      }
+    }
+    const float m = kmax == kNegInf ? kEmptyM : ref;
+    if constexpr (STAGE == 1) {
+      bt_carries<NT, L, true, kBtProduce>(Agg{m, fF, fG}, Agg{m, cF, cG}, X, Y, sh, p.sums1, p, ln);
+      return make_float2(0.f, 0.f);
+    }
+    bt_carries<NT, L, true, MODE>(Agg{m, fF, fG}, Agg{m, cF, cG}, X, Y, sh, p.sums1, p, ln);
+  }
+  kv.fence();
+  bt_fence(gg);
+
+  // ---- round 1 sweep: y and log2 of the denominator at every token, against 2^M ----
+  const float top = fmaxf(fmaxf(kmax, X.m), Y.m);
+  const float M = top + span;
+  const float sig = fast_exp2(kmax - top);  // the caps' scale against 2^M
+  const float sx = fast_exp2(X.m - M), sy = fast_exp2(Y.m - M);
+  const float YF = Y.F * sy, YG = Y.G * sy;
+  float y[L], nl[L];  // output and -log2 of the denominator (-inf in empty slots)
+  {
+    float A = X.F * sx, Cs = X.G * sx;
+#pragma unroll
+    for (int q = 0; q < NSB; ++q) {
+      float ph[SB];
+#pragma unroll
+      for (int i = 0; i < SB; ++i) {
+        const int j = q * SB + i;
+        ph[i] = fast_exp2(kl(j) - M);
+        sw[0][i][tid] = A;
+        sw[1][i][tid] = Cs;
+        A = fmaf(A, lam, ph[i] * kv.v(j));
+        Cs = fmaf(Cs, lam, ph[i]);
+      }
+      // backward states entering from the right: the lane's later sub-blocks and later tokens
+      const float lr = fast_exp2(-static_cast<float>(L - (q + 1) * SB) * D);
+      float Bs = fmaf(YF, lr, sig * capF[q]), Ds = fmaf(YG, lr, sig * capG[q]);
+#pragma unroll
+      for (int i = SB - 1; i >= 0; --i) {
+        const int j = q * SB + i;
+        const float vj = kv.v(j);
+        const float e = ph[i] * eU;
+        const float num = sw[0][i][tid] + fmaf(e, vj, Bs);
+        const float den = sw[1][i][tid] + Ds + e;
+        const bool live = kv.k(j) != kNegInf;
+        y[j] = live ? num * fast_rcp(den) : 0.f;
+        nl[j] = live ? -(M + fast_log2(den)) : kNegInf;
+        Bs = fmaf(Bs, lam, ph[i] * vj);
+        Ds = fmaf(Ds, lam, ph[i]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  kv.fence();
+  bt_fence(gg);
+  bt_fence(y);
+  bt_fence(nl);
+
+  // ---- round 2 lane sums of (q, r) = (g, g y) 2^{-log2 D} and caps; du terms ----
+  float qmax = kNegInf;
+#pragma unroll
+  for (int i = 0; i < L; ++i) qmax = fmaxf(qmax, nl[i]);
+  float capQ[NSB], capR[NSB];
+  Agg X2, Y2;
+  float du = 0.f;
+  {
+    const float ref = qmax == kNegInf ? 0.f : qmax + span;
+    float qq[L];
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      qq[i] = fast_exp2(nl[i] - ref) * gg[i];
+      // e^{u+k} (q v - r) = p_tt g (v - y)
+      du = fmaf(fast_exp2(U + kl(i) + nl[i]) * gg[i], kv.v(i) - y[i], du);
+    }
+    float fQ = 0.f, fR = 0.f, cQ = 0.f, cR = 0.f;
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      fQ = fmaf(fQ, lam, qq[i]);
+      fR = fmaf(fR, lam, qq[i] * y[i]);
+    }
+#pragma unroll
+    for (int q = NSB - 1; q >= 0; --q) {
+      capQ[q] = cQ;
+      capR[q] = cR;
+#pragma unroll
+      for (int i = (q + 1) * SB - 1; i >= q * SB; --i) {
+        cQ = fmaf(cQ, lam, qq[i]);
+        cR = fmaf(cR, lam, qq[i] * y[i]);
+      }
+    }
+    const float m = qmax == kNegInf ? kEmptyM : ref;
+    if constexpr (STAGE == 2) {
+      bt_carries<NT, L, true, kBtProduce>(Agg{m, fQ, fR}, Agg{m, cQ, cR}, X2, Y2, sh, p.sums2, p, ln);
+      return make_float2(0.f, 0.f);
+    }
+    bt_carries<NT, L, true, MODE>(Agg{m, fQ, fR}, Agg{m, cQ, cR}, X2, Y2, sh, p.sums2, p, ln);
+  }
+  kv.fence();
+  bt_fence(gg);
+  bt_fence(y);
+  bt_fence(nl);
+
+  // ---- round 2 sweep: dv, dk and the dw terms, against 2^M (round 1) and 2^Mq (round 2) ----
+  const float topq = fmaxf(fmaxf(qmax, X2.m), Y2.m);
+  const float Mq = topq + span;
+  const float sigq = fast_exp2(qmax - topq);
+  const float sqx = fast_exp2(X2.m - Mq), sqy = fast_exp2(Y2.m - Mq);
+  const float YQ = Y2.F * sqy, YR = Y2.G * sqy;
+  float dwacc = 0.f;  // sum over tokens of b Qpre - d Rpre + a Qsuf - c Rsuf, against 2^{M + Mq}
+  {
+    float A = X.F * sx, Cs = X.G * sx, QA = X2.F * sqx, QR = X2.G * sqx;
+#pragma unroll
+    for (int q = 0; q < NSB; ++q) {
+      float ph[SB], qh[SB];
+#pragma unroll
+      for (int i = 0; i < SB; ++i) {
+        const int j = q * SB + i;
+        ph[i] = fast_exp2(kl(j) - M);
+        qh[i] = fast_exp2(nl[j] - Mq) * gg[j];
+        sw[0][i][tid] = A;
+        sw[1][i][tid] = Cs;
+        sw[2][i][tid] = QA;
+        sw[3][i][tid] = QR;
+        A = fmaf(A, lam, ph[i] * kv.v(j));
+        Cs = fmaf(Cs, lam, ph[i]);
+        QA = fmaf(QA, lam, qh[i]);
+        QR = fmaf(QR, lam, qh[i] * y[j]);
+      }
+      const float lr = fast_exp2(-static_cast<float>(L - (q + 1) * SB) * D);
+      float Bs = fmaf(YF, lr, sig * capF[q]), Ds = fmaf(YG, lr, sig * capG[q]);
+      float QB = fmaf(YQ, lr, sigq * capQ[q]), QRB = fmaf(YR, lr, sigq * capR[q]);
+#pragma unroll
+      for (int i = SB - 1; i >= 0; --i) {
+        const int j = q * SB + i;
+        const long long tt = ln.s_g + j;
+        const float a = sw[0][i][tid], c = sw[1][i][tid], qa = sw[2][i][tid], qr = sw[3][i][tid];
+        dwacc = fmaf(Bs, qa, fmaf(-Ds, qr, fmaf(a, QB, fmaf(-c, QRB, dwacc))));
+        // e^{k} (Qpre + Qsuf + e^u q) and the same over r
+        const float vj = kv.v(j);
+        const float K = fast_exp2(kl(j) + Mq);
+        const float self = qh[i] * eU;
+        const float dvj = K * (qa + QB + self);
+        const float rj = K * (qr + QRB + self * y[j]);
+        if (ln.on && tt < p.T) {
+          const long long e = ln.row0 + tt * p.C;
+          p.dv[e] = dvj;
+          p.dk[e] = fmaf(vj, dvj, -rj);
+        }
+        Bs = fmaf(Bs, lam, ph[i] * vj);
+        Ds = fmaf(Ds, lam, ph[i]);
+        QB = fmaf(QB, lam, qh[i]);
+        QRB = fmaf(QRB, lam, qh[i] * y[j]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // a lane with no token (the end of a row) has no dw terms; its anchored carries may have moved
+  // through many empty slots of growth, so 2^{M + Mq} is not formed for it
+  const float dw = kmax != kNegInf && dwacc != 0.f ? dwacc * fast_exp2(M + Mq) : 0.f;
+  return make_float2(dw, du);
+}
+
+// STAGE 0: a row of one chunk, the whole backward. STAGE 1, 2, 3: the three launches of a longer
+// row (see the top of this file).
+template <int DT, int L, int NT, int WPE, int STAGE>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE)))
+    bwd_tile_kernel(BwdTileParams p) {
+  static_assert(L % kBtSB == 0 && NT % kBtTile == 0 && NT <= 1024, "bad backward tile shape");
+  static_assert(((NT / kBtTile) & (NT / kBtTile - 1)) == 0, "a channel's groups share a wavefront");
+  __shared__ BtShared<NT> sh;
+  const BtLane ln = bt_lane<L, NT>(p, blockIdx.x);
+  if (ln.g == 0) sh.dch[ln.c] = ln.D;  // read by the scans, after their first barrier
+  // The whole workgroup takes the wide form when any of its channels needs it; every wavefront
+  // holds all 64 channels, so a wavefront vote is the workgroup's vote (and every chunk of the
+  // row, in every stage, votes the same way).
+  const bool wide_lane =
+      fabsf(ln.D) * static_cast<float>(L - 1) > kBtFastRange || fabsf(ln.U) > kBonusRange;
+  float2 r;
+  if (__ballot(wide_lane) != 0ull) {
+    const auto* args = (const BwdTileParams*)(__builtin_amdgcn_kernarg_segment_ptr());
+    r = bt_body_wide<DT, L, NT, STAGE>(args, &sh);
+  } else {
+    r = bt_body_fast<DT, L, NT, STAGE>(p, ln, &sh);
+  }
+  if constexpr (STAGE == 0 || STAGE == 3) {
+    // ---- per-channel fold of the lanes' dw and du terms over the groups, in order ----
+    sh.fold[0][ln.g][ln.c] = r.x;
+    sh.fold[1][ln.g][ln.c] = r.y;
+    __syncthreads();
+    if (ln.g == 0 && ln.on) {
+      float a = 0.f, b = 0.f;
+#pragma unroll
+      for (int i = 0; i < NT / kBtTile; ++i) {
+        a += sh.fold[0][i][ln.c];
+        b += sh.fold[1][i][ln.c];
+      }
+      const long long at = (static_cast<long long>(ln.bi) * p.n_chunks + ln.chunk) * p.C + ln.ch;
+      p.pw[at] = a;
+      p.pu[at] = b;
+    }
+  }
+}
+
+}  // namespace
