@@ -90,7 +90,8 @@ int biwkv_forward(const void* k, const void* v, const float* w, const float* u, 
  * stream must not be made under graph capture). dw and du are folded in a fixed order: results
  * are bitwise reproducible. With B * T == 0 (and C > 0), dw and du are set to 0.
  * Errors: BIWKV_ERR_NULL, _SHAPE, _DTYPE, _ALIAS, _ALIGN, _NO_DEVICE, _HIP, and _UNSUPPORTED for
- * T >= 2^24 (token positions must be exact in fp32).
+ * T >= 2^24 (token positions must be exact in fp32) or (T + 64) * C * 4 >= 2^31 (one batch item
+ * of g is addressed with 32-bit byte offsets).
  */
 int biwkv_backward(const void* k, const void* v, const float* w, const float* u, const float* g,
                    float* dk, float* dv, float* dw, float* du, int64_t B, int64_t T, int64_t C,

@@ -457,6 +457,8 @@ int launch_bwd_tile(const void* k, const void* v, const float* w, const float* u
   const int64_t n_chunks = (T + CT - 1) / CT;
   const int64_t total = B * n_tiles * n_chunks;
   if (total > 0x7FFFFFFFll) return BIWKV_ERR_SHAPE;
+  // the loads address a batch item (fp32 g, and the row's padding) with 32-bit byte offsets
+  if ((T + CT) * C * 4 >= (1ll << 31)) return BIWKV_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
   BwdTileParams tp{};
   {
@@ -488,7 +490,11 @@ int launch_bwd_tile(const void* k, const void* v, const float* w, const float* u
   if (n_chunks == 1) {
     hipLaunchKernelGGL((bwd_tile_kernel<DT, L, NT, WPE, 0>), grid, block, 0, st, tp);
   } else {
-    hipLaunchKernelGGL((bwd_tile_kernel<DT, L, NT, WPE, 1>), grid, block, 0, st, tp);
+    // stage 1: one lane per (channel, chunk); 8 chunks of a row per workgroup
+    constexpr int SNT = 512;
+    const dim3 sgrid(static_cast<unsigned>((n_chunks + SNT / kBtTile - 1) / (SNT / kBtTile)),
+                     static_cast<unsigned>(B * n_tiles));
+    hipLaunchKernelGGL((bwd_chunk_sums_kernel<DT, CT, SNT>), sgrid, dim3(SNT), 0, st, tp);
     hipLaunchKernelGGL((bwd_tile_kernel<DT, L, NT, WPE, 2>), grid, block, 0, st, tp);
     hipLaunchKernelGGL((bwd_tile_kernel<DT, L, NT, WPE, 3>), grid, block, 0, st, tp);
   }

@@ -87,11 +87,12 @@ struct BtKV<BIWKV_BF16, L> {
 #pragma unroll
     for (int i = 0; i < L; ++i) asm volatile("" : "+v"(r[i]));
   }
-  __device__ __forceinline__ void load(const void* kp, const void* vp, long long e, bool ok, int i) {
-    const uint32_t kx = ok ? static_cast<const uint16_t*>(kp)[e] : 0xff80u;  // bf16 -inf
-    const uint32_t vx = ok ? static_cast<const uint16_t*>(vp)[e] : 0u;
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t km, __amdgpu_buffer_rsrc_t vm, uint32_t off, int i) {
+    const uint32_t kx = __builtin_amdgcn_raw_buffer_load_b16(km, off, 0, kStream);
+    const uint32_t vx = __builtin_amdgcn_raw_buffer_load_b16(vm, off, 0, kStream);
     r[i] = kx | (vx << 16);
   }
+  __device__ __forceinline__ void empty(int i) { r[i] = (r[i] & 0xffff0000u) | 0xff80u; }  // k = -inf
 };
 template <int L>
 struct BtKV<BIWKV_F32, L> {
@@ -102,10 +103,11 @@ struct BtKV<BIWKV_F32, L> {
     bt_fence(kk);
     bt_fence(vv);
   }
-  __device__ __forceinline__ void load(const void* kp, const void* vp, long long e, bool ok, int i) {
-    kk[i] = ok ? static_cast<const float*>(kp)[e] : kNegInf;
-    vv[i] = ok ? static_cast<const float*>(vp)[e] : 0.f;
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t km, __amdgpu_buffer_rsrc_t vm, uint32_t off, int i) {
+    kk[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(km, off, 0, kStream));
+    vv[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vm, off, 0, kStream));
   }
+  __device__ __forceinline__ void empty(int i) { kk[i] = kNegInf; }
 };
 
 // The larger of an aggregate's exponent and mx, and the aggregate rescaled to it.
@@ -174,15 +176,44 @@ __device__ __forceinline__ BtLane bt_lane(const BwdTileParams& p, unsigned unit)
   return ln;
 }
 
-template <int DT, int L>
-__device__ __forceinline__ void bt_load(const BwdTileParams& p, const BtLane& ln, BtKV<DT, L>& kv, float (&gg)[L]) {
+// Loads N consecutive tokens of a wavefront, starting at t0 (the same for every lane), of batch
+// item bi: k and v, and g when gg is given. Each token goes through a buffer resource over the
+// rest of the batch item (a uniform base, so scalar registers) and the lane's channel offset, so
+// one vector register addresses every token; tokens past the row read 0 and are then marked empty
+// (k = -inf), masked channels read 0. The host keeps a batch item below 2^31 bytes.
+template <int DT, int N>
+__device__ __forceinline__ void bt_load(const BwdTileParams& p, int bi, long long t0, int ch, bool on,
+                                        BtKV<DT, N>& kv, float* gg) {
+  constexpr int ES = DT == BIWKV_F32 ? 4 : 2;
+  const long long plane = p.T * p.C;  // elements of one batch item
+  const char* kb = reinterpret_cast<const char*>(
+      uniform_u64(reinterpret_cast<unsigned long long>(p.k) + static_cast<unsigned long long>(bi) * plane * ES));
+  const char* vb = reinterpret_cast<const char*>(
+      uniform_u64(reinterpret_cast<unsigned long long>(p.v) + static_cast<unsigned long long>(bi) * plane * ES));
+  const char* gb = reinterpret_cast<const char*>(
+      uniform_u64(reinterpret_cast<unsigned long long>(p.g) + static_cast<unsigned long long>(bi) * plane * 4));
+  const int t0u = __builtin_amdgcn_readfirstlane(static_cast<int>(t0));
+  const int rb = p.C * ES, rg = p.C * 4;                     // bytes per token
+  const int avail = static_cast<int>(plane * ES), availg = static_cast<int>(plane * 4);
+  const uint32_t off = on ? static_cast<uint32_t>(ch) * ES : kOutOfRange;
+  const uint32_t offg = on ? static_cast<uint32_t>(ch) * 4 : kOutOfRange;
 #pragma unroll
-  for (int i = 0; i < L; ++i) {
-    const long long t = ln.s_g + i;
-    const bool ok = ln.on && t < p.T;
-    const long long e = ln.row0 + t * p.C;
-    kv.load(p.k, p.v, e, ok, i);
-    gg[i] = ok ? p.g[e] : 0.f;
+  for (int i = 0; i < N; ++i) {
+    const int a = (t0u + i) * rb;  // below 2^31: T < 2^31 / (4 C) and the row's padding
+    const int left = avail - a;
+    const uint32_t n = static_cast<uint32_t>(left > 0 ? left : 0);
+    kv.load(make_rsrc(kb + a, n), make_rsrc(vb + a, n), off, i);
+    if (gg) {
+      const int ag = (t0u + i) * rg;
+      const int lg = availg - ag;
+      gg[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          make_rsrc(gb + ag, static_cast<uint32_t>(lg > 0 ? lg : 0)), offg, 0, kStream));
+    }
+  }
+  if (t0u + N > p.T) {  // uniform: only wavefronts at the end of a row
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (t0u + i >= p.T) kv.empty(i);
   }
 }
 
@@ -317,7 +348,7 @@ __device__ __noinline__ float2 bt_body_wide(const BwdTileParams* args, BtShared<
   auto& sw = sh->sw;
   BtKV<DT, L> kv;
   float gg[L];
-  bt_load<DT, L>(p, lnv, kv, gg);
+  bt_load<DT, L>(p, lnv.bi, lnv.s_g, lnv.ch, lnv.on, kv, gg);
   // token position times D, exact for t < 2^24
   float Dp = D;  // the copy positions are formed from, made opaque between phases
   auto tD = [&](int i) { return static_cast<float>(s_g + i) * Dp; };
@@ -563,7 +594,7 @@ __device__ __forceinline__ float2 bt_body_fast(const BwdTileParams& p, const BtL
   auto& sw = sh->sw;
   BtKV<DT, L> kv;
   float gg[L];
-  bt_load<DT, L>(p, ln, kv, gg);
+  bt_load<DT, L>(p, ln.bi, ln.s_g, ln.ch, ln.on, kv, gg);
   auto kl = [&](int i) { return kv.k(i) * kLog2e; };  // -inf in empty slots
 
   // ---- round 1 lane sums (against 2^{kmax + span}) and the caps: backward sums of the lane's
@@ -751,6 +782,97 @@ __device__ __forceinline__ float2 bt_body_fast(const BwdTileParams& p, const BtL
   // through many empty slots of growth, so 2^{M + Mq} is not formed for it
   const float dw = kmax != kNegInf && dwacc != 0.f ? dwacc * fast_exp2(M + Mq) : 0.f;
   return make_float2(dw, du);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Stage 1 of a multi-chunk row: the round-1 sums of every chunk. A lane holds one channel of one
+// chunk (64 tokens, like a lane of the forward tile kernel), so the chunk's sums are the lane's
+// and no scan is needed. The form matches what stages 2 and 3 read: anchored sums (forward at the
+// chunk's last slot, backward at its first token) formed per 8-token sub-block against the
+// sub-block's own reference and combined with exponent shifts, or position-free sums (wide form).
+// The tile's channels vote on the form exactly as the tile kernel's workgroups do.
+// ---------------------------------------------------------------------------------------------
+// (Two waves per SIMD: 64 tokens of k and v per lane in registers; each lane keeps 128 loads in
+// flight, so fewer waves still cover the memory latency.)
+template <int DT, int CT, int NT>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
+    bwd_chunk_sums_kernel(BwdTileParams p) {
+  constexpr int SUB = 8;  // tokens per sub-block: the tile kernel's lane length
+  constexpr int NSUB = CT / SUB;
+  const int tid = threadIdx.x;
+  const int c = tid % kBtTile;
+  const int row = blockIdx.y;
+  const int chunk = blockIdx.x * (NT / kBtTile) + tid / kBtTile;
+  const int bi = row / p.n_tiles;
+  const int tile = row - bi * p.n_tiles;
+  const int ch = tile * kBtTile + c;
+  const bool on = ch < p.C && chunk < p.n_chunks;
+  const long long T = p.T;
+  const float D = on ? (p.w[ch] / static_cast<float>(T)) * kLog2e : 0.f;
+  const float U = on ? p.u[ch] * kLog2e : 0.f;
+  // the tile kernel's vote (a wavefront holds the tile's 64 channels)
+  const bool wide =
+      __ballot(fabsf(D) * static_cast<float>(SUB - 1) > kBtFastRange || fabsf(U) > kBonusRange) != 0ull;
+  if (chunk >= p.n_chunks) return;  // (after the vote: every lane of the wavefront took part)
+  const long long t0 = static_cast<long long>(chunk) * CT;
+  BtKV<DT, CT> kv;
+  bt_load<DT, CT>(p, bi, t0, ch, on, kv, nullptr);
+  Agg fw = row_empty(), bw = row_empty();
+  if (!wide) {
+    const float lam = fast_exp2(-D);
+    const float span = fmaxf(-D, 0.f) * static_cast<float>(SUB - 1);
+#pragma unroll
+    for (int q = 0; q < NSUB; ++q) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int i = 0; i < SUB; ++i) mx = fmaxf(mx, kv.k(q * SUB + i) * kLog2e);
+      const float ref = mx == kNegInf ? 0.f : mx + span;
+      float fF = 0.f, fG = 0.f, bF = 0.f, bG = 0.f;
+      float pp[SUB];
+#pragma unroll
+      for (int i = 0; i < SUB; ++i) {
+        pp[i] = fast_exp2(kv.k(q * SUB + i) * kLog2e - ref);
+        fF = fmaf(fF, lam, pp[i] * kv.v(q * SUB + i));
+        fG = fmaf(fG, lam, pp[i]);
+      }
+#pragma unroll
+      for (int i = SUB - 1; i >= 0; --i) {
+        bF = fmaf(bF, lam, pp[i] * kv.v(q * SUB + i));
+        bG = fmaf(bG, lam, pp[i]);
+      }
+      const float m = mx == kNegInf ? kEmptyM : ref;
+      // forward: from the sub-block's last token to the chunk's last slot; backward: from its
+      // first token to the chunk's first token
+      fw = agg_add_f(agg_shift(fw, static_cast<float>(SUB), D), Agg{m, fF, fG});
+      bw = agg_add_f(bw, agg_shift(Agg{m, bF, bG}, static_cast<float>(q * SUB), D));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < NSUB; ++q) {
+      float xp[SUB], xs[SUB], vv[SUB], one[SUB];
+#pragma unroll
+      for (int i = 0; i < SUB; ++i) {
+        const int j = q * SUB + i;
+        const float kl = kv.k(j) * kLog2e, tD = static_cast<float>(t0 + j) * D;
+        xp[i] = kl + tD;
+        xs[i] = kl - tD;
+        vv[i] = kv.v(j);
+        one[i] = 1.f;
+      }
+      fw = agg_add_f(fw, bt_block<SUB>(xp, vv, one));
+      bw = agg_add_f(bw, bt_block<SUB>(xs, vv, one));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  float* o = p.sums1 + ((static_cast<size_t>(row) * p.n_chunks + chunk) * 2 * kBtTile + c) * 3;
+  o[0] = fw.m;
+  o[1] = fw.F;
+  o[2] = fw.G;
+  o += kBtTile * 3;
+  o[0] = bw.m;
+  o[1] = bw.F;
+  o[2] = bw.G;
 }
 
 // STAGE 0: a row of one chunk, the whole backward. STAGE 1, 2, 3: the three launches of a longer
