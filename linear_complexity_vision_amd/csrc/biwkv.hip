@@ -468,12 +468,14 @@ int launch_bwd_tile(const void* k, const void* v, const float* w, const float* u
     if (rc) return rc;
     const long long terms = B * n_chunks * C;                         // dw, du terms
     const long long sums = n_chunks > 1 ? total * 2 * kBtTile * 3 : 0;  // chunk sums per round
-    rc = grow_zeroed(&sc->bwd, &sc->bwd_floats, 2 * terms + 2 * sums, 1ll << 20, st, &sc->retired);
+    rc = grow_zeroed(&sc->bwd, &sc->bwd_floats, 2 * terms + 4 * sums, 1ll << 20, st, &sc->retired);
     if (rc) return rc;
     tp.pw = sc->bwd;
     tp.pu = sc->bwd + terms;
     tp.sums1 = sc->bwd + 2 * terms;
-    tp.sums2 = sc->bwd + 2 * terms + sums;
+    tp.sums2 = tp.sums1 + sums;
+    tp.carry1 = tp.sums2 + sums;
+    tp.carry2 = tp.carry1 + sums;
   }
   tp.k = k;
   tp.v = v;
@@ -495,7 +497,10 @@ int launch_bwd_tile(const void* k, const void* v, const float* w, const float* u
     const dim3 sgrid(static_cast<unsigned>((n_chunks + SNT / kBtTile - 1) / (SNT / kBtTile)),
                      static_cast<unsigned>(B * n_tiles));
     hipLaunchKernelGGL((bwd_chunk_sums_kernel<DT, CT, SNT>), sgrid, dim3(SNT), 0, st, tp);
+    const dim3 rows(static_cast<unsigned>(B * n_tiles)), cblock(64 * kCarryGroups);
+    hipLaunchKernelGGL((bwd_carry_kernel<CT>), rows, cblock, 0, st, tp, tp.sums1, tp.carry1);
     hipLaunchKernelGGL((bwd_tile_kernel<DT, L, NT, WPE, 2>), grid, block, 0, st, tp);
+    hipLaunchKernelGGL((bwd_carry_kernel<CT>), rows, cblock, 0, st, tp, tp.sums2, tp.carry2);
     hipLaunchKernelGGL((bwd_tile_kernel<DT, L, NT, WPE, 3>), grid, block, 0, st, tp);
   }
   BwdParams rp{};

@@ -46,6 +46,7 @@ namespace {
 
 constexpr int kBtTile = 64;  // channels per tile (one wavefront)
 constexpr int kBtSB = 4;     // tokens per sub-block of the sweeps
+constexpr int kBwdLane = 8;  // tokens per lane of the tile kernel (its fast / wide vote)
 
 struct BwdTileParams {
   const void* k;
@@ -57,8 +58,10 @@ struct BwdTileParams {
   float* dv;
   float* pw;  // dw terms per (batch item, chunk, channel), before the factor -lam / T
   float* pu;  // du terms per (batch item, chunk, channel)
-  float* sums1;  // round-1 chunk sums: [row][chunk][dir][64][3] floats (m, F, G)
-  float* sums2;  // round-2 chunk sums, same layout
+  float* sums1;   // round-1 chunk sums: [row][chunk][dir][64][3] floats (m, F, G)
+  float* sums2;   // round-2 chunk sums, same layout
+  float* carry1;  // round-1 carries of every chunk (earlier chunks, later chunks), same layout
+  float* carry2;  // round-2 carries, same layout
   long long T;
   int C;
   int n_tiles;   // channel tiles per batch item
@@ -229,8 +232,8 @@ enum : int { kBtLocal = 0, kBtProduce = 1, kBtConsume = 2 };
 //   kBtLocal: the row is one chunk, X and Y come from the scan;
 //   kBtProduce: the chunk's sums (forward at its last slot, backward at its first token) go to
 //     sums for a later launch, and X, Y are not formed;
-//   kBtConsume: the sums of the row's other chunks, written by an earlier launch, are folded in a
-//     fixed order into X and Y (entries in order per lane, then a fixed tree over the lanes).
+//   kBtConsume: the chunk's carries (the sums of the row's earlier and later chunks, formed by
+//     bwd_carry_kernel from the sums an earlier launch wrote) are added to X and Y.
 template <int NT, int L, bool ANCHORED, int MODE>
 __device__ __forceinline__ void bt_carries(Agg f, Agg b, Agg& X, Agg& Y, BtShared<NT>* sh, float* sums,
                                            const BwdTileParams& p, const BtLane& ln) {
@@ -256,6 +259,7 @@ __device__ __forceinline__ void bt_carries(Agg f, Agg b, Agg& X, Agg& Y, BtShare
   Agg sb{red[3 * RS + ti], red[4 * RS + ti], red[5 * RS + ti]};
   group_scan<GROUPS, L, true>(sf, sb, tg, Dt);
   const int nch = p.n_chunks, chunk = ln.chunk;
+  (void)CT;
   float* rs = sums + static_cast<size_t>(ln.row) * nch * 2 * kBtTile * 3;
   auto slot = [&](int ck, int dir) { return rs + (static_cast<size_t>(ck * 2 + dir) * kBtTile + tc) * 3; };
   if constexpr (MODE == kBtProduce) {
@@ -276,41 +280,12 @@ __device__ __forceinline__ void bt_carries(Agg f, Agg b, Agg& X, Agg& Y, BtShare
     if (tg == 0) x = row_empty();
     if (tg == GROUPS - 1) y = row_empty();
     if constexpr (MODE == kBtConsume) {
-      // entries: forward sums of chunks 0 .. chunk-1, then backward sums of chunks chunk+1 ..
-      // nch-1; lane tg takes entries tg, tg + GROUPS, ..., EB of them in flight at once
-      const int ne = nch - 1;
-      Agg pf = row_empty(), pb = row_empty();
-      constexpr int EB = 4;
-      for (int e0 = tg; e0 < ne; e0 += EB * GROUPS) {
-        float ev[EB][3];
-#pragma unroll
-        for (int j = 0; j < EB; ++j) {
-          const int e = e0 + j * GROUPS;
-          if (e < ne) {
-            const float* s = slot(e < chunk ? e : e + 1, e < chunk ? kFwd : kBwd);
-            ev[j][0] = s[0];
-            ev[j][1] = s[1];
-            ev[j][2] = s[2];
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < EB; ++j) {
-          const int e = e0 + j * GROUPS;
-          if (e >= ne) break;
-          const bool fwd = e < chunk;
-          Agg a{ev[j][0], ev[j][1], ev[j][2]};
-          if constexpr (ANCHORED)  // from the entry's anchor to this chunk's carry anchor
-            a = agg_shift(a, static_cast<float>(fwd ? (chunk - 1 - e) : (e - chunk)) * CT, Dt);
-          if (fwd)
-            pf = agg_add_f(pf, a);
-          else
-            pb = agg_add_f(pb, a);
-        }
-      }
-      group_fold<GROUPS, true>(pf, pb, tg);
-      pf = agg_from_first<GROUPS>(pf);
-      pb = agg_from_first<GROUPS>(pb);
-      if constexpr (ANCHORED) {  // from just before (after) the chunk to just before (after) group tg
+      // the chunk's carries (every earlier chunk, anchored just before it; every later chunk,
+      // just after it), moved to just before (after) group tg
+      const float* cf = slot(chunk, kFwd);
+      const float* cb = slot(chunk, kBwd);
+      Agg pf{cf[0], cf[1], cf[2]}, pb{cb[0], cb[1], cb[2]};
+      if constexpr (ANCHORED) {
         pf = agg_shift(pf, static_cast<float>(tg * L), Dt);
         pb = agg_shift(pb, static_cast<float>((GROUPS - 1 - tg) * L), Dt);
       }
@@ -385,7 +360,7 @@ __device__ __noinline__ float2 bt_body_wide(const BwdTileParams* args, BtShared<
       bt_carries<NT, L, false, kBtProduce>(lane_f, run, Xc, Yc, sh, p.sums1, p, lnv);
       return make_float2(0.f, 0.f);
     }
-    bt_carries<NT, L, false, MODE>(lane_f, run, Xc, Yc, sh, p.sums1, p, lnv);
+    bt_carries<NT, L, false, MODE>(lane_f, run, Xc, Yc, sh, p.carry1, p, lnv);
     lane_f = Xc;
     // from here cap1[q] is the suffix-form sum of every token after sub-block q
 #pragma unroll
@@ -475,7 +450,7 @@ __device__ __noinline__ float2 bt_body_wide(const BwdTileParams* args, BtShared<
       bt_carries<NT, L, false, kBtProduce>(lane2, run, X2, Y2, sh, p.sums2, p, lnv);
       return make_float2(0.f, 0.f);
     }
-    bt_carries<NT, L, false, MODE>(lane2, run, X2, Y2, sh, p.sums2, p, lnv);
+    bt_carries<NT, L, false, MODE>(lane2, run, X2, Y2, sh, p.carry2, p, lnv);
 #pragma unroll
     for (int q = 0; q < NSB; ++q) cap2[q] = agg_add_f(Y2, cap2[q]);
   }
@@ -581,6 +556,12 @@ __device__ __noinline__ float2 bt_body_wide(const BwdTileParams* args, BtShared<
 // ---------------------------------------------------------------------------------------------
 constexpr float kBtFastRange = 24.f;
 
+// Whether a channel needs the wide form. Every kernel of a backward call takes the same vote over
+// the 64 channels of a tile, so all stages of a row use the same form.
+__device__ __forceinline__ bool bt_wide_lane(float D, float U) {
+  return fabsf(D) * static_cast<float>(kBwdLane - 1) > kBtFastRange || fabsf(U) > kBonusRange;
+}
+
 template <int DT, int L, int NT, int STAGE>
 __device__ __forceinline__ float2 bt_body_fast(const BwdTileParams& p, const BtLane& ln, BtShared<NT>* sh) {
   constexpr int SB = kBtSB;
@@ -630,7 +611,7 @@ __device__ __forceinline__ float2 bt_body_fast(const BwdTileParams& p, const BtL
       bt_carries<NT, L, true, kBtProduce>(Agg{m, fF, fG}, Agg{m, cF, cG}, X, Y, sh, p.sums1, p, ln);
       return make_float2(0.f, 0.f);
     }
-    bt_carries<NT, L, true, MODE>(Agg{m, fF, fG}, Agg{m, cF, cG}, X, Y, sh, p.sums1, p, ln);
+    bt_carries<NT, L, true, MODE>(Agg{m, fF, fG}, Agg{m, cF, cG}, X, Y, sh, p.carry1, p, ln);
   }
   kv.fence();
   bt_fence(gg);
@@ -717,7 +698,7 @@ __device__ __forceinline__ float2 bt_body_fast(const BwdTileParams& p, const BtL
       bt_carries<NT, L, true, kBtProduce>(Agg{m, fQ, fR}, Agg{m, cQ, cR}, X2, Y2, sh, p.sums2, p, ln);
       return make_float2(0.f, 0.f);
     }
-    bt_carries<NT, L, true, MODE>(Agg{m, fQ, fR}, Agg{m, cQ, cR}, X2, Y2, sh, p.sums2, p, ln);
+    bt_carries<NT, L, true, MODE>(Agg{m, fQ, fR}, Agg{m, cQ, cR}, X2, Y2, sh, p.carry2, p, ln);
   }
   kv.fence();
   bt_fence(gg);
@@ -797,7 +778,7 @@ __device__ __forceinline__ float2 bt_body_fast(const BwdTileParams& p, const BtL
 template <int DT, int CT, int NT>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
     bwd_chunk_sums_kernel(BwdTileParams p) {
-  constexpr int SUB = 8;  // tokens per sub-block: the tile kernel's lane length
+  constexpr int SUB = kBwdLane;  // tokens per sub-block: the tile kernel's lane length
   constexpr int NSUB = CT / SUB;
   const int tid = threadIdx.x;
   const int c = tid % kBtTile;
@@ -812,7 +793,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
   const float U = on ? p.u[ch] * kLog2e : 0.f;
   // the tile kernel's vote (a wavefront holds the tile's 64 channels)
   const bool wide =
-      __ballot(fabsf(D) * static_cast<float>(SUB - 1) > kBtFastRange || fabsf(U) > kBonusRange) != 0ull;
+      __ballot(bt_wide_lane(D, U)) != 0ull;
   if (chunk >= p.n_chunks) return;  // (after the vote: every lane of the wavefront took part)
   const long long t0 = static_cast<long long>(chunk) * CT;
   BtKV<DT, CT> kv;
@@ -875,6 +856,93 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
   o[2] = bw.G;
 }
 
+// ---------------------------------------------------------------------------------------------
+// Carries of every chunk of a row from the chunk sums: forward, the sum over the earlier chunks
+// anchored just before the chunk; backward, over the later chunks anchored just after it (moved
+// CT tokens per chunk; position-free sums of the wide form are plain sums). Thread (c, grp) of a
+// workgroup of 64 channels x kCarryGroups groups folds a contiguous range of the row's chunks;
+// one thread per channel folds the group sums; each thread then writes its chunks' carries. Fixed
+// order, so the result is reproducible. The tile's channels vote on the form as the tile kernel's
+// workgroups do (a wavefront holds the tile's 64 channels).
+// ---------------------------------------------------------------------------------------------
+constexpr int kCarryGroups = 16;
+
+template <int CT>
+__global__ void __launch_bounds__(64 * kCarryGroups)
+    bwd_carry_kernel(BwdTileParams p, const float* __restrict__ sums, float* __restrict__ carry) {
+  __shared__ float gs[kCarryGroups][6][kBtTile];  // group sums
+  __shared__ float gc[kCarryGroups][6][kBtTile];  // group carries
+  const int c = threadIdx.x % kBtTile, grp = threadIdx.x / kBtTile;
+  const int row = blockIdx.x;
+  const int bi = row / p.n_tiles;
+  const int ch = (row - bi * p.n_tiles) * kBtTile + c;
+  const bool on = ch < p.C;
+  const float Dc = on ? (p.w[ch] / static_cast<float>(p.T)) * kLog2e : 0.f;
+  const float Uc = on ? p.u[ch] * kLog2e : 0.f;
+  const bool wide = __ballot(bt_wide_lane(Dc, Uc)) != 0ull;
+  const float D = wide ? 0.f : Dc;  // exponent shift per token (none for position-free sums)
+  const float step = static_cast<float>(CT);
+  const int nch = p.n_chunks;
+  const int per = (nch + kCarryGroups - 1) / kCarryGroups;
+  const int j0 = grp * per, j1 = j0 + per < nch ? j0 + per : nch;
+  const size_t base = static_cast<size_t>(row) * nch * 2 * kBtTile * 3 + static_cast<size_t>(c) * 3;
+  auto at = [&](int j, int dir) { return base + static_cast<size_t>(j * 2 + dir) * kBtTile * 3; };
+  auto get = [&](const float* a, size_t i) { return Agg{a[i], a[i + 1], a[i + 2]}; };
+  // group sums: forward anchored at the group's last chunk's last slot, backward at its first
+  // chunk's first token
+  Agg f = row_empty(), b = row_empty();
+#pragma unroll 4
+  for (int j = j0; j < j1; ++j) f = agg_add_f(agg_shift(f, step, D), get(sums, at(j, kFwd)));
+#pragma unroll 4
+  for (int j = j1 - 1; j >= j0; --j) b = agg_add_f(get(sums, at(j, kBwd)), agg_shift(b, step, D));
+  gs[grp][0][c] = f.m;
+  gs[grp][1][c] = f.F;
+  gs[grp][2][c] = f.G;
+  gs[grp][3][c] = b.m;
+  gs[grp][4][c] = b.F;
+  gs[grp][5][c] = b.G;
+  __syncthreads();
+  if (grp == 0) {
+    Agg x = row_empty();
+    for (int k = 0; k < kCarryGroups; ++k) {
+      const int a0 = k * per, a1 = a0 + per < nch ? a0 + per : nch;
+      const int len = a1 > a0 ? a1 - a0 : 0;
+      gc[k][0][c] = x.m;
+      gc[k][1][c] = x.F;
+      gc[k][2][c] = x.G;
+      x = agg_add_f(agg_shift(x, step * len, D), Agg{gs[k][0][c], gs[k][1][c], gs[k][2][c]});
+    }
+    Agg y = row_empty();
+    for (int k = kCarryGroups - 1; k >= 0; --k) {
+      const int a0 = k * per, a1 = a0 + per < nch ? a0 + per : nch;
+      const int len = a1 > a0 ? a1 - a0 : 0;
+      gc[k][3][c] = y.m;
+      gc[k][4][c] = y.F;
+      gc[k][5][c] = y.G;
+      y = agg_add_f(Agg{gs[k][3][c], gs[k][4][c], gs[k][5][c]}, agg_shift(y, step * len, D));
+    }
+  }
+  __syncthreads();
+  Agg x{gc[grp][0][c], gc[grp][1][c], gc[grp][2][c]};
+#pragma unroll 4
+  for (int j = j0; j < j1; ++j) {
+    const size_t o = at(j, kFwd);
+    carry[o] = x.m;
+    carry[o + 1] = x.F;
+    carry[o + 2] = x.G;
+    x = agg_add_f(agg_shift(x, step, D), get(sums, o));
+  }
+  Agg y{gc[grp][3][c], gc[grp][4][c], gc[grp][5][c]};
+#pragma unroll 4
+  for (int j = j1 - 1; j >= j0; --j) {
+    const size_t o = at(j, kBwd);
+    carry[o] = y.m;
+    carry[o + 1] = y.F;
+    carry[o + 2] = y.G;
+    y = agg_add_f(get(sums, o), agg_shift(y, step, D));
+  }
+}
+
 // STAGE 0: a row of one chunk, the whole backward. STAGE 1, 2, 3: the three launches of a longer
 // row (see the top of this file).
 template <int DT, int L, int NT, int WPE, int STAGE>
@@ -888,8 +956,8 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE)))
   // The whole workgroup takes the wide form when any of its channels needs it; every wavefront
   // holds all 64 channels, so a wavefront vote is the workgroup's vote (and every chunk of the
   // row, in every stage, votes the same way).
-  const bool wide_lane =
-      fabsf(ln.D) * static_cast<float>(L - 1) > kBtFastRange || fabsf(ln.U) > kBonusRange;
+  static_assert(L == kBwdLane, "the fast / wide vote assumes this lane length");
+  const bool wide_lane = bt_wide_lane(ln.D, ln.U);
   float2 r;
   if (__ballot(wide_lane) != 0ull) {
     const auto* args = (const BwdTileParams*)(__builtin_amdgcn_kernarg_segment_ptr());
