@@ -83,9 +83,9 @@ int biwkv_forward(const void* k, const void* v, const float* w, const float* u, 
  *   dw, du : [C] float32, device memory (dL/dw, dL/du summed over the batch; written).
  *   k, v, w, u, B, T, C, dtype: as for biwkv_forward; g: [B, T, C] float32, device memory.
  * Outputs must not overlap each other or any input. The pass recomputes the forward sums, so it
- * needs no forward state. A row of up to 64 tokens runs in one launch; a longer row in three
- * launches that pass per-chunk sums (64-token chunks) through library-owned scratch per (device,
- * stream) of 4 * (2 * B * ceil(T / 64) * C + 2 * 384 * B * ceil(C / 64) * ceil(T / 64)) bytes,
+ * needs no forward state. A row of up to 64 tokens runs in one launch; a longer row in five
+ * that pass per-chunk sums and carries (64-token chunks) through library-owned scratch per
+ * (device, stream) of 4 * (2 * B * ceil(T / 64) * C + 4 * 384 * B * ceil(C / 64) * ceil(T / 64)) bytes,
  * allocated on the first call and grown when a larger problem arrives (so the first call on a
  * stream must not be made under graph capture). dw and du are folded in a fixed order: results
  * are bitwise reproducible. With B * T == 0 (and C > 0), dw and du are set to 0.

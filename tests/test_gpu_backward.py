@@ -81,6 +81,22 @@ def test_backward_extreme_values(case):
     _check_against_sum(wl, gy, tol=tol, label=case)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_mixed_forms_across_tiles(dtype):
+    """Three 64-channel tiles: the middle one holds a channel with w = -1e4 (its tile takes the
+    wide form), the others are ordinary (fast form); T = 1000 spans many chunks, so every stage of
+    the call must take the same form per tile."""
+    wl = workloads.make_random(123, 2, 1000, 192, dtype=dtype, w_range=5.0, k_std=1.5)
+    w = wl.w.copy()
+    w[70] = -1e4
+    w[100] = 3e3
+    wl.w = w
+    gy = _upstream(wl, 124)
+    print(f"[case] biwkv_backward mixed fast / wide tiles {dtype}", flush=True)
+    tol = max(1e-4, 4.0 * float(np.abs(w).max()) * np.log2(np.e) * 2.0 ** -24)
+    _check_against_sum(wl, gy, tol=tol, label=f"mixed tiles {dtype}")
+
+
 @pytest.mark.parametrize("index", [1, 3, 4, 5])
 def test_backward_workload_shapes(index):
     """Full-size workloads. dk and dv of every element against the linear-time oracle (pinned to the
