@@ -155,7 +155,7 @@ struct BtShared {
 struct BtLane {
   int row, chunk, bi, ch, c, g;
   bool on;
-  long long s_g, row0;  // first token; element index of (bi, token 0, ch)
+  long long s_g;  // first token
   float D, U;           // w log2(e) / T and u log2(e) of the channel (0 when masked)
 };
 
@@ -175,7 +175,6 @@ __device__ __forceinline__ BtLane bt_lane(const BwdTileParams& p, unsigned unit)
   ln.s_g = static_cast<long long>(ln.chunk) * CT + static_cast<long long>(ln.g) * L;
   ln.D = ln.on ? (p.w[ln.ch] / static_cast<float>(p.T)) * kLog2e : 0.f;
   ln.U = ln.on ? p.u[ln.ch] * kLog2e : 0.f;
-  ln.row0 = static_cast<long long>(ln.bi) * p.T * p.C + ln.ch;
   return ln;
 }
 
@@ -218,6 +217,24 @@ __device__ __forceinline__ void bt_load(const BwdTileParams& p, int bi, long lon
     for (int i = 0; i < N; ++i)
       if (t0u + i >= p.T) kv.empty(i);
   }
+}
+
+// Stores dv and dk of token t (the same for every lane of the wavefront) of batch item bi through
+// a buffer resource over the rest of the batch item and the lane's channel offset: tokens past
+// the row and masked channels fall out of range and the hardware drops them, so no lane branches.
+__device__ __forceinline__ void bt_store(const BwdTileParams& p, int bi, long long t, int ch, bool on, float dv,
+                                         float dk) {
+  const long long plane = p.T * p.C;
+  const unsigned long long item = static_cast<unsigned long long>(bi) * plane * 4;
+  const int tu = __builtin_amdgcn_readfirstlane(static_cast<int>(t));
+  const int a = tu * p.C * 4;  // below 2^31 (host check)
+  const int left = static_cast<int>(plane * 4) - a;
+  const uint32_t n = static_cast<uint32_t>(left > 0 ? left : 0);
+  const uint32_t off = on ? static_cast<uint32_t>(ch) * 4 : kOutOfRange;
+  const char* dvb = reinterpret_cast<const char*>(uniform_u64(reinterpret_cast<unsigned long long>(p.dv) + item));
+  const char* dkb = reinterpret_cast<const char*>(uniform_u64(reinterpret_cast<unsigned long long>(p.dk) + item));
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dv), make_rsrc(dvb + a, n), off, 0, kStream);
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dk), make_rsrc(dkb + a, n), off, 0, kStream);
 }
 
 enum : int { kBtLocal = 0, kBtProduce = 1, kBtConsume = 2 };
@@ -318,7 +335,7 @@ __device__ __noinline__ float2 bt_body_wide(const BwdTileParams* args, BtShared<
   const BtLane lnv = bt_lane<L, NT>(p, blockIdx.x);
   const int tid = threadIdx.x;
   const bool on = lnv.on;
-  const long long T = p.T, s_g = lnv.s_g, row0 = lnv.row0;
+  const long long s_g = lnv.s_g;
   const float D = lnv.D, U = lnv.U;
   auto& sw = sh->sw;
   BtKV<DT, L> kv;
@@ -515,11 +532,7 @@ __device__ __noinline__ float2 bt_body_wide(const BwdTileParams* args, BtShared<
         const float dvj = fmaf(qF, c1, fmaf(QB.F, c2, gg[j] * c3));
         const float rj = fmaf(qG, c1, fmaf(QB.G, c2, gg[j] * y[j] * c3));
         const float dkj = fmaf(kv.v(j), dvj, -rj);
-        if (on && tt < T) {
-          const long long e = row0 + tt * p.C;
-          p.dv[e] = dvj;
-          p.dk[e] = dkj;
-        }
+        bt_store(p, lnv.bi, tt, lnv.ch, on, dvj, dkj);
         const float e = fast_exp2(k2 - tD(j) - Bs.m);
         Bs.F = fmaf(e, kv.v(j), Bs.F);
         Bs.G += e;
@@ -746,11 +759,7 @@ __device__ __forceinline__ float2 bt_body_fast(const BwdTileParams& p, const BtL
         const float self = qh[i] * eU;
         const float dvj = K * (qa + QB + self);
         const float rj = K * (qr + QRB + self * y[j]);
-        if (ln.on && tt < p.T) {
-          const long long e = ln.row0 + tt * p.C;
-          p.dv[e] = dvj;
-          p.dk[e] = fmaf(vj, dvj, -rj);
-        }
+        bt_store(p, ln.bi, tt, ln.ch, ln.on, dvj, fmaf(vj, dvj, -rj));
         Bs = fmaf(Bs, lam, ph[i] * vj);
         Ds = fmaf(Ds, lam, ph[i]);
         QB = fmaf(QB, lam, qh[i]);
