@@ -629,13 +629,15 @@ __device__ __forceinline__ float2 bt_body_fast(const BwdTileParams& p, const BtL
   kv.fence();
   bt_fence(gg);
 
-  // ---- round 1 sweep: y and log2 of the denominator at every token, against 2^M ----
+  // ---- round 1 sweep: y and the reciprocal of the denominator at every token, against 2^M
+  //      (D_t = den_t 2^M); the self weight p_tt = e / den gives the du terms ----
   const float top = fmaxf(fmaxf(kmax, X.m), Y.m);
   const float M = top + span;
   const float sig = fast_exp2(kmax - top);  // the caps' scale against 2^M
   const float sx = fast_exp2(X.m - M), sy = fast_exp2(Y.m - M);
   const float YF = Y.F * sy, YG = Y.G * sy;
-  float y[L], nl[L];  // output and -log2 of the denominator (-inf in empty slots)
+  float y[L], rd[L];  // output and 1 / den (0 in empty slots)
+  float du = 0.f;
   {
     float A = X.F * sx, Cs = X.G * sx;
 #pragma unroll
@@ -661,8 +663,11 @@ __device__ __forceinline__ float2 bt_body_fast(const BwdTileParams& p, const BtL
         const float num = sw[0][i][tid] + fmaf(e, vj, Bs);
         const float den = sw[1][i][tid] + Ds + e;
         const bool live = kv.k(j) != kNegInf;
-        y[j] = live ? num * fast_rcp(den) : 0.f;
-        nl[j] = live ? -(M + fast_log2(den)) : kNegInf;
+        const float r = fast_rcp(den);
+        y[j] = live ? num * r : 0.f;
+        rd[j] = live ? r : 0.f;
+        // e^{u+k} (q v - r) = p_tt g (v - y), with p_tt = e / den
+        if constexpr (STAGE == 0 || STAGE == 3) du = fmaf(e * rd[j] * gg[j], vj - y[j], du);
         Bs = fmaf(Bs, lam, ph[i] * vj);
         Ds = fmaf(Ds, lam, ph[i]);
       }
@@ -672,24 +677,23 @@ __device__ __forceinline__ float2 bt_body_fast(const BwdTileParams& p, const BtL
   kv.fence();
   bt_fence(gg);
   bt_fence(y);
-  bt_fence(nl);
+  bt_fence(rd);
 
-  // ---- round 2 lane sums of (q, r) = (g, g y) 2^{-log2 D} and caps; du terms ----
-  float qmax = kNegInf;
+  // ---- round 2 lane sums of (q, r) = (g, g y) / D and caps. With log2 D_t = M - log2 rd_t the
+  //      lane's reference is qmax + span, qmax = -M + log2(max rd), and a term against it is
+  //      g (rd / max rd) 2^{-span}: no exponential per token ----
+  float rmax = 0.f;
 #pragma unroll
-  for (int i = 0; i < L; ++i) qmax = fmaxf(qmax, nl[i]);
+  for (int i = 0; i < L; ++i) rmax = fmaxf(rmax, rd[i]);
+  const float qmax = rmax > 0.f ? fast_log2(rmax) - M : kNegInf;
   float capQ[NSB], capR[NSB];
   Agg X2, Y2;
-  float du = 0.f;
   {
     const float ref = qmax == kNegInf ? 0.f : qmax + span;
+    const float qs = rmax > 0.f ? fast_rcp(rmax) * fast_exp2(-span) : 0.f;
     float qq[L];
 #pragma unroll
-    for (int i = 0; i < L; ++i) {
-      qq[i] = fast_exp2(nl[i] - ref) * gg[i];
-      // e^{u+k} (q v - r) = p_tt g (v - y)
-      du = fmaf(fast_exp2(U + kl(i) + nl[i]) * gg[i], kv.v(i) - y[i], du);
-    }
+    for (int i = 0; i < L; ++i) qq[i] = rd[i] * qs * gg[i];
     float fQ = 0.f, fR = 0.f, cQ = 0.f, cR = 0.f;
 #pragma unroll
     for (int i = 0; i < L; ++i) {
@@ -716,13 +720,14 @@ __device__ __forceinline__ float2 bt_body_fast(const BwdTileParams& p, const BtL
   kv.fence();
   bt_fence(gg);
   bt_fence(y);
-  bt_fence(nl);
+  bt_fence(rd);
 
   // ---- round 2 sweep: dv, dk and the dw terms, against 2^M (round 1) and 2^Mq (round 2) ----
   const float topq = fmaxf(fmaxf(qmax, X2.m), Y2.m);
   const float Mq = topq + span;
   const float sigq = fast_exp2(qmax - topq);
   const float sqx = fast_exp2(X2.m - Mq), sqy = fast_exp2(Y2.m - Mq);
+  const float S3 = fast_exp2(-M - Mq);  // q_t against 2^Mq is g_t rd_t 2^{-M - Mq}
   const float YQ = Y2.F * sqy, YR = Y2.G * sqy;
   float dwacc = 0.f;  // sum over tokens of b Qpre - d Rpre + a Qsuf - c Rsuf, against 2^{M + Mq}
   {
@@ -734,7 +739,7 @@ __device__ __forceinline__ float2 bt_body_fast(const BwdTileParams& p, const BtL
       for (int i = 0; i < SB; ++i) {
         const int j = q * SB + i;
         ph[i] = fast_exp2(kl(j) - M);
-        qh[i] = fast_exp2(nl[j] - Mq) * gg[j];
+        qh[i] = rd[j] * S3 * gg[j];
         sw[0][i][tid] = A;
         sw[1][i][tid] = Cs;
         sw[2][i][tid] = QA;
