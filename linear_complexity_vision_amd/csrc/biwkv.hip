@@ -494,8 +494,7 @@ int launch_bwd_tile(const void* k, const void* v, const float* w, const float* u
   } else {
     // stage 1: one lane per (channel, chunk); 8 chunks of a row per workgroup
     constexpr int SNT = 512;
-    const dim3 sgrid(static_cast<unsigned>((n_chunks + SNT / kBtTile - 1) / (SNT / kBtTile)),
-                     static_cast<unsigned>(B * n_tiles));
+    const dim3 sgrid(static_cast<unsigned>((n_chunks + SNT / kBtTile - 1) / (SNT / kBtTile) * B * n_tiles));
     hipLaunchKernelGGL((bwd_chunk_sums_kernel<DT, CT, SNT>), sgrid, dim3(SNT), 0, st, tp);
     const dim3 rows(static_cast<unsigned>(B * n_tiles)), cblock(64 * kCarryGroups);
     hipLaunchKernelGGL((bwd_carry_kernel<CT>), rows, cblock, 0, st, tp, tp.sums1, tp.carry1);

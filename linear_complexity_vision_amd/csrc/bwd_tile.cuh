@@ -796,8 +796,10 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
   constexpr int NSUB = CT / SUB;
   const int tid = threadIdx.x;
   const int c = tid % kBtTile;
-  const int row = blockIdx.y;
-  const int chunk = blockIdx.x * (NT / kBtTile) + tid / kBtTile;
+  // workgroup x: row x / per_row, chunks (x % per_row) * NT / 64 onwards (one wavefront each)
+  const int per_row = (p.n_chunks + NT / kBtTile - 1) / (NT / kBtTile);
+  const int row = static_cast<int>(blockIdx.x) / per_row;
+  const int chunk = (static_cast<int>(blockIdx.x) - row * per_row) * (NT / kBtTile) + tid / kBtTile;
   const int bi = row / p.n_tiles;
   const int tile = row - bi * p.n_tiles;
   const int ch = tile * kBtTile + c;
