@@ -148,3 +148,30 @@ def test_backward_deterministic_and_identities():
     # sum_i dv_i = sum_t g_t and sum_i dk_i = 0 per (batch, channel)
     np.testing.assert_allclose(dv.sum(axis=1), gy.astype(np.float64).sum(axis=1), rtol=1e-4, atol=1e-3)
     assert np.abs(dk.sum(axis=1)).max() <= 1e-4 * np.abs(dk).sum(axis=1).max()
+
+
+def test_backward_on_two_streams_matches_default_stream():
+    """Scratch is kept per (device, stream): two calls of different shapes queued on two side
+    streams at once give the same bits as the same calls on the default stream."""
+    import torch
+
+    import linear_complexity_vision_amd as L
+    wa = workloads.make_random(201, 2, 1500, 130, dtype="bf16", w_range=5.0)
+    wb = workloads.make_random(202, 1, 700, 64, dtype="f32", w_range=5.0)
+    ga, gb = _upstream(wa, 203), _upstream(wb, 204)
+    ta, tb = to_device_kv(wa), to_device_kv(wb)
+    gda, gdb = torch.from_numpy(ga).cuda(), torch.from_numpy(gb).cuda()
+    print("[case] backward on two side streams", flush=True)
+    ref_a = [x.cpu().numpy() for x in L.biwkv_backward(*ta, gda)]
+    ref_b = [x.cpu().numpy() for x in L.biwkv_backward(*tb, gdb)]
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s1):
+        out_a = L.biwkv_backward(*ta, gda)
+    with torch.cuda.stream(s2):
+        out_b = L.biwkv_backward(*tb, gdb)
+    torch.cuda.synchronize()
+    for x, r in zip(out_a, ref_a):
+        np.testing.assert_array_equal(x.cpu().numpy(), r)
+    for x, r in zip(out_b, ref_b):
+        np.testing.assert_array_equal(x.cpu().numpy(), r)
