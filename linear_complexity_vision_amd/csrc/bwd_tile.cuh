@@ -243,28 +243,27 @@ __device__ __forceinline__ void bt_store(const BwdTileParams& p, int bi, long lo
 
 enum : int { kBtLocal = 0, kBtProduce = 1, kBtConsume = 2 };
 
-// Scan of the lane sums over the workgroup's groups, and the chunk sums of the row. In: the lane's
-// forward sum f and backward sum b. Out: X, the sum over every token of the row before the lane,
-// and Y, over every token after it. Position-free sums (ANCHORED false) are plain sums in a fixed
-// order; anchored sums (f at the lane's last slot, b at its first token; X anchored just before
-// the lane, Y just after it) move by n tokens with exponent shifts of n D, as in the forward tile
-// kernel. The lane sums go through LDS into the forward tile kernel's transposed layout (a
-// channel's groups on consecutive lanes of one wavefront). MODE:
-//   kBtLocal: the row is one chunk, X and Y come from the scan;
+// Carries of the lanes from their sums. In: the lane's forward sum f and backward sum b. Out: X,
+// the sum over every token of the row before the lane, and Y, over every token after it.
+// Position-free sums (ANCHORED false) are plain sums in a fixed order; anchored sums (f at the
+// lane's last slot, b at its first token; X anchored just before the lane, Y just after it) move
+// by n tokens with exponent shifts of n D. The lane sums go to LDS; the first wavefront, one lane
+// per channel, scans the channel's GROUPS groups in order (work-efficient: the other wavefronts
+// wait at the barrier while the CU's other workgroup uses the vector unit), and the carries come
+// back through LDS. MODE:
+//   kBtLocal: the row is one chunk, the scan starts empty;
 //   kBtProduce: the chunk's sums (forward at its last slot, backward at its first token) go to
 //     sums for a later launch, and X, Y are not formed;
-//   kBtConsume: the chunk's carries (the sums of the row's earlier and later chunks, formed by
-//     bwd_carry_kernel from the sums an earlier launch wrote) are added to X and Y.
+//   kBtConsume: the scan starts from the chunk's carries (the sums of the row's earlier and later
+//     chunks, formed by bwd_carry_kernel from the sums an earlier launch wrote).
 template <int NT, int L, bool ANCHORED, int MODE>
 __device__ __forceinline__ void bt_carries(Agg f, Agg b, Agg& X, Agg& Y, BtShared<NT>* sh, float* sums,
                                            const BwdTileParams& p, const BtLane& ln) {
   constexpr int GROUPS = NT / kBtTile;
   constexpr int PAD = kBtTile + 1;
   constexpr int RS = GROUPS * PAD;
-  constexpr int CT = GROUPS * L;
   float* red = sh->red;
   float* xy = sh->xy;
-  const int tid = threadIdx.x;
   const int wi = ln.g * PAD + ln.c;
   red[0 * RS + wi] = f.m;
   red[1 * RS + wi] = f.F;
@@ -273,52 +272,53 @@ __device__ __forceinline__ void bt_carries(Agg f, Agg b, Agg& X, Agg& Y, BtShare
   red[4 * RS + wi] = b.F;
   red[5 * RS + wi] = b.G;
   __syncthreads();
-  const int tg = tid % GROUPS, tc = tid / GROUPS;
-  const int ti = tg * PAD + tc;
-  const float Dt = ANCHORED ? sh->dch[tc] : 0.f;
-  Agg sf{red[0 * RS + ti], red[1 * RS + ti], red[2 * RS + ti]};
-  Agg sb{red[3 * RS + ti], red[4 * RS + ti], red[5 * RS + ti]};
-  group_scan<GROUPS, L, true>(sf, sb, tg, Dt);
-  const int nch = p.n_chunks, chunk = ln.chunk;
-  (void)CT;
-  float* rs = sums + static_cast<size_t>(ln.row) * nch * 2 * kBtTile * 3;
-  auto slot = [&](int ck, int dir) { return rs + (static_cast<size_t>(ck * 2 + dir) * kBtTile + tc) * 3; };
-  if constexpr (MODE == kBtProduce) {
-    if (tg == GROUPS - 1) {
-      float* o = slot(chunk, kFwd);
-      o[0] = sf.m;
-      o[1] = sf.F;
-      o[2] = sf.G;
-    }
-    if (tg == 0) {
-      float* o = slot(chunk, kBwd);
-      o[0] = sb.m;
-      o[1] = sb.F;
-      o[2] = sb.G;
-    }
-  } else {
-    Agg x = agg_from_below<GROUPS, 1>(sf), y = agg_from_above<GROUPS, 1>(sb);
-    if (tg == 0) x = row_empty();
-    if (tg == GROUPS - 1) y = row_empty();
+  if (ln.g == 0) {  // the first wavefront: lane c scans channel c
+    const int c = ln.c;
+    const float Dt = ANCHORED ? ln.D : 0.f;
+    const float step = static_cast<float>(L);
+    const int nch = p.n_chunks, chunk = ln.chunk;
+    float* rs = sums + static_cast<size_t>(ln.row) * nch * 2 * kBtTile * 3;
+    auto slot = [&](int ck, int dir) { return rs + (static_cast<size_t>(ck * 2 + dir) * kBtTile + c) * 3; };
+    Agg x = row_empty(), y = row_empty();
     if constexpr (MODE == kBtConsume) {
-      // the chunk's carries (every earlier chunk, anchored just before it; every later chunk,
-      // just after it), moved to just before (after) group tg
       const float* cf = slot(chunk, kFwd);
       const float* cb = slot(chunk, kBwd);
-      Agg pf{cf[0], cf[1], cf[2]}, pb{cb[0], cb[1], cb[2]};
-      if constexpr (ANCHORED) {
-        pf = agg_shift(pf, static_cast<float>(tg * L), Dt);
-        pb = agg_shift(pb, static_cast<float>((GROUPS - 1 - tg) * L), Dt);
-      }
-      x = agg_add_f(pf, x);
-      y = agg_add_f(y, pb);
+      x = Agg{cf[0], cf[1], cf[2]};  // anchored just before the chunk: before group 0
+      y = Agg{cb[0], cb[1], cb[2]};  // just after the chunk: after the last group
     }
-    xy[0 * RS + ti] = x.m;
-    xy[1 * RS + ti] = x.F;
-    xy[2 * RS + ti] = x.G;
-    xy[3 * RS + ti] = y.m;
-    xy[4 * RS + ti] = y.F;
-    xy[5 * RS + ti] = y.G;
+#pragma unroll
+    for (int gi = 0; gi < GROUPS; ++gi) {
+      const int o = gi * PAD + c;
+      if constexpr (MODE != kBtProduce) {
+        xy[0 * RS + o] = x.m;
+        xy[1 * RS + o] = x.F;
+        xy[2 * RS + o] = x.G;
+      }
+      // from just before group gi to its last slot, where its own sum is anchored
+      x = agg_add_f(agg_shift(x, step, Dt), Agg{red[0 * RS + o], red[1 * RS + o], red[2 * RS + o]});
+    }
+#pragma unroll
+    for (int gi = GROUPS - 1; gi >= 0; --gi) {
+      const int o = gi * PAD + c;
+      if constexpr (MODE != kBtProduce) {
+        xy[3 * RS + o] = y.m;
+        xy[4 * RS + o] = y.F;
+        xy[5 * RS + o] = y.G;
+      }
+      y = agg_add_f(Agg{red[3 * RS + o], red[4 * RS + o], red[5 * RS + o]}, agg_shift(y, step, Dt));
+    }
+    if constexpr (MODE == kBtProduce) {  // the chunk's own sums
+      float* o = slot(chunk, kFwd);
+      o[0] = x.m;
+      o[1] = x.F;
+      o[2] = x.G;
+      o = slot(chunk, kBwd);
+      o[0] = y.m;
+      o[1] = y.F;
+      o[2] = y.G;
+    }
+  }
+  if constexpr (MODE != kBtProduce) {
     __syncthreads();
     X = Agg{xy[0 * RS + wi], xy[1 * RS + wi], xy[2 * RS + wi]};
     Y = Agg{xy[3 * RS + wi], xy[4 * RS + wi], xy[5 * RS + wi]};
