@@ -198,3 +198,25 @@ def test_bidir_validation(L):
         no_dev = _code("BIWKV_ERR_NO_DEVICE")
         assert qb(shift=3) == no_dev
         assert fb(shift=8) == no_dev
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="not built"):
+        lib.load_library(str(tmp_path / "libbiwkv.so"))
+
+
+def test_package_never_reaches_the_oracle():
+    """The product path is the HIP library only: no module of the package imports the oracle or
+    computes with numpy, and the library's sources include nothing from oracle/."""
+    import os
+    import re
+
+    pkg = os.path.dirname(lib.__file__)
+    for root, _, files in os.walk(pkg):
+        for f in files:
+            path = os.path.join(root, f)
+            if f.endswith(".py"):
+                text = open(path).read()
+                assert not re.search(r"^\s*(import|from)\s+(oracle|numpy)\b", text, flags=re.M), path
+            elif f.endswith((".hip", ".cuh", ".h", ".cpp")):
+                assert "oracle" not in open(path).read().lower(), path
