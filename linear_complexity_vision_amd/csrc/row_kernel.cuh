@@ -732,7 +732,7 @@ __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
     }
 #pragma unroll
     for (int q = 0; q < NSB; ++q) {
-      float ph[SB];
+      float ph[SB], pv[SB];  // the sub-block's terms and terms times v, kept for the backward sweep
       uint32_t r_cur[GATED ? SB : 1];
       if constexpr (GATED) {  // this sub-block's gate inputs; the next one's start loading
 #pragma unroll
@@ -745,10 +745,11 @@ __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
         const float kf = kv.k(t), vf = kv.v(t);
         const float pi = fast_exp2(fmaf(kf, kLog2e, -M));
         ph[i] = pi;
-        const float al = fmaf(-Cs, vf, A);
-        const float be = fmaf(pi, eU, Cs);
-        lds_ab[i][tid] = make_float2(al, be);
-        A = fmaf(A, lam, pi * vf);
+        pv[i] = pi * vf;
+        // numerator and denominator of Eq. (5) over the earlier tokens and the token itself (the
+        // bonus term); the backward sweep adds the later tokens
+        lds_ab[i][tid] = make_float2(fmaf(pv[i], eU, A), fmaf(pi, eU, Cs));
+        A = fmaf(A, lam, pv[i]);
         Cs = fmaf(Cs, lam, pi);
       }
       // backward state entering this sub-block from the right: the later sub-blocks of the lane
@@ -759,21 +760,20 @@ __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
 #pragma unroll
       for (int i = SB - 1; i >= 0; --i) {
         const int t = q * SB + i;
-        const float vf = kv.v(t);
         const float2 ab2 = lds_ab[i][tid];
-        const float num = fmaf(-Ds, vf, ab2.x + Bs);
+        const float num = ab2.x + Bs;
         const float den = ab2.y + Ds;  // >= the lane's largest term, a normal number
         float y;
         if constexpr (GATED) {
-          // sigma(r) y = (v den + num) / (den (1 + e^{-r})): one reciprocal for both divisions
+          // sigma(r) y = num / (den (1 + e^{-r})): one reciprocal for both divisions
           const float er = fast_exp2(-kLog2e * gate.value(r_cur[i]));
-          y = fmaf(vf, den, num) * fast_rcp(den * (1.f + er));
+          y = num * fast_rcp(den * (1.f + er));
         } else {
-          y = fmaf(num, fast_rcp(den), vf);
+          y = num * fast_rcp(den);
         }
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), orr, out0 + t * row_bytes, 0,
                                               kStream);
-        Bs = fmaf(Bs, lam, ph[i] * vf);
+        Bs = fmaf(Bs, lam, pv[i]);
         Ds = fmaf(Ds, lam, ph[i]);
       }
     }
