@@ -348,8 +348,13 @@ __device__ __forceinline__ void row_load(const RowParams& p, const RowLane& ln, 
 // which first holds the lane sums, then the carries and the per-channel D outside it.
 template <int NT>
 constexpr int kRowSweepFloats = 8 * NT * 2;
+// Row pitch of the group-major lane-sum and carry buffers. Lane (tg, tc) of the transposed layout
+// reads word tg * pitch + tc with tg = lane % GROUPS: a pitch of TILE + 64 / GROUPS puts the 64
+// lanes of a wavefront on 64 different banks (a pitch of TILE + 1 put up to 8 on one).
 template <int TILE, int NT>
-constexpr int kRowLdsFloats = kRowSweepFloats<NT> + 6 * (NT / TILE) * (TILE + 1) + TILE;
+constexpr int kRowPad = TILE + (NT / TILE < 64 ? 64 / (NT / TILE) : 1);
+template <int TILE, int NT>
+constexpr int kRowLdsFloats = kRowSweepFloats<NT> + 6 * (NT / TILE) * kRowPad<TILE, NT> + TILE;
 
 // The scans and the exchange use a finite exponent for an empty aggregate (F = G = 0), far below
 // any real one: 2^(empty - m) is then exactly 0 against a real exponent and 1 against another
@@ -589,7 +594,7 @@ __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
   //      (tg, tc) = (tid % GROUPS, tid / GROUPS) then takes group tg of channel tc, so the groups
   //      of a channel are GROUPS consecutive lanes of one wavefront and the scans (and the
   //      exchange) run on lane shuffles without barriers. Carries go back the same way. ----
-  constexpr int PAD = TILE + 1;         // row pitch of the group-major buffers (no bank conflicts)
+  constexpr int PAD = kRowPad<TILE, NT>;  // row pitch of the group-major buffers
   constexpr int RS = GROUPS * PAD;      // floats per quantity
   float* red = lds;                     // [6][RS] lane sums (inside the sweep buffer)
   float* xy = lds + kRowSweepFloats<NT>;  // [6][RS] carries (outside it: read during the sweeps)
