@@ -659,14 +659,27 @@ __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
         // are full, so slot positions are token positions)
         const float dist = static_cast<float>(fwd ? (chunk - 1 - ck) : (ck - chunk - 1)) * CT;
         const unsigned long long* sp = slot(ck, fwd ? kFwd : kBwd);
-        unsigned spins = 0;
-        while (!slot_ready(wv[j], epoch)) {
-          if (++spins > kSpinLimit) {
-            timed_out = true;
-            break;
+        if (!slot_ready(wv[j], epoch)) {
+          // Two polls in flight, issued a short sleep apart: a slot published just after one
+          // poll was served is seen by the next one instead of a full round trip later.
+          unsigned long long w2[2];
+          slot_load(sp, w2);
+          for (unsigned spins = 0;; spins += 2) {
+            __builtin_amdgcn_s_sleep(2);
+            slot_load(sp, wv[j]);
+            if (slot_ready(w2, epoch)) {  // the older poll
+              wv[j][0] = w2[0];
+              wv[j][1] = w2[1];
+              break;
+            }
+            if (spins > kSpinLimit) {
+              timed_out = true;
+              break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+            slot_load(sp, w2);
+            if (slot_ready(wv[j], epoch)) break;
           }
-          __builtin_amdgcn_s_sleep(2);
-          slot_load(sp, wv[j]);
         }
         Agg a = slot_value(wv[j]);
         a.m = fmaxf(a.m, kEmptyM);
