@@ -659,7 +659,18 @@ __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
         // are full, so slot positions are token positions)
         const float dist = static_cast<float>(fwd ? (chunk - 1 - ck) : (ck - chunk - 1)) * CT;
         const unsigned long long* sp = slot(ck, fwd ? kFwd : kBwd);
-        if (!slot_ready(wv[j], epoch)) {
+        if (GATED) {
+          // one poll at a time: the gated kernel holds its first gate inputs in flight here,
+          // and a second poll's registers cost it spills and waits
+          for (unsigned spins = 0; !slot_ready(wv[j], epoch); ++spins) {
+            if (spins > kSpinLimit) {
+              timed_out = true;
+              break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+            slot_load(sp, wv[j]);
+          }
+        } else if (!slot_ready(wv[j], epoch)) {
           // Two polls in flight, issued a short sleep apart: a slot published just after one
           // poll was served is seen by the next one instead of a full round trip later.
           unsigned long long w2[2];
