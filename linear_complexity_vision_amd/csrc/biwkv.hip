@@ -389,16 +389,26 @@ int launch_qshift(const float* x, float* out, int64_t B, int64_t H, int64_t W, i
   hipStream_t st = static_cast<hipStream_t>(stream);
   const uint32_t* xi = reinterpret_cast<const uint32_t*>(x);
   uint32_t* oi = reinterpret_cast<uint32_t*>(out);
-  if (vec4)
-    hipLaunchKernelGGL(qshift_kernel<4>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, xi,
-                       oi, rows, static_cast<int>(H), static_cast<int>(W), static_cast<int>(C),
-                       shift, static_cast<int>(g[0]), static_cast<int>(g[1]),
-                       static_cast<int>(g[2]), static_cast<int>(g[3]), bidir);
+  // index divisors of the launch (channel groups per row, tokens per image, columns)
+  const FastDiv cv = make_fastdiv(static_cast<uint32_t>(vec4 ? C / 4 : C));
+  const FastDiv hw = make_fastdiv(static_cast<uint32_t>(H * W)), wd = make_fastdiv(static_cast<uint32_t>(W));
+  const bool big = items >= (1ll << 31);
+  const dim3 grid(static_cast<unsigned>(blocks)), block(256);
+  const int Hi = static_cast<int>(H), Wi = static_cast<int>(W), Ci = static_cast<int>(C);
+  const int g0 = static_cast<int>(g[0]), g1 = static_cast<int>(g[1]), g2 = static_cast<int>(g[2]),
+            g3 = static_cast<int>(g[3]);
+  if (vec4 && !big)
+    hipLaunchKernelGGL((qshift_kernel<4, false>), grid, block, 0, st, xi, oi, rows, cv, hw, wd, Hi, Wi, Ci,
+                       shift, g0, g1, g2, g3, bidir);
+  else if (vec4)
+    hipLaunchKernelGGL((qshift_kernel<4, true>), grid, block, 0, st, xi, oi, rows, cv, hw, wd, Hi, Wi, Ci,
+                       shift, g0, g1, g2, g3, bidir);
+  else if (!big)
+    hipLaunchKernelGGL((qshift_kernel<1, false>), grid, block, 0, st, xi, oi, rows, cv, hw, wd, Hi, Wi, Ci,
+                       shift, g0, g1, g2, g3, bidir);
   else
-    hipLaunchKernelGGL(qshift_kernel<1>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, xi,
-                       oi, rows, static_cast<int>(H), static_cast<int>(W), static_cast<int>(C),
-                       shift, static_cast<int>(g[0]), static_cast<int>(g[1]),
-                       static_cast<int>(g[2]), static_cast<int>(g[3]), bidir);
+    hipLaunchKernelGGL((qshift_kernel<1, true>), grid, block, 0, st, xi, oi, rows, cv, hw, wd, Hi, Wi, Ci,
+                       shift, g0, g1, g2, g3, bidir);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e);
   return BIWKV_OK;
@@ -691,16 +701,25 @@ int qshift_mix(const float* x, const float* mu, float* out, int64_t B, int64_t H
   long long blocks = (items + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (vec4)
-    hipLaunchKernelGGL(qshift_mix_kernel<4>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
-                       x, mu, out, rows, static_cast<int>(H), static_cast<int>(W),
-                       static_cast<int>(C), n_mix, shift, static_cast<int>(g[0]),
-                       static_cast<int>(g[1]), static_cast<int>(g[2]), static_cast<int>(g[3]));
+  const FastDiv cv = make_fastdiv(static_cast<uint32_t>(vec4 ? C / 4 : C));
+  const FastDiv hw = make_fastdiv(static_cast<uint32_t>(H * W)), wd = make_fastdiv(static_cast<uint32_t>(W));
+  const bool big = items >= (1ll << 31);
+  const dim3 grid(static_cast<unsigned>(blocks)), block(256);
+  const int Hi = static_cast<int>(H), Wi = static_cast<int>(W), Ci = static_cast<int>(C);
+  const int g0 = static_cast<int>(g[0]), g1 = static_cast<int>(g[1]), g2 = static_cast<int>(g[2]),
+            g3 = static_cast<int>(g[3]);
+  if (vec4 && !big)
+    hipLaunchKernelGGL((qshift_mix_kernel<4, false>), grid, block, 0, st, x, mu, out, rows, cv, hw, wd, Hi,
+                       Wi, Ci, n_mix, shift, g0, g1, g2, g3);
+  else if (vec4)
+    hipLaunchKernelGGL((qshift_mix_kernel<4, true>), grid, block, 0, st, x, mu, out, rows, cv, hw, wd, Hi,
+                       Wi, Ci, n_mix, shift, g0, g1, g2, g3);
+  else if (!big)
+    hipLaunchKernelGGL((qshift_mix_kernel<1, false>), grid, block, 0, st, x, mu, out, rows, cv, hw, wd, Hi,
+                       Wi, Ci, n_mix, shift, g0, g1, g2, g3);
   else
-    hipLaunchKernelGGL(qshift_mix_kernel<1>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
-                       x, mu, out, rows, static_cast<int>(H), static_cast<int>(W),
-                       static_cast<int>(C), n_mix, shift, static_cast<int>(g[0]),
-                       static_cast<int>(g[1]), static_cast<int>(g[2]), static_cast<int>(g[3]));
+    hipLaunchKernelGGL((qshift_mix_kernel<1, true>), grid, block, 0, st, x, mu, out, rows, cv, hw, wd, Hi,
+                       Wi, Ci, n_mix, shift, g0, g1, g2, g3);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e);
   return BIWKV_OK;

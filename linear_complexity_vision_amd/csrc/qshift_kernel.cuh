@@ -15,28 +15,80 @@ template <int V>
 struct Bits;
 template <>
 struct Bits<4> {
-  using t = uint4;
+  using t = uint32_t __attribute__((ext_vector_type(4)));  // a native vector (one 16-byte access)
 };
 template <>
 struct Bits<1> {
   using t = uint32_t;
 };
 
-template <int V>
+// Unsigned division of 0 <= n < 2^31 by a divisor fixed for the launch: a high multiply, an add
+// and a shift (Granlund and Montgomery, "Division by invariant integers using multiplication",
+// 1994: m = floor(2^32 (2^l - d) / d) + 1 with l = ceil(log2 d), q = (mulhi(m, n) + n) >> l).
+struct FastDiv {
+  uint32_t d, m, l;
+  __device__ __forceinline__ uint32_t div(uint32_t n) const {
+    const uint32_t t = __umulhi(n, m);
+    return static_cast<uint32_t>((static_cast<unsigned long long>(t) + n) >> l);
+  }
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  const unsigned long long m = ((1ull << 32) * ((1ull << l) - d)) / d + 1;
+  return FastDiv{d, static_cast<uint32_t>(m), l};
+}
+
+// Index of item i (V channels of one token): row r, first channel c, and the token's (h, w).
+// Below 2^31 items the divisions are multiply-shifts; beyond, plain 64-bit arithmetic.
+struct QsIndex {
+  long long r;
+  int c, h, w;
+};
+template <bool BIG>
+__device__ __forceinline__ QsIndex qs_index(long long i, FastDiv cv, FastDiv hw, FastDiv wd, int V) {
+  QsIndex q;
+  if constexpr (BIG) {
+    q.r = i / cv.d;
+    q.c = static_cast<int>(i - q.r * cv.d) * V;
+    const long long t = q.r % hw.d;
+    q.h = static_cast<int>(t / wd.d);
+    q.w = static_cast<int>(t - static_cast<long long>(q.h) * wd.d);
+  } else {
+    const uint32_t iu = static_cast<uint32_t>(i);
+    const uint32_t r = cv.div(iu);
+    q.r = r;
+    q.c = static_cast<int>(iu - r * cv.d) * V;
+    const uint32_t t = r - hw.div(r) * hw.d;
+    const uint32_t h = wd.div(t);
+    q.h = static_cast<int>(h);
+    q.w = static_cast<int>(t - h * wd.d);
+  }
+  return q;
+}
+
+// Every byte is read or written once: non-temporal loads and stores.
+template <class T>
+__device__ __forceinline__ T nt_load(const T* p) {
+  return __builtin_nontemporal_load(p);
+}
+template <class T>
+__device__ __forceinline__ void nt_store(T v, T* p) {
+  __builtin_nontemporal_store(v, p);
+}
+
+template <int V, bool BIG>
 __global__ void __launch_bounds__(256)
     qshift_kernel(const uint32_t* __restrict__ x, uint32_t* __restrict__ out, long long rows,
-                  int H, int W, int C, int s, int g1, int g2, int g3, int g4, int bidir) {
+                  FastDiv cv, FastDiv hw, FastDiv wd, int H, int W, int C, int s, int g1, int g2,
+                  int g3, int g4, int bidir) {
   using vec_t = typename Bits<V>::t;
-  const int CV = C / V;
-  const long long n = rows * CV;
-  const long long HW = static_cast<long long>(H) * W;
+  const long long n = rows * cv.d;
   for (long long i = blockIdx.x * static_cast<long long>(blockDim.x) + threadIdx.x; i < n;
        i += static_cast<long long>(gridDim.x) * blockDim.x) {
-    const long long r = i / CV;
-    const int c = static_cast<int>(i - r * CV) * V;
-    const long long t = r % HW;
-    const int h = static_cast<int>(t / W);
-    const int w = static_cast<int>(t - static_cast<long long>(h) * W);
+    const QsIndex q = qs_index<BIG>(i, cv, hw, wd, V);
+    const long long r = q.r;
+    const int c = q.c, h = q.h, w = q.w;
     // the vertical groups' coordinate, extent and token step
     const int hv = bidir ? w : h, Hv = bidir ? W : H;
     const long long step = bidir ? 1 : W;
@@ -56,8 +108,8 @@ __global__ void __launch_bounds__(256)
       src = r + s * step;
     }
     vec_t val{};
-    if (ok) val = *reinterpret_cast<const vec_t*>(x + src * C + c);
-    *reinterpret_cast<vec_t*>(out + r * C + c) = val;
+    if (ok) val = nt_load(reinterpret_cast<const vec_t*>(x + src * C + c));
+    nt_store(val, reinterpret_cast<vec_t*>(out + r * C + c));
   }
 }
 
@@ -78,10 +130,11 @@ __device__ __forceinline__ void load_floats(float* d, const float* p) {
 template <int V>
 __device__ __forceinline__ void store_floats(float* p, const float* d) {
   if constexpr (V == 4) {
-    *reinterpret_cast<float4*>(p) = make_float4(d[0], d[1], d[2], d[3]);
+    using f4 = float __attribute__((ext_vector_type(4)));
+    nt_store(f4{d[0], d[1], d[2], d[3]}, reinterpret_cast<f4*>(p));
   } else {
 #pragma unroll
-    for (int e = 0; e < V; ++e) p[e] = d[e];
+    for (int e = 0; e < V; ++e) nt_store(d[e], p + e);
   }
 }
 
@@ -90,22 +143,18 @@ __device__ __forceinline__ void store_floats(float* p, const float* d) {
 // n, c] for j < n_mix. One pass reads x and its shifted source once and writes every mix (the
 // inputs of the R, K, V projections), V consecutive channels per thread.
 // ---------------------------------------------------------------------------------------------
-template <int V>
+template <int V, bool BIG>
 __global__ void __launch_bounds__(256)
     qshift_mix_kernel(const float* __restrict__ x, const float* __restrict__ mu,
-                      float* __restrict__ out, long long rows, int H, int W, int C, int n_mix,
-                      int s, int g1, int g2, int g3, int g4) {
-  const int CV = C / V;
-  const long long n = rows * CV;
-  const long long HW = static_cast<long long>(H) * W;
+                      float* __restrict__ out, long long rows, FastDiv cv, FastDiv hw, FastDiv wd,
+                      int H, int W, int C, int n_mix, int s, int g1, int g2, int g3, int g4) {
+  const long long n = rows * cv.d;
   const long long plane = rows * C;  // elements of one mix
   for (long long i = blockIdx.x * static_cast<long long>(blockDim.x) + threadIdx.x; i < n;
        i += static_cast<long long>(gridDim.x) * blockDim.x) {
-    const long long r = i / CV;
-    const int c = static_cast<int>(i - r * CV) * V;
-    const long long t = r % HW;
-    const int h = static_cast<int>(t / W);
-    const int w = static_cast<int>(t - static_cast<long long>(h) * W);
+    const QsIndex q = qs_index<BIG>(i, cv, hw, wd, V);
+    const long long r = q.r;
+    const int c = q.c, h = q.h, w = q.w;
     long long src = r;
     bool ok = true;
     if (c < g1) {  // right
