@@ -36,7 +36,8 @@ def test_mix_workload():
 
 @pytest.mark.parametrize("B,H,W,C,shift,gamma,J", [
     (1, 5, 7, 100, 2, 0.125, 1), (3, 4, 4, 17, 3, 0.25, 3), (2, 6, 2, 10, 2, 0.2, 8),
-    (1, 3, 3, 12, 0, 0.25, 2), (2, 4, 4, 8, 4, 0.25, 3), (1, 64, 64, 96, 1, 0.25, 3)])
+    (1, 3, 3, 12, 0, 0.25, 2), (2, 4, 4, 8, 4, 0.25, 3), (1, 64, 64, 96, 1, 0.25, 3),
+    (2, 37, 41, 1000, 2, 0.25, 3)])  # odd index divisors, 0.76M items
 def test_mix_edge_shapes(B, H, W, C, shift, gamma, J):
     g = np.random.Generator(np.random.PCG64(B * 1000 + H * 100 + W * 10 + C + J))
     x = (g.standard_normal((B, H * W, C)) * 3).astype(np.float32)

@@ -103,6 +103,8 @@ def test_qshift_workload_bit_exact():
 
 
 @pytest.mark.parametrize("B,H,W,C,shift,gamma", [
+    (4, 64, 64, 1024, 1, 0.25),  # the benchmark shape: 4M items of 16 bytes
+    (3, 37, 41, 1000, 2, 0.25),  # odd divisors (250 groups, 1517 tokens, 41 columns), 1.1M items
     (2, 14, 14, 384, 1, 0.25), (1, 5, 7, 100, 2, 0.125), (3, 4, 4, 17, 3, 0.25), (2, 6, 2, 10, 2, 0.2),
     (1, 1, 9, 8, 1, 0.25), (1, 3, 3, 12, 0, 0.25), (1, 3, 3, 12, 1, 0.0), (2, 4, 4, 8, 4, 0.25)])
 def test_qshift_bit_patterns(B, H, W, C, shift, gamma):
