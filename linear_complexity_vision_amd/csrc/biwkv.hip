@@ -505,7 +505,12 @@ int launch_bwd_tile(const void* k, const void* v, const float* w, const float* u
     // stage 1: one lane per (channel, chunk); 8 chunks of a row per workgroup
     constexpr int SNT = 512;
     const dim3 sgrid(static_cast<unsigned>((n_chunks + SNT / kBtTile - 1) / (SNT / kBtTile) * B * n_tiles));
-    hipLaunchKernelGGL((bwd_chunk_sums_kernel<DT, CT, SNT>), sgrid, dim3(SNT), 0, st, tp);
+    // bf16 k and v as 32-bit channel pairs when every pair is whole and aligned
+    const bool pairs = DT == BIWKV_BF16 && C % 2 == 0 && aligned(k, 4) && aligned(v, 4);
+    if (pairs)
+      hipLaunchKernelGGL((bwd_chunk_sums_kernel<DT, CT, SNT, DT == BIWKV_BF16>), sgrid, dim3(SNT), 0, st, tp);
+    else
+      hipLaunchKernelGGL((bwd_chunk_sums_kernel<DT, CT, SNT, false>), sgrid, dim3(SNT), 0, st, tp);
     const dim3 rows(static_cast<unsigned>(B * n_tiles)), cblock(64 * kCarryGroups);
     hipLaunchKernelGGL((bwd_carry_kernel<CT>), rows, cblock, 0, st, tp, tp.sums1, tp.carry1);
     hipLaunchKernelGGL((bwd_tile_kernel<DT, L, NT, WPE, 2>), grid, block, 0, st, tp);

@@ -223,6 +223,35 @@ __device__ __forceinline__ void bt_load(const BwdTileParams& p, int bi, long lon
   }
 }
 
+// bf16 k and v of N consecutive tokens from t0, as channel pairs (C even, 4-byte aligned k and v):
+// lanes 2j and 2j + 1 read channels (2j, 2j + 1) as one 32-bit word, at even and odd tokens, as
+// the forward tile kernel does (RowKVPair: prepare(q) then gives each lane its own channel). Half
+// the load instructions of 16-bit loads, and each lands in its final register. Tokens past the
+// row are marked empty.
+template <int N>
+__device__ __forceinline__ void bt_load_pairs(const BwdTileParams& p, int bi, long long t0, int ch, bool on,
+                                              RowKVPair<N>& kv) {
+  const long long plane = p.T * p.C;
+  const char* kb = reinterpret_cast<const char*>(
+      uniform_u64(reinterpret_cast<unsigned long long>(p.k) + static_cast<unsigned long long>(bi) * plane * 2));
+  const char* vb = reinterpret_cast<const char*>(
+      uniform_u64(reinterpret_cast<unsigned long long>(p.v) + static_cast<unsigned long long>(bi) * plane * 2));
+  const int t0u = __builtin_amdgcn_readfirstlane(static_cast<int>(t0));
+  const int rb = p.C * 2;                     // bytes per token
+  const int avail = static_cast<int>(plane * 2);
+  const int odd = ch & 1;                     // tiles start at even channels
+  const uint32_t off = on ? static_cast<uint32_t>(odd * rb + (ch - odd) * 2) : kOutOfRange;
+#pragma unroll
+  for (int m = 0; m < N / 2; ++m) {
+    const int a = (t0u + 2 * m) * rb;  // below 2^31 (host check)
+    const int left = avail - a;
+    const uint32_t n = static_cast<uint32_t>(left > 0 ? left : 0);
+    kv.kk[m] = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(kb + a, n), off, 0, kBtLoadPolicy);
+    kv.vv[m] = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(vb + a, n), off, 0, kBtLoadPolicy);
+  }
+  if (t0u + N > p.T) kv.pad(static_cast<int>(p.T - t0u), odd);  // only wavefronts at a row's end
+}
+
 // Stores dv and dk of token t (the same for every lane of the wavefront) of batch item bi through
 // a buffer resource over the rest of the batch item and the lane's channel offset: tokens past
 // the row and masked channels fall out of range and the hardware drops them, so no lane branches.
@@ -791,11 +820,49 @@ __device__ __forceinline__ float2 bt_body_fast(const BwdTileParams& p, const BtL
 // sub-block's own reference and combined with exponent shifts, or position-free sums (wide form).
 // The tile's channels vote on the form exactly as the tile kernel's workgroups do.
 // ---------------------------------------------------------------------------------------------
-// (Two waves per SIMD: 64 tokens of k and v per lane in registers; each lane keeps 128 loads in
-// flight, so fewer waves still cover the memory latency.)
-template <int DT, int CT, int NT>
-__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
+// (bf16 channel pairs: 64 tokens of k and v per lane in 64 registers, four waves per SIMD. The
+// 16-bit and fp32 loads need more registers while in flight: two waves per SIMD. The wide form
+// lives out of line.)
+// Wide form of a chunk's sums: position-free, against running maxima. Rare, so out of line with
+// its own register allocation; it loads the chunk itself.
+template <int DT, int CT>
+__device__ __noinline__ void bwd_chunk_sums_wide(const BwdTileParams* args, int bi, long long t0, int ch,
+                                                 bool on, float D, float* o) {
+  constexpr int SUB = kBwdLane;
+  constexpr int NSUB = CT / SUB;
+  const BwdTileParams& p = *args;
+  BtKV<DT, CT> kv;
+  bt_load<DT, CT>(p, bi, t0, ch, on, kv, nullptr);
+  Agg fw = row_empty(), bw = row_empty();
+#pragma unroll
+  for (int q = 0; q < NSUB; ++q) {
+    float xp[SUB], xs[SUB], vv[SUB], one[SUB];
+#pragma unroll
+    for (int i = 0; i < SUB; ++i) {
+      const int j = q * SUB + i;
+      const float kl = kv.k(j) * kLog2e, tD = static_cast<float>(t0 + j) * D;
+      xp[i] = kl + tD;
+      xs[i] = kl - tD;
+      vv[i] = kv.v(j);
+      one[i] = 1.f;
+    }
+    fw = agg_add_f(fw, bt_block<SUB>(xp, vv, one));
+    bw = agg_add_f(bw, bt_block<SUB>(xs, vv, one));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  o[0] = fw.m;
+  o[1] = fw.F;
+  o[2] = fw.G;
+  o += kBtTile * 3;
+  o[0] = bw.m;
+  o[1] = bw.F;
+  o[2] = bw.G;
+}
+
+template <int DT, int CT, int NT, bool PAIR>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(PAIR ? 4 : 2)))
     bwd_chunk_sums_kernel(BwdTileParams p) {
+  static_assert(!PAIR || DT == BIWKV_BF16, "pairs are bf16 channel pairs");
   constexpr int SUB = kBwdLane;  // tokens per sub-block: the tile kernel's lane length
   constexpr int NSUB = CT / SUB;
   const int tid = threadIdx.x;
@@ -816,14 +883,25 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
       __ballot(bt_wide_lane(D, U)) != 0ull;
   if (chunk >= p.n_chunks) return;  // (after the vote: every lane of the wavefront took part)
   const long long t0 = static_cast<long long>(chunk) * CT;
-  BtKV<DT, CT> kv;
-  bt_load<DT, CT>(p, bi, t0, ch, on, kv, nullptr);
+  float* o = p.sums1 + ((static_cast<size_t>(row) * p.n_chunks + chunk) * 2 * kBtTile + c) * 3;
+  if (wide) {
+    // the kernel's only argument is p, at the start of the argument segment
+    const auto* args = (const BwdTileParams*)(__builtin_amdgcn_kernarg_segment_ptr());
+    bwd_chunk_sums_wide<DT, CT>(args, bi, t0, ch, on, D, o);
+    return;
+  }
+  std::conditional_t<PAIR, RowKVPair<CT>, BtKV<DT, CT>> kv;
+  if constexpr (PAIR)
+    bt_load_pairs<CT>(p, bi, t0, ch, on, kv);
+  else
+    bt_load<DT, CT>(p, bi, t0, ch, on, kv, nullptr);
   Agg fw = row_empty(), bw = row_empty();
-  if (!wide) {
+  {
     const float lam = fast_exp2(-D);
     const float span = fmaxf(-D, 0.f) * static_cast<float>(SUB - 1);
 #pragma unroll
     for (int q = 0; q < NSUB; ++q) {
+      if constexpr (PAIR) kv.prepare(q);  // waits only for this sub-block's words
       float mx = kNegInf;
 #pragma unroll
       for (int i = 0; i < SUB; ++i) mx = fmaxf(mx, kv.k(q * SUB + i) * kLog2e);
@@ -848,25 +926,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
       bw = agg_add_f(bw, agg_shift(Agg{m, bF, bG}, static_cast<float>(q * SUB), D));
       __builtin_amdgcn_sched_barrier(0);
     }
-  } else {
-#pragma unroll
-    for (int q = 0; q < NSUB; ++q) {
-      float xp[SUB], xs[SUB], vv[SUB], one[SUB];
-#pragma unroll
-      for (int i = 0; i < SUB; ++i) {
-        const int j = q * SUB + i;
-        const float kl = kv.k(j) * kLog2e, tD = static_cast<float>(t0 + j) * D;
-        xp[i] = kl + tD;
-        xs[i] = kl - tD;
-        vv[i] = kv.v(j);
-        one[i] = 1.f;
-      }
-      fw = agg_add_f(fw, bt_block<SUB>(xp, vv, one));
-      bw = agg_add_f(bw, bt_block<SUB>(xs, vv, one));
-      __builtin_amdgcn_sched_barrier(0);
-    }
   }
-  float* o = p.sums1 + ((static_cast<size_t>(row) * p.n_chunks + chunk) * 2 * kBtTile + c) * 3;
   o[0] = fw.m;
   o[1] = fw.F;
   o[2] = fw.G;
