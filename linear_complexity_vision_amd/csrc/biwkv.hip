@@ -458,7 +458,7 @@ constexpr int kBwdNT = 512;
 
 // The backward: bwd_tile_kernel in one launch (a row of one chunk) or three (stages 1, 2, 3),
 // then the dw / du fold. Arguments already checked, nothing empty.
-template <int DT, int L, int NT, int WPE>
+template <int DT, int L, int NT, int WPE, bool PAIR>
 int launch_bwd_tile(const void* k, const void* v, const float* w, const float* u, const float* g,
                     float* dk, float* dv, float* dw, float* du, int64_t B, int64_t T, int64_t C, int dev,
                     void* stream) {
@@ -500,22 +500,17 @@ int launch_bwd_tile(const void* k, const void* v, const float* w, const float* u
   tp.n_chunks = static_cast<int>(n_chunks);
   const dim3 grid(static_cast<unsigned>(total)), block(NT);
   if (n_chunks == 1) {
-    hipLaunchKernelGGL((bwd_tile_kernel<DT, L, NT, WPE, 0>), grid, block, 0, st, tp);
+    hipLaunchKernelGGL((bwd_tile_kernel<DT, L, NT, WPE, 0, PAIR>), grid, block, 0, st, tp);
   } else {
     // stage 1: one lane per (channel, chunk); 8 chunks of a row per workgroup
     constexpr int SNT = 512;
     const dim3 sgrid(static_cast<unsigned>((n_chunks + SNT / kBtTile - 1) / (SNT / kBtTile) * B * n_tiles));
-    // bf16 k and v as 32-bit channel pairs when every pair is whole and aligned
-    const bool pairs = DT == BIWKV_BF16 && C % 2 == 0 && aligned(k, 4) && aligned(v, 4);
-    if (pairs)
-      hipLaunchKernelGGL((bwd_chunk_sums_kernel<DT, CT, SNT, DT == BIWKV_BF16>), sgrid, dim3(SNT), 0, st, tp);
-    else
-      hipLaunchKernelGGL((bwd_chunk_sums_kernel<DT, CT, SNT, false>), sgrid, dim3(SNT), 0, st, tp);
+    hipLaunchKernelGGL((bwd_chunk_sums_kernel<DT, CT, SNT, PAIR>), sgrid, dim3(SNT), 0, st, tp);
     const dim3 rows(static_cast<unsigned>(B * n_tiles)), cblock(64 * kCarryGroups);
     hipLaunchKernelGGL((bwd_carry_kernel<CT>), rows, cblock, 0, st, tp, tp.sums1, tp.carry1);
-    hipLaunchKernelGGL((bwd_tile_kernel<DT, L, NT, WPE, 2>), grid, block, 0, st, tp);
+    hipLaunchKernelGGL((bwd_tile_kernel<DT, L, NT, WPE, 2, PAIR>), grid, block, 0, st, tp);
     hipLaunchKernelGGL((bwd_carry_kernel<CT>), rows, cblock, 0, st, tp, tp.sums2, tp.carry2);
-    hipLaunchKernelGGL((bwd_tile_kernel<DT, L, NT, WPE, 3>), grid, block, 0, st, tp);
+    hipLaunchKernelGGL((bwd_tile_kernel<DT, L, NT, WPE, 3, PAIR>), grid, block, 0, st, tp);
   }
   BwdParams rp{};
   rp.w = w;
@@ -631,9 +626,12 @@ int biwkv_backward(const void* k, const void* v, const float* w, const float* u,
   }
   // token positions times D must be exact in fp32
   if (T >= (1ll << 24)) return BIWKV_ERR_UNSUPPORTED;
-  return dtype == BIWKV_F32
-             ? launch_bwd_tile<BIWKV_F32, kBwdL, kBwdNT, 4>(k, v, w, u, g, dk, dv, dw, du, B, T, C, dev, stream)
-             : launch_bwd_tile<BIWKV_BF16, kBwdL, kBwdNT, 4>(k, v, w, u, g, dk, dv, dw, du, B, T, C, dev, stream);
+  if (dtype == BIWKV_F32)
+    return launch_bwd_tile<BIWKV_F32, kBwdL, kBwdNT, 4, false>(k, v, w, u, g, dk, dv, dw, du, B, T, C, dev, stream);
+  // bf16 k and v load as 32-bit channel pairs when every pair is whole and aligned
+  if (C % 2 == 0 && aligned(k, 4) && aligned(v, 4))
+    return launch_bwd_tile<BIWKV_BF16, kBwdL, kBwdNT, 4, true>(k, v, w, u, g, dk, dv, dw, du, B, T, C, dev, stream);
+  return launch_bwd_tile<BIWKV_BF16, kBwdL, kBwdNT, 4, false>(k, v, w, u, g, dk, dv, dw, du, B, T, C, dev, stream);
 }
 
 int biwkv_causal_forward(const void* k, const void* v, const float* w, const float* u, float* out,

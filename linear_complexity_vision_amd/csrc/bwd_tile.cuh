@@ -230,7 +230,7 @@ __device__ __forceinline__ void bt_load(const BwdTileParams& p, int bi, long lon
 // row are marked empty.
 template <int N>
 __device__ __forceinline__ void bt_load_pairs(const BwdTileParams& p, int bi, long long t0, int ch, bool on,
-                                              RowKVPair<N>& kv) {
+                                              RowKVPair<N>& kv, float* gg) {
   const long long plane = p.T * p.C;
   const char* kb = reinterpret_cast<const char*>(
       uniform_u64(reinterpret_cast<unsigned long long>(p.k) + static_cast<unsigned long long>(bi) * plane * 2));
@@ -248,6 +248,19 @@ __device__ __forceinline__ void bt_load_pairs(const BwdTileParams& p, int bi, lo
     const uint32_t n = static_cast<uint32_t>(left > 0 ? left : 0);
     kv.kk[m] = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(kb + a, n), off, 0, kBtLoadPolicy);
     kv.vv[m] = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(vb + a, n), off, 0, kBtLoadPolicy);
+  }
+  if (gg) {  // the upstream gradient: fp32, each lane its own channel
+    const char* gb = reinterpret_cast<const char*>(
+        uniform_u64(reinterpret_cast<unsigned long long>(p.g) + static_cast<unsigned long long>(bi) * plane * 4));
+    const int rg = p.C * 4, availg = static_cast<int>(plane * 4);
+    const uint32_t offg = on ? static_cast<uint32_t>(ch) * 4 : kOutOfRange;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int ag = (t0u + i) * rg;
+      const int lg = availg - ag;
+      gg[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          make_rsrc(gb + ag, static_cast<uint32_t>(lg > 0 ? lg : 0)), offg, 0, kBtLoadPolicy));
+    }
   }
   if (t0u + N > p.T) kv.pad(static_cast<int>(p.T - t0u), odd);  // only wavefronts at a row's end
 }
@@ -608,7 +621,7 @@ __device__ __forceinline__ bool bt_wide_lane(float D, float U) {
   return fabsf(D) * static_cast<float>(kBwdLane - 1) > kBtFastRange || fabsf(U) > kBonusRange;
 }
 
-template <int DT, int L, int NT, int STAGE>
+template <int DT, int L, int NT, int STAGE, bool PAIR>
 __device__ __forceinline__ float2 bt_body_fast(const BwdTileParams& p, const BtLane& ln, BtShared<NT>* sh) {
   constexpr int SB = kBtSB;
   constexpr int NSB = L / SB;
@@ -619,9 +632,15 @@ __device__ __forceinline__ float2 bt_body_fast(const BwdTileParams& p, const BtL
   const float span = fmaxf(-D, 0.f) * static_cast<float>(L - 1);  // largest growth inside a lane
   const float eU = fast_exp2(U);
   auto& sw = sh->sw;
-  BtKV<DT, L> kv;
+  std::conditional_t<PAIR, RowKVPair<L>, BtKV<DT, L>> kv;
   float gg[L];
-  bt_load<DT, L>(p, ln.bi, ln.s_g, ln.ch, ln.on, kv, gg);
+  if constexpr (PAIR) {
+    bt_load_pairs<L>(p, ln.bi, ln.s_g, ln.ch, ln.on, kv, gg);
+#pragma unroll
+    for (int q = 0; q < L / 8; ++q) kv.prepare(q);
+  } else {
+    bt_load<DT, L>(p, ln.bi, ln.s_g, ln.ch, ln.on, kv, gg);
+  }
   auto kl = [&](int i) { return kv.k(i) * kLog2e; };  // -inf in empty slots
 
   // ---- round 1 lane sums (against 2^{kmax + span}) and the caps: backward sums of the lane's
@@ -892,7 +911,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(PAIR ? 
   }
   std::conditional_t<PAIR, RowKVPair<CT>, BtKV<DT, CT>> kv;
   if constexpr (PAIR)
-    bt_load_pairs<CT>(p, bi, t0, ch, on, kv);
+    bt_load_pairs<CT>(p, bi, t0, ch, on, kv, nullptr);
   else
     bt_load<DT, CT>(p, bi, t0, ch, on, kv, nullptr);
   Agg fw = row_empty(), bw = row_empty();
@@ -1025,9 +1044,11 @@ __global__ void __launch_bounds__(64 * kCarryGroups)
 
 // STAGE 0: a row of one chunk, the whole backward. STAGE 1, 2, 3: the three launches of a longer
 // row (see the top of this file).
-template <int DT, int L, int NT, int WPE, int STAGE>
+// PAIR: bf16 k and v as 32-bit channel pairs (bt_load_pairs).
+template <int DT, int L, int NT, int WPE, int STAGE, bool PAIR>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE)))
     bwd_tile_kernel(BwdTileParams p) {
+  static_assert(!PAIR || (DT == BIWKV_BF16 && L % 8 == 0), "pairs are bf16 channel pairs");
   static_assert(L % kBtSB == 0 && NT % kBtTile == 0 && NT <= 1024, "bad backward tile shape");
   static_assert(((NT / kBtTile) & (NT / kBtTile - 1)) == 0, "a channel's groups share a wavefront");
   __shared__ BtShared<NT> sh;
@@ -1043,7 +1064,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE)))
     const auto* args = (const BwdTileParams*)(__builtin_amdgcn_kernarg_segment_ptr());
     r = bt_body_wide<DT, L, NT, STAGE>(args, &sh);
   } else {
-    r = bt_body_fast<DT, L, NT, STAGE>(p, ln, &sh);
+    r = bt_body_fast<DT, L, NT, STAGE, PAIR>(p, ln, &sh);
   }
   if constexpr (STAGE == 0 || STAGE == 3) {
     // ---- per-channel fold of the lanes' dw and du terms over the groups, in order ----
