@@ -626,12 +626,10 @@ __device__ __forceinline__ float2 bt_body_fast(const BwdTileParams& p, const BtL
   constexpr int SB = kBtSB;
   constexpr int NSB = L / SB;
   constexpr int MODE = STAGE == 0 ? kBtLocal : kBtConsume;  // when a round's carries are formed
-  const int tid = threadIdx.x;
   const float D = ln.D, U = ln.U;
   const float lam = fast_exp2(-D);
   const float span = fmaxf(-D, 0.f) * static_cast<float>(L - 1);  // largest growth inside a lane
   const float eU = fast_exp2(U);
-  auto& sw = sh->sw;
   std::conditional_t<PAIR, RowKVPair<L>, BtKV<DT, L>> kv;
   float gg[L];
   if constexpr (PAIR) {
@@ -694,13 +692,13 @@ __device__ __forceinline__ float2 bt_body_fast(const BwdTileParams& p, const BtL
     float A = X.F * sx, Cs = X.G * sx;
 #pragma unroll
     for (int q = 0; q < NSB; ++q) {
-      float ph[SB];
+      float ph[SB], ra[SB], rc[SB];  // terms, and the forward states before each token
 #pragma unroll
       for (int i = 0; i < SB; ++i) {
         const int j = q * SB + i;
         ph[i] = fast_exp2(kl(j) - M);
-        sw[0][i][tid] = A;
-        sw[1][i][tid] = Cs;
+        ra[i] = A;
+        rc[i] = Cs;
         A = fmaf(A, lam, ph[i] * kv.v(j));
         Cs = fmaf(Cs, lam, ph[i]);
       }
@@ -712,8 +710,8 @@ __device__ __forceinline__ float2 bt_body_fast(const BwdTileParams& p, const BtL
         const int j = q * SB + i;
         const float vj = kv.v(j);
         const float e = ph[i] * eU;
-        const float num = sw[0][i][tid] + fmaf(e, vj, Bs);
-        const float den = sw[1][i][tid] + Ds + e;
+        const float num = ra[i] + fmaf(e, vj, Bs);
+        const float den = rc[i] + Ds + e;
         const bool live = kv.k(j) != kNegInf;
         const float r = fast_rcp(den);
         y[j] = live ? num * r : 0.f;
@@ -786,16 +784,16 @@ __device__ __forceinline__ float2 bt_body_fast(const BwdTileParams& p, const BtL
     float A = X.F * sx, Cs = X.G * sx, QA = X2.F * sqx, QR = X2.G * sqx;
 #pragma unroll
     for (int q = 0; q < NSB; ++q) {
-      float ph[SB], qh[SB];
+      float ph[SB], qh[SB], ra[SB], rc[SB], rqa[SB], rqr[SB];  // forward states before each token
 #pragma unroll
       for (int i = 0; i < SB; ++i) {
         const int j = q * SB + i;
         ph[i] = fast_exp2(kl(j) - M);
         qh[i] = rd[j] * S3 * gg[j];
-        sw[0][i][tid] = A;
-        sw[1][i][tid] = Cs;
-        sw[2][i][tid] = QA;
-        sw[3][i][tid] = QR;
+        ra[i] = A;
+        rc[i] = Cs;
+        rqa[i] = QA;
+        rqr[i] = QR;
         A = fmaf(A, lam, ph[i] * kv.v(j));
         Cs = fmaf(Cs, lam, ph[i]);
         QA = fmaf(QA, lam, qh[i]);
@@ -808,7 +806,7 @@ __device__ __forceinline__ float2 bt_body_fast(const BwdTileParams& p, const BtL
       for (int i = SB - 1; i >= 0; --i) {
         const int j = q * SB + i;
         const long long tt = ln.s_g + j;
-        const float a = sw[0][i][tid], c = sw[1][i][tid], qa = sw[2][i][tid], qr = sw[3][i][tid];
+        const float a = ra[i], c = rc[i], qa = rqa[i], qr = rqr[i];
         dwacc = fmaf(Bs, qa, fmaf(-Ds, qr, fmaf(a, QB, fmaf(-c, QRB, dwacc))));
         // e^{k} (Qpre + Qsuf + e^u q) and the same over r
         const float vj = kv.v(j);
