@@ -147,7 +147,7 @@ constexpr int kBtRedFloats = 6 * (NT / kBtTile) * (kBtTile + 1);
 // LDS of the backward tile kernel.
 template <int NT>
 struct BtShared {
-  float sw[4][kBtSB][NT];          // sweep records of one sub-block
+  float sw[4][kBtSB][NT];          // sweep records of one sub-block (wide form)
   float red[kBtRedFloats<NT>];     // lane sums (group-major)
   float xy[kBtRedFloats<NT>];      // carries
   float dch[kBtTile];              // D of each channel of the tile

@@ -344,7 +344,7 @@ __device__ __forceinline__ void row_load(const RowParams& p, const RowLane& ln, 
 // the other chunks, sweeps (phase C). WIDE selects the per-token running-maximum arithmetic; the fast form scales
 // the terms of a sub-block against one exponent, which keeps every significant term a normal
 // fp32 number while the decay or growth across a lane stays within kFastRange.
-// LDS of the tile kernel: the sweeps' (alpha, beta) buffer (8 tokens x NT lanes of float2),
+// LDS of the tile kernel: the wide form's per-token sweep buffer (8 tokens x NT lanes of float2),
 // which first holds the lane sums, then the carries and the per-channel D outside it.
 template <int NT>
 constexpr int kRowSweepFloats = 8 * NT * 2;
@@ -762,6 +762,7 @@ __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
 #pragma unroll
     for (int q = 0; q < NSB; ++q) {
       float ph[SB], pv[SB];  // the sub-block's terms and terms times v, kept for the backward sweep
+      float s1[SB], s2[SB];  // numerator and denominator so far, per token
       uint32_t r_cur[GATED ? SB : 1];
       if constexpr (GATED) {  // this sub-block's gate inputs; the next one's start loading
 #pragma unroll
@@ -777,7 +778,8 @@ __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
         pv[i] = pi * vf;
         // numerator and denominator of Eq. (5) over the earlier tokens and the token itself (the
         // bonus term); the backward sweep adds the later tokens
-        lds_ab[i][tid] = make_float2(fmaf(pv[i], eU, A), fmaf(pi, eU, Cs));
+        s1[i] = fmaf(pv[i], eU, A);
+        s2[i] = fmaf(pi, eU, Cs);
         A = fmaf(A, lam, pv[i]);
         Cs = fmaf(Cs, lam, pi);
       }
@@ -789,9 +791,8 @@ __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
 #pragma unroll
       for (int i = SB - 1; i >= 0; --i) {
         const int t = q * SB + i;
-        const float2 ab2 = lds_ab[i][tid];
-        const float num = ab2.x + Bs;
-        const float den = ab2.y + Ds;  // >= the lane's largest term, a normal number
+        const float num = s1[i] + Bs;
+        const float den = s2[i] + Ds;  // >= the lane's largest term, a normal number
         float y;
         if constexpr (GATED) {
           // sigma(r) y = num / (den (1 + e^{-r})): one reciprocal for both divisions
