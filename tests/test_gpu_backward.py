@@ -175,3 +175,38 @@ def test_backward_on_two_streams_matches_default_stream():
         np.testing.assert_array_equal(x.cpu().numpy(), r)
     for x, r in zip(out_b, ref_b):
         np.testing.assert_array_equal(x.cpu().numpy(), r)
+
+
+def _misaligned(t):
+    """The same values at a 2-byte offset from a 4-byte boundary (a bf16 view one element into a
+    larger buffer), so the bf16 channel-pair loads cannot be used."""
+    import torch
+    flat = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+    m = flat[1:].view(t.shape)
+    m.copy_(t)
+    assert m.data_ptr() % 4 == 2
+    return m
+
+
+def test_backward_bf16_misaligned_even_channels():
+    """Even C but k and v 2 bytes off a 4-byte boundary: the 16-bit loads instead of channel pairs,
+    over several chunks per row, against the definition form."""
+    import torch
+
+    import linear_complexity_vision_amd as L
+    wl = workloads.make_random(301, 2, 700, 66, dtype="bf16", w_range=6.0, k_std=1.5)
+    gy = _upstream(wl, 302)
+    k, v, w, u = to_device_kv(wl)
+    print("[case] biwkv_backward bf16 misaligned k, v", flush=True)
+    dk, dv, dw, du = L.biwkv_backward(_misaligned(k), _misaligned(v), w, u, torch.from_numpy(gy).cuda())
+    torch.cuda.synchronize()
+    got = (dk.cpu().numpy(), dv.cpu().numpy(), dw.cpu().numpy(), du.cpu().numpy())
+    ref = oracle.biwkv_backward_sum(f64(wl.k), f64(wl.v), f64(wl.w), f64(wl.u), f64(gy), with_scale=True)
+    for name, x, r, s in zip(("dk", "dv", "dw", "du"), got, ref[:4], ref[4:]):
+        err = _scaled_err(x, r, s)
+        print(f"[parity] backward misaligned {name}: scaled error {err:.3e}", flush=True)
+        assert err <= 1e-4, (name, err)
+    # the same bits as the aligned call (which takes the channel-pair loads)
+    aligned = L.biwkv_backward(k, v, w, u, torch.from_numpy(gy).cuda())
+    for x, a in zip(got, aligned):
+        np.testing.assert_array_equal(x, a.cpu().numpy())

@@ -140,6 +140,34 @@ def test_biwkv_edge_shapes(B, T, C, dtype):
     assert err <= 1e-4
 
 
+@pytest.mark.parametrize("T", [900, 2500])
+def test_biwkv_bf16_misaligned_even_channels(T):
+    """Even C but k and v 2 bytes off a 4-byte boundary: the 16-bit loads instead of channel pairs
+    (one chunk, and several chunks per row), against the definition form and bit for bit against
+    the aligned call."""
+    import torch
+    L = _lib()
+    wl = workloads.make_random(401 + T, 2, T, 66, dtype="bf16", w_range=6.0, k_std=2.0)
+    k, v, w, u = to_device_kv(wl)
+
+    def misaligned(t):
+        flat = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+        m = flat[1:].view(t.shape)
+        m.copy_(t)
+        assert m.data_ptr() % 4 == 2
+        return m
+
+    print(f"[case] biwkv_forward bf16 misaligned k, v T={T}", flush=True)
+    y = L.biwkv_forward(misaligned(k), misaligned(v), w, u)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    y_ref, s_ref = oracle.biwkv_sum(f64(wl.k), f64(wl.v), f64(wl.w), f64(wl.u), with_scale=True)
+    err = r3(y, y_ref, s_ref)
+    _report(f"misaligned T={T}", err, 1e-4)
+    assert err <= 1e-4
+    np.testing.assert_array_equal(y, L.biwkv_forward(k, v, w, u).cpu().numpy())
+
+
 @pytest.mark.parametrize("T", [600, 2500])
 @pytest.mark.parametrize("case", ["k_plus_100", "k_minus_100", "u_100", "u_minus_60", "w_plus_1e4",
                                   "w_minus_1e4", "w_mixed_wide", "w_zero", "k_spread_40"])
