@@ -1,20 +1,27 @@
 """Benchmark: Bi-WKV forward (+ Q-Shift) throughput and HBM roofline on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--entry fused|biwkv|causal|gated|qshift|mix|backward|bidir]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1..5]
+                    [--entry auto|fused|biwkv|causal|gated|qshift|mix|backward|bidir]
 
-One step = one pass of the whole hot path over one batch: the fused Q-Shift + Bi-WKV entry on the
-high-resolution workload (B=4, 64x64 grid so T=4096, C=1024, bf16 k/v, fp32 accumulate and
-output). Inputs are resident in HBM before timing; R copies of inputs and outputs are rotated so
-each step's buffers were last touched more than 256 MB of traffic ago (the MALL size), i.e. every
-step streams from HBM. Prints ONE JSON line.
+One step = one pass of the whole hot path over one batch: on the default workload (config 4: B=4,
+64x64 grid so T=4096, C=1024, bf16 k/v, fp32 accumulate and output) the fused Q-Shift + Bi-WKV
+entry. The same run also times the plain Bi-WKV forward (biwkv_forward) on the same inputs and
+reports it under "gate_entry" with its own roofline. --config N runs workload N instead (its
+fused entry on configs 2 and 4, biwkv_forward on 1, 3 and 5). Inputs are resident in HBM before
+timing; R copies of inputs and outputs are rotated so each step's buffers were last touched more
+than 2 x 256 MB (the memory-side cache) of traffic ago, i.e. every step streams from HBM. Prints
+ONE JSON line.
 
-Also:
+Also reported: per-launch times (median, p10, p90 of event pairs around single launches), and a
+measured memory ceiling for the same byte mix (libhbmceiling: k and v read, out written, nothing
+else computed), with the kernel's fraction of it.
+
     python bench.py --calibrate-copy      plain device copy of a known size (for counter scaling)
     python bench.py --summarize DIR       summarise rocprofv3 output (kernel stats / counters)
-    python bench.py --record-counters KF KW CF CW
+    python bench.py --record-counters KF KW CF CW [--config N --entry E]
         turn four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE of the bench, the same two of
-        --calibrate-copy) into profiles/hbm_counters_*.json: HBM bytes per launch, scaled so that
-        the copy's counters read its known size, stamped with the hash of the kernel sources
+        --calibrate-copy) into profiles/hbm_counters.json: HBM bytes per call, scaled so that the
+        copy's counters read its known size, stamped with the hash of the kernel sources
 """
 from __future__ import annotations
 
@@ -34,9 +41,19 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E peak
 MALL_BYTES = 256 * 1024 * 1024
 KERNEL_DIR = os.path.join(ROOT, "linear_complexity_vision_amd", "csrc")
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters_biwkv_qshift_B4_T4096_C1024_bf16.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.json")
 CALIBRATION_BYTES = 512 * 1024 * 1024
-MIN_CPU_SECONDS = 3.0
+MIN_CPU_SECONDS = 10.0
+# entry timed by default per workload (the fused entry where the workload has Q-Shift), and the
+# plain forward timed beside it
+DEFAULT_ENTRY = {1: "biwkv", 2: "fused", 3: "biwkv", 4: "fused", 5: "biwkv"}
+GATE_ENTRY = {2: "biwkv", 4: "biwkv"}
+# entries whose byte mix is the forward's (k, v read once, fp32 out written): the memory ceiling
+# applies to them
+CEILING_ENTRIES = ("biwkv", "fused", "causal", "bidir")
+# grid-stride streaming variants tried for the ceiling (blocks, unroll, policy: non-temporal loads
+# and stores); the fastest is the ceiling
+CEILING_VARIANTS = [(512, 1, 3), (2048, 1, 3), (8192, 2, 3), (8192, 4, 3), (1024, 1, 1), (4096, 2, 1)]
 COPY_KERNEL = "copy"  # substring of the device copy kernel's name in the counter output
 KERNEL_NAMES = {"fused": "biwkv_row_kernel", "biwkv": "biwkv_row_kernel", "causal": "biwkv_row_kernel",
                 "gated": "biwkv_row_kernel", "qshift": "qshift_kernel", "mix": "qshift_mix_kernel",
@@ -90,8 +107,12 @@ def alg_bytes(entry: str, B: int, H: int, W: int, C: int, kv_bytes: int, shift: 
     raise ValueError(entry)
 
 
+def counter_key(config: int, entry: str) -> str:
+    return f"config{config}:{entry}"
+
+
 def _load_counters():
-    """Counter-derived HBM bytes per launch, valid only for the kernel source they were taken on."""
+    """Counter-derived HBM bytes per call, valid only for the kernel source they were taken on."""
     try:
         rec = json.load(open(COUNTERS_FILE))
     except (OSError, ValueError):
@@ -205,6 +226,70 @@ def _rotation(bytes_per_set: int) -> int:
     return max(2, -(-2 * MALL_BYTES // bytes_per_set) + 1)
 
 
+def _percentiles(xs):
+    d = sorted(xs)
+    pick = lambda q: d[min(len(d) - 1, int(q * (len(d) - 1) + 0.5))]
+    return {"median": pick(0.5), "p10": pick(0.1), "p90": pick(0.9)}
+
+
+def _time_calls(torch, stream, step, steps, warmup):
+    """Warm-up, then the timed span of `steps` back-to-back calls (HIP events on the launch stream,
+    a barrier and a device synchronisation on both sides), then `steps` more calls each between its
+    own event pair. Returns (span seconds / call, wall seconds, per-call microseconds)."""
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        step(warmup + i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    span = start.elapsed_time(end) * 1e-3 / steps
+    pairs = []
+    for i in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step(warmup + steps + i)
+        e1.record(stream)
+        pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) * 1e3 for a, b in pairs]
+    return span, wall, per
+
+
+def copy_ceiling(torch, stream, ks_, vs_, outs, n, kv_bytes, steps, warmup):
+    """The memory ceiling of the forward's byte mix on this device: libhbmceiling's streaming
+    kernels (k, v read, out = k + v written; nothing else) on the bench's own rotated buffers, the
+    fastest of CEILING_VARIANTS. Returns (GB/s, microseconds per call, variant)."""
+    import ctypes
+
+    from linear_complexity_vision_amd import build
+
+    lib = ctypes.CDLL(build.CEILING_LIB)
+    f = lib.hbm_stream
+    f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64] + [ctypes.c_int] * 5 + [ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    R = len(outs)
+    dt = 1 if kv_bytes == 2 else 0
+    best = None
+    for blocks, unroll, policy in CEILING_VARIANTS:
+        def step(i, blocks=blocks, unroll=unroll, policy=policy):
+            r = i % R
+            rc = f(ks_[r].data_ptr(), vs_[r].data_ptr(), outs[r].data_ptr(), n, dt, 0, blocks, unroll, policy,
+                   stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"hbm_stream failed ({rc})")
+        span, _, _ = _time_calls(torch, stream, step, max(20, steps // 4), 5)
+        if best is None or span < best[0]:
+            best = (span, (blocks, unroll, policy))
+    byts = 2 * kv_bytes * n + 4 * n
+    return byts / best[0] / 1e9, best[0] * 1e6, {"blocks": best[1][0], "unroll": best[1][1], "policy": best[1][2],
+                                                "bytes": byts}
+
+
 def run_bench(args) -> dict:
     import numpy as np
     import torch
@@ -214,21 +299,29 @@ def run_bench(args) -> dict:
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    entry = DEFAULT_ENTRY[args.config] if args.entry == "auto" else args.entry
     # the sparse-input entry runs on the masked-image workload of the same element count
-    wl = workloads.make_mae(2) if args.entry == "bidir" else workloads.make(4)
+    wl = workloads.make_mae(2) if entry == "bidir" else workloads.make(args.config)
     B, H, W, C = wl.B, wl.H, wl.W, wl.C
     T = H * W
-    entry = args.entry
+    n = B * T * C
+    bf16 = wl.dtype == "bf16"
+    kv_bytes = 2 if bf16 else 4
     ks, vs = wl.kv_storage()
-    kb = torch.from_numpy(np.ascontiguousarray(ks)).view(torch.bfloat16).to(dev)
-    vb = torch.from_numpy(np.ascontiguousarray(vs)).view(torch.bfloat16).to(dev)
+
+    def dev_kv(a):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        return (t.view(torch.bfloat16) if bf16 else t).to(dev)
+
+    kb, vb = dev_kv(ks), dev_kv(vs)
     w = torch.from_numpy(wl.w).to(dev)
     u = torch.from_numpy(wl.u).to(dev)
-    set_bytes = (kb.numel() + vb.numel()) * 2 + B * T * C * (16 if entry == "backward" else 4)
+    set_bytes = (kb.numel() + vb.numel()) * kv_bytes + n * (16 if entry == "backward" else 4)
     R = _rotation(set_bytes)
     ks_ = [kb] + [kb.clone() for _ in range(R - 1)]
     vs_ = [vb] + [vb.clone() for _ in range(R - 1)]
     outs = [torch.empty((B, T, C), dtype=torch.float32, device=dev) for _ in range(R)]
+    dt = lib.BF16 if bf16 else lib.F32
     if entry in ("qshift", "mix"):
         xs = [torch.from_numpy(wl.k).to(dev).contiguous() for _ in range(R)]
     if entry == "mix":
@@ -239,122 +332,134 @@ def run_bench(args) -> dict:
         dvs = [torch.empty((B, T, C), dtype=torch.float32, device=dev) for _ in range(R)]
         dws = [torch.empty((2, C), dtype=torch.float32, device=dev) for _ in range(R)]
     if entry == "gated":
-        rb = torch.from_numpy(np.ascontiguousarray(workloads.round_to_bf16_bits(_gate_input(wl)))).view(
-            torch.bfloat16).to(dev)
+        r32 = _gate_input(wl)
+        rb = dev_kv(workloads.round_to_bf16_bits(r32) if bf16 else r32)
         rs_ = [rb] + [rb.clone() for _ in range(R - 1)]
 
     # One checked call per buffer set through the package, then the same C entry point called
     # with the already marshalled arguments (the timed loop measures the library, not Python).
     stream = torch.cuda.current_stream(dev)
     cl = lib.load_library()
-    calls = []
-    for r in range(R):
-        if entry == "fused":
-            lib.biwkv_qshift_forward(ks_[r], vs_[r], w, u, H, W, wl.shift, wl.gamma, out=outs[r])
-            calls.append((cl.biwkv_qshift_forward,
-                          (ks_[r].data_ptr(), vs_[r].data_ptr(), w.data_ptr(), u.data_ptr(),
-                           outs[r].data_ptr(), B, H, W, C, wl.shift, wl.gamma, lib.BF16,
-                           stream.cuda_stream)))
-        elif entry == "bidir":
-            lib.biwkv_qshift_bidir_forward(ks_[r], vs_[r], w, u, wl.shift, wl.gamma, out=outs[r])
-            calls.append((cl.biwkv_qshift_bidir_forward,
-                          (ks_[r].data_ptr(), vs_[r].data_ptr(), w.data_ptr(), u.data_ptr(),
-                           outs[r].data_ptr(), B, T, C, wl.shift, wl.gamma, lib.BF16, stream.cuda_stream)))
-        elif entry == "biwkv":
-            lib.biwkv_forward(ks_[r], vs_[r], w, u, out=outs[r])
-            calls.append((cl.biwkv_forward,
-                          (ks_[r].data_ptr(), vs_[r].data_ptr(), w.data_ptr(), u.data_ptr(),
-                           outs[r].data_ptr(), B, T, C, lib.BF16, stream.cuda_stream)))
-        elif entry == "causal":
-            lib.biwkv_causal_forward(ks_[r], vs_[r], w, u, out=outs[r])
-            calls.append((cl.biwkv_causal_forward,
-                          (ks_[r].data_ptr(), vs_[r].data_ptr(), w.data_ptr(), u.data_ptr(),
-                           outs[r].data_ptr(), B, T, C, lib.BF16, stream.cuda_stream)))
-        elif entry == "gated":
-            lib.biwkv_gated_forward(ks_[r], vs_[r], rs_[r], w, u, out=outs[r])
-            calls.append((cl.biwkv_gated_forward,
-                          (ks_[r].data_ptr(), vs_[r].data_ptr(), rs_[r].data_ptr(), w.data_ptr(),
-                           u.data_ptr(), outs[r].data_ptr(), B, T, C, lib.BF16, stream.cuda_stream)))
-        elif entry == "backward":
-            dk, dv, dw, du = lib.biwkv_backward(ks_[r], vs_[r], w, u, gs_[r])
-            outs[r].copy_(dk)
-            dvs[r].copy_(dv)
-            dws[r][0].copy_(dw)
-            dws[r][1].copy_(du)
-            calls.append((cl.biwkv_backward,
-                          (ks_[r].data_ptr(), vs_[r].data_ptr(), w.data_ptr(), u.data_ptr(),
-                           gs_[r].data_ptr(), outs[r].data_ptr(), dvs[r].data_ptr(), dws[r][0].data_ptr(),
-                           dws[r][1].data_ptr(), B, T, C, lib.BF16, stream.cuda_stream)))
-        elif entry == "mix":
-            lib.qshift_mix(xs[r], mu, H, W, wl.shift, wl.gamma, out=outs[r])
-            calls.append((cl.qshift_mix, (xs[r].data_ptr(), mu.data_ptr(), outs[r].data_ptr(), B, H, W,
-                                          C, N_MIX, wl.shift, wl.gamma, stream.cuda_stream)))
-        else:
-            lib.qshift(xs[r], H, W, wl.shift, wl.gamma, out=outs[r])
-            calls.append((cl.qshift, (xs[r].data_ptr(), outs[r].data_ptr(), B, H, W, C, wl.shift,
-                                      wl.gamma, stream.cuda_stream)))
 
-    def step(i):
-        fn, a = calls[i % R]
-        rc = fn(*a)
-        if rc != 0:
-            raise lib.BiwkvError(rc, lib.status_string(rc))
+    def calls_for(e):
+        calls = []
+        for r in range(R):
+            if e == "fused":
+                lib.biwkv_qshift_forward(ks_[r], vs_[r], w, u, H, W, wl.shift, wl.gamma, out=outs[r])
+                calls.append((cl.biwkv_qshift_forward,
+                              (ks_[r].data_ptr(), vs_[r].data_ptr(), w.data_ptr(), u.data_ptr(),
+                               outs[r].data_ptr(), B, H, W, C, wl.shift, wl.gamma, dt, stream.cuda_stream)))
+            elif e == "bidir":
+                lib.biwkv_qshift_bidir_forward(ks_[r], vs_[r], w, u, wl.shift, wl.gamma, out=outs[r])
+                calls.append((cl.biwkv_qshift_bidir_forward,
+                              (ks_[r].data_ptr(), vs_[r].data_ptr(), w.data_ptr(), u.data_ptr(),
+                               outs[r].data_ptr(), B, T, C, wl.shift, wl.gamma, dt, stream.cuda_stream)))
+            elif e == "biwkv":
+                lib.biwkv_forward(ks_[r], vs_[r], w, u, out=outs[r])
+                calls.append((cl.biwkv_forward,
+                              (ks_[r].data_ptr(), vs_[r].data_ptr(), w.data_ptr(), u.data_ptr(),
+                               outs[r].data_ptr(), B, T, C, dt, stream.cuda_stream)))
+            elif e == "causal":
+                lib.biwkv_causal_forward(ks_[r], vs_[r], w, u, out=outs[r])
+                calls.append((cl.biwkv_causal_forward,
+                              (ks_[r].data_ptr(), vs_[r].data_ptr(), w.data_ptr(), u.data_ptr(),
+                               outs[r].data_ptr(), B, T, C, dt, stream.cuda_stream)))
+            elif e == "gated":
+                lib.biwkv_gated_forward(ks_[r], vs_[r], rs_[r], w, u, out=outs[r])
+                calls.append((cl.biwkv_gated_forward,
+                              (ks_[r].data_ptr(), vs_[r].data_ptr(), rs_[r].data_ptr(), w.data_ptr(),
+                               u.data_ptr(), outs[r].data_ptr(), B, T, C, dt, stream.cuda_stream)))
+            elif e == "backward":
+                dk, dv, dw, du = lib.biwkv_backward(ks_[r], vs_[r], w, u, gs_[r])
+                outs[r].copy_(dk)
+                dvs[r].copy_(dv)
+                dws[r][0].copy_(dw)
+                dws[r][1].copy_(du)
+                calls.append((cl.biwkv_backward,
+                              (ks_[r].data_ptr(), vs_[r].data_ptr(), w.data_ptr(), u.data_ptr(),
+                               gs_[r].data_ptr(), outs[r].data_ptr(), dvs[r].data_ptr(), dws[r][0].data_ptr(),
+                               dws[r][1].data_ptr(), B, T, C, dt, stream.cuda_stream)))
+            elif e == "mix":
+                lib.qshift_mix(xs[r], mu, H, W, wl.shift, wl.gamma, out=outs[r])
+                calls.append((cl.qshift_mix, (xs[r].data_ptr(), mu.data_ptr(), outs[r].data_ptr(), B, H, W,
+                                              C, N_MIX, wl.shift, wl.gamma, stream.cuda_stream)))
+            else:
+                lib.qshift(xs[r], H, W, wl.shift, wl.gamma, out=outs[r])
+                calls.append((cl.qshift, (xs[r].data_ptr(), outs[r].data_ptr(), B, H, W, C, wl.shift,
+                                          wl.gamma, stream.cuda_stream)))
+        return calls
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    assert lib.stream_fault_flags(dev) == 0
-
-    # HIP events on the launch stream bracket the timed region; the launches queue back to back
-    # (host submission is faster than the kernel), so the event span / K is the average launch
-    # duration including the short gaps between kernels.
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i)
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    assert lib.stream_fault_flags(dev) == 0
-
-    avg_ms = start.elapsed_time(end) / args.steps
-    ms_per_step = wall * 1e3 / args.steps
-    elems = B * T * C
-    kv_bytes = 4 if entry in ("qshift", "mix") else 2
-    ab = alg_bytes(entry, B, H, W, C, kv_bytes, wl.shift, wl.gamma)
-    achieved = ab / (avg_ms * 1e-3) / 1e9
-    counters = _load_counters()
-    traffic = None
-    if counters is not None and entry in counters.get("entries", {}):
-        traffic = counters["entries"][entry]["hbm_bytes_per_launch"]
     names = {"fused": "biwkv_qshift_forward", "biwkv": "biwkv_forward", "causal": "biwkv_causal_forward",
              "gated": "biwkv_gated_forward", "qshift": "qshift", "mix": "qshift_mix",
              "backward": "biwkv_backward", "bidir": "biwkv_qshift_bidir_forward"}
-    return {
+    counters = _load_counters()
+
+    def measure(e):
+        calls = calls_for(e)
+
+        def step(i):
+            fn, a = calls[i % R]
+            rc = fn(*a)
+            if rc != 0:
+                raise lib.BiwkvError(rc, lib.status_string(rc))
+
+        torch.cuda.synchronize()
+        assert lib.stream_fault_flags(dev) == 0
+        span, wall, per = _time_calls(torch, stream, step, args.steps, args.warmup)
+        assert lib.stream_fault_flags(dev) == 0
+        ab = alg_bytes(e, B, H, W, C, 4 if e in ("qshift", "mix") else kv_bytes, wl.shift, wl.gamma)
+        achieved = ab / span / 1e9
+        traffic = None
+        if counters is not None:
+            rec = counters.get("entries", {}).get(counter_key(args.config, e))
+            traffic = rec["hbm_bytes_per_call"] if rec else None
+        pct = _percentiles(per)
+        return {"entry": names[e], "wall": wall, "span": span,
+                "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                             "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic, "alg_bytes_per_launch": ab,
+                             "avg_launch_ms": span * 1e3,
+                             "launch_us": {k: round(v, 3) for k, v in pct.items()}}}
+
+    main = measure(entry)
+    gate = measure(GATE_ENTRY[args.config]) if entry == DEFAULT_ENTRY[args.config] and args.config in GATE_ENTRY \
+        else None
+    ceiling = None
+    if entry in CEILING_ENTRIES and not args.no_ceiling:
+        gbps, us, variant = copy_ceiling(torch, stream, ks_, vs_, outs, n, kv_bytes, args.steps, args.warmup)
+        ceiling = {"gbps": gbps, "us": us, "variant": variant}
+        for m in (main, gate):
+            if m is not None:
+                m["roofline"]["copy_ceiling_gbps"] = gbps
+                m["roofline"]["frac_of_copy_ceiling"] = m["roofline"]["achieved"] / gbps
+
+    metric_shape = ("N=1024 visible tokens (sparse, MAE) C=1024" if entry == "bidir" else f"T={T} C={C}")
+    res = {
         "metric": ("Bi-WKV bwd" if entry == "backward" else "Bi-WKV fwd")
-                  + " Gtoken*ch/s + achieved HBM GB/s (% peak) at "
-                  + ("N=1024 visible tokens (sparse, MAE) C=1024" if entry == "bidir" else "T=4096 C=1024"),
-        "value": elems * args.steps / wall / 1e9,
+                  + " Gtoken*ch/s + achieved HBM GB/s (% peak) at " + metric_shape,
+        "value": n * args.steps / main["wall"] / 1e9,
         "unit": "Gtoken*ch/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": main["wall"] * 1e3 / args.steps,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": wl.name, "entry": names[entry], "B": B, "T": T, "H": H, "W": W, "C": C,
-                   "kv_storage": "bf16" if entry not in ("qshift", "mix") else "f32", "shift": wl.shift,
+        "config": {"workload": wl.name, "entry": main["entry"], "B": B, "T": T, "H": H, "W": W, "C": C,
+                   "kv_storage": "f32" if entry in ("qshift", "mix") else wl.dtype, "shift": wl.shift,
                    "gamma": wl.gamma, "buffer_sets_rotated": R},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "alg_bytes_per_launch": ab, "avg_launch_ms": avg_ms},
+        "roofline": main["roofline"],
         "_wl": wl,
+        "_entry": entry,
     }
+    if gate is not None:
+        res["gate_entry"] = {"entry": gate["entry"], "value": n * args.steps / gate["wall"] / 1e9,
+                             "unit": "Gtoken*ch/s", "roofline": gate["roofline"]}
+    if ceiling is not None:
+        res["copy_ceiling"] = ceiling
+    return res
 
 
 def calibrate_copy(args) -> None:
@@ -376,55 +481,68 @@ def calibrate_copy(args) -> None:
                       "bytes_written": CALIBRATION_BYTES, "launches": args.steps}))
 
 
-def _counter_means(path: str, counter: str, kernel: str) -> float:
-    """Mean per-dispatch value of `counter` over the largest-grid dispatches of kernels whose name
-    contains `kernel` (smaller dispatches of the same kernel, e.g. set-up copies, are skipped)."""
+def _counter_rows(path: str, counter: str):
+    """(kernel name, dispatch key, grid size, value) per dispatch of `counter` (values of one
+    dispatch's instances summed)."""
     vals = {}
     for f in glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True):
         for row in csv.DictReader(open(f)):
-            if row.get("Counter_Name") != counter or kernel not in row.get("Kernel_Name", ""):
+            if row.get("Counter_Name") != counter:
                 continue
-            # one row per dispatch and counter (values of one dispatch's instances are summed)
             key = (f, row.get("Dispatch_Id", row.get("Correlation_Id")))
-            grid = int(row.get("Grid_Size", "0"))
-            v = vals.setdefault(key, [grid, 0.0])
-            v[1] += float(row["Counter_Value"])
-    if not vals:
+            name = row.get("Kernel_Name", "")
+            v = vals.setdefault(key, [name, int(row.get("Grid_Size", "0")), 0.0])
+            v[2] += float(row["Counter_Value"])
+    return [(name, key, grid, val) for key, (name, grid, val) in vals.items()]
+
+
+def _counter_means(path: str, counter: str, kernel: str) -> float:
+    """Mean per-dispatch value of `counter` over the largest-grid dispatches of kernels whose name
+    contains `kernel` (smaller dispatches of the same kernel, e.g. set-up copies, are skipped)."""
+    rows = [r for r in _counter_rows(path, counter) if kernel in r[0]]
+    if not rows:
         raise SystemExit(f"no {counter} values for {kernel} under {path}")
-    top = max(g for g, _ in vals.values())
-    sel = [x for g, x in vals.values() if g == top]
+    top = max(r[2] for r in rows)
+    sel = [r[3] for r in rows if r[2] == top]
     return sum(sel) / len(sel)
+
+
+def _counter_call_sum(path: str, counter: str, kernel: str) -> float:
+    """Per call of an entry made of one or more distinct kernels (same grid) whose names contain
+    `kernel`: the sum over those kernels of each one's mean per dispatch, at the largest grid
+    (a two-pass forward is a sums launch and an output launch)."""
+    rows = [r for r in _counter_rows(path, counter) if kernel in r[0]]
+    if not rows:
+        raise SystemExit(f"no {counter} values for {kernel} under {path}")
+    top = max(r[2] for r in rows)
+    by_name = {}
+    for name, _, grid, val in rows:
+        if grid == top:
+            by_name.setdefault(name, []).append(val)
+    return sum(sum(v) / len(v) for v in by_name.values())
 
 
 def _counter_per_call(path: str, counter: str, kernel: str, marker: str) -> float:
     """Sum of `counter` over every dispatch of kernels whose name contains `kernel`, divided by the
     number of dispatches of the once-per-call kernel `marker`: the value per call of an entry point
     that launches several kernels."""
-    total, calls = 0.0, set()
-    for f in glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True):
-        for row in csv.DictReader(open(f)):
-            if row.get("Counter_Name") != counter:
-                continue
-            name = row.get("Kernel_Name", "")
-            if kernel in name:
-                total += float(row["Counter_Value"])
-            if marker in name:
-                calls.add((f, row.get("Dispatch_Id", row.get("Correlation_Id"))))
+    rows = _counter_rows(path, counter)
+    total = sum(val for name, _, _, val in rows if kernel in name)
+    calls = sum(1 for name, _, _, _ in rows if marker in name)
     if not calls:
         raise SystemExit(f"no {counter} values for {marker} under {path}")
-    return total / len(calls)
+    return total / calls
 
 
-def record_counters(kf: str, kw: str, cf: str, cw: str, entry: str) -> None:
-    """HBM traffic per launch of the bench kernel (per call, for entries of several kernels) from
-    FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by what it reads for a device copy of
-    CALIBRATION_BYTES."""
+def record_counters(kf: str, kw: str, cf: str, cw: str, config: int, entry: str) -> None:
+    """HBM traffic per call of the entry on workload `config` from FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), each scaled by what it reads for a device copy of CALIBRATION_BYTES."""
     if entry in CALL_MARKER:
         fetch = _counter_per_call(kf, "FETCH_SIZE", KERNEL_NAMES[entry], CALL_MARKER[entry])
         write = _counter_per_call(kw, "WRITE_SIZE", KERNEL_NAMES[entry], CALL_MARKER[entry])
     else:
-        fetch = _counter_means(kf, "FETCH_SIZE", KERNEL_NAMES[entry])
-        write = _counter_means(kw, "WRITE_SIZE", KERNEL_NAMES[entry])
+        fetch = _counter_call_sum(kf, "FETCH_SIZE", KERNEL_NAMES[entry])
+        write = _counter_call_sum(kw, "WRITE_SIZE", KERNEL_NAMES[entry])
     cal_fetch = _counter_means(cf, "FETCH_SIZE", COPY_KERNEL)
     cal_write = _counter_means(cw, "WRITE_SIZE", COPY_KERNEL)
     f_scale = CALIBRATION_BYTES / cal_fetch
@@ -439,11 +557,12 @@ def record_counters(kf: str, kw: str, cf: str, cw: str, entry: str) -> None:
     rec["kernel_source_sha256_16"] = kernel_source_hash()
     rec["calibration"] = {"bytes": CALIBRATION_BYTES, "fetch_kib": cal_fetch, "write_kib": cal_write,
                           "fetch_bytes_per_unit": f_scale, "write_bytes_per_unit": w_scale}
-    rec["entries"][entry] = {"fetch_kib_per_launch": fetch, "write_kib_per_launch": write,
-                             "hbm_bytes_per_launch": fetch * f_scale + write * w_scale}
+    rec["entries"][counter_key(config, entry)] = {
+        "fetch_kib_per_call": fetch, "write_kib_per_call": write,
+        "hbm_bytes_per_call": fetch * f_scale + write * w_scale}
     os.makedirs(os.path.dirname(COUNTERS_FILE), exist_ok=True)
     json.dump(rec, open(COUNTERS_FILE, "w"), indent=1, sort_keys=True)
-    print(json.dumps(rec["entries"][entry]))
+    print(json.dumps(rec["entries"][counter_key(config, entry)]))
 
 
 def summarize(path: str) -> None:
@@ -470,11 +589,13 @@ def summarize(path: str) -> None:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--entry", choices=["fused", "biwkv", "causal", "gated", "qshift", "mix", "backward", "bidir"],
-                    default="fused")
+    ap.add_argument("--config", type=int, choices=[1, 2, 3, 4, 5], default=4)
+    ap.add_argument("--entry", choices=["auto", "fused", "biwkv", "causal", "gated", "qshift", "mix", "backward",
+                                        "bidir"], default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize", metavar="DIR")
     ap.add_argument("--record-counters", nargs=4, metavar=("KF", "KW", "CF", "CW"))
@@ -484,7 +605,8 @@ def main() -> int:
         summarize(args.summarize)
         return 0
     if args.record_counters:
-        record_counters(*args.record_counters, entry=args.entry)
+        entry = DEFAULT_ENTRY[args.config] if args.entry == "auto" else args.entry
+        record_counters(*args.record_counters, config=args.config, entry=entry)
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -496,7 +618,8 @@ def main() -> int:
         return 0
     res = run_bench(args)
     wl = res.pop("_wl")
-    res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(wl, args.entry)
+    entry = res.pop("_entry")
+    res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(wl, entry)
     print(json.dumps(res), flush=True)
     return 0
 

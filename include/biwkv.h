@@ -25,10 +25,18 @@
  *   - The caller owns every buffer. The library keeps no pointer to caller memory after the
  *     enqueued work completes. Bi-WKV calls whose sequence is split over several workgroups
  *     (T above 1024 for bf16, above 512 for fp32) use library-owned scratch (chunk sums and a
- *     small counter block) kept per (device, stream); it is allocated on the first such call on
- *     a stream and grown when a larger problem arrives, so those calls must not be made under
- *     HIP graph capture. Replaying a captured call is safe: launches are told apart by a
+ *     small counter block) kept per (device, stream); it is allocated in stream order
+ *     (hipMallocAsync) on the first such call on a stream, grown when a larger problem arrives
+ *     (the outgrown buffer is freed in stream order), and released by biwkv_release_scratch. So
+ *     those calls must not be made under HIP graph capture unless an earlier call on the stream
+ *     already sized the scratch. Replaying a captured call is safe: launches are told apart by a
  *     device-side epoch, not by arguments.
+ *   - A row split over several workgroups is combined either in one launch, where the chunks
+ *     exchange their sums while resident (used when every workgroup of the launch fits on the
+ *     device at once), or in two launches (chunk sums, then outputs). In one launch a workgroup
+ *     waits a bounded time for a peer chunk's sums and then recomputes them from that chunk's k
+ *     and v, so results never depend on the peers being resident (for example when other work
+ *     occupies the device); biwkv_stream_fault_flags reports that this happened.
  *   - All argument validation happens on the host before any HIP call. A problem with zero
  *     elements returns BIWKV_OK without enqueuing anything. Nothing is printed; no C++ exception
  *     crosses this interface.
@@ -58,7 +66,15 @@ extern "C" {
 #define BIWKV_ERR_ALIGN (-6)       /* a pointer is not aligned to its element size               */
 #define BIWKV_ERR_NO_DEVICE (-7)   /* no usable HIP device                                       */
 #define BIWKV_ERR_HIP (-8)         /* a HIP runtime call or launch failed; see biwkv_last_hip_error */
-#define BIWKV_ERR_UNSUPPORTED (-9) /* T needs more chunks than can be resident at once          */
+#define BIWKV_ERR_UNSUPPORTED (-9) /* a shape outside the kernels' addressing (limits per entry)  */
+
+/* Options (biwkv_set_option). Process-wide; they apply to calls made after they are set. */
+#define BIWKV_OPT_SPIN_LIMIT 1 /* polls of a peer chunk's sums before recomputing them (default 4096;
+                                  0: recompute every peer's sums without waiting)             */
+#define BIWKV_OPT_TWO_PASS 2   /* 0 (default): one launch when all workgroups fit at once;
+                                  1: rows of several chunks always take two launches          */
+#define BIWKV_OPT_WIDE_INDEX 3 /* 0 (default): Q-Shift gathers use 32-bit index arithmetic below
+                                  2^31 items; 1: always the 64-bit form                       */
 
 /*
  * Bi-WKV forward, Eq. (5) of the Vision-RWKV article.
@@ -66,11 +82,9 @@ extern "C" {
  *   w, u : [C] float32, device memory (decay, divided by T inside; bonus).
  *   out  : [B, T, C] float32, device memory; must not overlap k, v, w or u.
  * Errors: BIWKV_ERR_NULL, _SHAPE (B, T, C < 0 or B*T*C*4 bytes overflow), _DTYPE, _ALIAS, _ALIGN,
- * _NO_DEVICE, _HIP, and _UNSUPPORTED when a row needs more chunks than fit on the device at once:
- * while (T + 1024) * C * 4 bytes stay below 2^31, a row that needs several chunks has chunks of
- * 512 tokens (two workgroups per CU for bf16, one for fp32), so T may reach 512 times the number
- * of resident workgroups: 262144 (bf16) or 131072 (fp32) on MI355X's 256 CUs; beyond that,
- * 128-token chunks (T up to about 32768).
+ * _NO_DEVICE, _HIP, and _UNSUPPORTED when one chunk of a row spans 2^31 bytes of out: chunks are
+ * 512 tokens (bf16, T > 1024) or 512 (fp32, T > 512), so C * 512 * 4 must stay below 2^31
+ * (C < 1048576). Any T up to 2^31 - 1 is addressed.
  */
 int biwkv_forward(const void* k, const void* v, const float* w, const float* u, float* out,
                   int64_t B, int64_t T, int64_t C, int dtype, void* stream);
@@ -104,8 +118,7 @@ int biwkv_backward(const void* k, const void* v, const float* w, const float* u,
  *   out_t = ( sum_{i<t} e^{-((t-1-i)/T) w + k_i} v_i + e^{u+k_t} v_t )
  *         / ( sum_{i<t} e^{-((t-1-i)/T) w + k_i}     + e^{u+k_t}     )
  * w is divided by T as in Eq. (5); the original, undivided decay w0 is w = T * w0.
- * Arguments, layout, ownership, scratch and errors are those of biwkv_forward, except that there
- * is no 128-token fallback: a row whose chunks cannot all be resident returns _UNSUPPORTED.
+ * Arguments, layout, ownership, scratch and errors are those of biwkv_forward.
  */
 int biwkv_causal_forward(const void* k, const void* v, const float* w, const float* u, float* out,
                          int64_t B, int64_t T, int64_t C, int dtype, void* stream);
@@ -115,8 +128,7 @@ int biwkv_causal_forward(const void* k, const void* v, const float* w, const flo
  * projection: out = sigmoid(r) * Bi-WKV(k, v), elementwise, with sigmoid(x) = 1 / (1 + e^{-x}).
  *   r : [B, T, C] gate input (the R projection), storage type `dtype` like k and v, device memory;
  *       must not overlap out.
- * Other arguments, layout, ownership, scratch and errors are those of biwkv_forward, except that
- * there is no 128-token fallback (a row whose chunks cannot all be resident returns _UNSUPPORTED).
+ * Other arguments, layout, ownership, scratch and errors are those of biwkv_forward.
  */
 int biwkv_gated_forward(const void* k, const void* v, const void* r, const float* w, const float* u,
                         float* out, int64_t B, int64_t T, int64_t C, int dtype, void* stream);
@@ -151,7 +163,8 @@ int qshift_mix(const float* x, const float* mu, float* out, int64_t B, int64_t H
  * while k and v are loaded; no shifted copy is written to memory.
  *   k, v : [B, H*W, C], storage type `dtype`; w, u : [C] float32; out : [B, H*W, C] float32.
  *   shift, gamma as for qshift().
- * Errors: as biwkv_forward() plus BIWKV_ERR_PARAM.
+ * Errors: as biwkv_forward() plus BIWKV_ERR_PARAM; _UNSUPPORTED when (512 + 2 shift W) * C * 4
+ * reaches 2^31 (a chunk's loads reach s W tokens on either side).
  */
 int biwkv_qshift_forward(const void* k, const void* v, const float* w, const float* u, float* out,
                          int64_t B, int64_t H, int64_t W, int64_t C, int shift, double gamma,
@@ -176,8 +189,8 @@ int qshift_bidir(const float* x, float* out, int64_t B, int64_t N, int64_t C, in
  * (the spatial mix of a sparse, MAE-masked input). The shift is applied while k and v are loaded.
  *   k, v : [B, N, C], storage type `dtype`; w, u : [C] float32; out : [B, N, C] float32.
  *   shift, gamma as for qshift_bidir().
- * Errors: as biwkv_forward() plus BIWKV_ERR_PARAM; no 128-token fallback (a row whose chunks
- * cannot all be resident returns _UNSUPPORTED).
+ * Errors: as biwkv_forward() plus BIWKV_ERR_PARAM; _UNSUPPORTED when (512 + 2 shift) * C * 4
+ * reaches 2^31.
  */
 int biwkv_qshift_bidir_forward(const void* k, const void* v, const float* w, const float* u,
                                float* out, int64_t B, int64_t N, int64_t C, int shift, double gamma,
@@ -191,14 +204,29 @@ int biwkv_last_hip_error(void);
 
 /*
  * Diagnostic: synchronises `stream`, then reports and clears the device-side fault word of that
- * stream's scratch. *flags receives 0 when every Bi-WKV launch on the stream since the last query
- * completed its cross-chunk exchange normally; bit 0 set means a chunk stopped waiting for a
- * neighbour's aggregate after its bounded wait ran out, bit 1 that a launch found its ticket
- * counter left non-zero by an earlier, interrupted launch (outputs are then invalid). Returns
- * BIWKV_OK, BIWKV_ERR_NULL (flags NULL), _NO_DEVICE or _HIP. A stream with no scratch yet
- * reports 0.
+ * stream's scratch. *flags receives 0 when every single-launch Bi-WKV call on the stream since
+ * the last query found its peer chunks' sums published in time; bit 0 set means that at least one
+ * workgroup's bounded wait ran out and it recomputed a peer chunk's sums from k and v (the outputs
+ * are still correct: this is a slow path, not an error). Returns BIWKV_OK, BIWKV_ERR_NULL (flags
+ * NULL), _NO_DEVICE or _HIP. A stream with no scratch yet reports 0.
  */
 int biwkv_stream_fault_flags(void* stream, uint32_t* flags);
+
+/*
+ * Releases the library's scratch for (current device, `stream`) in stream order: the memory is
+ * freed once the work already queued on the stream is done. Call it before destroying a stream
+ * that made Bi-WKV calls; a later call on the stream allocates fresh scratch. Returns BIWKV_OK
+ * (also when the stream has no scratch), _NO_DEVICE or _HIP.
+ */
+int biwkv_release_scratch(void* stream);
+
+/*
+ * Sets process-wide option `option` (BIWKV_OPT_*) to `value`; the previous value is written to
+ * *previous unless it is NULL. BIWKV_OPT_SPIN_LIMIT takes 0 .. 2^32 - 1, the others 0 or 1.
+ * Calls already enqueued are not affected. Returns BIWKV_OK or BIWKV_ERR_PARAM (unknown option or
+ * value out of range; nothing changed).
+ */
+int biwkv_set_option(int option, int64_t value, int64_t* previous);
 
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 int biwkv_version(void);

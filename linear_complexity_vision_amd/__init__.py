@@ -7,6 +7,9 @@ from ._lib import (  # noqa: F401
     BF16,
     F32,
     LIB_PATH,
+    OPT_SPIN_LIMIT,
+    OPT_TWO_PASS,
+    OPT_WIDE_INDEX,
     BiwkvError,
     biwkv_backward,
     biwkv_causal_forward,
@@ -16,9 +19,12 @@ from ._lib import (  # noqa: F401
     biwkv_qshift_forward,
     header_symbols,
     load_library,
+    option,
     qshift,
     qshift_bidir,
     qshift_mix,
+    release_scratch,
+    set_option,
     status_codes,
     status_string,
     stream_fault_flags,

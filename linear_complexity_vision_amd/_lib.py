@@ -76,6 +76,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.biwkv_stream_fault_flags.restype = ctypes.c_int
     lib.biwkv_version.argtypes = []
     lib.biwkv_version.restype = ctypes.c_int
+    lib.biwkv_release_scratch.argtypes = [_P]
+    lib.biwkv_release_scratch.restype = ctypes.c_int
+    lib.biwkv_set_option.argtypes = [ctypes.c_int, _I64, ctypes.POINTER(_I64)]
+    lib.biwkv_set_option.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -301,3 +305,38 @@ def stream_fault_flags(device=None) -> int:
     with torch.cuda.device(dev):
         _check(load_library().biwkv_stream_fault_flags(_stream_handle(dev), ctypes.byref(flags)))
     return int(flags.value)
+
+
+OPT_SPIN_LIMIT = 1
+OPT_TWO_PASS = 2
+OPT_WIDE_INDEX = 3
+
+
+def set_option(option: int, value: int) -> int:
+    """Sets a process-wide library option (OPT_*); returns the previous value."""
+    prev = _I64(0)
+    _check(load_library().biwkv_set_option(int(option), int(value), ctypes.byref(prev)))
+    return int(prev.value)
+
+
+class option:
+    """Context manager that sets a library option and restores its previous value."""
+
+    def __init__(self, opt: int, value: int):
+        self.opt, self.value, self.prev = opt, value, None
+
+    def __enter__(self):
+        self.prev = set_option(self.opt, self.value)
+        return self
+
+    def __exit__(self, *exc):
+        set_option(self.opt, self.prev)
+        return False
+
+
+def release_scratch(device=None) -> None:
+    """Releases the library's scratch for torch's current stream (stream-ordered free)."""
+    torch = _torch()
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    with torch.cuda.device(dev):
+        _check(load_library().biwkv_release_scratch(_stream_handle(dev)))

@@ -14,25 +14,36 @@ ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "biwkv.hip")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libbiwkv.so")
+# measurement only: streaming kernels with the forward's byte mix (a memory ceiling for the bench)
+CEILING_SRC = os.path.join(PKG, "csrc", "hbm_ceiling.hip")
+CEILING_LIB = os.path.join(PKG, "libhbmceiling.so")
 ARCH = "gfx950"
 
 
-def hipcc_command(out: str = LIB, extra: list[str] | None = None) -> list[str]:
+def hipcc_command(out: str = LIB, extra: list[str] | None = None, src: str = SRC) -> list[str]:
     hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
     return [hipcc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
             "-Wall", "-Wno-unused-function",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-I", INCLUDE, "-o", out, SRC] + (extra or [])
+            "-I", INCLUDE, "-o", out, src] + (extra or [])
+
+
+def _compile(src: str, lib: str, verbose: bool) -> subprocess.Popen:
+    cmd = hipcc_command(lib + ".tmp", src=src)
+    if verbose:
+        print(" ".join(cmd), file=sys.stderr)
+    return subprocess.Popen(cmd)
 
 
 def build(verbose: bool = False) -> str:
-    """Compile the library (always recompiles) and return its path."""
-    tmp = LIB + ".tmp"
-    cmd = hipcc_command(tmp)
-    if verbose:
-        print(" ".join(cmd), file=sys.stderr)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    """Compile both libraries (always recompiles; the two compile at once) and return the path of
+    libbiwkv.so."""
+    jobs = [(_compile(SRC, LIB, verbose), LIB), (_compile(CEILING_SRC, CEILING_LIB, verbose), CEILING_LIB)]
+    failed = [lib for proc, lib in jobs if proc.wait() != 0]
+    if failed:
+        raise subprocess.CalledProcessError(1, "hipcc", f"failed to build {failed}")
+    for _, lib in jobs:
+        os.replace(lib + ".tmp", lib)
     return LIB
 
 

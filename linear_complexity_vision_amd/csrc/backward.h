@@ -1,7 +1,7 @@
 // Bi-WKV backward: gradients of Eq. (5) with respect to k, v, w and u.
 #pragma once
 
-#include "common.cuh"
+#include "common.h"
 
 namespace {
 
@@ -19,7 +19,7 @@ namespace {
 // number of tokens strictly between t and i and splits lam^{|t-i|-1} at each of them, so every
 // sum above is an ordinary decayed prefix or suffix sum.
 //
-// The kernels that compute them are in bwd_tile.cuh; this file holds what the last step of every
+// The kernels that compute them are in bwd_tile.h; this file holds what the last step of every
 // backward call shares: the fold of the per-chunk dw and du terms.
 
 constexpr int kReduceGroups = 16;  // row segments per channel in the dw / du fold

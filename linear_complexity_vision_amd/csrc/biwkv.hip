@@ -15,12 +15,10 @@
 //     it forms the Eq. (6) partial sums of its tokens (the aggregate of a decayed sum is a
 //     triple (m, F, G) meaning F*2^m, G*2^m; appending n tokens shifts m by -n*w*log2(e)/T,
 //     so e^{-w/T} powers are never formed by repeated multiplication across chunks).
-//   * Chunks of a row are combined by a decoupled look-back in both directions: every chunk
-//     publishes its aggregate as soon as it has read its data, then walks towards the row start
-//     (forward states a, c) and towards the row end (backward states b, d) until it meets an
-//     inclusive prefix/suffix. Chunk identities come from a ticket counter, so a chunk only waits
-//     for chunks that hold tickets or will get them while it waits (the host limits the chunks
-//     per row to what can be resident), and every wait is bounded.
+//   * The chunks of a row are combined through their decayed sums: in one launch, by an exchange
+//     of epoch-tagged slots between resident workgroups (a wait that runs out recomputes the
+//     peer's sums from k and v, so no result depends on residency), or in two launches when the
+//     workgroups cannot all be resident (every chunk's totals, then the outputs).
 //   * Exponents are kept relative to a running maximum (base 2), so any sign of w and large k
 //     or u never overflow fp32.
 //   * Q-Shift for the fused entry is an index remap applied to the k/v loads (zero-filled
@@ -33,6 +31,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
 #include <cmath>
 #include <map>
 #include <mutex>
@@ -42,12 +41,11 @@
 
 #include "biwkv.h"
 
-#include "backward.cuh"
-#include "bwd_tile.cuh"
-#include "chunk_kernel.cuh"
-#include "common.cuh"
-#include "qshift_kernel.cuh"
-#include "row_kernel.cuh"
+#include "backward.h"
+#include "bwd_tile.h"
+#include "common.h"
+#include "qshift_kernel.h"
+#include "row_kernel.h"
 
 namespace {
 
@@ -64,16 +62,20 @@ int hip_fail(hipError_t e) {
 
 struct StreamScratch {
   Counters* ctr = nullptr;
-  unsigned long long* slots = nullptr;
+  unsigned long long* slots = nullptr;  // single-pass slots, or two-pass chunk totals
   long long slot_words = 0;
   float* bwd = nullptr;  // backward pass sums, carries and per-chunk terms
   long long bwd_floats = 0;
-  std::vector<void*> retired;  // outgrown buffers; pending launches may still use them
 };
 
 std::mutex g_mu;
 std::map<std::pair<int, void*>, StreamScratch*> g_scratch;
 std::map<std::pair<int, const void*>, int> g_capacity;  // (device, kernel) -> resident workgroups
+
+// Options (biwkv_set_option).
+std::atomic<unsigned> g_spin_limit{kSpinDefault};
+std::atomic<int> g_two_pass{0};
+std::atomic<int> g_wide_index{0};
 
 int current_device(int* dev) {
   int n = 0;
@@ -83,26 +85,34 @@ int current_device(int* dev) {
   return BIWKV_OK;
 }
 
+// Grows a zero-filled scratch buffer in stream order: the new buffer is allocated and cleared on
+// `st`, and the outgrown one is freed on `st` behind every launch already queued that uses it.
 template <typename Tp>
-int grow_zeroed(Tp** buf, long long* cap, long long need, long long min_cap, hipStream_t st,
-                std::vector<void*>* retired) {
+int grow_zeroed(Tp** buf, long long* cap, long long need, long long min_cap, hipStream_t st) {
   if (*cap >= need) return BIWKV_OK;
   long long want = *cap ? *cap : min_cap;
   while (want < need) want *= 2;
   const long long words = (want * static_cast<long long>(sizeof(Tp)) + 7) / 8;
-  unsigned long long* fresh = nullptr;
-  hipError_t e = hipMalloc(&fresh, static_cast<size_t>(words) * 8);
+  void* fresh = nullptr;
+  hipError_t e = hipMallocAsync(&fresh, static_cast<size_t>(words) * 8, st);
   if (e != hipSuccess) return hip_fail(e);
   long long blocks = (words + 255) / 256;
   if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(fill_u64_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, fresh, words);
+  hipLaunchKernelGGL(fill_u64_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
+                     static_cast<unsigned long long*>(fresh), words);
   e = hipGetLastError();
   if (e != hipSuccess) {
-    (void)hipFree(fresh);
+    (void)hipFreeAsync(fresh, st);
     return hip_fail(e);
   }
-  if (*buf) retired->push_back(*buf);
-  *buf = reinterpret_cast<Tp*>(fresh);
+  if (*buf) {
+    e = hipFreeAsync(*buf, st);
+    if (e != hipSuccess) {
+      (void)hipFreeAsync(fresh, st);
+      return hip_fail(e);
+    }
+  }
+  *buf = static_cast<Tp*>(fresh);
   *cap = want;
   return BIWKV_OK;
 }
@@ -114,7 +124,7 @@ int get_scratch(int dev, void* stream, long long words, StreamScratch** out) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (!sc) {
     StreamScratch* fresh = new StreamScratch();
-    hipError_t e = hipMalloc(&fresh->ctr, 256);
+    hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&fresh->ctr), 256, st);
     if (e != hipSuccess) {
       delete fresh;
       g_scratch.erase(key);
@@ -123,14 +133,14 @@ int get_scratch(int dev, void* stream, long long words, StreamScratch** out) {
     hipLaunchKernelGGL(init_counters_kernel, dim3(1), dim3(1), 0, st, fresh->ctr);
     e = hipGetLastError();
     if (e != hipSuccess) {
-      (void)hipFree(fresh->ctr);
+      (void)hipFreeAsync(fresh->ctr, st);
       delete fresh;
       g_scratch.erase(key);
       return hip_fail(e);
     }
     sc = fresh;
   }
-  int rc = grow_zeroed(&sc->slots, &sc->slot_words, words, 1ll << 16, st, &sc->retired);
+  int rc = grow_zeroed(&sc->slots, &sc->slot_words, words, 1ll << 16, st);
   if (rc) return rc;
   *out = sc;
   return BIWKV_OK;
@@ -192,64 +202,17 @@ int check_bitc_shape(int64_t B, int64_t T, int64_t C) {
   return BIWKV_OK;
 }
 
-// Tile shapes: LW tokens per wavefront, NW wavefronts per workgroup.
-constexpr int kLW = 16;
-constexpr int kNW = 8;
-
-template <int DT, int V, bool FUSED>
-int launch_biwkv(BiwkvParams prm, int64_t B, int dev, void* stream) {
-  constexpr int TILE = 64 * V;
-  constexpr int LWG = kLW * kNW;
-  const void* kfn = reinterpret_cast<const void*>(&biwkv_chunk_scan_kernel<DT, V, kLW, kNW, FUSED>);
-  const int64_t n_tiles = (prm.C + TILE - 1) / TILE;
-  const int64_t n_chunks = (prm.T + LWG - 1) / LWG;
-  const int64_t total = B * n_tiles * n_chunks;
-  if (total > 0x7FFFFFFFll) return BIWKV_ERR_SHAPE;
-  // Exchange groups: about sqrt(n) chunks each, so a chunk reads at most (groups - 1) group sums
-  // and (group - 1) member sums; both passes must fit the per-thread slot budget.
-  constexpr int KQ = kNW * 64 / TILE;
-  int64_t group = 1;
-  while (group * group < n_chunks) ++group;
-  const int64_t n_groups = (n_chunks + group - 1) / group;
-  const int64_t budget = static_cast<int64_t>(KQ) * kMaxSlotsPerThread;
-  if ((n_groups - 1) + (group - 1) > budget || 2 * (group - 1) > budget) return BIWKV_ERR_UNSUPPORTED;
-  std::lock_guard<std::mutex> lock(g_mu);
-  int cap = 0;
-  int rc = resident_capacity(dev, kfn, kNW * 64, &cap);
-  if (rc) return rc;
-  if (n_chunks > cap) return BIWKV_ERR_UNSUPPORTED;
-  StreamScratch* sc = nullptr;
-  const long long agg_words = total * 2 * TILE * 2;
-  const long long gagg_words = B * n_tiles * n_groups * 2 * TILE * 2;
-  rc = get_scratch(dev, stream, agg_words + gagg_words, &sc);
-  if (rc) return rc;
-  prm.n_tiles = static_cast<int>(n_tiles);
-  prm.n_chunks = static_cast<int>(n_chunks);
-  prm.total = static_cast<unsigned>(total);
-  prm.group = static_cast<int>(group);
-  prm.n_groups = static_cast<int>(n_groups);
-  prm.agg = sc->slots;
-  prm.gagg = sc->slots + agg_words;
-  prm.ctr = sc->ctr;
-  hipLaunchKernelGGL((biwkv_chunk_scan_kernel<DT, V, kLW, kNW, FUSED>),
-                     dim3(static_cast<unsigned>(total)), dim3(kNW * 64), 0,
-                     static_cast<hipStream_t>(stream), prm);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return hip_fail(e);
-  return BIWKV_OK;
-}
-
-// Tile kernel launch: rows of TILE channels, chunks of (NT / TILE) * L tokens. Returns 1 when
-// the shape is outside what the kernel addresses (the caller then uses the chunk-scan kernel).
+// Tile kernel launch: rows of TILE channels, chunks of (NT / TILE) * L tokens. A row of several
+// chunks runs in one launch when every workgroup fits on the device at once (and two passes are
+// not asked for), otherwise in two.
 template <int DT, int TILE, int L, int NT, bool FUSED, bool PAIR, bool CAUSAL, bool GATED>
 int launch_row(const BiwkvParams& bp, int64_t B, int dev, void* stream) {
   constexpr int CT = (NT / TILE) * L;
   const long long T = bp.T;
-  // byte offsets into one batch item of out (and so of k, v), including the empty slots past
-  // the row end, must stay below 2^31
-  // (the fused loads also start each word's resource s W tokens early and reach s W tokens late)
+  // byte offsets inside one chunk of out (and so of k, v) must stay below 2^31 (the fused loads
+  // also start each word's resource s W tokens early and reach s W tokens late)
   const long long reach = FUSED ? 2ll * bp.shift * bp.W : 0;
-  if ((T + CT + reach) * static_cast<long long>(bp.C) * 4 >= (1ll << 31)) return 1;
+  if ((CT + reach) * static_cast<long long>(bp.C) * 4 >= (1ll << 31)) return BIWKV_ERR_UNSUPPORTED;
   const int64_t n_tiles = (bp.C + TILE - 1) / TILE;
   const int64_t n_chunks = (T + CT - 1) / CT;
   const int64_t total = B * n_tiles * n_chunks;
@@ -274,27 +237,37 @@ int launch_row(const BiwkvParams& bp, int64_t B, int dev, void* stream) {
   rp.n_tiles = static_cast<int>(n_tiles);
   rp.n_chunks = static_cast<int>(n_chunks);
   rp.total = static_cast<unsigned>(total);
-  if (n_chunks > 1) {
-    // The chunks of a row wait for each other: they must all fit on the device at once.
-    const void* kfn = reinterpret_cast<const void*>(&biwkv_row_kernel<DT, TILE, L, NT, FUSED, PAIR, CAUSAL, GATED>);
+  rp.spin_limit = g_spin_limit.load();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid(static_cast<unsigned>(total)), block(NT);
+  if (n_chunks == 1) {
+    hipLaunchKernelGGL((biwkv_row_kernel<DT, TILE, L, NT, FUSED, PAIR, CAUSAL, GATED, kSinglePass>), grid, block,
+                       0, st, rp);
+  } else {
+    const void* kfn =
+        reinterpret_cast<const void*>(&biwkv_row_kernel<DT, TILE, L, NT, FUSED, PAIR, CAUSAL, GATED, kSinglePass>);
     std::lock_guard<std::mutex> lock(g_mu);
     int cap = 0;
     int rc = resident_capacity(dev, kfn, NT, &cap);
     if (rc) return rc;
-    if (n_chunks > cap) return 1;
-    rp.ordered = total > cap ? 1 : 0;
+    const bool two = g_two_pass.load() != 0 || total > cap;
     StreamScratch* sc = nullptr;
-    rc = get_scratch(dev, stream, total * 2 * TILE * 2, &sc);
+    // single pass: two tagged 64-bit words per (chunk, direction, channel); two passes: one
+    // (l, mu) float pair
+    rc = get_scratch(dev, stream, total * 2 * TILE * (two ? 1 : 2), &sc);
     if (rc) return rc;
-    rp.ctr = sc->ctr;
-    rp.slots = sc->slots;
-    hipLaunchKernelGGL((biwkv_row_kernel<DT, TILE, L, NT, FUSED, PAIR, CAUSAL, GATED>),
-                       dim3(static_cast<unsigned>(total)), dim3(NT), 0,
-                       static_cast<hipStream_t>(stream), rp);
-  } else {
-    hipLaunchKernelGGL((biwkv_row_kernel<DT, TILE, L, NT, FUSED, PAIR, CAUSAL, GATED>),
-                       dim3(static_cast<unsigned>(total)), dim3(NT), 0,
-                       static_cast<hipStream_t>(stream), rp);
+    if (!two) {
+      rp.ctr = sc->ctr;
+      rp.slots = sc->slots;
+      hipLaunchKernelGGL((biwkv_row_kernel<DT, TILE, L, NT, FUSED, PAIR, CAUSAL, GATED, kSinglePass>), grid,
+                         block, 0, st, rp);
+    } else {
+      rp.sums = reinterpret_cast<float2*>(sc->slots);
+      hipLaunchKernelGGL((biwkv_row_kernel<DT, TILE, L, NT, FUSED, PAIR, CAUSAL, false, kSumsPass>), grid, block,
+                         0, st, rp);
+      hipLaunchKernelGGL((biwkv_row_kernel<DT, TILE, L, NT, FUSED, PAIR, CAUSAL, GATED, kOutPass>), grid, block,
+                         0, st, rp);
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e);
@@ -338,15 +311,9 @@ int try_row(const BiwkvParams& bp, int64_t B, int dev, void* stream) {
 }
 
 template <bool FUSED>
-int dispatch_biwkv(BiwkvParams prm, int64_t B, int dtype, bool vec2, int dev, void* stream) {
-  const int rrc = dtype == BIWKV_F32 ? try_row<BIWKV_F32, FUSED>(prm, B, dev, stream)
-                                     : try_row<BIWKV_BF16, FUSED>(prm, B, dev, stream);
-  if (rrc != 1) return rrc;
-  if (dtype == BIWKV_F32)
-    return vec2 ? launch_biwkv<BIWKV_F32, 2, FUSED>(prm, B, dev, stream)
-                : launch_biwkv<BIWKV_F32, 1, FUSED>(prm, B, dev, stream);
-  return vec2 ? launch_biwkv<BIWKV_BF16, 2, FUSED>(prm, B, dev, stream)
-              : launch_biwkv<BIWKV_BF16, 1, FUSED>(prm, B, dev, stream);
+int dispatch_biwkv(const BiwkvParams& prm, int64_t B, int dtype, int dev, void* stream) {
+  return dtype == BIWKV_F32 ? try_row<BIWKV_F32, FUSED>(prm, B, dev, stream)
+                            : try_row<BIWKV_BF16, FUSED>(prm, B, dev, stream);
 }
 
 int validate_biwkv(const void* k, const void* v, const float* w, const float* u, const float* out,
@@ -392,7 +359,7 @@ int launch_qshift(const float* x, float* out, int64_t B, int64_t H, int64_t W, i
   // index divisors of the launch (channel groups per row, tokens per image, columns)
   const FastDiv cv = make_fastdiv(static_cast<uint32_t>(vec4 ? C / 4 : C));
   const FastDiv hw = make_fastdiv(static_cast<uint32_t>(H * W)), wd = make_fastdiv(static_cast<uint32_t>(W));
-  const bool big = items >= (1ll << 31);
+  const bool big = items >= (1ll << 31) || g_wide_index.load() != 0;
   const dim3 grid(static_cast<unsigned>(blocks)), block(256);
   const int Hi = static_cast<int>(H), Wi = static_cast<int>(W), Ci = static_cast<int>(C);
   const int g0 = static_cast<int>(g[0]), g1 = static_cast<int>(g[1]), g2 = static_cast<int>(g[2]),
@@ -424,10 +391,6 @@ int fused_forward(const void* k, const void* v, const float* w, const float* u, 
   if (rc) return rc;
   int64_t g[4];
   group_bounds(C, gamma, g);
-  const size_t es = dtype == BIWKV_F32 ? 4 : 2;
-  const bool groups_even = (g[0] % 2 == 0) && (g[1] % 2 == 0) && (g[2] % 2 == 0) && (g[3] % 2 == 0);
-  const bool vec2 = (C % 2 == 0) && groups_even && aligned(k, 2 * es) && aligned(v, 2 * es) &&
-                    aligned(out, 8);
   BiwkvParams prm{};
   prm.k = k;
   prm.v = v;
@@ -444,11 +407,7 @@ int fused_forward(const void* k, const void* v, const float* w, const float* u, 
   prm.g3 = static_cast<int>(g[2]);
   prm.g4 = static_cast<int>(g[3]);
   prm.bidir = bidir;
-  if (!bidir) return dispatch_biwkv<true>(prm, B, dtype, vec2, dev, stream);
-  // the sequence shift exists in the tile kernel only: a shape it does not address has no fallback
-  rc = dtype == BIWKV_F32 ? try_row<BIWKV_F32, true>(prm, B, dev, stream)
-                          : try_row<BIWKV_BF16, true>(prm, B, dev, stream);
-  return rc == 1 ? BIWKV_ERR_UNSUPPORTED : rc;
+  return dispatch_biwkv<true>(prm, B, dtype, dev, stream);
 }
 
 // Backward tile shape: 8 tokens per lane, 512 threads (two workgroups per CU, so one's loads
@@ -471,22 +430,22 @@ int launch_bwd_tile(const void* k, const void* v, const float* w, const float* u
   if ((T + CT) * C * 4 >= (1ll << 31)) return BIWKV_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
   BwdTileParams tp{};
-  {
-    std::lock_guard<std::mutex> lock(g_mu);
-    StreamScratch* sc = nullptr;
-    int rc = get_scratch(dev, stream, 0, &sc);
-    if (rc) return rc;
-    const long long terms = B * n_chunks * C;                         // dw, du terms
-    const long long sums = n_chunks > 1 ? total * 2 * kBtTile * 3 : 0;  // chunk sums per round
-    rc = grow_zeroed(&sc->bwd, &sc->bwd_floats, 2 * terms + 4 * sums, 1ll << 20, st, &sc->retired);
-    if (rc) return rc;
-    tp.pw = sc->bwd;
-    tp.pu = sc->bwd + terms;
-    tp.sums1 = sc->bwd + 2 * terms;
-    tp.sums2 = tp.sums1 + sums;
-    tp.carry1 = tp.sums2 + sums;
-    tp.carry2 = tp.carry1 + sums;
-  }
+  // The launches of one call share the stream's scratch: the lock is held until the last one is
+  // queued, so calls from several host threads on one stream cannot interleave their stages.
+  std::lock_guard<std::mutex> lock(g_mu);
+  StreamScratch* sc = nullptr;
+  int rc = get_scratch(dev, stream, 0, &sc);
+  if (rc) return rc;
+  const long long terms = B * n_chunks * C;                         // dw, du terms
+  const long long sums = n_chunks > 1 ? total * 2 * kBtTile * 3 : 0;  // chunk sums per round
+  rc = grow_zeroed(&sc->bwd, &sc->bwd_floats, 2 * terms + 4 * sums, 1ll << 20, st);
+  if (rc) return rc;
+  tp.pw = sc->bwd;
+  tp.pu = sc->bwd + terms;
+  tp.sums1 = sc->bwd + 2 * terms;
+  tp.sums2 = tp.sums1 + sums;
+  tp.carry1 = tp.sums2 + sums;
+  tp.carry2 = tp.carry1 + sums;
   tp.k = k;
   tp.v = v;
   tp.w = w;
@@ -545,8 +504,6 @@ int biwkv_forward(const void* k, const void* v, const float* w, const float* u, 
   int dev = 0;
   rc = current_device(&dev);
   if (rc) return rc;
-  const size_t es = dtype == BIWKV_F32 ? 4 : 2;
-  const bool vec2 = (C % 2 == 0) && aligned(k, 2 * es) && aligned(v, 2 * es) && aligned(out, 8);
   BiwkvParams prm{};
   prm.k = k;
   prm.v = v;
@@ -555,7 +512,7 @@ int biwkv_forward(const void* k, const void* v, const float* w, const float* u, 
   prm.out = out;
   prm.T = T;
   prm.C = static_cast<int>(C);
-  return dispatch_biwkv<false>(prm, B, dtype, vec2, dev, stream);
+  return dispatch_biwkv<false>(prm, B, dtype, dev, stream);
 }
 
 int biwkv_gated_forward(const void* k, const void* v, const void* r, const float* w, const float* u,
@@ -579,10 +536,8 @@ int biwkv_gated_forward(const void* k, const void* v, const void* r, const float
   prm.out = out;
   prm.T = T;
   prm.C = static_cast<int>(C);
-  // tile kernel only: a shape it does not address has no fallback
-  rc = dtype == BIWKV_F32 ? try_row<BIWKV_F32, false, false, true>(prm, B, dev, stream)
-                          : try_row<BIWKV_BF16, false, false, true>(prm, B, dev, stream);
-  return rc == 1 ? BIWKV_ERR_UNSUPPORTED : rc;
+  return dtype == BIWKV_F32 ? try_row<BIWKV_F32, false, false, true>(prm, B, dev, stream)
+                            : try_row<BIWKV_BF16, false, false, true>(prm, B, dev, stream);
 }
 
 int biwkv_backward(const void* k, const void* v, const float* w, const float* u, const float* g,
@@ -649,10 +604,8 @@ int biwkv_causal_forward(const void* k, const void* v, const float* w, const flo
   prm.out = out;
   prm.T = T;
   prm.C = static_cast<int>(C);
-  // tile kernel only: a shape it does not address has no fallback
-  rc = dtype == BIWKV_F32 ? try_row<BIWKV_F32, false, true>(prm, B, dev, stream)
-                          : try_row<BIWKV_BF16, false, true>(prm, B, dev, stream);
-  return rc == 1 ? BIWKV_ERR_UNSUPPORTED : rc;
+  return dtype == BIWKV_F32 ? try_row<BIWKV_F32, false, true>(prm, B, dev, stream)
+                            : try_row<BIWKV_BF16, false, true>(prm, B, dev, stream);
 }
 
 int biwkv_qshift_forward(const void* k, const void* v, const float* w, const float* u, float* out,
@@ -706,7 +659,7 @@ int qshift_mix(const float* x, const float* mu, float* out, int64_t B, int64_t H
   hipStream_t st = static_cast<hipStream_t>(stream);
   const FastDiv cv = make_fastdiv(static_cast<uint32_t>(vec4 ? C / 4 : C));
   const FastDiv hw = make_fastdiv(static_cast<uint32_t>(H * W)), wd = make_fastdiv(static_cast<uint32_t>(W));
-  const bool big = items >= (1ll << 31);
+  const bool big = items >= (1ll << 31) || g_wide_index.load() != 0;
   const dim3 grid(static_cast<unsigned>(blocks)), block(256);
   const int Hi = static_cast<int>(H), Wi = static_cast<int>(W), Ci = static_cast<int>(C);
   const int g0 = static_cast<int>(g[0]), g1 = static_cast<int>(g[1]), g2 = static_cast<int>(g[2]),
@@ -757,12 +710,12 @@ const char* biwkv_status_string(int status) {
     case BIWKV_ERR_NULL: return "a required pointer is NULL";
     case BIWKV_ERR_SHAPE: return "invalid shape (negative, too large, or T != H*W)";
     case BIWKV_ERR_DTYPE: return "unknown dtype (expected BIWKV_F32 or BIWKV_BF16)";
-    case BIWKV_ERR_PARAM: return "invalid shift parameter (gamma outside [0, 1/4], or shift < 0 or beyond the grid (min(H, W)) or the sequence (N))";
+    case BIWKV_ERR_PARAM: return "invalid parameter (gamma outside [0, 1/4], shift < 0 or beyond the grid (min(H, W)) or the sequence (N), or an unknown option or option value)";
     case BIWKV_ERR_ALIAS: return "output overlaps an input";
     case BIWKV_ERR_ALIGN: return "pointer not aligned to its element size";
     case BIWKV_ERR_NO_DEVICE: return "no usable HIP device";
     case BIWKV_ERR_HIP: return "HIP runtime error (see biwkv_last_hip_error)";
-    case BIWKV_ERR_UNSUPPORTED: return "sequence needs more chunks than can be resident at once";
+    case BIWKV_ERR_UNSUPPORTED: return "shape outside what the kernels address (see the entry point's limits)";
     default: return "unknown status";
   }
 }
@@ -786,11 +739,8 @@ int biwkv_stream_fault_flags(void* stream, uint32_t* flags) {
   if (e != hipSuccess) return hip_fail(e);
   *flags = c.fault;
   if (c.fault) {
-    // Clear the fault word, and the ticket and arrival counts that an interrupted launch may
-    // have left behind (the stream is idle here); the epoch keeps counting.
+    // Clear the fault word (the stream is idle here); the epoch keeps counting.
     Counters fresh = c;
-    fresh.ticket = 0;
-    fresh.done = 0;
     fresh.fault = 0;
     e = hipMemcpy(it->second->ctr, &fresh, sizeof(Counters), hipMemcpyHostToDevice);
     if (e != hipSuccess) return hip_fail(e);
@@ -798,6 +748,49 @@ int biwkv_stream_fault_flags(void* stream, uint32_t* flags) {
   return BIWKV_OK;
 }
 
-int biwkv_version(void) { return 100; }
+int biwkv_release_scratch(void* stream) {
+  int dev = 0;
+  int rc = current_device(&dev);
+  if (rc) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lock(g_mu);
+  auto it = g_scratch.find(std::make_pair(dev, stream));
+  if (it == g_scratch.end()) return BIWKV_OK;
+  StreamScratch* sc = it->second;
+  g_scratch.erase(it);
+  if (!sc) return BIWKV_OK;
+  // stream-ordered frees: they take effect once the launches already queued on the stream are done
+  hipError_t e = hipSuccess;
+  for (void* p : {static_cast<void*>(sc->ctr), static_cast<void*>(sc->slots), static_cast<void*>(sc->bwd)}) {
+    if (!p) continue;
+    const hipError_t ei = hipFreeAsync(p, st);
+    if (e == hipSuccess) e = ei;
+  }
+  delete sc;
+  return e == hipSuccess ? BIWKV_OK : hip_fail(e);
+}
+
+int biwkv_set_option(int option, int64_t value, int64_t* previous) {
+  switch (option) {
+    case BIWKV_OPT_SPIN_LIMIT: {
+      if (value < 0 || value > 0xffffffffll) return BIWKV_ERR_PARAM;
+      const unsigned old = g_spin_limit.exchange(static_cast<unsigned>(value));
+      if (previous) *previous = old;
+      return BIWKV_OK;
+    }
+    case BIWKV_OPT_TWO_PASS:
+    case BIWKV_OPT_WIDE_INDEX: {
+      if (value != 0 && value != 1) return BIWKV_ERR_PARAM;
+      std::atomic<int>& opt = option == BIWKV_OPT_TWO_PASS ? g_two_pass : g_wide_index;
+      const int old = opt.exchange(static_cast<int>(value));
+      if (previous) *previous = old;
+      return BIWKV_OK;
+    }
+    default:
+      return BIWKV_ERR_PARAM;
+  }
+}
+
+int biwkv_version(void) { return 20000; }
 
 }  // extern "C"

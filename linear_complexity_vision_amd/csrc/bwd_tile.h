@@ -1,8 +1,8 @@
-// Bi-WKV backward in one launch: the gradients of Eq. (5) (see backward.cuh for the formulas) with
+// Bi-WKV backward in one launch: the gradients of Eq. (5) (see backward.h for the formulas) with
 // the tile kernel's work split.
 #pragma once
 
-#include "row_kernel.cuh"
+#include "row_kernel.h"
 
 namespace {
 

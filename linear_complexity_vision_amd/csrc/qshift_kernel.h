@@ -1,7 +1,7 @@
 // Q-Shift gather kernel and scratch initialisation kernels.
 #pragma once
 
-#include "common.cuh"
+#include "common.h"
 
 namespace {
 
@@ -194,10 +194,10 @@ __global__ void fill_u64_kernel(unsigned long long* p, long long n) {
 }
 
 __global__ void init_counters_kernel(Counters* c) {
-  c->ticket = 0u;
   c->done = 0u;
   c->epoch = 1u;
   c->fault = 0u;
+  c->pad = 0u;
 }
 
 }  // namespace

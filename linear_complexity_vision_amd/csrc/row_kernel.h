@@ -4,7 +4,7 @@
 
 #include <type_traits>
 
-#include "common.cuh"
+#include "common.h"
 
 namespace {
 
@@ -17,20 +17,25 @@ namespace {
 // Lane (c, g) holds channel c of the tile and token group g (L consecutive tokens) in registers
 // from load to store. The GROUPS = NT / TILE group sums of a channel are combined by scans on
 // lane shuffles: the sums go through LDS into a transposed layout in which one channel's groups
-// are consecutive lanes of one wavefront. When a row has several chunks, each workgroup
-// publishes its chunk's forward and backward sums (epoch-tagged slots, see slot_store) and folds
-// the sums of the other chunks of its row, in a fixed order, into its carries. When the whole
-// grid fits on the device the chunks follow the grid order; otherwise workgroups take tickets in
-// launch order and the chunks of a row hold consecutive tickets, so a workgroup only waits for
-// workgroups that have started or will start once earlier rows finish. Each lane then sweeps its
-// tokens in sub-blocks of 8: forward states (a, c) left to right, keeping (alpha, beta) = (a - c
-// v, c + e^{u+k}) per token in LDS, then backward states (b, d) right to left, writing Eq. (7).
+// are consecutive lanes of one wavefront. A row of several chunks is combined in one of two ways:
+//
+//  * single pass (every workgroup of the launch fits on the device at once): each workgroup
+//    publishes its chunk's forward and backward sums (epoch-tagged slots, see slot_store) and
+//    folds the sums of the other chunks of its row, in a fixed order, into its carries. Every
+//    wait is bounded; a workgroup that does not see a peer's sums in time recomputes them from
+//    that chunk's k and v in HBM (the sums are plain decayed sums of Eq. (6)), so the result
+//    never depends on the peers being resident.
+//  * two passes: a sums launch writes every chunk's totals, and an output launch folds them into
+//    its carries; nothing waits.
+//
+// Each lane then sweeps its tokens in sub-blocks of 8: forward states (a, c) left to right, then
+// backward states (b, d) right to left, writing Eq. (7).
 //
 // Every lane holds exactly L token slots. Slots past the end of the row hold k = -inf, i.e. a
 // weight of exactly 0, so the sweeps need no per-token bounds: a lane's forward sum is anchored
 // at its last slot, and such slots are only ever followed by more empty slots. Loads and stores
-// go through range-checked buffer resources over one batch item, so slots past the row read 0
-// and their stores are dropped by the hardware.
+// go through range-checked buffer resources that start at the chunk, so slots past the row read 0
+// and their stores are dropped by the hardware, and the 32-bit offsets only span one chunk.
 
 // Per-lane token storage: bf16 k and v packed in one 32-bit register per token (k in the low
 // half, v in the high half); fp32 k and v in two registers. fence() makes the stored words
@@ -135,6 +140,13 @@ constexpr int kStream = 2;
 // out below 2^31 bytes), and adding up to 2^31 - 1 more does not wrap.
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
+// How a launch combines the chunks of a row (one chunk per row needs neither).
+enum : int {
+  kSinglePass = 0,  // slot exchange between resident workgroups, recompute on a timed-out wait
+  kSumsPass = 1,    // two passes, first: write every chunk's totals to RowParams::sums
+  kOutPass = 2,     // two passes, second: carries from the totals, then the outputs
+};
+
 struct RowParams {
   const void* k;
   const void* v;
@@ -147,20 +159,21 @@ struct RowParams {
   int n_tiles;   // channel tiles per batch item
   int n_chunks;  // workgroups per row
   unsigned total;                // workgroups of the launch
-  int ordered;                   // 1: workgroups take tickets (more than fit on the device)
-  Counters* ctr;                 // ticket / epoch block (n_chunks > 1)
-  unsigned long long* slots;     // [row][chunk][dir][TILE] (l, mu) slot pairs (n_chunks > 1)
+  unsigned spin_limit;           // single pass: polls of a peer's slot before recomputing its sums
+                                 // (0: recompute every peer without polling)
+  Counters* ctr;                 // single pass: epoch block (n_chunks > 1)
+  unsigned long long* slots;     // single pass: [row][chunk][dir][TILE] (l, mu) tagged slot pairs
+  float2* sums;                  // two passes: [row][chunk][dir][TILE] (l, mu) chunk totals
   int H, W, shift, g1, g2, g3, g4;  // Q-Shift (fused entry only)
   int bidir;  // fused: the bidirectional shift along a sparse token sequence (the host sets W = 1)
 };
 
-// Counts a workgroup out of a chunked launch once none of its wavefronts reads the epoch or a slot
-// again; the last one resets the counters for the next launch on the stream. Nothing else waits
-// for it, so only the calling wavefront sees the round trip.
+// Counts a workgroup out of a single-pass launch once none of its wavefronts reads the epoch or a
+// slot again; the last one resets the count and moves the epoch on for the next launch on the
+// stream. Nothing else waits for it, so only the calling wavefront sees the round trip.
 __device__ __forceinline__ void row_retire(const RowParams& p) {
   const unsigned fin = __hip_atomic_fetch_add(&p.ctr->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (fin + 1u == p.total) {
-    __hip_atomic_store(&p.ctr->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(&p.ctr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_fetch_add(&p.ctr->epoch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -212,36 +225,46 @@ __device__ __forceinline__ RowLane row_lane(const RowParams& p, unsigned unit) {
 }
 
 // Loads word m of the lane's k and v (one token, or a channel pair at one token) at byte offset off
-// of the resources km and vm.
-template <int DT, bool PAIR, class Store>
+// of the resources km and vm, with cache policy POL.
+template <int DT, bool PAIR, int POL, class Store>
 __device__ __forceinline__ void row_load_word(Store& kv, int m, __amdgpu_buffer_rsrc_t km,
                                               __amdgpu_buffer_rsrc_t vm, uint32_t off) {
   if constexpr (PAIR) {
-    kv.kk[m] = __builtin_amdgcn_raw_buffer_load_b32(km, off, 0, kStream);
-    kv.vv[m] = __builtin_amdgcn_raw_buffer_load_b32(vm, off, 0, kStream);
+    kv.kk[m] = __builtin_amdgcn_raw_buffer_load_b32(km, off, 0, POL);
+    kv.vv[m] = __builtin_amdgcn_raw_buffer_load_b32(vm, off, 0, POL);
   } else if constexpr (DT == BIWKV_F32) {
-    kv.kk[m] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(km, off, 0, kStream));
-    kv.vv[m] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vm, off, 0, kStream));
+    kv.kk[m] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(km, off, 0, POL));
+    kv.vv[m] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vm, off, 0, POL));
   } else {
-    const uint32_t kx = __builtin_amdgcn_raw_buffer_load_b16(km, off, 0, kStream);
-    const uint32_t vx = __builtin_amdgcn_raw_buffer_load_b16(vm, off, 0, kStream);
+    const uint32_t kx = __builtin_amdgcn_raw_buffer_load_b16(km, off, 0, POL);
+    const uint32_t vx = __builtin_amdgcn_raw_buffer_load_b16(vm, off, 0, POL);
     kv.r[m] = kx | (vx << 16);
   }
 }
 
+// Bytes of a resource that starts `start` bytes into an array of `size` bytes: what is left of the
+// array, clamped to what a 32-bit range check can express (an offset inside one chunk never
+// reaches the clamp, so the check still drops exactly the accesses past the array).
+__device__ __forceinline__ uint32_t row_span(long long size, long long start) {
+  const long long left = size - start;
+  return static_cast<uint32_t>(left <= 0 ? 0 : (left < 0x7fffffffll ? left : 0x7fffffffll));
+}
+
 // Issues every load of the lane's k and v (Q-Shift applied when FUSED: padded sources read 0) and
 // marks the slots past the row empty. Nothing waits here: phase A consumes the words in load
-// order as they arrive.
-template <int DT, int TILE, int L, int NT, bool FUSED, bool PAIR, class Store>
+// order as they arrive. Every resource starts at (or, fused, s W tokens before) the chunk, so the
+// 32-bit offsets span one chunk whatever the size of a batch item.
+template <int DT, int TILE, int L, int NT, bool FUSED, bool PAIR, int POL, class Store>
 __device__ __forceinline__ void row_load(const RowParams& p, const RowLane& ln, Store& kv) {
   const long long T = p.T;
   const int C = p.C;
   const long long plane = T * C;  // elements of one batch item
   constexpr int ES = DT == BIWKV_F32 ? 4 : 2;
+  const long long item = plane * ES;  // bytes of one batch item
   const char* kb = reinterpret_cast<const char*>(
-      uniform_u64(reinterpret_cast<unsigned long long>(p.k) + ln.b * plane * ES));
+      uniform_u64(reinterpret_cast<unsigned long long>(p.k) + ln.b * item));
   const char* vb = reinterpret_cast<const char*>(
-      uniform_u64(reinterpret_cast<unsigned long long>(p.v) + ln.b * plane * ES));
+      uniform_u64(reinterpret_cast<unsigned long long>(p.v) + ln.b * item));
   const uint32_t row_bytes = static_cast<uint32_t>(C) * ES;
   // PAIR: lane 2j + odd reads channels (2j, 2j + 1) at tokens 2m + odd
   constexpr int STEP = PAIR ? 2 : 1;
@@ -253,19 +276,17 @@ __device__ __forceinline__ void row_load(const RowParams& p, const RowLane& ln, 
     // The token offset of word m is uniform, so it moves the resource base (scalar work) and the
     // lane keeps one vector offset. Tokens past the row fall past the shortened resource and
     // read 0, and so does every slot of a masked lane.
-    // byte counts below 2^31 (the host checks (T + CT) * C * 4), so 32-bit scalar arithmetic
-    const int c0 = ln.chunk * CT * static_cast<int>(row_bytes);  // chunk start
-    const int avail = static_cast<int>(plane * ES) - c0;       // bytes from there to the end
+    const long long c0 = static_cast<long long>(ln.chunk) * CT * row_bytes;  // chunk start
+    // offsets below 2^31 (the host checks CT * C * 4)
     const uint32_t lane_off =
         ln.on ? static_cast<uint32_t>(ln.g * L + odd) * row_bytes + lane_byte : kOutOfRange;
 #pragma unroll
     for (int m = 0; m < NW; ++m) {
-      const int adv = m * STEP * static_cast<int>(row_bytes);
-      const int left = avail - adv;
-      const uint32_t n = static_cast<uint32_t>(left > 0 ? left : 0);
-      const __amdgpu_buffer_rsrc_t km = make_rsrc(kb + c0 + adv, n);
-      const __amdgpu_buffer_rsrc_t vm = make_rsrc(vb + c0 + adv, n);
-      row_load_word<DT, PAIR>(kv, m, km, vm, lane_off);
+      const long long adv = c0 + static_cast<long long>(m * STEP) * row_bytes;
+      const uint32_t n = row_span(item, adv);
+      const __amdgpu_buffer_rsrc_t km = make_rsrc(kb + adv, n);
+      const __amdgpu_buffer_rsrc_t vm = make_rsrc(vb + adv, n);
+      row_load_word<DT, PAIR, POL>(kv, m, km, vm, lane_off);
     }
   } else {
     // Q-Shift: the lane reads its own channel at token t + delta, where delta is fixed by the
@@ -296,7 +317,7 @@ __device__ __forceinline__ void row_load(const RowParams& p, const RowLane& ln, 
     } else if (ln.ch < p.g4) {
       delta = SH;
     }
-    const int t0 = ln.chunk * CT + ln.g * L + odd;  // token of word 0 (T < 2^31 / (4 C))
+    const int t0 = ln.chunk * CT + ln.g * L + odd;  // token of word 0 (T < 2^31)
     // bit m: word m (token t0 + STEP m) reads a source inside the grid
     using Mask = std::conditional_t<(NW > 32), unsigned long long, uint32_t>;
     constexpr int MB = 8 * sizeof(Mask);
@@ -317,22 +338,20 @@ __device__ __forceinline__ void row_load(const RowParams& p, const RowLane& ln, 
       }
     }
     if (down) clear(t0, SH);
+    // offsets below 2^31 (the host checks (CT + 2 s W) * C * 4)
     const uint32_t lane_off = static_cast<uint32_t>(ln.g * L + odd + delta + SH) * row_bytes + lane_byte;
-    // byte counts below 2^31 (the host checks (T + CT + 2 s W) * C * 4), so 32-bit arithmetic
-    const int c0 = (ln.chunk * CT - SH) * static_cast<int>(row_bytes);  // may be negative
-    const int avail = static_cast<int>(plane * ES) - c0;
+    const long long c0 = (static_cast<long long>(ln.chunk) * CT - SH) * row_bytes;  // may be negative
 #pragma unroll
     for (int m = 0; m < NW; ++m) {
-      const int adv = m * STEP * static_cast<int>(row_bytes);
-      const int left = avail - adv;
-      const uint32_t n = static_cast<uint32_t>(left > 0 ? left : 0);
-      const __amdgpu_buffer_rsrc_t km = make_rsrc(kb + c0 + adv, n);
-      const __amdgpu_buffer_rsrc_t vm = make_rsrc(vb + c0 + adv, n);
+      const long long adv = c0 + static_cast<long long>(m * STEP) * row_bytes;
+      const uint32_t n = row_span(item, adv);
+      const __amdgpu_buffer_rsrc_t km = make_rsrc(kb + adv, n);
+      const __amdgpu_buffer_rsrc_t vm = make_rsrc(vb + adv, n);
       // all ones when word m is valid (bit m of the mask, sign-extended)
       const uint32_t keep =
           static_cast<uint32_t>(static_cast<std::make_signed_t<Mask>>(valid << (MB - 1 - m)) >> (MB - 1));
       const uint32_t off = (lane_off & keep) | (kOutOfRange & ~keep);
-      row_load_word<DT, PAIR>(kv, m, km, vm, off);
+      row_load_word<DT, PAIR, POL>(kv, m, km, vm, off);
     }
   }
   // all loads in flight before anything consumes them
@@ -425,33 +444,103 @@ __device__ __forceinline__ void group_fold(Agg& a, Agg& b, int tg) {
   }
 }
 
+// One token of channel ch of batch item b as the chunk's sums see it (Q-Shift applied when FUSED;
+// a zero-filled source is k = 0, v = 0), by plain loads. Used only to recompute a peer chunk's sums.
+template <int DT, bool FUSED>
+__device__ __forceinline__ void row_token(const RowParams& p, long long b, int ch, long long t, float& kf,
+                                          float& vf) {
+  long long src = t;
+  bool ok = true;
+  if constexpr (FUSED) {
+    const long long s = p.shift, W = p.W;
+    if (p.bidir) {
+      if (ch < p.g4) {
+        const bool back = ch < p.g1 || (ch >= p.g2 && ch < p.g3);
+        src = back ? t - s : t + s;
+        ok = src >= 0 && src < p.T;
+      }
+    } else {
+      const long long col = t % W;
+      if (ch < p.g1) {
+        ok = col >= s;
+        src = t - s;
+      } else if (ch < p.g2) {
+        ok = col < W - s;
+        src = t + s;
+      } else if (ch < p.g3) {
+        ok = t >= s * W;
+        src = t - s * W;
+      } else if (ch < p.g4) {
+        ok = t < static_cast<long long>(p.H - s) * W;
+        src = t + s * W;
+      }
+    }
+  }
+  if (!ok) {
+    kf = 0.f;
+    vf = 0.f;
+    return;
+  }
+  const long long idx = (b * p.T + src) * p.C + ch;
+  if constexpr (DT == BIWKV_F32) {
+    kf = static_cast<const float*>(p.k)[idx];
+    vf = static_cast<const float*>(p.v)[idx];
+  } else {
+    kf = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p.k)[idx]) << 16);
+    vf = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p.v)[idx]) << 16);
+  }
+}
+
+// The sums of chunk ck of batch item b, channel ch, recomputed from k and v: forward anchored at
+// the chunk's last slot, or backward anchored at its first token. This is what the chunk
+// publishes, so a workgroup whose wait for a peer runs out takes it from here instead; a masked
+// channel gives the empty sum. Each token's exponent is formed from its distance to the anchor
+// (k log2 e - n D, one product), never by stepping a running exponent, and the terms are summed
+// against their running maximum, so any w, u and k stay finite and accurate.
+template <int DT, int CT, bool FUSED>
+__device__ __noinline__ Agg row_recompute(const RowParams* args, long long b, int ch, int ck, bool fwd, float D) {
+  const RowParams& p = *args;
+  if (ch >= p.C) return row_empty();
+  const long long s = static_cast<long long>(ck) * CT;
+  const long long e = s + CT < p.T ? s + CT : p.T;  // exclusive
+  const long long anchor = fwd ? s + CT - 1 : s;
+  Agg a = agg_empty();
+#pragma unroll 8
+  for (long long t = s; t < e; ++t) {
+    float kf, vf;
+    row_token<DT, FUSED>(p, b, ch, t, kf, vf);
+    const float n = static_cast<float>(fwd ? anchor - t : t - anchor);
+    a = agg_add(a, Agg{fmaf(-n, D, kf * kLog2e), vf, 1.f});
+  }
+  a.m = fmaxf(a.m, kEmptyM);
+  return a;
+}
+
 // Gate inputs r of Eq. (2) for the SB tokens of a lane's sub-block q (raw bits: an fp32 value, or
 // a bf16 value in the low half), through per-token resources like the unfused k, v loads.
 template <int DT, int TILE, int L, int NT, int SB>
 struct RowGate {
-  const char* base;   // the batch item's r
-  int c0, avail;      // chunk start (bytes) and bytes from there to the item's end
+  const char* base;   // the chunk's first token of r in the lane's batch item
+  long long left;     // bytes from there to the end of the batch item
   uint32_t lane_off;  // this lane's offset from the chunk start (out of range when masked)
   int row_bytes;
   __device__ __forceinline__ void init(const RowParams& p, const RowLane& ln) {
     constexpr int ES = DT == BIWKV_F32 ? 4 : 2;
     constexpr int CT = (NT / TILE) * L;
-    const long long plane = p.T * p.C;
-    base = reinterpret_cast<const char*>(
-        uniform_u64(reinterpret_cast<unsigned long long>(p.r) + ln.b * plane * ES));
+    const long long item = p.T * p.C * ES;
     row_bytes = p.C * ES;
-    c0 = ln.chunk * CT * row_bytes;
-    avail = static_cast<int>(plane * ES) - c0;
+    const long long c0 = static_cast<long long>(ln.chunk) * CT * row_bytes;
+    base = reinterpret_cast<const char*>(
+        uniform_u64(reinterpret_cast<unsigned long long>(p.r) + ln.b * item + c0));
+    left = item - c0;
     lane_off = ln.on ? static_cast<uint32_t>(ln.g * L) * row_bytes + static_cast<uint32_t>(ln.ch) * ES
                      : kOutOfRange;
   }
   __device__ __forceinline__ void load(int q, uint32_t (&dst)[SB]) const {
 #pragma unroll
     for (int i = 0; i < SB; ++i) {
-      const int adv = (q * SB + i) * row_bytes;
-      const int left = avail - adv;
-      const __amdgpu_buffer_rsrc_t rr =
-          make_rsrc(base + c0 + adv, static_cast<uint32_t>(left > 0 ? left : 0));
+      const long long adv = static_cast<long long>(q * SB + i) * row_bytes;
+      const __amdgpu_buffer_rsrc_t rr = make_rsrc(base + adv, row_span(left, adv));
       if constexpr (DT == BIWKV_F32)
         dst[i] = __builtin_amdgcn_raw_buffer_load_b32(rr, lane_off, 0, kStream);
       else
@@ -467,11 +556,15 @@ template <int DT, int TILE, int L, bool PAIR>
 using RowStore = std::conditional_t<PAIR, RowKVPair<L>, RowKV<DT, L>>;
 
 // CAUSAL: the causal attention (Eq. (7) without the backward states b, d): only forward sums
-// are formed, scanned and exchanged, and the output comes out of the forward sweep.
-template <int DT, int TILE, int L, int NT, bool FUSED, bool PAIR, bool WIDE, bool CAUSAL, bool GATED>
-__device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
+// are formed, scanned and exchanged, and the output comes out of the forward sweep. MODE: how the
+// chunks of a row are combined (kSinglePass, kSumsPass, kOutPass). Returns false only in the fast
+// form of a single pass whose wait for a peer ran out: nothing is stored then, and the caller
+// runs the chunk again through the wide form, which recomputes the missing sums (its own slot is
+// already published: `published`).
+template <int DT, int TILE, int L, int NT, bool FUSED, bool PAIR, bool WIDE, bool CAUSAL, bool GATED, int MODE>
+__device__ __forceinline__ bool row_body(const RowParams& p, const RowParams* args, const RowLane& ln,
                                          RowStore<DT, TILE, L, PAIR>& kv, float* lds,
-                                         const unsigned* sh_epoch) {
+                                         const unsigned* sh_epoch, bool published) {
   constexpr int GROUPS = NT / TILE;
   constexpr int CT = GROUPS * L;  // tokens per chunk
   constexpr int SB = 8;  // tokens per sub-block of the sweeps
@@ -585,7 +678,7 @@ __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
   // GATED: the gate inputs of sub-block 0 load during the scan and the exchange
   RowGate<DT, TILE, L, NT, SB> gate;
   uint32_t r_next[GATED ? SB : 1];
-  if constexpr (GATED) {
+  if constexpr (GATED && MODE != kSumsPass) {
     gate.init(p, ln);
     gate.load(0, r_next);
   }
@@ -623,31 +716,48 @@ __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
   Agg X = agg_from_below<GROUPS, 1>(f), Y = agg_from_above<GROUPS, 1>(bk);
   if (tg == 0) X = row_empty();
   if (CAUSAL || tg == GROUPS - 1) Y = row_empty();
+  bool timed_out = false;  // fast single pass: a peer's sums did not arrive in time
   if (p.n_chunks > 1) {
-    // ---- exchange with the other chunks of the row ----
+    // ---- the other chunks of the row ----
     const int nch = p.n_chunks, chunk = ln.chunk;
-    const unsigned epoch = __builtin_amdgcn_readfirstlane(*sh_epoch);  // set before the barrier
-    unsigned long long* rs = p.slots + static_cast<size_t>(ln.row) * nch * 2 * TILE * 2;
+    const size_t row_base = static_cast<size_t>(ln.row) * nch * 2 * TILE;
+    if constexpr (MODE == kSumsPass) {
+      // the chunk's totals: forward (inclusive at the last group, anchored at the chunk's last
+      // slot) and backward (inclusive at group 0, anchored at the chunk's first token)
+      if (tg == GROUPS - 1) p.sums[row_base + (chunk * 2 + kFwd) * TILE + tc] = slot_pack(f);
+      if (!CAUSAL && tg == 0) p.sums[row_base + (chunk * 2 + kBwd) * TILE + tc] = slot_pack(bk);
+      return true;
+    }
+    unsigned epoch = 0;
+    unsigned long long* rs = p.slots + row_base * 2;
     auto slot = [&](int ck, int dir) { return rs + (static_cast<size_t>(ck * 2 + dir) * TILE + tc) * 2; };
-    // the chunk's own sums: forward (inclusive at the last group, anchored at the chunk's last
-    // slot) and backward (inclusive at group 0, anchored at the chunk's first token)
-    if (tg == GROUPS - 1) slot_store(slot(chunk, kFwd), f, epoch);
-    if (!CAUSAL && tg == 0) slot_store(slot(chunk, kBwd), bk, epoch);
+    if constexpr (MODE == kSinglePass) {
+      epoch = __builtin_amdgcn_readfirstlane(*sh_epoch);  // set before the first barrier
+      // the chunk's own sums, anchored as the totals above
+      if (!published) {
+        if (tg == GROUPS - 1) slot_store(slot(chunk, kFwd), f, epoch);
+        if (!CAUSAL && tg == 0) slot_store(slot(chunk, kBwd), bk, epoch);
+      }
+    }
     // Entries: forward sums of chunks 0 .. chunk-1, then backward sums of chunks chunk+1 ..
     // nch-1. Lane tg folds entries tg, tg + GROUPS, ... in order; the lanes' partials are then
     // folded in a fixed tree, so the result does not depend on arrival order.
     const int nf = chunk, ne = CAUSAL ? chunk : nch - 1;
     Agg pf = row_empty(), pb = row_empty();
-    bool timed_out = false;
+    bool recomputed = false;
+    // a poll limit of 0 recomputes every peer's sums without polling
+    const bool poll = MODE == kSinglePass && p.spin_limit != 0;
     // A lane issues the loads of up to EB entries before it waits for any of them, so a lane
     // with several entries pays one round trip, not one per entry.
     constexpr int EB = GROUPS >= 8 ? 1 : 8 / GROUPS;
     for (int e0 = tg; e0 < ne; e0 += EB * GROUPS) {
       unsigned long long wv[EB][2];
+      if (poll) {
 #pragma unroll
-      for (int j = 0; j < EB; ++j) {
-        const int e = e0 + j * GROUPS;
-        if (e < ne) slot_load(slot(e < nf ? e : e + 1, e < nf ? kFwd : kBwd), wv[j]);
+        for (int j = 0; j < EB; ++j) {
+          const int e = e0 + j * GROUPS;
+          if (e < ne) slot_load(slot(e < nf ? e : e + 1, e < nf ? kFwd : kBwd), wv[j]);
+        }
       }
 #pragma unroll
       for (int j = 0; j < EB; ++j) {
@@ -658,42 +768,57 @@ __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
         // distance from the entry's anchor to this chunk's carry anchor (chunks before this one
         // are full, so slot positions are token positions)
         const float dist = static_cast<float>(fwd ? (chunk - 1 - ck) : (ck - chunk - 1)) * CT;
-        const unsigned long long* sp = slot(ck, fwd ? kFwd : kBwd);
-        if (GATED) {
-          // one poll at a time: the gated kernel holds its first gate inputs in flight here,
-          // and a second poll's registers cost it spills and waits
-          for (unsigned spins = 0; !slot_ready(wv[j], epoch); ++spins) {
-            if (spins > kSpinLimit) {
-              timed_out = true;
-              break;
+        Agg a;
+        if constexpr (MODE == kOutPass) {
+          a = slot_unpack(p.sums[row_base + (ck * 2 + (fwd ? kFwd : kBwd)) * TILE + tc]);
+        } else {
+          const unsigned long long* sp = slot(ck, fwd ? kFwd : kBwd);
+          bool ready = false;
+          if (poll) {
+            ready = slot_ready(wv[j], epoch);
+            if (!ready && GATED) {
+              // one poll at a time: the gated kernel holds its first gate inputs in flight here,
+              // and a second poll's registers cost it spills and waits
+              for (unsigned spins = 0; spins < p.spin_limit && !ready; ++spins) {
+                __builtin_amdgcn_s_sleep(2);
+                slot_load(sp, wv[j]);
+                ready = slot_ready(wv[j], epoch);
+              }
+            } else if (!ready) {
+              // Two polls in flight, issued a short sleep apart: a slot published just after one
+              // poll was served is seen by the next one instead of a full round trip later.
+              unsigned long long w2[2];
+              slot_load(sp, w2);
+              for (unsigned spins = 0; spins < p.spin_limit; spins += 2) {
+                __builtin_amdgcn_s_sleep(2);
+                slot_load(sp, wv[j]);
+                if (slot_ready(w2, epoch)) {  // the older poll
+                  wv[j][0] = w2[0];
+                  wv[j][1] = w2[1];
+                  ready = true;
+                  break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+                slot_load(sp, w2);
+                if (slot_ready(wv[j], epoch)) {
+                  ready = true;
+                  break;
+                }
+              }
             }
-            __builtin_amdgcn_s_sleep(2);
-            slot_load(sp, wv[j]);
           }
-        } else if (!slot_ready(wv[j], epoch)) {
-          // Two polls in flight, issued a short sleep apart: a slot published just after one
-          // poll was served is seen by the next one instead of a full round trip later.
-          unsigned long long w2[2];
-          slot_load(sp, w2);
-          for (unsigned spins = 0;; spins += 2) {
-            __builtin_amdgcn_s_sleep(2);
-            slot_load(sp, wv[j]);
-            if (slot_ready(w2, epoch)) {  // the older poll
-              wv[j][0] = w2[0];
-              wv[j][1] = w2[1];
-              break;
-            }
-            if (spins > kSpinLimit) {
-              timed_out = true;
-              break;
-            }
-            __builtin_amdgcn_s_sleep(2);
-            slot_load(sp, w2);
-            if (slot_ready(wv[j], epoch)) break;
+          if (ready) {
+            a = slot_value(wv[j]);
+            a.m = fmaxf(a.m, kEmptyM);
+          } else if constexpr (WIDE) {
+            // the peer has not published in time (it may not be resident): its sums from k, v
+            a = row_recompute<DT, CT, FUSED>(args, ln.b, ln.ch - ln.c + tc, ck, fwd, Dt);
+            recomputed = true;
+          } else {
+            timed_out = true;
+            a = row_empty();
           }
         }
-        Agg a = slot_value(wv[j]);
-        a.m = fmaxf(a.m, kEmptyM);
         a = agg_shift(a, dist, Dt);
         if (fwd)
           pf = agg_add_f(pf, a);
@@ -701,8 +826,10 @@ __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
           pb = agg_add_f(pb, a);
       }
     }
-    if (timed_out)
-      __hip_atomic_fetch_or(&p.ctr->fault, kFaultSpin, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if constexpr (MODE == kSinglePass && WIDE) {
+      if (recomputed)
+        __hip_atomic_fetch_or(&p.ctr->fault, kFaultSpin, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     group_fold<GROUPS, !CAUSAL>(pf, pb, tg);
     // pf (from the first lane of the channel) is anchored just before the chunk, pb just after it
     pf = agg_from_first<GROUPS>(pf);
@@ -718,23 +845,29 @@ __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
   xy[3 * RS + ti] = Y.m;
   xy[4 * RS + ti] = Y.F;
   xy[5 * RS + ti] = Y.G;
-  __syncthreads();  // past it, the sum buffer becomes the (alpha, beta) buffer
+  // past this barrier the sum buffer becomes the (alpha, beta) buffer; the fast form of a single
+  // pass gives up there as a workgroup if any wait ran out (the wide form recomputes what is
+  // missing), having stored nothing
+  if constexpr (MODE == kSinglePass && !WIDE) {
+    if (block_any(timed_out)) return false;
+  } else {
+    __syncthreads();
+  }
   X = Agg{xy[0 * RS + wi], xy[1 * RS + wi], xy[2 * RS + wi]};
   Y = Agg{xy[3 * RS + wi], xy[4 * RS + wi], xy[5 * RS + wi]};
   // every wavefront is past its last read of the epoch and of the slots
-  if (p.n_chunks > 1 && tid == 0) row_retire(p);
+  if (MODE == kSinglePass && p.n_chunks > 1 && tid == 0) row_retire(p);
   kv.fence();
 
   // ---- phase C: sweep each sub-block forward, then backward, writing Eq. (7) ----
-  if (ln.n_g <= 0) return;  // no barrier follows
+  if (ln.n_g <= 0) return true;  // no barrier follows
   const long long plane = T * C;
-  const __amdgpu_buffer_rsrc_t orr =
-      make_rsrc(p.out + ln.b * plane, static_cast<uint32_t>(plane * 4));
+  const long long o0 = static_cast<long long>(ln.chunk) * CT * C;  // the chunk's first output
+  const __amdgpu_buffer_rsrc_t orr = make_rsrc(p.out + ln.b * plane + o0, row_span((plane - o0) * 4, 0));
   const uint32_t row_bytes = static_cast<uint32_t>(C) * 4u;
-  // slots past the row (and masked lanes) store out of range
+  // slots past the row (and masked lanes) store out of range; offsets span one chunk
   const uint32_t out0 =
-      ln.on ? static_cast<uint32_t>(ln.s_g) * row_bytes + static_cast<uint32_t>(ln.ch) * 4u
-            : kOutOfRange;
+      ln.on ? static_cast<uint32_t>(g * L) * row_bytes + static_cast<uint32_t>(ln.ch) * 4u : kOutOfRange;
   if constexpr (!WIDE) {
     // every scaled term is <= 1 against M
     const float top = fmaxf(fmaxf(kmax, X.m), Y.m);
@@ -757,7 +890,7 @@ __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
         A = fmaf(A, lam, pi * vf);
         Cs = fmaf(Cs, lam, pi);
       }
-      return;
+      return true;
     }
 #pragma unroll
     for (int q = 0; q < NSB; ++q) {
@@ -826,7 +959,7 @@ __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
                                               kStream);
         xs = agg_add(agg_shift(xs, 1.f, D), Agg{kl, vf, 1.f});
       }
-      return;
+      return true;
     }
 #pragma unroll
     for (int q = 0; q < NSB; ++q) {
@@ -875,72 +1008,64 @@ __device__ __forceinline__ void row_body(const RowParams& p, const RowLane& ln,
       }
     }
   }
+  return true;
 }
 
 // The wide form is rare (extreme w or u) and needs more registers than the fast form: keeping it
 // out of line gives it its own register allocation, so its spills never touch the fast form. It
 // reads the parameters from the kernel's argument segment (a pointer, so the kernel keeps them in
-// scalar registers instead of building a private copy).
-template <int DT, int TILE, int L, int NT, bool FUSED, bool PAIR, bool CAUSAL, bool GATED>
+// scalar registers instead of building a private copy). It also takes over a fast-form chunk of a
+// single pass whose wait ran out (`published`: that chunk's slot is already out).
+template <int DT, int TILE, int L, int NT, bool FUSED, bool PAIR, bool CAUSAL, bool GATED, int MODE, int POL>
 __device__ __noinline__ void row_body_wide(const RowParams* args, float* lds, unsigned unit,
-                                           const unsigned* sh_epoch) {
+                                           const unsigned* sh_epoch, bool published) {
   const RowParams p = *args;
   const RowLane ln = row_lane<TILE, L, NT>(p, unit);
   RowStore<DT, TILE, L, PAIR> kv;
-  row_load<DT, TILE, L, NT, FUSED, PAIR>(p, ln, kv);
-  row_body<DT, TILE, L, NT, FUSED, PAIR, true, CAUSAL, GATED>(p, ln, kv, lds, sh_epoch);
+  row_load<DT, TILE, L, NT, FUSED, PAIR, POL>(p, ln, kv);
+  row_body<DT, TILE, L, NT, FUSED, PAIR, true, CAUSAL, GATED, MODE>(p, args, ln, kv, lds, sh_epoch, published);
 }
 
-template <int DT, int TILE, int L, int NT, bool FUSED, bool PAIR, bool CAUSAL, bool GATED>
+// Cache policy of a launch's k, v loads: the sums pass of two keeps the default policy, so the
+// output pass finds the chunks it reads again in the memory-side cache; every other launch
+// touches them once.
+template <int MODE>
+constexpr int kRowLoadPolicy = MODE == kSumsPass ? 0 : kStream;
+
+template <int DT, int TILE, int L, int NT, bool FUSED, bool PAIR, bool CAUSAL, bool GATED, int MODE>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4)))
     biwkv_row_kernel(RowParams p) {
   static_assert(!PAIR || (DT == BIWKV_BF16 && TILE % 2 == 0), "pairs are bf16 channel pairs");
   static_assert(!(GATED && (CAUSAL || FUSED)), "the gate is built for the bidirectional entry");
+  static_assert(!(GATED && MODE == kSumsPass), "the sums pass has no outputs to gate");
   static_assert(64 % TILE == 0 || TILE % 64 == 0, "bad row-kernel tile");
   static_assert(TILE <= 64, "a wavefront must hold every channel of the tile");
   static_assert(NT % 256 == 0 && NT <= 1024 && NT >= 2 * TILE, "bad row-kernel workgroup size");
+  constexpr int POL = kRowLoadPolicy<MODE>;
   __shared__ float lds[kRowLdsFloats<TILE, NT>];
-  __shared__ unsigned sh_ticket, sh_epoch;
+  __shared__ unsigned sh_epoch;
   const int tid = threadIdx.x;
-  const bool chunked = p.n_chunks > 1;
-  unsigned unit = blockIdx.x;
-  bool valid = true;
-  if (chunked && !p.ordered) {
-    // Every workgroup of the launch fits on the device at once: chunks follow the grid order,
-    // and the launch epoch is only needed once the scan (and its barriers) is done.
-    if (tid == 0)
-      sh_epoch = __hip_atomic_load(&p.ctr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  } else if (chunked) {
-    if (tid == 0) {
-      sh_ticket = __hip_atomic_fetch_add(&p.ctr->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      sh_epoch = __hip_atomic_load(&p.ctr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    // A ticket beyond the grid can only come from a counter left non-zero by an earlier launch;
-    // such a workgroup touches no data and only retires.
-    valid = __builtin_amdgcn_readfirstlane(sh_ticket) < p.total;
-    if (!valid && tid == 0)
-      __hip_atomic_fetch_or(&p.ctr->fault, kFaultTicket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // uniform values: keep them in scalar registers (buffer resources are built from them)
-    unit = __builtin_amdgcn_readfirstlane(sh_ticket);
+  const unsigned unit = blockIdx.x;
+  // a single pass exchanges through epoch-tagged slots; the epoch is only needed once the scan
+  // (and its barriers) is done
+  if (MODE == kSinglePass && p.n_chunks > 1 && tid == 0)
+    sh_epoch = __hip_atomic_load(&p.ctr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const RowLane ln = row_lane<TILE, L, NT>(p, unit);
+  // The whole workgroup takes the wide form when any of its channels needs it. Every wavefront
+  // holds all TILE channels, so a wavefront vote is the workgroup's vote.
+  const bool wide_lane = fabsf(ln.D) * static_cast<float>(L - 1) > kFastRange || ln.U > kBonusRange ||
+                         ln.U < -kBonusRange;
+  // the kernel's only argument is p, at the start of the argument segment (the argument segment
+  // pointer exists only here, in the kernel: out-of-line functions get it passed down)
+  const auto* args = (const RowParams*)(__builtin_amdgcn_kernarg_segment_ptr());
+  if (__ballot(wide_lane) != 0ull) {
+    row_body_wide<DT, TILE, L, NT, FUSED, PAIR, CAUSAL, GATED, MODE, POL>(args, lds, unit, &sh_epoch, false);
+  } else {
+    RowStore<DT, TILE, L, PAIR> kv;
+    row_load<DT, TILE, L, NT, FUSED, PAIR, POL>(p, ln, kv);
+    if (!row_body<DT, TILE, L, NT, FUSED, PAIR, false, CAUSAL, GATED, MODE>(p, args, ln, kv, lds, &sh_epoch, false))
+      row_body_wide<DT, TILE, L, NT, FUSED, PAIR, CAUSAL, GATED, MODE, POL>(args, lds, unit, &sh_epoch, true);
   }
-  if (valid) {  // uniform over the workgroup
-    const RowLane ln = row_lane<TILE, L, NT>(p, unit);
-    // The whole workgroup takes the wide form when any of its channels needs it. Every
-    // wavefront holds all TILE channels, so a wavefront vote is the workgroup's vote.
-    const bool wide_lane = fabsf(ln.D) * static_cast<float>(L - 1) > kFastRange ||
-                           ln.U > kBonusRange || ln.U < -kBonusRange;
-    if (__ballot(wide_lane) != 0ull) {
-      // the kernel's only argument is p, at the start of the argument segment
-      const auto* args = (const RowParams*)(__builtin_amdgcn_kernarg_segment_ptr());
-      row_body_wide<DT, TILE, L, NT, FUSED, PAIR, CAUSAL, GATED>(args, lds, unit, &sh_epoch);
-    } else {
-      RowStore<DT, TILE, L, PAIR> kv;
-      row_load<DT, TILE, L, NT, FUSED, PAIR>(p, ln, kv);
-      row_body<DT, TILE, L, NT, FUSED, PAIR, false, CAUSAL, GATED>(p, ln, kv, lds, &sh_epoch);
-    }
-  }
-  if (!valid && tid == 0) row_retire(p);  // (a valid workgroup retires after its exchange)
 }
 
 }  // namespace

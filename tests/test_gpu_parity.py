@@ -16,7 +16,9 @@ from tests.metrics import r3
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-4, "bf16": 2e-2}
+# The bar is 1e-4 (fp32 inputs) and 2e-2 (bf16 inputs); the oracle consumes the exact bf16 values
+# and the arithmetic is fp32 either way, so every case here is held to 1e-4.
+TOL = {"f32": 1e-4, "bf16": 1e-4}
 
 
 def _lib():
