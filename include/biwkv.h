@@ -67,6 +67,7 @@ extern "C" {
 #define BIWKV_ERR_NO_DEVICE (-7)   /* no usable HIP device                                       */
 #define BIWKV_ERR_HIP (-8)         /* a HIP runtime call or launch failed; see biwkv_last_hip_error */
 #define BIWKV_ERR_UNSUPPORTED (-9) /* a shape outside the kernels' addressing (limits per entry)  */
+#define BIWKV_ERR_SCRATCH (-10)    /* biwkv_forward_noalloc: chunk sums beyond its static buffer */
 
 /* Options (biwkv_set_option). Process-wide; they apply to calls made after they are set. */
 #define BIWKV_OPT_SPIN_LIMIT 1 /* polls of a peer chunk's sums before recomputing them (default 4096;
@@ -88,6 +89,23 @@ extern "C" {
  */
 int biwkv_forward(const void* k, const void* v, const float* w, const float* u, float* out,
                   int64_t B, int64_t T, int64_t C, int dtype, void* stream);
+
+/*
+ * Allocation-free Bi-WKV forward, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the same computation,
+ * arguments, layout and errors as biwkv_forward, with the same kernels, but the scratch of rows
+ * split over several workgroups lives in a static device array of the library (256 bytes of
+ * counters and 8 MiB of chunk sums per device, held until the process ends) instead of
+ * per-stream buffers. The call allocates nothing: no hipMalloc, hipFree or allocating library
+ * routine (the array's address is looked up once per device, on the first call there). Every
+ * call on a device shares that array, and it keeps the last call's contents: calls that overlap
+ * on one device (several streams or threads at once) race and must not be made. A row of several
+ * chunks needs 2 KiB per chunk in one launch and 1 KiB in two (B * ceil(C / 64) * ceil(T / 512)
+ * chunks for T above 1024 with bf16, above 512 with fp32); a problem that needs more than 8 MiB
+ * returns BIWKV_ERR_SCRATCH before anything is enqueued.
+ */
+int biwkv_forward_noalloc(const void* k, const void* v, const float* w, const float* u, float* out,
+                          int64_t B, int64_t T, int64_t C, int dtype, void* stream);
 
 /*
  * Bi-WKV backward: gradients of a loss L through out = Bi-WKV(k, v) (Eq. (5) of the Vision-RWKV

@@ -49,6 +49,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib = ctypes.CDLL(p)
     lib.biwkv_forward.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P]
     lib.biwkv_forward.restype = ctypes.c_int
+    lib.biwkv_forward_noalloc.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P]
+    lib.biwkv_forward_noalloc.restype = ctypes.c_int
     lib.biwkv_causal_forward.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P]
     lib.biwkv_causal_forward.restype = ctypes.c_int
     lib.biwkv_backward.argtypes = [_P] * 9 + [_I64, _I64, _I64, ctypes.c_int, _P]

@@ -72,6 +72,15 @@ std::mutex g_mu;
 std::map<std::pair<int, void*>, StreamScratch*> g_scratch;
 std::map<std::pair<int, const void*>, int> g_capacity;  // (device, kernel) -> resident workgroups
 
+// The allocation-free entry's scratch: one counter block (256 bytes) and the chunk sums of one
+// launch, as a file-scope device array. Each device holds its own copy at its own address, found
+// with hipGetSymbolAddress once per device; host code uses only that address (the array's name
+// here is a host-side stand-in, not a device address). All calls on a device share it.
+constexpr size_t kStaticCounterBytes = 256;
+constexpr size_t kStaticScratchBytes = kStaticCounterBytes + (8u << 20);
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+std::map<int, void*> g_static_scratch;  // device -> address of its scratch (guarded by g_mu)
+
 // Options (biwkv_set_option).
 std::atomic<unsigned> g_spin_limit{kSpinDefault};
 std::atomic<int> g_two_pass{0};
@@ -205,8 +214,16 @@ int check_bitc_shape(int64_t B, int64_t T, int64_t C) {
 // Tile kernel launch: rows of TILE channels, chunks of (NT / TILE) * L tokens. A row of several
 // chunks runs in one launch when every workgroup fits on the device at once (and two passes are
 // not asked for), otherwise in two.
+// Scratch that the caller provides instead of the per-stream buffers: a counter block followed by
+// `words` 64-bit words (the allocation-free entry's static array).
+struct FixedScratch {
+  Counters* ctr;
+  unsigned long long* words;
+  long long n_words;
+};
+
 template <int DT, int TILE, int L, int NT, bool FUSED, bool PAIR, bool CAUSAL, bool GATED>
-int launch_row(const BiwkvParams& bp, int64_t B, int dev, void* stream) {
+int launch_row(const BiwkvParams& bp, int64_t B, int dev, void* stream, const FixedScratch* fixed) {
   constexpr int CT = (NT / TILE) * L;
   const long long T = bp.T;
   // byte offsets inside one chunk of out (and so of k, v) must stay below 2^31 (the fused loads
@@ -251,18 +268,29 @@ int launch_row(const BiwkvParams& bp, int64_t B, int dev, void* stream) {
     int rc = resident_capacity(dev, kfn, NT, &cap);
     if (rc) return rc;
     const bool two = g_two_pass.load() != 0 || total > cap;
-    StreamScratch* sc = nullptr;
     // single pass: two tagged 64-bit words per (chunk, direction, channel); two passes: one
     // (l, mu) float pair
-    rc = get_scratch(dev, stream, total * 2 * TILE * (two ? 1 : 2), &sc);
-    if (rc) return rc;
+    const long long words = total * 2 * TILE * (two ? 1 : 2);
+    Counters* ctr = nullptr;
+    unsigned long long* slots = nullptr;
+    if (fixed) {
+      if (words > fixed->n_words) return BIWKV_ERR_SCRATCH;
+      ctr = fixed->ctr;
+      slots = fixed->words;
+    } else {
+      StreamScratch* sc = nullptr;
+      rc = get_scratch(dev, stream, words, &sc);
+      if (rc) return rc;
+      ctr = sc->ctr;
+      slots = sc->slots;
+    }
     if (!two) {
-      rp.ctr = sc->ctr;
-      rp.slots = sc->slots;
+      rp.ctr = ctr;
+      rp.slots = slots;
       hipLaunchKernelGGL((biwkv_row_kernel<DT, TILE, L, NT, FUSED, PAIR, CAUSAL, GATED, kSinglePass>), grid,
                          block, 0, st, rp);
     } else {
-      rp.sums = reinterpret_cast<float2*>(sc->slots);
+      rp.sums = reinterpret_cast<float2*>(slots);
       hipLaunchKernelGGL((biwkv_row_kernel<DT, TILE, L, NT, FUSED, PAIR, CAUSAL, false, kSumsPass>), grid, block,
                          0, st, rp);
       hipLaunchKernelGGL((biwkv_row_kernel<DT, TILE, L, NT, FUSED, PAIR, CAUSAL, GATED, kOutPass>), grid, block,
@@ -281,16 +309,16 @@ int launch_row(const BiwkvParams& bp, int64_t B, int dev, void* stream) {
 // overlap. fp32 rows keep 1024 threads: at 32 tokens per lane their 512-thread chunks are short
 // and the exchange between them dominates.
 template <int DT, bool FUSED, bool PAIR, bool CAUSAL, bool GATED>
-int try_row_shape(const BiwkvParams& bp, int64_t B, int dev, void* stream) {
+int try_row_shape(const BiwkvParams& bp, int64_t B, int dev, void* stream, const FixedScratch* fixed) {
   const long long T = bp.T;
   if constexpr (DT == BIWKV_BF16) {
-    if (T <= 256) return launch_row<DT, 64, 16, 1024, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream);
-    if (T <= 512) return launch_row<DT, 64, 32, 1024, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream);
-    if (T <= 1024) return launch_row<DT, 64, 64, 1024, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream);
-    return launch_row<DT, 64, 64, 512, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream);
+    if (T <= 256) return launch_row<DT, 64, 16, 1024, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream, fixed);
+    if (T <= 512) return launch_row<DT, 64, 32, 1024, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream, fixed);
+    if (T <= 1024) return launch_row<DT, 64, 64, 1024, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream, fixed);
+    return launch_row<DT, 64, 64, 512, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream, fixed);
   } else {
-    if (T <= 256) return launch_row<DT, 64, 16, 1024, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream);
-    return launch_row<DT, 64, 32, 1024, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream);
+    if (T <= 256) return launch_row<DT, 64, 16, 1024, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream, fixed);
+    return launch_row<DT, 64, 32, 1024, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream, fixed);
   }
 }
 
@@ -303,17 +331,18 @@ bool pairs_ok(const BiwkvParams& bp, bool fused) {
 }
 
 template <int DT, bool FUSED, bool CAUSAL = false, bool GATED = false>
-int try_row(const BiwkvParams& bp, int64_t B, int dev, void* stream) {
+int try_row(const BiwkvParams& bp, int64_t B, int dev, void* stream, const FixedScratch* fixed = nullptr) {
   if constexpr (DT == BIWKV_BF16) {
-    if (pairs_ok(bp, FUSED)) return try_row_shape<DT, FUSED, true, CAUSAL, GATED>(bp, B, dev, stream);
+    if (pairs_ok(bp, FUSED)) return try_row_shape<DT, FUSED, true, CAUSAL, GATED>(bp, B, dev, stream, fixed);
   }
-  return try_row_shape<DT, FUSED, false, CAUSAL, GATED>(bp, B, dev, stream);
+  return try_row_shape<DT, FUSED, false, CAUSAL, GATED>(bp, B, dev, stream, fixed);
 }
 
 template <bool FUSED>
-int dispatch_biwkv(const BiwkvParams& prm, int64_t B, int dtype, int dev, void* stream) {
-  return dtype == BIWKV_F32 ? try_row<BIWKV_F32, FUSED>(prm, B, dev, stream)
-                            : try_row<BIWKV_BF16, FUSED>(prm, B, dev, stream);
+int dispatch_biwkv(const BiwkvParams& prm, int64_t B, int dtype, int dev, void* stream,
+                   const FixedScratch* fixed = nullptr) {
+  return dtype == BIWKV_F32 ? try_row<BIWKV_F32, FUSED>(prm, B, dev, stream, fixed)
+                            : try_row<BIWKV_BF16, FUSED>(prm, B, dev, stream, fixed);
 }
 
 int validate_biwkv(const void* k, const void* v, const float* w, const float* u, const float* out,
@@ -513,6 +542,40 @@ int biwkv_forward(const void* k, const void* v, const float* w, const float* u, 
   prm.T = T;
   prm.C = static_cast<int>(C);
   return dispatch_biwkv<false>(prm, B, dtype, dev, stream);
+}
+
+int biwkv_forward_noalloc(const void* k, const void* v, const float* w, const float* u, float* out,
+                          int64_t B, int64_t T, int64_t C, int dtype, void* stream) {
+  int rc = validate_biwkv(k, v, w, u, out, B, T, C, dtype);
+  if (rc || !(B && T && C)) return rc;
+  int dev = 0;
+  rc = current_device(&dev);
+  if (rc) return rc;
+  void* base = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    auto it = g_static_scratch.find(dev);
+    if (it != g_static_scratch.end()) {
+      base = it->second;
+    } else {
+      hipError_t e = hipGetSymbolAddress(&base, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_fail(e);
+      g_static_scratch[dev] = base;
+    }
+  }
+  FixedScratch fixed{};
+  fixed.ctr = static_cast<Counters*>(base);
+  fixed.words = reinterpret_cast<unsigned long long*>(static_cast<char*>(base) + kStaticCounterBytes);
+  fixed.n_words = static_cast<long long>((kStaticScratchBytes - kStaticCounterBytes) / 8);
+  BiwkvParams prm{};
+  prm.k = k;
+  prm.v = v;
+  prm.w = w;
+  prm.u = u;
+  prm.out = out;
+  prm.T = T;
+  prm.C = static_cast<int>(C);
+  return dispatch_biwkv<false>(prm, B, dtype, dev, stream, &fixed);
 }
 
 int biwkv_gated_forward(const void* k, const void* v, const void* r, const float* w, const float* u,
@@ -715,6 +778,7 @@ const char* biwkv_status_string(int status) {
     case BIWKV_ERR_ALIGN: return "pointer not aligned to its element size";
     case BIWKV_ERR_NO_DEVICE: return "no usable HIP device";
     case BIWKV_ERR_HIP: return "HIP runtime error (see biwkv_last_hip_error)";
+    case BIWKV_ERR_SCRATCH: return "problem needs more scratch than the allocation-free entry's static buffer holds (8 MiB of chunk sums)";
     case BIWKV_ERR_UNSUPPORTED: return "shape outside what the kernels address (see the entry point's limits)";
     default: return "unknown status";
   }

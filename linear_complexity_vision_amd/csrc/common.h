@@ -23,8 +23,8 @@ constexpr float kFastRange = 64.f;
 // Bonus (u log2 e) above which the self weight is formed per token in the wide path.
 constexpr float kBonusRange = 60.f;
 
-// Per-(device, stream) counter block of the single-pass exchange. epoch starts at 1 so that
-// zeroed slot words never match.
+// Counter block of the single-pass exchange (per (device, stream), or the allocation-free
+// entry's static one). Slots are tagged with epoch + 1, so an all-zero block is a valid start.
 struct Counters {
   unsigned int done;   // workgroups finished in the running launch
   unsigned int epoch;  // launch generation, part of every published word's tag

@@ -1046,10 +1046,11 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4)))
   __shared__ unsigned sh_epoch;
   const int tid = threadIdx.x;
   const unsigned unit = blockIdx.x;
-  // a single pass exchanges through epoch-tagged slots; the epoch is only needed once the scan
-  // (and its barriers) is done
+  // a single pass exchanges through slots tagged with the launch's epoch + 1 (never 0, so zeroed
+  // slots never match, whatever the counter block started at); the tag is only needed once the
+  // scan (and its barriers) is done
   if (MODE == kSinglePass && p.n_chunks > 1 && tid == 0)
-    sh_epoch = __hip_atomic_load(&p.ctr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sh_epoch = __hip_atomic_load(&p.ctr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
   const RowLane ln = row_lane<TILE, L, NT>(p, unit);
   // The whole workgroup takes the wide form when any of its channels needs it. Every wavefront
   // holds all TILE channels, so a wavefront vote is the workgroup's vote.
