@@ -596,6 +596,8 @@ def main() -> int:
                                         "bidir"], default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
+    ap.add_argument("--two-pass", action="store_true",
+                    help="every row through the two-pass form (BIWKV_OPT_TWO_PASS = 1), for comparison")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize", metavar="DIR")
     ap.add_argument("--record-counters", nargs=4, metavar=("KF", "KW", "CF", "CW"))
@@ -616,7 +618,12 @@ def main() -> int:
     if args.calibrate_copy:
         calibrate_copy(args)
         return 0
+    if args.two_pass:
+        import linear_complexity_vision_amd as lib
+        lib.set_option(lib.OPT_TWO_PASS, 1)
     res = run_bench(args)
+    if args.two_pass:
+        res["config"]["two_pass"] = True
     wl = res.pop("_wl")
     entry = res.pop("_entry")
     res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(wl, entry)

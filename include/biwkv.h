@@ -33,7 +33,9 @@
  *     device-side epoch, not by arguments.
  *   - A row split over several workgroups is combined either in one launch, where the chunks
  *     exchange their sums while resident (used when every workgroup of the launch fits on the
- *     device at once), or in two launches (chunk sums, then outputs). In one launch a workgroup
+ *     device at once), or in the two-pass form: 128-token chunks' sums, a per-row scan of them
+ *     into each chunk's carries, then the outputs (three launches, nothing waits). In one launch a
+ *     workgroup
  *     waits a bounded time for a peer chunk's sums and then recomputes them from that chunk's k
  *     and v, so results never depend on the peers being resident (for example when other work
  *     occupies the device); biwkv_stream_fault_flags reports that this happened.
@@ -73,7 +75,7 @@ extern "C" {
 #define BIWKV_OPT_SPIN_LIMIT 1 /* polls of a peer chunk's sums before recomputing them (default 4096;
                                   0: recompute every peer's sums without waiting)             */
 #define BIWKV_OPT_TWO_PASS 2   /* 0 (default): one launch when all workgroups fit at once;
-                                  1: rows of several chunks always take two launches          */
+                                  1: every row takes the two-pass form                         */
 #define BIWKV_OPT_WIDE_INDEX 3 /* 0 (default): Q-Shift gathers use 32-bit index arithmetic below
                                   2^31 items; 1: always the 64-bit form                       */
 
@@ -100,9 +102,9 @@ int biwkv_forward(const void* k, const void* v, const float* w, const float* u, 
  * routine (the array's address is looked up once per device, on the first call there). Every
  * call on a device shares that array, and it keeps the last call's contents: calls that overlap
  * on one device (several streams or threads at once) race and must not be made. A row of several
- * chunks needs 2 KiB per chunk in one launch and 1 KiB in two (B * ceil(C / 64) * ceil(T / 512)
- * chunks for T above 1024 with bf16, above 512 with fp32); a problem that needs more than 8 MiB
- * returns BIWKV_ERR_SCRATCH before anything is enqueued.
+ * chunks needs 2 KiB per chunk in one launch (B * ceil(C / 64) * ceil(T / 512) chunks for T above
+ * 1024 with bf16, above 512 with fp32) and 2 KiB per 128-token chunk in the two-pass form; a
+ * problem that needs more than 8 MiB returns BIWKV_ERR_SCRATCH before anything is enqueued.
  */
 int biwkv_forward_noalloc(const void* k, const void* v, const float* w, const float* u, float* out,
                           int64_t B, int64_t T, int64_t C, int dtype, void* stream);

@@ -46,6 +46,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     p = path or LIB_PATH
     if not os.path.exists(p):
         raise RuntimeError(f"libbiwkv.so is not built ({p}); run __graft_entry__.build() first")
+    # torch (which supplies device memory and streams) loads its HIP runtime first, so the library
+    # binds to that same runtime instead of bringing a second one into the process
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(p)
     lib.biwkv_forward.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P]
     lib.biwkv_forward.restype = ctypes.c_int

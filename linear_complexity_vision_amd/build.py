@@ -11,39 +11,57 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "biwkv.hip")
+CSRC = os.path.join(PKG, "csrc")
+# the library's translation units (compiled at once, then linked into one shared library)
+SOURCES = ["biwkv.hip", "fwd_f32.hip", "fwd_bf16.hip", "fwd_bf16_pair.hip", "bwd.hip"]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libbiwkv.so")
 # measurement only: streaming kernels with the forward's byte mix (a memory ceiling for the bench)
-CEILING_SRC = os.path.join(PKG, "csrc", "hbm_ceiling.hip")
+CEILING_SRC = os.path.join(CSRC, "hbm_ceiling.hip")
 CEILING_LIB = os.path.join(PKG, "libhbmceiling.so")
 ARCH = "gfx950"
+FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def hipcc_command(out: str = LIB, extra: list[str] | None = None, src: str = SRC) -> list[str]:
-    hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
-    return [hipcc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-            "-Wall", "-Wno-unused-function",
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-I", INCLUDE, "-o", out, src] + (extra or [])
+def _hipcc() -> str:
+    return os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
 
 
-def _compile(src: str, lib: str, verbose: bool) -> subprocess.Popen:
-    cmd = hipcc_command(lib + ".tmp", src=src)
-    if verbose:
-        print(" ".join(cmd), file=sys.stderr)
-    return subprocess.Popen(cmd)
+def compile_command(src: str, obj: str, extra: list[str] | None = None) -> list[str]:
+    return [_hipcc(), f"--offload-arch={ARCH}"] + FLAGS + ["-I", INCLUDE, "-c", "-o", obj, src] + (extra or [])
 
 
-def build(verbose: bool = False) -> str:
-    """Compile both libraries (always recompiles; the two compile at once) and return the path of
-    libbiwkv.so."""
-    jobs = [(_compile(SRC, LIB, verbose), LIB), (_compile(CEILING_SRC, CEILING_LIB, verbose), CEILING_LIB)]
-    failed = [lib for proc, lib in jobs if proc.wait() != 0]
+def hipcc_command(out: str = CEILING_LIB, extra: list[str] | None = None, src: str = CEILING_SRC) -> list[str]:
+    """One-step compile and link of a single-file shared library."""
+    return [_hipcc(), f"--offload-arch={ARCH}"] + FLAGS + ["-shared", "-I", INCLUDE, "-o", out, src] + (extra or [])
+
+
+def build(verbose: bool = False, build_dir: str | None = None) -> str:
+    """Compile both libraries (always recompiles; every translation unit at once) and return the
+    path of libbiwkv.so."""
+    bdir = build_dir or os.path.join(PKG, "_build")
+    os.makedirs(bdir, exist_ok=True)
+    jobs = []
+    objs = []
+    for name in SOURCES:
+        obj = os.path.join(bdir, name.replace(".hip", ".o"))
+        cmd = compile_command(os.path.join(CSRC, name), obj)
+        if verbose:
+            print(" ".join(cmd), file=sys.stderr)
+        jobs.append((subprocess.Popen(cmd), name))
+        objs.append(obj)
+    cmd = hipcc_command(CEILING_LIB + ".tmp")
+    jobs.append((subprocess.Popen(cmd), "hbm_ceiling.hip"))
+    failed = [name for proc, name in jobs if proc.wait() != 0]
     if failed:
-        raise subprocess.CalledProcessError(1, "hipcc", f"failed to build {failed}")
-    for _, lib in jobs:
-        os.replace(lib + ".tmp", lib)
+        raise subprocess.CalledProcessError(1, "hipcc", f"failed to compile {failed}")
+    link = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", LIB + ".tmp"] + objs
+    if verbose:
+        print(" ".join(link), file=sys.stderr)
+    subprocess.run(link, check=True)
+    os.replace(LIB + ".tmp", LIB)
+    os.replace(CEILING_LIB + ".tmp", CEILING_LIB)
     return LIB
 
 

@@ -41,58 +41,18 @@
 
 #include "biwkv.h"
 
-#include "backward.h"
-#include "bwd_tile.h"
 #include "common.h"
+#include "host.h"
 #include "qshift_kernel.h"
-#include "row_kernel.h"
+
+namespace biwkv_host {
 
 namespace {
 
-// ---------------------------------------------------------------------------------------------
-// Host side
-// ---------------------------------------------------------------------------------------------
-
 thread_local int t_last_hip_error = 0;
 
-int hip_fail(hipError_t e) {
-  t_last_hip_error = static_cast<int>(e);
-  return BIWKV_ERR_HIP;
-}
-
-struct StreamScratch {
-  Counters* ctr = nullptr;
-  unsigned long long* slots = nullptr;  // single-pass slots, or two-pass chunk totals
-  long long slot_words = 0;
-  float* bwd = nullptr;  // backward pass sums, carries and per-chunk terms
-  long long bwd_floats = 0;
-};
-
-std::mutex g_mu;
 std::map<std::pair<int, void*>, StreamScratch*> g_scratch;
 std::map<std::pair<int, const void*>, int> g_capacity;  // (device, kernel) -> resident workgroups
-
-// The allocation-free entry's scratch: one counter block (256 bytes) and the chunk sums of one
-// launch, as a file-scope device array. Each device holds its own copy at its own address, found
-// with hipGetSymbolAddress once per device; host code uses only that address (the array's name
-// here is a host-side stand-in, not a device address). All calls on a device share it.
-constexpr size_t kStaticCounterBytes = 256;
-constexpr size_t kStaticScratchBytes = kStaticCounterBytes + (8u << 20);
-static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
-std::map<int, void*> g_static_scratch;  // device -> address of its scratch (guarded by g_mu)
-
-// Options (biwkv_set_option).
-std::atomic<unsigned> g_spin_limit{kSpinDefault};
-std::atomic<int> g_two_pass{0};
-std::atomic<int> g_wide_index{0};
-
-int current_device(int* dev) {
-  int n = 0;
-  if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) return BIWKV_ERR_NO_DEVICE;
-  hipError_t e = hipGetDevice(dev);
-  if (e != hipSuccess) return hip_fail(e);
-  return BIWKV_OK;
-}
 
 // Grows a zero-filled scratch buffer in stream order: the new buffer is allocated and cleared on
 // `st`, and the outgrown one is freed on `st` behind every launch already queued that uses it.
@@ -126,8 +86,8 @@ int grow_zeroed(Tp** buf, long long* cap, long long need, long long min_cap, hip
   return BIWKV_OK;
 }
 
-// Scratch of (device, stream) with at least `words` slot words. Caller holds g_mu.
-int get_scratch(int dev, void* stream, long long words, StreamScratch** out) {
+// The stream's scratch record, created (with its counter block) on first use. Caller holds g_mu.
+int stream_scratch(int dev, void* stream, StreamScratch** out) {
   auto key = std::make_pair(dev, stream);
   StreamScratch*& sc = g_scratch[key];
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -149,9 +109,47 @@ int get_scratch(int dev, void* stream, long long words, StreamScratch** out) {
     }
     sc = fresh;
   }
-  int rc = grow_zeroed(&sc->slots, &sc->slot_words, words, 1ll << 16, st);
+  *out = sc;
+  return BIWKV_OK;
+}
+
+}  // namespace
+
+std::mutex g_mu;
+std::atomic<unsigned> g_spin_limit{kSpinDefault};
+std::atomic<int> g_two_pass{0};
+std::atomic<int> g_wide_index{0};
+
+int hip_fail(hipError_t e) {
+  t_last_hip_error = static_cast<int>(e);
+  return BIWKV_ERR_HIP;
+}
+
+int current_device(int* dev) {
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) return BIWKV_ERR_NO_DEVICE;
+  hipError_t e = hipGetDevice(dev);
+  if (e != hipSuccess) return hip_fail(e);
+  return BIWKV_OK;
+}
+
+int get_scratch(int dev, void* stream, long long words, StreamScratch** out) {
+  StreamScratch* sc = nullptr;
+  int rc = stream_scratch(dev, stream, &sc);
+  if (rc) return rc;
+  rc = grow_zeroed(&sc->slots, &sc->slot_words, words, 1ll << 16, static_cast<hipStream_t>(stream));
   if (rc) return rc;
   *out = sc;
+  return BIWKV_OK;
+}
+
+int get_bwd_scratch(int dev, void* stream, long long floats, float** out) {
+  StreamScratch* sc = nullptr;
+  int rc = stream_scratch(dev, stream, &sc);
+  if (rc) return rc;
+  rc = grow_zeroed(&sc->bwd, &sc->bwd_floats, floats, 1ll << 20, static_cast<hipStream_t>(stream));
+  if (rc) return rc;
+  *out = sc->bwd;
   return BIWKV_OK;
 }
 
@@ -172,13 +170,27 @@ int resident_capacity(int dev, const void* kernel, int block, int* cap) {
   return BIWKV_OK;
 }
 
+}  // namespace biwkv_host
+
+using namespace biwkv_host;
+
+namespace {
+
+// The allocation-free entry's scratch: one counter block (256 bytes) and the chunk sums of one
+// launch, as a file-scope device array. Each device holds its own copy at its own address, found
+// with hipGetSymbolAddress once per device; host code uses only that address (the array's name
+// here is a host-side stand-in, not a device address). All calls on a device share it.
+constexpr size_t kStaticCounterBytes = 256;
+constexpr size_t kStaticScratchBytes = kStaticCounterBytes + (8u << 20);
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+std::map<int, void*> g_static_scratch;  // device -> address of its scratch (guarded by g_mu)
+
 bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
   if (!na || !nb) return false;
   const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
   return a0 < b0 + nb && b0 < a0 + na;
 }
 
-bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // Q-Shift group bounds exactly as the listing computes them: int(C * gamma * j) in double.
 void group_bounds(int64_t C, double gamma, int64_t g[4]) {
@@ -214,114 +226,6 @@ int check_bitc_shape(int64_t B, int64_t T, int64_t C) {
 // Tile kernel launch: rows of TILE channels, chunks of (NT / TILE) * L tokens. A row of several
 // chunks runs in one launch when every workgroup fits on the device at once (and two passes are
 // not asked for), otherwise in two.
-// Scratch that the caller provides instead of the per-stream buffers: a counter block followed by
-// `words` 64-bit words (the allocation-free entry's static array).
-struct FixedScratch {
-  Counters* ctr;
-  unsigned long long* words;
-  long long n_words;
-};
-
-template <int DT, int TILE, int L, int NT, bool FUSED, bool PAIR, bool CAUSAL, bool GATED>
-int launch_row(const BiwkvParams& bp, int64_t B, int dev, void* stream, const FixedScratch* fixed) {
-  constexpr int CT = (NT / TILE) * L;
-  const long long T = bp.T;
-  // byte offsets inside one chunk of out (and so of k, v) must stay below 2^31 (the fused loads
-  // also start each word's resource s W tokens early and reach s W tokens late)
-  const long long reach = FUSED ? 2ll * bp.shift * bp.W : 0;
-  if ((CT + reach) * static_cast<long long>(bp.C) * 4 >= (1ll << 31)) return BIWKV_ERR_UNSUPPORTED;
-  const int64_t n_tiles = (bp.C + TILE - 1) / TILE;
-  const int64_t n_chunks = (T + CT - 1) / CT;
-  const int64_t total = B * n_tiles * n_chunks;
-  if (total > 0x7FFFFFFFll) return BIWKV_ERR_SHAPE;
-  RowParams rp{};
-  rp.k = bp.k;
-  rp.v = bp.v;
-  rp.r = bp.r;
-  rp.w = bp.w;
-  rp.u = bp.u;
-  rp.out = bp.out;
-  rp.T = T;
-  rp.C = bp.C;
-  rp.H = bp.H;
-  rp.W = bp.W;
-  rp.shift = bp.shift;
-  rp.g1 = bp.g1;
-  rp.g2 = bp.g2;
-  rp.g3 = bp.g3;
-  rp.g4 = bp.g4;
-  rp.bidir = bp.bidir;
-  rp.n_tiles = static_cast<int>(n_tiles);
-  rp.n_chunks = static_cast<int>(n_chunks);
-  rp.total = static_cast<unsigned>(total);
-  rp.spin_limit = g_spin_limit.load();
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const dim3 grid(static_cast<unsigned>(total)), block(NT);
-  if (n_chunks == 1) {
-    hipLaunchKernelGGL((biwkv_row_kernel<DT, TILE, L, NT, FUSED, PAIR, CAUSAL, GATED, kSinglePass>), grid, block,
-                       0, st, rp);
-  } else {
-    const void* kfn =
-        reinterpret_cast<const void*>(&biwkv_row_kernel<DT, TILE, L, NT, FUSED, PAIR, CAUSAL, GATED, kSinglePass>);
-    std::lock_guard<std::mutex> lock(g_mu);
-    int cap = 0;
-    int rc = resident_capacity(dev, kfn, NT, &cap);
-    if (rc) return rc;
-    const bool two = g_two_pass.load() != 0 || total > cap;
-    // single pass: two tagged 64-bit words per (chunk, direction, channel); two passes: one
-    // (l, mu) float pair
-    const long long words = total * 2 * TILE * (two ? 1 : 2);
-    Counters* ctr = nullptr;
-    unsigned long long* slots = nullptr;
-    if (fixed) {
-      if (words > fixed->n_words) return BIWKV_ERR_SCRATCH;
-      ctr = fixed->ctr;
-      slots = fixed->words;
-    } else {
-      StreamScratch* sc = nullptr;
-      rc = get_scratch(dev, stream, words, &sc);
-      if (rc) return rc;
-      ctr = sc->ctr;
-      slots = sc->slots;
-    }
-    if (!two) {
-      rp.ctr = ctr;
-      rp.slots = slots;
-      hipLaunchKernelGGL((biwkv_row_kernel<DT, TILE, L, NT, FUSED, PAIR, CAUSAL, GATED, kSinglePass>), grid,
-                         block, 0, st, rp);
-    } else {
-      rp.sums = reinterpret_cast<float2*>(slots);
-      hipLaunchKernelGGL((biwkv_row_kernel<DT, TILE, L, NT, FUSED, PAIR, CAUSAL, false, kSumsPass>), grid, block,
-                         0, st, rp);
-      hipLaunchKernelGGL((biwkv_row_kernel<DT, TILE, L, NT, FUSED, PAIR, CAUSAL, GATED, kOutPass>), grid, block,
-                         0, st, rp);
-    }
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return hip_fail(e);
-  return BIWKV_OK;
-}
-
-// Tile shapes: 64 channels per tile (one 128-byte line of bf16 k, two of fp32), 64 registers of
-// k and v per lane, and chunks no longer than the sequence needs. Rows longer than one chunk of
-// 1024 tokens use 512-thread workgroups (two per CU): the workgroup a CU received first gets its
-// data first and computes and writes while the other one still reads, so reads and writes
-// overlap. fp32 rows keep 1024 threads: at 32 tokens per lane their 512-thread chunks are short
-// and the exchange between them dominates.
-template <int DT, bool FUSED, bool PAIR, bool CAUSAL, bool GATED>
-int try_row_shape(const BiwkvParams& bp, int64_t B, int dev, void* stream, const FixedScratch* fixed) {
-  const long long T = bp.T;
-  if constexpr (DT == BIWKV_BF16) {
-    if (T <= 256) return launch_row<DT, 64, 16, 1024, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream, fixed);
-    if (T <= 512) return launch_row<DT, 64, 32, 1024, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream, fixed);
-    if (T <= 1024) return launch_row<DT, 64, 64, 1024, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream, fixed);
-    return launch_row<DT, 64, 64, 512, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream, fixed);
-  } else {
-    if (T <= 256) return launch_row<DT, 64, 16, 1024, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream, fixed);
-    return launch_row<DT, 64, 32, 1024, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream, fixed);
-  }
-}
-
 // bf16 rows read channel pairs as 32-bit words when every pair is whole: C even, 4-byte aligned
 // k and v, and Q-Shift group boundaries on even channels.
 bool pairs_ok(const BiwkvParams& bp, bool fused) {
@@ -330,19 +234,12 @@ bool pairs_ok(const BiwkvParams& bp, bool fused) {
   return true;
 }
 
-template <int DT, bool FUSED, bool CAUSAL = false, bool GATED = false>
-int try_row(const BiwkvParams& bp, int64_t B, int dev, void* stream, const FixedScratch* fixed = nullptr) {
-  if constexpr (DT == BIWKV_BF16) {
-    if (pairs_ok(bp, FUSED)) return try_row_shape<DT, FUSED, true, CAUSAL, GATED>(bp, B, dev, stream, fixed);
-  }
-  return try_row_shape<DT, FUSED, false, CAUSAL, GATED>(bp, B, dev, stream, fixed);
-}
-
-template <bool FUSED>
-int dispatch_biwkv(const BiwkvParams& prm, int64_t B, int dtype, int dev, void* stream,
-                   const FixedScratch* fixed = nullptr) {
-  return dtype == BIWKV_F32 ? try_row<BIWKV_F32, FUSED>(prm, B, dev, stream, fixed)
-                            : try_row<BIWKV_BF16, FUSED>(prm, B, dev, stream, fixed);
+// The tile kernel for a storage type and entry (parameters already checked, nothing empty).
+int forward_dispatch(const BiwkvParams& bp, int64_t B, int dtype, int kind, int dev, void* stream,
+                     const FixedScratch* fixed = nullptr) {
+  if (dtype == BIWKV_F32) return forward_f32(bp, B, kind, dev, stream, fixed);
+  if (pairs_ok(bp, kind == kFused)) return forward_bf16_pair(bp, B, kind, dev, stream, fixed);
+  return forward_bf16(bp, B, kind, dev, stream, fixed);
 }
 
 int validate_biwkv(const void* k, const void* v, const float* w, const float* u, const float* out,
@@ -436,86 +333,7 @@ int fused_forward(const void* k, const void* v, const float* w, const float* u, 
   prm.g3 = static_cast<int>(g[2]);
   prm.g4 = static_cast<int>(g[3]);
   prm.bidir = bidir;
-  return dispatch_biwkv<true>(prm, B, dtype, dev, stream);
-}
-
-// Backward tile shape: 8 tokens per lane, 512 threads (two workgroups per CU, so one's loads
-// overlap the other's arithmetic), 64-token chunks.
-constexpr int kBwdL = 8;
-constexpr int kBwdNT = 512;
-
-// The backward: bwd_tile_kernel in one launch (a row of one chunk) or three (stages 1, 2, 3),
-// then the dw / du fold. Arguments already checked, nothing empty.
-template <int DT, int L, int NT, int WPE, bool PAIR>
-int launch_bwd_tile(const void* k, const void* v, const float* w, const float* u, const float* g,
-                    float* dk, float* dv, float* dw, float* du, int64_t B, int64_t T, int64_t C, int dev,
-                    void* stream) {
-  constexpr int CT = (NT / kBtTile) * L;
-  const int64_t n_tiles = (C + kBtTile - 1) / kBtTile;
-  const int64_t n_chunks = (T + CT - 1) / CT;
-  const int64_t total = B * n_tiles * n_chunks;
-  if (total > 0x7FFFFFFFll) return BIWKV_ERR_SHAPE;
-  // the loads address a batch item (fp32 g, and the row's padding) with 32-bit byte offsets
-  if ((T + CT) * C * 4 >= (1ll << 31)) return BIWKV_ERR_UNSUPPORTED;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  BwdTileParams tp{};
-  // The launches of one call share the stream's scratch: the lock is held until the last one is
-  // queued, so calls from several host threads on one stream cannot interleave their stages.
-  std::lock_guard<std::mutex> lock(g_mu);
-  StreamScratch* sc = nullptr;
-  int rc = get_scratch(dev, stream, 0, &sc);
-  if (rc) return rc;
-  const long long terms = B * n_chunks * C;                         // dw, du terms
-  const long long sums = n_chunks > 1 ? total * 2 * kBtTile * 3 : 0;  // chunk sums per round
-  rc = grow_zeroed(&sc->bwd, &sc->bwd_floats, 2 * terms + 4 * sums, 1ll << 20, st);
-  if (rc) return rc;
-  tp.pw = sc->bwd;
-  tp.pu = sc->bwd + terms;
-  tp.sums1 = sc->bwd + 2 * terms;
-  tp.sums2 = tp.sums1 + sums;
-  tp.carry1 = tp.sums2 + sums;
-  tp.carry2 = tp.carry1 + sums;
-  tp.k = k;
-  tp.v = v;
-  tp.w = w;
-  tp.u = u;
-  tp.g = g;
-  tp.dk = dk;
-  tp.dv = dv;
-  tp.T = T;
-  tp.C = static_cast<int>(C);
-  tp.n_tiles = static_cast<int>(n_tiles);
-  tp.n_chunks = static_cast<int>(n_chunks);
-  const dim3 grid(static_cast<unsigned>(total)), block(NT);
-  if (n_chunks == 1) {
-    hipLaunchKernelGGL((bwd_tile_kernel<DT, L, NT, WPE, 0, PAIR>), grid, block, 0, st, tp);
-  } else {
-    // stage 1: one lane per (channel, chunk); 8 chunks of a row per workgroup
-    constexpr int SNT = 512;
-    const dim3 sgrid(static_cast<unsigned>((n_chunks + SNT / kBtTile - 1) / (SNT / kBtTile) * B * n_tiles));
-    hipLaunchKernelGGL((bwd_chunk_sums_kernel<DT, CT, SNT, PAIR>), sgrid, dim3(SNT), 0, st, tp);
-    const dim3 rows(static_cast<unsigned>(B * n_tiles)), cblock(64 * kCarryGroups);
-    hipLaunchKernelGGL((bwd_carry_kernel<CT>), rows, cblock, 0, st, tp, tp.sums1, tp.carry1);
-    hipLaunchKernelGGL((bwd_tile_kernel<DT, L, NT, WPE, 2, PAIR>), grid, block, 0, st, tp);
-    hipLaunchKernelGGL((bwd_carry_kernel<CT>), rows, cblock, 0, st, tp, tp.sums2, tp.carry2);
-    hipLaunchKernelGGL((bwd_tile_kernel<DT, L, NT, WPE, 3, PAIR>), grid, block, 0, st, tp);
-  }
-  BwdParams rp{};
-  rp.w = w;
-  rp.dw = dw;
-  rp.du = du;
-  rp.T = T;
-  rp.B = static_cast<int>(B);
-  rp.C = static_cast<int>(C);
-  rp.n_chunks = static_cast<int>(n_chunks);
-  rp.n_wg = static_cast<int>(n_chunks);
-  rp.s.pw = tp.pw;
-  rp.s.pu = tp.pu;
-  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(static_cast<unsigned>((C + 63) / 64)), dim3(64 * kReduceGroups), 0,
-                     st, rp);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return hip_fail(e);
-  return BIWKV_OK;
+  return forward_dispatch(prm, B, dtype, kFused, dev, stream);
 }
 
 }  // namespace
@@ -541,7 +359,7 @@ int biwkv_forward(const void* k, const void* v, const float* w, const float* u, 
   prm.out = out;
   prm.T = T;
   prm.C = static_cast<int>(C);
-  return dispatch_biwkv<false>(prm, B, dtype, dev, stream);
+  return forward_dispatch(prm, B, dtype, kPlain, dev, stream);
 }
 
 int biwkv_forward_noalloc(const void* k, const void* v, const float* w, const float* u, float* out,
@@ -575,7 +393,7 @@ int biwkv_forward_noalloc(const void* k, const void* v, const float* w, const fl
   prm.out = out;
   prm.T = T;
   prm.C = static_cast<int>(C);
-  return dispatch_biwkv<false>(prm, B, dtype, dev, stream, &fixed);
+  return forward_dispatch(prm, B, dtype, kPlain, dev, stream, &fixed);
 }
 
 int biwkv_gated_forward(const void* k, const void* v, const void* r, const float* w, const float* u,
@@ -599,8 +417,7 @@ int biwkv_gated_forward(const void* k, const void* v, const void* r, const float
   prm.out = out;
   prm.T = T;
   prm.C = static_cast<int>(C);
-  return dtype == BIWKV_F32 ? try_row<BIWKV_F32, false, false, true>(prm, B, dev, stream)
-                            : try_row<BIWKV_BF16, false, false, true>(prm, B, dev, stream);
+  return forward_dispatch(prm, B, dtype, kGated, dev, stream);
 }
 
 int biwkv_backward(const void* k, const void* v, const float* w, const float* u, const float* g,
@@ -635,21 +452,10 @@ int biwkv_backward(const void* k, const void* v, const float* w, const float* u,
   int dev = 0;
   rc = current_device(&dev);
   if (rc) return rc;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const unsigned cb = static_cast<unsigned>((C + 255) / 256);
-  if (!nonempty) {
-    hipLaunchKernelGGL(bwd_zero_kernel, dim3(cb), dim3(256), 0, st, dw, du, static_cast<int>(C));
-    hipError_t e = hipGetLastError();
-    return e == hipSuccess ? BIWKV_OK : hip_fail(e);
-  }
+  if (!nonempty) return backward_empty(dw, du, C, stream);
   // token positions times D must be exact in fp32
   if (T >= (1ll << 24)) return BIWKV_ERR_UNSUPPORTED;
-  if (dtype == BIWKV_F32)
-    return launch_bwd_tile<BIWKV_F32, kBwdL, kBwdNT, 4, false>(k, v, w, u, g, dk, dv, dw, du, B, T, C, dev, stream);
-  // bf16 k and v load as 32-bit channel pairs when every pair is whole and aligned
-  if (C % 2 == 0 && aligned(k, 4) && aligned(v, 4))
-    return launch_bwd_tile<BIWKV_BF16, kBwdL, kBwdNT, 4, true>(k, v, w, u, g, dk, dv, dw, du, B, T, C, dev, stream);
-  return launch_bwd_tile<BIWKV_BF16, kBwdL, kBwdNT, 4, false>(k, v, w, u, g, dk, dv, dw, du, B, T, C, dev, stream);
+  return backward(k, v, w, u, g, dk, dv, dw, du, B, T, C, dtype, dev, stream);
 }
 
 int biwkv_causal_forward(const void* k, const void* v, const float* w, const float* u, float* out,
@@ -667,8 +473,7 @@ int biwkv_causal_forward(const void* k, const void* v, const float* w, const flo
   prm.out = out;
   prm.T = T;
   prm.C = static_cast<int>(C);
-  return dtype == BIWKV_F32 ? try_row<BIWKV_F32, false, true>(prm, B, dev, stream)
-                            : try_row<BIWKV_BF16, false, true>(prm, B, dev, stream);
+  return forward_dispatch(prm, B, dtype, kCausal, dev, stream);
 }
 
 int biwkv_qshift_forward(const void* k, const void* v, const float* w, const float* u, float* out,

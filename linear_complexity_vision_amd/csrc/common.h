@@ -7,21 +7,8 @@
 
 #include "biwkv.h"
 
-namespace {
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kNegInf = -__builtin_huge_valf();
-// Polls of a peer chunk's slot before a waiting workgroup recomputes that chunk's sums itself
-// (each poll is a round trip to memory, about a microsecond under load): far above what an
-// exchange between resident workgroups takes, far below a stall.
-constexpr unsigned kSpinDefault = 1u << 12;
-constexpr unsigned kFaultSpin = 1u;  // fault-word bit: a wait ran out and a peer's sums were recomputed
-// Largest decay/growth range (in powers of two) across one wavefront's tokens for which a single
-// exponent reference per wavefront keeps every significant term a normal fp32 number. Beyond it
-// (|w|/T above ~3 for 16 tokens per wavefront) the wavefront uses per-token references.
-constexpr float kFastRange = 64.f;
-// Bonus (u log2 e) above which the self weight is formed per token in the wide path.
-constexpr float kBonusRange = 60.f;
+// Types shared by the translation units of the library (they appear in its internal
+// interfaces, so they have external linkage).
 
 // Counter block of the single-pass exchange (per (device, stream), or the allocation-free
 // entry's static one). Slots are tagged with epoch + 1, so an all-zero block is a valid start.
@@ -45,6 +32,22 @@ struct BiwkvParams {
   int g1, g2, g3, g4;    // Q-Shift channel-group bounds (fused entry only)
   int bidir;             // fused entry: shift along the token sequence (W = 1), not the grid
 };
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_huge_valf();
+// Polls of a peer chunk's slot before a waiting workgroup recomputes that chunk's sums itself
+// (each poll is a round trip to memory, about a microsecond under load): far above what an
+// exchange between resident workgroups takes, far below a stall.
+constexpr unsigned kSpinDefault = 1u << 12;
+constexpr unsigned kFaultSpin = 1u;  // fault-word bit: a wait ran out and a peer's sums were recomputed
+// Largest decay/growth range (in powers of two) across one wavefront's tokens for which a single
+// exponent reference per wavefront keeps every significant term a normal fp32 number. Beyond it
+// (|w|/T above ~3 for 16 tokens per wavefront) the wavefront uses per-token references.
+constexpr float kFastRange = 64.f;
+// Bonus (u log2 e) above which the self weight is formed per token in the wide path.
+constexpr float kBonusRange = 60.f;
 
 // ---------------------------------------------------------------------------------------------
 // Device helpers

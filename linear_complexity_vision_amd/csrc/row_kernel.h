@@ -144,7 +144,8 @@ constexpr uint32_t kOutOfRange = 0x80000000u;
 enum : int {
   kSinglePass = 0,  // slot exchange between resident workgroups, recompute on a timed-out wait
   kSumsPass = 1,    // two passes, first: write every chunk's totals to RowParams::sums
-  kOutPass = 2,     // two passes, second: carries from the totals, then the outputs
+  kOutPass = 2,     // two passes, second (after row_carry_kernel): the chunk's carries, then the
+                    // outputs
 };
 
 struct RowParams {
@@ -164,6 +165,7 @@ struct RowParams {
   Counters* ctr;                 // single pass: epoch block (n_chunks > 1)
   unsigned long long* slots;     // single pass: [row][chunk][dir][TILE] (l, mu) tagged slot pairs
   float2* sums;                  // two passes: [row][chunk][dir][TILE] (l, mu) chunk totals
+  float2* carries;               // two passes: [row][chunk][dir][TILE] (l, mu) exclusive carries
   int H, W, shift, g1, g2, g3, g4;  // Q-Shift (fused entry only)
   int bidir;  // fused: the bidirectional shift along a sparse token sequence (the host sets W = 1)
 };
@@ -728,6 +730,21 @@ __device__ __forceinline__ bool row_body(const RowParams& p, const RowParams* ar
       if (!CAUSAL && tg == 0) p.sums[row_base + (chunk * 2 + kBwd) * TILE + tc] = slot_pack(bk);
       return true;
     }
+    if constexpr (MODE == kOutPass) {
+      // the chunk's exclusive carries (row_carry_kernel): forward anchored just before the
+      // chunk's first token, backward just after its last slot
+      Agg pf = row_empty(), pb = row_empty();
+      if (tg == 0) {
+        pf = slot_unpack(p.carries[row_base + (chunk * 2 + kFwd) * TILE + tc]);
+        if (!CAUSAL) pb = slot_unpack(p.carries[row_base + (chunk * 2 + kBwd) * TILE + tc]);
+      }
+      pf = agg_from_first<GROUPS>(pf);
+      X = agg_add_f(agg_shift(pf, static_cast<float>(tg * L), Dt), X);
+      if constexpr (!CAUSAL) {
+        pb = agg_from_first<GROUPS>(pb);
+        Y = agg_add_f(Y, agg_shift(pb, static_cast<float>((GROUPS - 1 - tg) * L), Dt));
+      }
+    } else {
     unsigned epoch = 0;
     unsigned long long* rs = p.slots + row_base * 2;
     auto slot = [&](int ck, int dir) { return rs + (static_cast<size_t>(ck * 2 + dir) * TILE + tc) * 2; };
@@ -746,7 +763,7 @@ __device__ __forceinline__ bool row_body(const RowParams& p, const RowParams* ar
     Agg pf = row_empty(), pb = row_empty();
     bool recomputed = false;
     // a poll limit of 0 recomputes every peer's sums without polling
-    const bool poll = MODE == kSinglePass && p.spin_limit != 0;
+    const bool poll = p.spin_limit != 0;
     // A lane issues the loads of up to EB entries before it waits for any of them, so a lane
     // with several entries pays one round trip, not one per entry.
     constexpr int EB = GROUPS >= 8 ? 1 : 8 / GROUPS;
@@ -769,9 +786,7 @@ __device__ __forceinline__ bool row_body(const RowParams& p, const RowParams* ar
         // are full, so slot positions are token positions)
         const float dist = static_cast<float>(fwd ? (chunk - 1 - ck) : (ck - chunk - 1)) * CT;
         Agg a;
-        if constexpr (MODE == kOutPass) {
-          a = slot_unpack(p.sums[row_base + (ck * 2 + (fwd ? kFwd : kBwd)) * TILE + tc]);
-        } else {
+        {
           const unsigned long long* sp = slot(ck, fwd ? kFwd : kBwd);
           bool ready = false;
           if (poll) {
@@ -837,6 +852,7 @@ __device__ __forceinline__ bool row_body(const RowParams& p, const RowParams* ar
     if constexpr (!CAUSAL) {
       pb = agg_from_first<GROUPS>(pb);
       Y = agg_add_f(Y, agg_shift(pb, static_cast<float>((GROUPS - 1 - tg) * L), Dt));
+    }
     }
   }
   xy[0 * RS + ti] = X.m;
@@ -1009,6 +1025,129 @@ __device__ __forceinline__ bool row_body(const RowParams& p, const RowParams* ar
     }
   }
   return true;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Carries of the two-pass form: for every chunk j of a row and channel, the sum of the forward
+// totals of chunks 0 .. j-1 (anchored just before chunk j's first token, token j CT - 1) and of
+// the backward totals of chunks j+1 .. n-1 (anchored just after its last slot, token (j+1) CT).
+// One wavefront per (row, channel): lane s holds segment s of `per` consecutive chunks (64
+// segments), forms the segment's sums, and the lanes scan them with shuffles; each lane then
+// writes its chunks' carries. Every term and partial sum is moved to its anchor by an exponent
+// shift of its exact distance (one product, never stepped chunk by chunk), and the order of the
+// additions is fixed, so the carries are bitwise reproducible.
+// ---------------------------------------------------------------------------------------------
+constexpr int kCarryChans = 16;  // wavefronts (channels) per workgroup
+
+struct CarryParams {
+  const float2* sums;
+  float2* carries;
+  const float* w;
+  long long T;
+  int C, n_tiles, n_chunks, CT, causal;
+};
+
+// Chunks of a lane's segment held in registers (rows of up to 64 * 8 chunks); beyond that the
+// totals are read from memory as they are needed.
+constexpr int kCarryRegs = 8;
+
+template <int TILE>
+__global__ void __launch_bounds__(64 * kCarryChans) row_carry_kernel(CarryParams p) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  constexpr int SLICES = TILE / kCarryChans;
+  const int row = blockIdx.x / SLICES, slice = blockIdx.x - row * SLICES;
+  const int tc = slice * kCarryChans + wv;
+  const int ch = (row % p.n_tiles) * TILE + tc;
+  const int n = p.n_chunks;
+  const int per = (n + 63) / 64;
+  const int c0 = lane * per < n ? lane * per : n, c1 = c0 + per < n ? c0 + per : n;
+  const float seg = static_cast<float>(per) * static_cast<float>(p.CT);  // tokens per segment
+  const float ct = static_cast<float>(p.CT);
+  const size_t base = static_cast<size_t>(row) * n * 2 * TILE + tc;
+  auto at = [&](int j, int dir) { return base + static_cast<size_t>(j * 2 + dir) * TILE; };
+  const float2* __restrict__ sums = p.sums;
+  float2* __restrict__ carries = p.carries;
+  // every load of the lane is issued before any result is used (one round trip)
+  const bool inreg = per <= kCarryRegs;
+  float2 tf[kCarryRegs], tb[kCarryRegs];
+  if (inreg) {
+#pragma unroll
+    for (int i = 0; i < kCarryRegs; ++i) {
+      if (c0 + i < c1) {
+        tf[i] = sums[at(c0 + i, kFwd)];
+        tb[i] = p.causal ? make_float2(kNegInf, 0.f) : sums[at(c0 + i, kBwd)];
+      }
+    }
+  }
+  const float D = ch < p.C ? (p.w[ch] / static_cast<float>(p.T)) * kLog2e : 0.f;
+  // segment sums: forward anchored at the segment's last slot, (lane + 1) per CT - 1, and
+  // backward at its first token, lane per CT (a short or empty last segment keeps those anchors)
+  Agg f = row_empty(), b = row_empty();
+  const int cf = lane * per + per - 1;  // chunk whose last slot is the forward anchor
+  if (inreg) {
+#pragma unroll
+    for (int i = 0; i < kCarryRegs; ++i) {
+      const int j = c0 + i;
+      if (j < c1) {
+        f = agg_add_f(f, agg_shift(slot_unpack(tf[i]), static_cast<float>(cf - j) * ct, D));
+        b = agg_add_f(b, agg_shift(slot_unpack(tb[i]), static_cast<float>(i) * ct, D));
+      }
+    }
+  } else {
+    for (int j = c0; j < c1; ++j) {
+      f = agg_add_f(f, agg_shift(slot_unpack(sums[at(j, kFwd)]), static_cast<float>(cf - j) * ct, D));
+      if (!p.causal) b = agg_add_f(b, agg_shift(slot_unpack(sums[at(j, kBwd)]), static_cast<float>(j - c0) * ct, D));
+    }
+  }
+  // inclusive scans over the segments: forward over lanes 0 .. lane, backward over lane .. 63
+#pragma unroll
+  for (int d = 1; d < 64; d *= 2) {
+    const Agg pf{__shfl_up(f.m, d), __shfl_up(f.F, d), __shfl_up(f.G, d)};
+    if (lane >= d) f = agg_add_f(agg_shift(pf, static_cast<float>(d) * seg, D), f);
+    const Agg pb{__shfl_down(b.m, d), __shfl_down(b.F, d), __shfl_down(b.G, d)};
+    if (lane + d < 64) b = agg_add_f(b, agg_shift(pb, static_cast<float>(d) * seg, D));
+  }
+  // entering sums: the earlier segments' forward sum, anchored at c0 CT - 1, and the later
+  // segments' backward sum, anchored at (lane + 1) per CT
+  Agg X{__shfl_up(f.m, 1), __shfl_up(f.F, 1), __shfl_up(f.G, 1)};
+  Agg Y{__shfl_down(b.m, 1), __shfl_down(b.F, 1), __shfl_down(b.G, 1)};
+  if (lane == 0) X = row_empty();
+  if (p.causal || lane == 63) Y = row_empty();
+  const int ce = lane * per + per;  // first chunk after the segment (the backward anchor's chunk)
+  // each chunk's carries: the entering sum plus the segment's chunks on the near side, each
+  // moved once from its anchor to the chunk's
+  if (inreg) {
+    Agg x = X;
+#pragma unroll
+    for (int i = 0; i < kCarryRegs; ++i) {
+      if (c0 + i < c1) {
+        carries[at(c0 + i, kFwd)] = slot_pack(agg_shift(x, static_cast<float>(i) * ct, D));
+        x = agg_add_f(x, agg_shift(slot_unpack(tf[i]), -static_cast<float>(i + 1) * ct, D));
+      }
+    }
+    if (!p.causal) {
+      Agg y = Y;
+#pragma unroll
+      for (int i = kCarryRegs - 1; i >= 0; --i) {
+        const int j = c0 + i;
+        if (j < c1) {
+          carries[at(j, kBwd)] = slot_pack(agg_shift(y, static_cast<float>(ce - 1 - j) * ct, D));
+          y = agg_add_f(y, agg_shift(slot_unpack(tb[i]), -static_cast<float>(ce - j) * ct, D));
+        }
+      }
+    }
+  } else {
+    for (int j = c0; j < c1; ++j) {
+      carries[at(j, kFwd)] = slot_pack(agg_shift(X, static_cast<float>(j - c0) * ct, D));
+      X = agg_add_f(X, agg_shift(slot_unpack(sums[at(j, kFwd)]), -static_cast<float>(j + 1 - c0) * ct, D));
+    }
+    if (!p.causal) {
+      for (int j = c1 - 1; j >= c0; --j) {
+        carries[at(j, kBwd)] = slot_pack(agg_shift(Y, static_cast<float>(ce - 1 - j) * ct, D));
+        Y = agg_add_f(Y, agg_shift(slot_unpack(sums[at(j, kBwd)]), -static_cast<float>(ce - j) * ct, D));
+      }
+    }
+  }
 }
 
 // The wide form is rare (extreme w or u) and needs more registers than the fast form: keeping it

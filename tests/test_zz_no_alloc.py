@@ -52,7 +52,7 @@ def test_noalloc_matches_forward_on_two_calls_large_then_small():
 
 def test_noalloc_two_launch_rows_and_single_chunk_rows():
     import linear_complexity_vision_amd as L
-    print("[case] noalloc: config 5 (two launches), then single-chunk rows", flush=True)
+    print("[case] noalloc: config 5 (two-pass form), then single-chunk rows", flush=True)
     _check(L, workloads.make(5))
     _check(L, workloads.make_random(92, 3, 300, 100, dtype="f32", w_range=5.0))
     with L.option(L.OPT_TWO_PASS, 1):
@@ -60,8 +60,8 @@ def test_noalloc_two_launch_rows_and_single_chunk_rows():
 
 
 def test_noalloc_refuses_beyond_its_buffer():
-    """B = 32, T = 16384, C = 1024 bf16 needs 32 * 16 * 32 chunks of 1 KiB (16 MiB) in two
-    launches: refused before any launch (the pointers are never used)."""
+    """B = 32, T = 16384, C = 1024 bf16 needs 32 * 16 * 128 chunks of 2 KiB (128 MiB) in the
+    two-pass form: refused before any launch (the pointers are never used)."""
     import torch
 
     import linear_complexity_vision_amd as L
