@@ -102,8 +102,8 @@ int biwkv_forward(const void* k, const void* v, const float* w, const float* u, 
  * routine (the array's address is looked up once per device, on the first call there). Every
  * call on a device shares that array, and it keeps the last call's contents: calls that overlap
  * on one device (several streams or threads at once) race and must not be made. A row of several
- * chunks needs 2 KiB per chunk in one launch (B * ceil(C / 64) * ceil(T / 512) chunks for T above
- * 1024 with bf16, above 512 with fp32) and 2 KiB per 128-token chunk in the two-pass form; a
+ * chunks needs 3 KiB per chunk in one launch (B * ceil(C / 64) * ceil(T / 512) chunks for T above
+ * 1024 with bf16, above 512 with fp32) and 4 KiB per 128-token chunk in the two-pass form; a
  * problem that needs more than 8 MiB returns BIWKV_ERR_SCRATCH before anything is enqueued.
  */
 int biwkv_forward_noalloc(const void* k, const void* v, const float* w, const float* u, float* out,

@@ -163,9 +163,9 @@ struct RowParams {
   unsigned spin_limit;           // single pass: polls of a peer's slot before recomputing its sums
                                  // (0: recompute every peer without polling)
   Counters* ctr;                 // single pass: epoch block (n_chunks > 1)
-  unsigned long long* slots;     // single pass: [row][chunk][dir][TILE] (l, mu) tagged slot pairs
-  float2* sums;                  // two passes: [row][chunk][dir][TILE] (l, mu) chunk totals
-  float2* carries;               // two passes: [row][chunk][dir][TILE] (l, mu) exclusive carries
+  unsigned long long* slots;     // single pass: [row][chunk][dir][TILE] (q, l, mu) tagged slot words
+  float4* sums;                  // two passes: [row][chunk][dir][TILE] (q, l, mu) chunk totals
+  float4* carries;               // two passes: [row][chunk][dir][TILE] (q, l, mu) exclusive carries
   int H, W, shift, g1, g2, g3, g4;  // Q-Shift (fused entry only)
   int bidir;  // fused: the bidirectional shift along a sparse token sequence (the host sets W = 1)
 };
@@ -368,19 +368,16 @@ __device__ __forceinline__ void row_load(const RowParams& p, const RowLane& ln, 
 // LDS of the tile kernel: the wide form's per-token sweep buffer (8 tokens x NT lanes of float2),
 // which first holds the lane sums, then the carries and the per-channel D outside it.
 template <int NT>
-constexpr int kRowSweepFloats = 8 * NT * 2;
+constexpr int kRowSweepFloats = 8 * NT * 3;
 // Row pitch of the group-major lane-sum and carry buffers. Lane (tg, tc) of the transposed layout
 // reads word tg * pitch + tc with tg = lane % GROUPS: a pitch of TILE + 64 / GROUPS puts the 64
 // lanes of a wavefront on 64 different banks (a pitch of TILE + 1 put up to 8 on one).
 template <int TILE, int NT>
 constexpr int kRowPad = TILE + (NT / TILE < 64 ? 64 / (NT / TILE) : 1);
 template <int TILE, int NT>
-constexpr int kRowLdsFloats = kRowSweepFloats<NT> + 6 * (NT / TILE) * kRowPad<TILE, NT> + TILE;
+constexpr int kRowLdsFloats = kRowSweepFloats<NT> + 8 * (NT / TILE) * kRowPad<TILE, NT> + TILE;
 
-// The scans and the exchange use a finite exponent for an empty aggregate (F = G = 0), far below
-// any real one: 2^(empty - m) is then exactly 0 against a real exponent and 1 against another
-// empty one, so adding aggregates needs no branch.
-constexpr float kEmptyM = -1e30f;
+// Single-exponent sums for the backward's scans (an empty one has the finite exponent kEmptyM).
 __device__ __forceinline__ Agg row_empty() { return Agg{kEmptyM, 0.f, 0.f}; }
 __device__ __forceinline__ Agg agg_add_f(Agg a, Agg b) {
   const float m = fmaxf(a.m, b.m);
@@ -397,52 +394,125 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_move(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, 0xf, 0xf, false));
 }
+// The tile kernel works on single-exponent sums (Agg) in the fast form and on sums with exact
+// token counts (Sum) in the wide form; these overloads let the scans and the exchange serve both.
+template <class A>
+__device__ __forceinline__ A acc_empty();
+template <>
+__device__ __forceinline__ Agg acc_empty<Agg>() { return agg_none(); }
+template <>
+__device__ __forceinline__ Sum acc_empty<Sum>() { return sum_empty(); }
+__device__ __forceinline__ Agg acc_add(Agg a, Agg b, float) { return agg_add_f(a, b); }
+__device__ __forceinline__ Sum acc_add(Sum a, Sum b, float D) { return sum_add(a, b, D); }
+__device__ __forceinline__ Agg acc_shift(Agg a, float n, float D) { return agg_shift(a, n, D); }
+__device__ __forceinline__ Sum acc_shift(Sum a, float n, float) { return sum_shift(a, n); }
+// A two-pass total or carry as the kernel's sum type (a fast-form row's exponents are small, so
+// q D + l is exact enough there).
+template <class A>
+__device__ __forceinline__ A acc_unpack(float4 s, float D);
+template <>
+__device__ __forceinline__ Sum acc_unpack<Sum>(float4 s, float) { return slot_unpack(s); }
+template <>
+__device__ __forceinline__ Agg acc_unpack<Agg>(float4 s, float D) {
+  if (!(s.y > kEmptyM)) return agg_none();
+  return Agg{fmaf(s.x, D, s.y), s.z, 1.f};
+}
+// Sums in LDS: quantity j of lane i at base[j * RS + i] (3 quantities for Agg, 4 for Sum).
+__device__ __forceinline__ void acc_put(float* base, int RS, int i, const Agg& a) {
+  base[0 * RS + i] = a.m;
+  base[1 * RS + i] = a.F;
+  base[2 * RS + i] = a.G;
+}
+__device__ __forceinline__ void acc_put(float* base, int RS, int i, const Sum& a) {
+  base[0 * RS + i] = a.m;
+  base[1 * RS + i] = a.F;
+  base[2 * RS + i] = a.G;
+  base[3 * RS + i] = a.q;
+}
+template <class A>
+__device__ __forceinline__ A acc_get(const float* base, int RS, int i);
+template <>
+__device__ __forceinline__ Agg acc_get<Agg>(const float* base, int RS, int i) {
+  return Agg{base[0 * RS + i], base[1 * RS + i], base[2 * RS + i]};
+}
+template <>
+__device__ __forceinline__ Sum acc_get<Sum>(const float* base, int RS, int i) {
+  return Sum{base[3 * RS + i], base[0 * RS + i], base[1 * RS + i], base[2 * RS + i]};
+}
+
+// Sums moved between the W consecutive lanes that hold one channel's groups (W is a power of two
+// up to 64). from_below<W, d> gives a lane the value of the lane d below it and from_above<W, d>
+// that of the lane d above; the callers only use results from inside the segment. Segments of up
+// to 16 lanes lie inside one DPP row, so these are row shifts (plain VALU moves); wider segments go
+// through the LDS crossbar (ds_bpermute).
 template <int W, int d>
-__device__ __forceinline__ Agg agg_from_below(Agg a) {
+__device__ __forceinline__ float lane_from_below(float x) {
   if constexpr (W <= 16)
-    return Agg{dpp_move<0x110 + d>(a.m), dpp_move<0x110 + d>(a.F), dpp_move<0x110 + d>(a.G)};  // row_shr
+    return dpp_move<0x110 + d>(x);  // row_shr
   else
-    return Agg{__shfl_up(a.m, d, W), __shfl_up(a.F, d, W), __shfl_up(a.G, d, W)};
+    return __shfl_up(x, d, W);
 }
 template <int W, int d>
-__device__ __forceinline__ Agg agg_from_above(Agg a) {
+__device__ __forceinline__ float lane_from_above(float x) {
   if constexpr (W <= 16)
-    return Agg{dpp_move<0x100 + d>(a.m), dpp_move<0x100 + d>(a.F), dpp_move<0x100 + d>(a.G)};  // row_shl
+    return dpp_move<0x100 + d>(x);  // row_shl
   else
-    return Agg{__shfl_down(a.m, d, W), __shfl_down(a.F, d, W), __shfl_down(a.G, d, W)};
+    return __shfl_down(x, d, W);
+}
+template <int W, int d>
+__device__ __forceinline__ Agg acc_from_below(Agg a) {
+  return Agg{lane_from_below<W, d>(a.m), lane_from_below<W, d>(a.F), lane_from_below<W, d>(a.G)};
+}
+template <int W, int d>
+__device__ __forceinline__ Sum acc_from_below(Sum a) {
+  return Sum{lane_from_below<W, d>(a.q), lane_from_below<W, d>(a.m), lane_from_below<W, d>(a.F),
+             lane_from_below<W, d>(a.G)};
+}
+template <int W, int d>
+__device__ __forceinline__ Agg acc_from_above(Agg a) {
+  return Agg{lane_from_above<W, d>(a.m), lane_from_above<W, d>(a.F), lane_from_above<W, d>(a.G)};
+}
+template <int W, int d>
+__device__ __forceinline__ Sum acc_from_above(Sum a) {
+  return Sum{lane_from_above<W, d>(a.q), lane_from_above<W, d>(a.m), lane_from_above<W, d>(a.F),
+             lane_from_above<W, d>(a.G)};
 }
 template <int W>
-__device__ __forceinline__ Agg agg_from_first(Agg a) {
+__device__ __forceinline__ Agg acc_from_first(Agg a) {
   return Agg{__shfl(a.m, 0, W), __shfl(a.F, 0, W), __shfl(a.G, 0, W)};
+}
+template <int W>
+__device__ __forceinline__ Sum acc_from_first(Sum a) {
+  return Sum{__shfl(a.q, 0, W), __shfl(a.m, 0, W), __shfl(a.F, 0, W), __shfl(a.G, 0, W)};
 }
 
 // Inclusive scans over the W groups of a channel (lane tg holds group tg; groups are L slots
 // apart): forward over groups 0..tg, anchored at tg's last slot, and (BWD) backward over
 // tg..W-1, anchored at tg's first token. Hillis-Steele, fixed order.
-template <int W, int L, bool BWD, int d = 1>
-__device__ __forceinline__ void group_scan(Agg& f, Agg& bk, int tg, float D) {
+template <int W, int L, bool BWD, int d = 1, class A>
+__device__ __forceinline__ void group_scan(A& f, A& bk, int tg, float D) {
   if constexpr (d < W) {
-    const Agg pf = agg_from_below<W, d>(f);
-    if (tg >= d) f = agg_add_f(agg_shift(pf, static_cast<float>(d * L), D), f);
+    const A pf = acc_from_below<W, d>(f);
+    if (tg >= d) f = acc_add(acc_shift(pf, static_cast<float>(d * L), D), f, D);
     if constexpr (BWD) {
-      const Agg pb = agg_from_above<W, d>(bk);
-      if (tg + d < W) bk = agg_add_f(bk, agg_shift(pb, static_cast<float>(d * L), D));
+      const A pb = acc_from_above<W, d>(bk);
+      if (tg + d < W) bk = acc_add(bk, acc_shift(pb, static_cast<float>(d * L), D), D);
     }
     group_scan<W, L, BWD, 2 * d>(f, bk, tg, D);
   }
 }
 
 // Folds the W lanes' sums (a, and b when BWD) into the segment's first lane in a fixed tree.
-template <int W, bool BWD, int s = 1>
-__device__ __forceinline__ void group_fold(Agg& a, Agg& b, int tg) {
+template <int W, bool BWD, int s = 1, class A>
+__device__ __forceinline__ void group_fold(A& a, A& b, int tg, float D) {
   if constexpr (s < W) {
-    const Agg oa = agg_from_above<W, s>(a);
-    if ((tg & (2 * s - 1)) == 0) a = agg_add_f(a, oa);
+    const A oa = acc_from_above<W, s>(a);
+    if ((tg & (2 * s - 1)) == 0) a = acc_add(a, oa, D);
     if constexpr (BWD) {
-      const Agg ob = agg_from_above<W, s>(b);
-      if ((tg & (2 * s - 1)) == 0) b = agg_add_f(b, ob);
+      const A ob = acc_from_above<W, s>(b);
+      if ((tg & (2 * s - 1)) == 0) b = acc_add(b, ob, D);
     }
-    group_fold<W, BWD, 2 * s>(a, b, tg);
+    group_fold<W, BWD, 2 * s>(a, b, tg, D);
   }
 }
 
@@ -496,25 +566,23 @@ __device__ __forceinline__ void row_token(const RowParams& p, long long b, int c
 // The sums of chunk ck of batch item b, channel ch, recomputed from k and v: forward anchored at
 // the chunk's last slot, or backward anchored at its first token. This is what the chunk
 // publishes, so a workgroup whose wait for a peer runs out takes it from here instead; a masked
-// channel gives the empty sum. Each token's exponent is formed from its distance to the anchor
-// (k log2 e - n D, one product), never by stepping a running exponent, and the terms are summed
-// against their running maximum, so any w, u and k stay finite and accurate.
+// channel gives the empty sum. Each token enters with its exact distance to the anchor, and the
+// terms are summed against their running maximum, so any w, u and k stay finite and accurate.
 template <int DT, int CT, bool FUSED>
-__device__ __noinline__ Agg row_recompute(const RowParams* args, long long b, int ch, int ck, bool fwd, float D) {
+__device__ __noinline__ Sum row_recompute(const RowParams* args, long long b, int ch, int ck, bool fwd, float D) {
   const RowParams& p = *args;
-  if (ch >= p.C) return row_empty();
+  if (ch >= p.C) return sum_empty();
   const long long s = static_cast<long long>(ck) * CT;
   const long long e = s + CT < p.T ? s + CT : p.T;  // exclusive
   const long long anchor = fwd ? s + CT - 1 : s;
-  Agg a = agg_empty();
+  Sum a = sum_empty();
 #pragma unroll 8
   for (long long t = s; t < e; ++t) {
     float kf, vf;
     row_token<DT, FUSED>(p, b, ch, t, kf, vf);
-    const float n = static_cast<float>(fwd ? anchor - t : t - anchor);
-    a = agg_add(a, Agg{fmaf(-n, D, kf * kLog2e), vf, 1.f});
+    const float n = static_cast<float>(fwd ? anchor - t : t - anchor);  // distance to the anchor
+    a = sum_add(a, Sum{-n, kf * kLog2e, vf, 1.f}, D);
   }
-  a.m = fmaxf(a.m, kEmptyM);
   return a;
 }
 
@@ -570,10 +638,16 @@ __device__ __forceinline__ bool row_body(const RowParams& p, const RowParams* ar
   constexpr int GROUPS = NT / TILE;
   constexpr int CT = GROUPS * L;  // tokens per chunk
   constexpr int SB = 8;  // tokens per sub-block of the sweeps
+  // the fast form's sums keep one exponent; the wide form's keep exact token counts
+  using A = std::conditional_t<WIDE, Sum, Agg>;
   constexpr int NSB = L / SB;
   static_assert(L % SB == 0, "bad row-kernel shape");
   static_assert((GROUPS & (GROUPS - 1)) == 0 && GROUPS <= 64, "a channel's groups share a wavefront");
-  float2 (*lds_ab)[NT] = reinterpret_cast<float2 (*)[NT]>(lds);
+  // wide-form sweep records, per token of a sub-block: the prefix mean, and the prefix weight's
+  // exponent as (token count, rest)
+  float (*lds_al)[NT] = reinterpret_cast<float (*)[NT]>(lds);
+  float (*lds_pq)[NT] = reinterpret_cast<float (*)[NT]>(lds + SB * NT);
+  float (*lds_pm)[NT] = reinterpret_cast<float (*)[NT]>(lds + 2 * SB * NT);
   const int tid = threadIdx.x;
   const int g = ln.g;
   const long long T = p.T;
@@ -583,10 +657,10 @@ __device__ __forceinline__ bool row_body(const RowParams& p, const RowParams* ar
 
   // ---- phase A: lane sums (forward anchored at its last slot, backward at its first) and, per
   //      sub-block, the backward sum of everything after it inside the lane ----
-  Agg af, ab;
+  A af, ab;
   float kmax = kNegInf;
   float capF[WIDE ? 1 : NSB], capG[WIDE ? 1 : NSB];  // fast form: anchored at (q + 1) * SB
-  Agg cap[WIDE ? NSB : 1];                           // wide form
+  Sum cap[WIDE ? NSB : 1];                           // wide form
   if constexpr (!WIDE) {
     // Each sub-block's terms are formed against its own largest key mq (k log2 e), as
     // 2^{k log2 e - mq - span} <= 1, and the running forward sum is rescaled when a larger key
@@ -649,30 +723,29 @@ __device__ __forceinline__ bool row_body(const RowParams& p, const RowParams* ar
     // the lane sums and the caps are against 2^{kmax + span}
     const float m_agg = kmax == kNegInf ? kEmptyM : kmax + span;
     af = Agg{m_agg, fF, fG};
-    ab = CAUSAL ? row_empty() : Agg{m_agg, cF, cG};
+    ab = CAUSAL ? agg_none() : Agg{m_agg, cF, cG};
   } else {
 #pragma unroll
     for (int q = 0; q < NSB; ++q) kv.prepare(q);
-    // Wide range: one decay step at a time, each sum against its own running maximum (an empty
-    // slot, k = -inf, adds nothing).
-    af = agg_empty();
+    // Wide range: one token at a time, each sum against its own running maximum; moving a sum
+    // one token on only changes its token count (an empty slot, k = -inf, adds nothing).
+    af = sum_empty();
 #pragma unroll
-    for (int i = 0; i < L; ++i)
-      af = agg_add(agg_shift(af, 1.f, D), Agg{kv.k(i) * kLog2e, kv.v(i), 1.f});
-    ab = agg_empty();
+    for (int i = 0; i < L; ++i) af = sum_add(sum_shift(af, 1.f), Sum{0.f, kv.k(i) * kLog2e, kv.v(i), 1.f}, D);
+    ab = sum_empty();
     if constexpr (!CAUSAL) {
-      Agg bs[NSB];
+      Sum bs[NSB];
 #pragma unroll
       for (int q = 0; q < NSB; ++q) {
-        bs[q] = agg_empty();
+        bs[q] = sum_empty();
 #pragma unroll
         for (int i = (q + 1) * SB - 1; i >= q * SB; --i)
-          bs[q] = agg_add(agg_shift(bs[q], 1.f, D), Agg{kv.k(i) * kLog2e, kv.v(i), 1.f});
+          bs[q] = sum_add(sum_shift(bs[q], 1.f), Sum{0.f, kv.k(i) * kLog2e, kv.v(i), 1.f}, D);
       }
 #pragma unroll
       for (int q = NSB - 1; q >= 0; --q) {
         cap[q] = ab;
-        ab = agg_add(bs[q], agg_shift(ab, static_cast<float>(SB), D));
+        ab = sum_add(bs[q], sum_shift(ab, static_cast<float>(SB)), D);
       }
     }
   }
@@ -691,33 +764,25 @@ __device__ __forceinline__ bool row_body(const RowParams& p, const RowParams* ar
   //      exchange) run on lane shuffles without barriers. Carries go back the same way. ----
   constexpr int PAD = kRowPad<TILE, NT>;  // row pitch of the group-major buffers
   constexpr int RS = GROUPS * PAD;      // floats per quantity
-  float* red = lds;                     // [6][RS] lane sums (inside the sweep buffer)
-  float* xy = lds + kRowSweepFloats<NT>;  // [6][RS] carries (outside it: read during the sweeps)
-  float* dch = xy + 6 * RS;             // [TILE] D of each channel
+  float* red = lds;                     // [8][RS] lane sums (inside the sweep buffer)
+  float* xy = lds + kRowSweepFloats<NT>;  // [8][RS] carries (outside it: read during the sweeps)
+  float* dch = xy + 8 * RS;             // [TILE] D of each channel
   const int wi = g * PAD + ln.c;
-  if constexpr (WIDE) {  // the wide sums mark an empty aggregate with -inf
-    af.m = fmaxf(af.m, kEmptyM);
-    ab.m = fmaxf(ab.m, kEmptyM);
-  }
-  red[0 * RS + wi] = af.m;
-  red[1 * RS + wi] = af.F;
-  red[2 * RS + wi] = af.G;
-  red[3 * RS + wi] = ab.m;
-  red[4 * RS + wi] = ab.F;
-  red[5 * RS + wi] = ab.G;
+  acc_put(red, RS, wi, af);
+  acc_put(red + 4 * RS, RS, wi, ab);
   if (g == 0) dch[ln.c] = D;
   __syncthreads();
   const int tg = tid % GROUPS, tc = tid / GROUPS;
   const int ti = tg * PAD + tc;
   const float Dt = dch[tc];
-  Agg f{red[0 * RS + ti], red[1 * RS + ti], red[2 * RS + ti]};
-  Agg bk{red[3 * RS + ti], red[4 * RS + ti], red[5 * RS + ti]};
+  A f = acc_get<A>(red, RS, ti);
+  A bk = acc_get<A>(red + 4 * RS, RS, ti);
   group_scan<GROUPS, L, !CAUSAL>(f, bk, tg, Dt);
   // exclusive carries: forward sum of the earlier groups (anchored just before the group's first
   // token), backward sum of the later groups (anchored just after its last slot)
-  Agg X = agg_from_below<GROUPS, 1>(f), Y = agg_from_above<GROUPS, 1>(bk);
-  if (tg == 0) X = row_empty();
-  if (CAUSAL || tg == GROUPS - 1) Y = row_empty();
+  A X = acc_from_below<GROUPS, 1>(f), Y = acc_from_above<GROUPS, 1>(bk);
+  if (tg == 0) X = acc_empty<A>();
+  if (CAUSAL || tg == GROUPS - 1) Y = acc_empty<A>();
   bool timed_out = false;  // fast single pass: a peer's sums did not arrive in time
   if (p.n_chunks > 1) {
     // ---- the other chunks of the row ----
@@ -733,21 +798,21 @@ __device__ __forceinline__ bool row_body(const RowParams& p, const RowParams* ar
     if constexpr (MODE == kOutPass) {
       // the chunk's exclusive carries (row_carry_kernel): forward anchored just before the
       // chunk's first token, backward just after its last slot
-      Agg pf = row_empty(), pb = row_empty();
+      A pf = acc_empty<A>(), pb = acc_empty<A>();
       if (tg == 0) {
-        pf = slot_unpack(p.carries[row_base + (chunk * 2 + kFwd) * TILE + tc]);
-        if (!CAUSAL) pb = slot_unpack(p.carries[row_base + (chunk * 2 + kBwd) * TILE + tc]);
+        pf = acc_unpack<A>(p.carries[row_base + (chunk * 2 + kFwd) * TILE + tc], Dt);
+        if (!CAUSAL) pb = acc_unpack<A>(p.carries[row_base + (chunk * 2 + kBwd) * TILE + tc], Dt);
       }
-      pf = agg_from_first<GROUPS>(pf);
-      X = agg_add_f(agg_shift(pf, static_cast<float>(tg * L), Dt), X);
+      pf = acc_from_first<GROUPS>(pf);
+      X = acc_add(acc_shift(pf, static_cast<float>(tg * L), Dt), X, Dt);
       if constexpr (!CAUSAL) {
-        pb = agg_from_first<GROUPS>(pb);
-        Y = agg_add_f(Y, agg_shift(pb, static_cast<float>((GROUPS - 1 - tg) * L), Dt));
+        pb = acc_from_first<GROUPS>(pb);
+        Y = acc_add(Y, acc_shift(pb, static_cast<float>((GROUPS - 1 - tg) * L), Dt), Dt);
       }
     } else {
     unsigned epoch = 0;
-    unsigned long long* rs = p.slots + row_base * 2;
-    auto slot = [&](int ck, int dir) { return rs + (static_cast<size_t>(ck * 2 + dir) * TILE + tc) * 2; };
+    unsigned long long* rs = p.slots + row_base * kSlotWords;
+    auto slot = [&](int ck, int dir) { return rs + (static_cast<size_t>(ck * 2 + dir) * TILE + tc) * kSlotWords; };
     if constexpr (MODE == kSinglePass) {
       epoch = __builtin_amdgcn_readfirstlane(*sh_epoch);  // set before the first barrier
       // the chunk's own sums, anchored as the totals above
@@ -760,7 +825,7 @@ __device__ __forceinline__ bool row_body(const RowParams& p, const RowParams* ar
     // nch-1. Lane tg folds entries tg, tg + GROUPS, ... in order; the lanes' partials are then
     // folded in a fixed tree, so the result does not depend on arrival order.
     const int nf = chunk, ne = CAUSAL ? chunk : nch - 1;
-    Agg pf = row_empty(), pb = row_empty();
+    A pf = acc_empty<A>(), pb = acc_empty<A>();
     bool recomputed = false;
     // a poll limit of 0 recomputes every peer's sums without polling
     const bool poll = p.spin_limit != 0;
@@ -768,12 +833,12 @@ __device__ __forceinline__ bool row_body(const RowParams& p, const RowParams* ar
     // with several entries pays one round trip, not one per entry.
     constexpr int EB = GROUPS >= 8 ? 1 : 8 / GROUPS;
     for (int e0 = tg; e0 < ne; e0 += EB * GROUPS) {
-      unsigned long long wv[EB][2];
+      unsigned long long wv[EB][kSlotUsed<A>];
       if (poll) {
 #pragma unroll
         for (int j = 0; j < EB; ++j) {
           const int e = e0 + j * GROUPS;
-          if (e < ne) slot_load(slot(e < nf ? e : e + 1, e < nf ? kFwd : kBwd), wv[j]);
+          if (e < ne) slot_load<A>(slot(e < nf ? e : e + 1, e < nf ? kFwd : kBwd), wv[j]);
         }
       }
 #pragma unroll
@@ -785,37 +850,37 @@ __device__ __forceinline__ bool row_body(const RowParams& p, const RowParams* ar
         // distance from the entry's anchor to this chunk's carry anchor (chunks before this one
         // are full, so slot positions are token positions)
         const float dist = static_cast<float>(fwd ? (chunk - 1 - ck) : (ck - chunk - 1)) * CT;
-        Agg a;
+        A a;
         {
           const unsigned long long* sp = slot(ck, fwd ? kFwd : kBwd);
           bool ready = false;
           if (poll) {
-            ready = slot_ready(wv[j], epoch);
+            ready = slot_ready<A>(wv[j], epoch);
             if (!ready && GATED) {
               // one poll at a time: the gated kernel holds its first gate inputs in flight here,
               // and a second poll's registers cost it spills and waits
               for (unsigned spins = 0; spins < p.spin_limit && !ready; ++spins) {
                 __builtin_amdgcn_s_sleep(2);
-                slot_load(sp, wv[j]);
-                ready = slot_ready(wv[j], epoch);
+                slot_load<A>(sp, wv[j]);
+                ready = slot_ready<A>(wv[j], epoch);
               }
             } else if (!ready) {
               // Two polls in flight, issued a short sleep apart: a slot published just after one
               // poll was served is seen by the next one instead of a full round trip later.
-              unsigned long long w2[2];
-              slot_load(sp, w2);
+              unsigned long long w2[kSlotUsed<A>];
+              slot_load<A>(sp, w2);
               for (unsigned spins = 0; spins < p.spin_limit; spins += 2) {
                 __builtin_amdgcn_s_sleep(2);
-                slot_load(sp, wv[j]);
-                if (slot_ready(w2, epoch)) {  // the older poll
-                  wv[j][0] = w2[0];
-                  wv[j][1] = w2[1];
+                slot_load<A>(sp, wv[j]);
+                if (slot_ready<A>(w2, epoch)) {  // the older poll
+#pragma unroll
+                  for (int x = 0; x < kSlotUsed<A>; ++x) wv[j][x] = w2[x];
                   ready = true;
                   break;
                 }
                 __builtin_amdgcn_s_sleep(2);
-                slot_load(sp, w2);
-                if (slot_ready(wv[j], epoch)) {
+                slot_load<A>(sp, w2);
+                if (slot_ready<A>(wv[j], epoch)) {
                   ready = true;
                   break;
                 }
@@ -823,44 +888,39 @@ __device__ __forceinline__ bool row_body(const RowParams& p, const RowParams* ar
             }
           }
           if (ready) {
-            a = slot_value(wv[j]);
-            a.m = fmaxf(a.m, kEmptyM);
+            a = slot_value<A>(wv[j]);
           } else if constexpr (WIDE) {
             // the peer has not published in time (it may not be resident): its sums from k, v
             a = row_recompute<DT, CT, FUSED>(args, ln.b, ln.ch - ln.c + tc, ck, fwd, Dt);
             recomputed = true;
           } else {
             timed_out = true;
-            a = row_empty();
+            a = acc_empty<A>();
           }
         }
-        a = agg_shift(a, dist, Dt);
+        a = acc_shift(a, dist, Dt);
         if (fwd)
-          pf = agg_add_f(pf, a);
+          pf = acc_add(pf, a, Dt);
         else
-          pb = agg_add_f(pb, a);
+          pb = acc_add(pb, a, Dt);
       }
     }
     if constexpr (MODE == kSinglePass && WIDE) {
       if (recomputed)
         __hip_atomic_fetch_or(&p.ctr->fault, kFaultSpin, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    group_fold<GROUPS, !CAUSAL>(pf, pb, tg);
+    group_fold<GROUPS, !CAUSAL>(pf, pb, tg, Dt);
     // pf (from the first lane of the channel) is anchored just before the chunk, pb just after it
-    pf = agg_from_first<GROUPS>(pf);
-    X = agg_add_f(agg_shift(pf, static_cast<float>(tg * L), Dt), X);
+    pf = acc_from_first<GROUPS>(pf);
+    X = acc_add(acc_shift(pf, static_cast<float>(tg * L), Dt), X, Dt);
     if constexpr (!CAUSAL) {
-      pb = agg_from_first<GROUPS>(pb);
-      Y = agg_add_f(Y, agg_shift(pb, static_cast<float>((GROUPS - 1 - tg) * L), Dt));
+      pb = acc_from_first<GROUPS>(pb);
+      Y = acc_add(Y, acc_shift(pb, static_cast<float>((GROUPS - 1 - tg) * L), Dt), Dt);
     }
     }
   }
-  xy[0 * RS + ti] = X.m;
-  xy[1 * RS + ti] = X.F;
-  xy[2 * RS + ti] = X.G;
-  xy[3 * RS + ti] = Y.m;
-  xy[4 * RS + ti] = Y.F;
-  xy[5 * RS + ti] = Y.G;
+  acc_put(xy, RS, ti, X);
+  acc_put(xy + 4 * RS, RS, ti, Y);
   // past this barrier the sum buffer becomes the (alpha, beta) buffer; the fast form of a single
   // pass gives up there as a workgroup if any wait ran out (the wide form recomputes what is
   // missing), having stored nothing
@@ -869,8 +929,8 @@ __device__ __forceinline__ bool row_body(const RowParams& p, const RowParams* ar
   } else {
     __syncthreads();
   }
-  X = Agg{xy[0 * RS + wi], xy[1 * RS + wi], xy[2 * RS + wi]};
-  Y = Agg{xy[3 * RS + wi], xy[4 * RS + wi], xy[5 * RS + wi]};
+  X = acc_get<A>(xy, RS, wi);
+  Y = acc_get<A>(xy + 4 * RS, RS, wi);
   // every wavefront is past its last read of the epoch and of the slots
   if (MODE == kSinglePass && p.n_chunks > 1 && tid == 0) row_retire(p);
   kv.fence();
@@ -891,16 +951,29 @@ __device__ __forceinline__ bool row_body(const RowParams& p, const RowParams* ar
     const float sig = fast_exp2(kmax - top);  // 2^{kmax + span - M}: the caps' scale against M
     const float sx = fast_exp2(X.m - M), sy = fast_exp2(Y.m - M);
     const float eU = ln.eU;
-    float A = X.F * sx, Cs = X.G * sx;
-    const float YF = Y.F * sy, YG = Y.G * sy;
-    if constexpr (CAUSAL) {  // Eq. (7) with b = d = 0, straight out of the forward sweep
+    if constexpr (CAUSAL) {
+      // Eq. (7) with b = d = 0, straight out of the forward sweep. Only earlier tokens count
+      // here, so one lane-wide reference would let a row's first tokens, with keys far below a
+      // later one, underflow to 0 / 0. The prefix's numerator and denominator are kept instead
+      // against a running reference 2^{r}: they start as (prefix mean, 1) with r the log2 of the
+      // prefix weight at the lane's start, and r rises to each larger key as it arrives. The
+      // largest term the prefix ever held is 1 and it decays by at most kFastRange binary orders
+      // across the lane, so the denominator stays a normal number.
+      const bool any = X.m > kEmptyM && X.G > 0.f;
+      float r = any ? X.m + fast_log2(X.G) : kEmptyM;
+      float A = any ? X.F * fast_rcp(X.G) : 0.f, Cs = any ? 1.f : 0.f;
 #pragma unroll
       for (int t = 0; t < L; ++t) {
         const float kf = kv.k(t), vf = kv.v(t);
-        const float pi = fast_exp2(fmaf(kf, kLog2e, -M));
-        const float al = fmaf(-Cs, vf, A);
-        const float be = fmaf(pi, eU, Cs);  // >= the token's own term, a normal number
-        const float y = fmaf(al, fast_rcp(be), vf);
+        const float kl = kf * kLog2e;
+        const float nr = fmaxf(r, kl);
+        const float sc = fast_exp2(r - nr);
+        A *= sc;
+        Cs *= sc;
+        r = nr;
+        const float pi = fast_exp2(kl - r);
+        const float pu = pi * eU;
+        const float y = fmaf(pu, vf, A) * fast_rcp(pu + Cs);
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), orr, out0 + t * row_bytes, 0,
                                               kStream);
         A = fmaf(A, lam, pi * vf);
@@ -908,6 +981,8 @@ __device__ __forceinline__ bool row_body(const RowParams& p, const RowParams* ar
       }
       return true;
     }
+    float A = X.F * sx, Cs = X.G * sx;
+    const float YF = Y.F * sy, YG = Y.G * sy;
 #pragma unroll
     for (int q = 0; q < NSB; ++q) {
       float ph[SB], pv[SB];  // the sub-block's terms and terms times v, kept for the backward sweep
@@ -958,22 +1033,24 @@ __device__ __forceinline__ bool row_body(const RowParams& p, const RowParams* ar
     }
   } else {
     const float U = ln.U;
-    Agg xs = X;
+    Sum xs = X;
     if constexpr (CAUSAL) {
 #pragma unroll
       for (int t = 0; t < L; ++t) {
         const float kf = kv.k(t), vf = kv.v(t);
-        const bool any = xs.m != kNegInf && xs.G > 0.f;
-        const float be = any ? xs.m + fast_log2(xs.G) : kNegInf;  // log2 of the prefix weight
-        const float al = any ? xs.F * fast_rcp(xs.G) - vf : 0.f;  // prefix mean minus v
+        const bool any = xs.m > kEmptyM && xs.G > 0.f;
         const float kl = kf * kLog2e;
         const float ks = kl + U;
-        const float Mt = fmaxf(be, ks);
-        const float sa = fast_exp2(be - Mt), e = fast_exp2(ks - Mt);
-        const float y = fmaf(al * sa, fast_rcp(sa + e), vf);
+        // log2 of the prefix weight over the token's own (bonus) weight
+        const float dp = any ? sum_rel(xs.q, xs.m + fast_log2(xs.G), 0.f, ks, D) : kNegInf;
+        const float mp = any ? xs.F * fast_rcp(xs.G) : 0.f;  // prefix mean
+        const float sa = fast_exp2(fminf(dp, 0.f)), e = fast_exp2(fminf(-dp, 0.f));
+        // the weighted mean itself (not v plus a correction), so the rounding error scales with
+        // the magnitudes the mean is formed from, not with |v| of a token of negligible weight
+        const float y = fmaf(mp, sa, e * vf) * fast_rcp(sa + e);
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), orr, out0 + t * row_bytes, 0,
                                               kStream);
-        xs = agg_add(agg_shift(xs, 1.f, D), Agg{kl, vf, 1.f});
+        xs = sum_add(sum_shift(xs, 1.f), Sum{0.f, kl, vf, 1.f}, D);
       }
       return true;
     }
@@ -983,13 +1060,13 @@ __device__ __forceinline__ bool row_body(const RowParams& p, const RowParams* ar
       for (int i = 0; i < SB; ++i) {
         const int t = q * SB + i;
         const float kf = kv.k(t), vf = kv.v(t);
-        const bool any = xs.m != kNegInf && xs.G > 0.f;
-        const float be = any ? xs.m + fast_log2(xs.G) : kNegInf;
-        const float al = any ? xs.F * fast_rcp(xs.G) - vf : 0.f;
-        lds_ab[i][tid] = make_float2(al, be);
-        xs = agg_add(agg_shift(xs, 1.f, D), Agg{kf * kLog2e, vf, 1.f});
+        const bool any = xs.m > kEmptyM && xs.G > 0.f;
+        lds_al[i][tid] = any ? xs.F * fast_rcp(xs.G) : 0.f;  // prefix mean
+        lds_pq[i][tid] = xs.q;
+        lds_pm[i][tid] = any ? xs.m + fast_log2(xs.G) : kEmptyM;  // log2 of the prefix weight
+        xs = sum_add(sum_shift(xs, 1.f), Sum{0.f, kf * kLog2e, vf, 1.f}, D);
       }
-      Agg ys = agg_add(cap[q], agg_shift(Y, static_cast<float>(L - (q + 1) * SB), D));
+      Sum ys = sum_add(cap[q], sum_shift(Y, static_cast<float>(L - (q + 1) * SB)), D);
       uint32_t r_cur[GATED ? SB : 1];
       if constexpr (GATED) {
         if (q == 0) {
@@ -1003,24 +1080,37 @@ __device__ __forceinline__ bool row_body(const RowParams& p, const RowParams* ar
       for (int i = SB - 1; i >= 0; --i) {
         const int t = q * SB + i;
         const float kf = kv.k(t), vf = kv.v(t);
-        const float2 ab2 = lds_ab[i][tid];
+        const float al = lds_al[i][tid], pq = lds_pq[i][tid], pm = lds_pm[i][tid];
         const float kl = kf * kLog2e;
         const float ks = kl + U;
-        const float Mt = fmaxf(fmaxf(ab2.y, ys.m), ks);
-        const float sa = fast_exp2(ab2.y - Mt), sb = fast_exp2(ys.m - Mt);
-        const float e = fast_exp2(ks - Mt);
-        const float num = ab2.x * sa + fmaf(-ys.G, vf, ys.F) * sb;
+        // The prefix, suffix and own (bonus) weights against the largest of them. Each pair is
+        // compared through its exact difference of token counts, so two far contributions of
+        // nearly equal weight (the two ends of a row with strong growth) keep their ratio.
+        float rq = 0.f, rm = ks;  // the largest so far
+        if (sum_rel(pq, pm, rq, rm, D) > 0.f) {
+          rq = pq;
+          rm = pm;
+        }
+        if (sum_rel(ys.q, ys.m, rq, rm, D) > 0.f) {
+          rq = ys.q;
+          rm = ys.m;
+        }
+        const float sa = fast_exp2(sum_rel(pq, pm, rq, rm, D)), sb = fast_exp2(sum_rel(ys.q, ys.m, rq, rm, D));
+        const float e = fast_exp2(sum_rel(0.f, ks, rq, rm, D));
+        // the weighted mean itself: its rounding error scales with the magnitudes it is formed
+        // from (den >= 1: one of the three weights is the largest, 1)
+        const float num = fmaf(al, sa, fmaf(ys.F, sb, e * vf));
         const float den = sa + ys.G * sb + e;
         float y;
         if constexpr (GATED) {
           const float er = fast_exp2(-kLog2e * gate.value(r_cur[i]));
-          y = fmaf(vf, den, num) * fast_rcp(den * (1.f + er));
+          y = num * fast_rcp(den * (1.f + er));
         } else {
-          y = fmaf(num, fast_rcp(den), vf);
+          y = num * fast_rcp(den);
         }
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), orr, out0 + t * row_bytes, 0,
                                               kStream);
-        ys = agg_add(agg_shift(ys, 1.f, D), Agg{kl, vf, 1.f});
+        ys = sum_add(sum_shift(ys, 1.f), Sum{0.f, kl, vf, 1.f}, D);
       }
     }
   }
@@ -1033,15 +1123,14 @@ __device__ __forceinline__ bool row_body(const RowParams& p, const RowParams* ar
 // the backward totals of chunks j+1 .. n-1 (anchored just after its last slot, token (j+1) CT).
 // One wavefront per (row, channel): lane s holds segment s of `per` consecutive chunks (64
 // segments), forms the segment's sums, and the lanes scan them with shuffles; each lane then
-// writes its chunks' carries. Every term and partial sum is moved to its anchor by an exponent
-// shift of its exact distance (one product, never stepped chunk by chunk), and the order of the
-// additions is fixed, so the carries are bitwise reproducible.
+// writes its chunks' carries. Moving a sum between anchors changes only its token count, and the
+// order of the additions is fixed, so the carries are bitwise reproducible.
 // ---------------------------------------------------------------------------------------------
 constexpr int kCarryChans = 16;  // wavefronts (channels) per workgroup
 
 struct CarryParams {
-  const float2* sums;
-  float2* carries;
+  const float4* sums;
+  float4* carries;
   const float* w;
   long long T;
   int C, n_tiles, n_chunks, CT, causal;
@@ -1050,6 +1139,13 @@ struct CarryParams {
 // Chunks of a lane's segment held in registers (rows of up to 64 * 8 chunks); beyond that the
 // totals are read from memory as they are needed.
 constexpr int kCarryRegs = 8;
+
+__device__ __forceinline__ Sum sum_shfl_up(Sum a, int d) {
+  return Sum{__shfl_up(a.q, d), __shfl_up(a.m, d), __shfl_up(a.F, d), __shfl_up(a.G, d)};
+}
+__device__ __forceinline__ Sum sum_shfl_down(Sum a, int d) {
+  return Sum{__shfl_down(a.q, d), __shfl_down(a.m, d), __shfl_down(a.F, d), __shfl_down(a.G, d)};
+}
 
 template <int TILE>
 __global__ void __launch_bounds__(64 * kCarryChans) row_carry_kernel(CarryParams p) {
@@ -1065,86 +1161,85 @@ __global__ void __launch_bounds__(64 * kCarryChans) row_carry_kernel(CarryParams
   const float ct = static_cast<float>(p.CT);
   const size_t base = static_cast<size_t>(row) * n * 2 * TILE + tc;
   auto at = [&](int j, int dir) { return base + static_cast<size_t>(j * 2 + dir) * TILE; };
-  const float2* __restrict__ sums = p.sums;
-  float2* __restrict__ carries = p.carries;
+  const float4* __restrict__ sums = p.sums;
+  float4* __restrict__ carries = p.carries;
   // every load of the lane is issued before any result is used (one round trip)
   const bool inreg = per <= kCarryRegs;
-  float2 tf[kCarryRegs], tb[kCarryRegs];
+  float4 tf[kCarryRegs], tb[kCarryRegs];
   if (inreg) {
 #pragma unroll
     for (int i = 0; i < kCarryRegs; ++i) {
       if (c0 + i < c1) {
         tf[i] = sums[at(c0 + i, kFwd)];
-        tb[i] = p.causal ? make_float2(kNegInf, 0.f) : sums[at(c0 + i, kBwd)];
+        tb[i] = p.causal ? make_float4(0.f, kNegInf, 0.f, 0.f) : sums[at(c0 + i, kBwd)];
       }
     }
   }
   const float D = ch < p.C ? (p.w[ch] / static_cast<float>(p.T)) * kLog2e : 0.f;
   // segment sums: forward anchored at the segment's last slot, (lane + 1) per CT - 1, and
   // backward at its first token, lane per CT (a short or empty last segment keeps those anchors)
-  Agg f = row_empty(), b = row_empty();
+  Sum f = sum_empty(), b = sum_empty();
   const int cf = lane * per + per - 1;  // chunk whose last slot is the forward anchor
   if (inreg) {
 #pragma unroll
     for (int i = 0; i < kCarryRegs; ++i) {
       const int j = c0 + i;
       if (j < c1) {
-        f = agg_add_f(f, agg_shift(slot_unpack(tf[i]), static_cast<float>(cf - j) * ct, D));
-        b = agg_add_f(b, agg_shift(slot_unpack(tb[i]), static_cast<float>(i) * ct, D));
+        f = sum_add(f, sum_shift(slot_unpack(tf[i]), static_cast<float>(cf - j) * ct), D);
+        b = sum_add(b, sum_shift(slot_unpack(tb[i]), static_cast<float>(i) * ct), D);
       }
     }
   } else {
     for (int j = c0; j < c1; ++j) {
-      f = agg_add_f(f, agg_shift(slot_unpack(sums[at(j, kFwd)]), static_cast<float>(cf - j) * ct, D));
-      if (!p.causal) b = agg_add_f(b, agg_shift(slot_unpack(sums[at(j, kBwd)]), static_cast<float>(j - c0) * ct, D));
+      f = sum_add(f, sum_shift(slot_unpack(sums[at(j, kFwd)]), static_cast<float>(cf - j) * ct), D);
+      if (!p.causal) b = sum_add(b, sum_shift(slot_unpack(sums[at(j, kBwd)]), static_cast<float>(j - c0) * ct), D);
     }
   }
   // inclusive scans over the segments: forward over lanes 0 .. lane, backward over lane .. 63
 #pragma unroll
   for (int d = 1; d < 64; d *= 2) {
-    const Agg pf{__shfl_up(f.m, d), __shfl_up(f.F, d), __shfl_up(f.G, d)};
-    if (lane >= d) f = agg_add_f(agg_shift(pf, static_cast<float>(d) * seg, D), f);
-    const Agg pb{__shfl_down(b.m, d), __shfl_down(b.F, d), __shfl_down(b.G, d)};
-    if (lane + d < 64) b = agg_add_f(b, agg_shift(pb, static_cast<float>(d) * seg, D));
+    const Sum pf = sum_shfl_up(f, d);
+    if (lane >= d) f = sum_add(sum_shift(pf, static_cast<float>(d) * seg), f, D);
+    const Sum pb = sum_shfl_down(b, d);
+    if (lane + d < 64) b = sum_add(b, sum_shift(pb, static_cast<float>(d) * seg), D);
   }
   // entering sums: the earlier segments' forward sum, anchored at c0 CT - 1, and the later
   // segments' backward sum, anchored at (lane + 1) per CT
-  Agg X{__shfl_up(f.m, 1), __shfl_up(f.F, 1), __shfl_up(f.G, 1)};
-  Agg Y{__shfl_down(b.m, 1), __shfl_down(b.F, 1), __shfl_down(b.G, 1)};
-  if (lane == 0) X = row_empty();
-  if (p.causal || lane == 63) Y = row_empty();
+  Sum X = sum_shfl_up(f, 1), Y = sum_shfl_down(b, 1);
+  if (lane == 0) X = sum_empty();
+  if (p.causal || lane == 63) Y = sum_empty();
   const int ce = lane * per + per;  // first chunk after the segment (the backward anchor's chunk)
-  // each chunk's carries: the entering sum plus the segment's chunks on the near side, each
-  // moved once from its anchor to the chunk's
+  // each chunk's carries: the entering sum plus the segment's chunks on the near side, moved to
+  // the chunk's own anchor
   if (inreg) {
-    Agg x = X;
+    Sum x = X;
 #pragma unroll
     for (int i = 0; i < kCarryRegs; ++i) {
       if (c0 + i < c1) {
-        carries[at(c0 + i, kFwd)] = slot_pack(agg_shift(x, static_cast<float>(i) * ct, D));
-        x = agg_add_f(x, agg_shift(slot_unpack(tf[i]), -static_cast<float>(i + 1) * ct, D));
+        carries[at(c0 + i, kFwd)] = slot_pack(sum_shift(x, static_cast<float>(i) * ct));
+        x = sum_add(x, sum_shift(slot_unpack(tf[i]), -static_cast<float>(i + 1) * ct), D);
       }
     }
     if (!p.causal) {
-      Agg y = Y;
+      Sum y = Y;
 #pragma unroll
       for (int i = kCarryRegs - 1; i >= 0; --i) {
         const int j = c0 + i;
         if (j < c1) {
-          carries[at(j, kBwd)] = slot_pack(agg_shift(y, static_cast<float>(ce - 1 - j) * ct, D));
-          y = agg_add_f(y, agg_shift(slot_unpack(tb[i]), -static_cast<float>(ce - j) * ct, D));
+          carries[at(j, kBwd)] = slot_pack(sum_shift(y, static_cast<float>(ce - 1 - j) * ct));
+          y = sum_add(y, sum_shift(slot_unpack(tb[i]), -static_cast<float>(ce - j) * ct), D);
         }
       }
     }
   } else {
     for (int j = c0; j < c1; ++j) {
-      carries[at(j, kFwd)] = slot_pack(agg_shift(X, static_cast<float>(j - c0) * ct, D));
-      X = agg_add_f(X, agg_shift(slot_unpack(sums[at(j, kFwd)]), -static_cast<float>(j + 1 - c0) * ct, D));
+      carries[at(j, kFwd)] = slot_pack(sum_shift(X, static_cast<float>(j - c0) * ct));
+      X = sum_add(X, sum_shift(slot_unpack(sums[at(j, kFwd)]), -static_cast<float>(j + 1 - c0) * ct), D);
     }
     if (!p.causal) {
       for (int j = c1 - 1; j >= c0; --j) {
-        carries[at(j, kBwd)] = slot_pack(agg_shift(Y, static_cast<float>(ce - 1 - j) * ct, D));
-        Y = agg_add_f(Y, agg_shift(slot_unpack(sums[at(j, kBwd)]), -static_cast<float>(ce - j) * ct, D));
+        carries[at(j, kBwd)] = slot_pack(sum_shift(Y, static_cast<float>(ce - 1 - j) * ct));
+        Y = sum_add(Y, sum_shift(slot_unpack(sums[at(j, kBwd)]), -static_cast<float>(ce - j) * ct), D);
       }
     }
   }
@@ -1191,10 +1286,12 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4)))
   if (MODE == kSinglePass && p.n_chunks > 1 && tid == 0)
     sh_epoch = __hip_atomic_load(&p.ctr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
   const RowLane ln = row_lane<TILE, L, NT>(p, unit);
-  // The whole workgroup takes the wide form when any of its channels needs it. Every wavefront
-  // holds all TILE channels, so a wavefront vote is the workgroup's vote.
+  // The whole workgroup takes the wide form when any of its channels needs it: decay or growth
+  // across one lane beyond kFastRange, a bonus beyond kBonusRange, or decay across the row beyond
+  // kExactRange (the sums' exponents then need exact token counts). Every wavefront holds all TILE
+  // channels, so a wavefront vote is the workgroup's vote, and every chunk of a row votes alike.
   const bool wide_lane = fabsf(ln.D) * static_cast<float>(L - 1) > kFastRange || ln.U > kBonusRange ||
-                         ln.U < -kBonusRange;
+                         ln.U < -kBonusRange || fabsf(ln.D) * static_cast<float>(p.T) > kExactRange;
   // the kernel's only argument is p, at the start of the argument segment (the argument segment
   // pointer exists only here, in the kernel: out-of-line functions get it passed down)
   const auto* args = (const RowParams*)(__builtin_amdgcn_kernarg_segment_ptr());

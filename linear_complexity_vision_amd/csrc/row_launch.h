@@ -58,8 +58,8 @@ int launch_two_pass(const BiwkvParams& bp, int64_t B, int dev, void* stream, con
   long long total = 0;
   int rc = row_params<TILE, CT, FUSED>(bp, B, &rp, &total);
   if (rc) return rc;
-  // totals and carries: one (l, mu) float pair each per (chunk, direction, channel)
-  const long long words = total * 2 * TILE * 2;
+  // totals and carries: one (q, l, mu, -) float4 each per (chunk, direction, channel)
+  const long long words = total * 2 * TILE * 4;
   unsigned long long* buf = nullptr;
   if (fixed) {
     if (words > fixed->n_words) return BIWKV_ERR_SCRATCH;
@@ -70,7 +70,7 @@ int launch_two_pass(const BiwkvParams& bp, int64_t B, int dev, void* stream, con
     if (rc) return rc;
     buf = sc->slots;
   }
-  rp.sums = reinterpret_cast<float2*>(buf);
+  rp.sums = reinterpret_cast<float4*>(buf);
   rp.carries = rp.sums + total * 2 * TILE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const dim3 grid(static_cast<unsigned>(total)), block(NT);
@@ -117,8 +117,8 @@ int launch_row(const BiwkvParams& bp, int64_t B, int dev, void* stream, const Fi
   if (opt == 1 || (rp.n_chunks > 1 && total > cap))
     return launch_two_pass<DT, TILE, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream, fixed);
   if (rp.n_chunks > 1) {
-    // single pass: two tagged 64-bit words per (chunk, direction, channel)
-    const long long words = total * 2 * TILE * 2;
+    // single pass: three tagged 64-bit words per (chunk, direction, channel)
+    const long long words = total * 2 * TILE * kSlotWords;
     if (fixed) {
       if (words > fixed->n_words) return BIWKV_ERR_SCRATCH;
       rp.ctr = fixed->ctr;

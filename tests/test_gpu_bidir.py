@@ -124,7 +124,7 @@ def test_fused_bidir_extreme_values(case):
     y = _fused(wl, 1, 0.25)
     assert np.isfinite(y).all()
     y_ref, s_ref = _ref(wl, 1, 0.25, use_sum=True)
-    tol = max(1e-4, 4.0 * float(np.abs(wl.w).max()) * np.log2(np.e) * 2.0 ** -24)
+    tol = 1e-4  # the wide form's exact token counts hold the plain bar at |w| = 1e4
     err = r3(y, y_ref, s_ref)
     print(f"[parity] fused bidir extreme {case}: R3 = {err:.3e} (tol {tol:.1e})", flush=True)
     assert err <= tol

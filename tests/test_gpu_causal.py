@@ -56,8 +56,12 @@ def test_causal_edge_shapes(B, T, C, dtype):
 
 
 @pytest.mark.parametrize("T", [600, 2500])
-@pytest.mark.parametrize("case", ["k_plus_100", "u_100", "w_plus_1e4", "w_minus_1e4", "w_mixed_wide"])
+@pytest.mark.parametrize("case", ["k_plus_100", "u_100", "w_plus_1e4", "w_minus_1e4", "w_mixed_wide",
+                                  "k_row_start_far_below", "u_minus_41", "k_spread_40"])
 def test_causal_extreme_values(case, T):
+    """k_row_start_far_below: the row's first tokens carry keys 100 below the rest, so their
+    outputs are weighted means of terms some 2^-144 below the lane's largest; u_minus_41 keeps the
+    bonus (u log2 e = -59.2) inside the fast form's range."""
     wl = workloads.make_random(98, 1, T, 64, dtype="f32", w_range=5.0, k_std=1.0)
     k, w, u = wl.k.copy(), wl.w.copy(), wl.u.copy()
     if case == "k_plus_100":
@@ -71,14 +75,19 @@ def test_causal_extreme_values(case, T):
     elif case == "w_mixed_wide":
         w[0::3] = -1e4
         w[1::3] = 3e3
+    elif case == "k_row_start_far_below":
+        k[:, :3] -= np.float32(100.0)
+    elif case == "u_minus_41":
+        u[:] = -41.0
+    elif case == "k_spread_40":
+        k *= np.float32(10.0)
     wl.k, wl.w, wl.u = k, w, u
     print(f"[case] biwkv_causal_forward extreme {case} T={T}", flush=True)
     y = _run(wl)
     assert np.isfinite(y).all()
     y_ref, s_ref = oracle.biwkv_causal_sum(f64(k), f64(wl.v), f64(w), f64(u), with_scale=True)
     err = r3(y, y_ref, s_ref)
-    # same fp32 exponent-resolution bound as the bidirectional extreme cases
-    tol = max(1e-4, 4.0 * float(np.abs(w).max()) * np.log2(np.e) * 2.0 ** -24)
+    tol = 1e-4  # the wide form's exact token counts hold the plain bar at |w| = 1e4
     print(f"[parity] causal extreme {case} T={T}: R3 = {err:.3e} (tol {tol:.1e})", flush=True)
     assert err <= tol
 

@@ -86,8 +86,7 @@ def _run(name, wl, r=None):
 
 
 def _tol(wl):
-    # A20: fp32 resolves the largest weight exponent |w| log2(e) to 2^-24 relative
-    return max(1e-4, 4.0 * float(np.abs(wl.w).max()) * np.log2(np.e) * 2.0 ** -24)
+    return 1e-4  # the wide form's exact token counts hold the plain bar for any w
 
 
 # (entry, B, H, W, C, dtype): several chunks per row, ragged last chunk or tile where possible

@@ -76,5 +76,5 @@ def test_gated_wide_form():
     # the summation form: the RNN form's lam^T leaves float64 at |w| = 1e4
     y_ref, s_ref = oracle.biwkv_gated(f64(wl.k), f64(wl.v), f64(r), f64(wl.w), f64(wl.u), with_scale=True,
                                       use_sum=True)
-    tol = max(1e-4, 4.0 * 1e4 * np.log2(np.e) * 2.0 ** -24)
+    tol = 1e-4  # the wide form's exact token counts hold the plain bar at |w| = 1e4
     assert r3(y, y_ref, s_ref) <= tol

@@ -60,7 +60,7 @@ def test_noalloc_two_launch_rows_and_single_chunk_rows():
 
 
 def test_noalloc_refuses_beyond_its_buffer():
-    """B = 32, T = 16384, C = 1024 bf16 needs 32 * 16 * 128 chunks of 2 KiB (128 MiB) in the
+    """B = 32, T = 16384, C = 1024 bf16 needs 32 * 16 * 128 chunks of 4 KiB (256 MiB) in the
     two-pass form: refused before any launch (the pointers are never used)."""
     import torch
 
