@@ -78,6 +78,9 @@ extern "C" {
                                   1: every row takes the two-pass form                         */
 #define BIWKV_OPT_WIDE_INDEX 3 /* 0 (default): Q-Shift gathers use 32-bit index arithmetic below
                                   2^31 items; 1: always the 64-bit form                       */
+#define BIWKV_OPT_XCD_LOCAL 4  /* 1 (default): a one-launch row runs all its chunks on one XCD
+                                  and exchanges their sums through that XCD's L2; 0: plain
+                                  block order, sums through the device-coherent level         */
 
 /*
  * Bi-WKV forward, Eq. (5) of the Vision-RWKV article.

@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     OPT_SPIN_LIMIT,
     OPT_TWO_PASS,
     OPT_WIDE_INDEX,
+    OPT_XCD_LOCAL,
     BiwkvError,
     biwkv_backward,
     biwkv_causal_forward,

@@ -318,6 +318,7 @@ def stream_fault_flags(device=None) -> int:
 OPT_SPIN_LIMIT = 1
 OPT_TWO_PASS = 2
 OPT_WIDE_INDEX = 3
+OPT_XCD_LOCAL = 4
 
 
 def set_option(option: int, value: int) -> int:

@@ -53,6 +53,7 @@ thread_local int t_last_hip_error = 0;
 
 std::map<std::pair<int, void*>, StreamScratch*> g_scratch;
 std::map<std::pair<int, const void*>, int> g_capacity;  // (device, kernel) -> resident workgroups
+std::map<int, int> g_xcds;                                // device -> XCDs
 
 // Grows a zero-filled scratch buffer in stream order: the new buffer is allocated and cleared on
 // `st`, and the outgrown one is freed on `st` behind every launch already queued that uses it.
@@ -119,6 +120,7 @@ std::mutex g_mu;
 std::atomic<unsigned> g_spin_limit{kSpinDefault};
 std::atomic<int> g_two_pass{0};
 std::atomic<int> g_wide_index{0};
+std::atomic<int> g_xcd_local{1};
 
 int hip_fail(hipError_t e) {
   t_last_hip_error = static_cast<int>(e);
@@ -167,6 +169,20 @@ int resident_capacity(int dev, const void* kernel, int block, int* cap) {
   if (e != hipSuccess) return hip_fail(e);
   *cap = per_cu * cus;
   g_capacity[key] = *cap;
+  return BIWKV_OK;
+}
+
+int device_xcds(int dev, int* n) {
+  auto it = g_xcds.find(dev);
+  if (it != g_xcds.end()) {
+    *n = it->second;
+    return BIWKV_OK;
+  }
+  int x = 0;
+  const hipError_t e = hipDeviceGetAttribute(&x, hipDeviceAttributeNumberOfXccs, dev);
+  if (e != hipSuccess) return hip_fail(e);
+  *n = x > 0 ? x : 1;
+  g_xcds[dev] = *n;
   return BIWKV_OK;
 }
 
@@ -648,9 +664,12 @@ int biwkv_set_option(int option, int64_t value, int64_t* previous) {
       return BIWKV_OK;
     }
     case BIWKV_OPT_TWO_PASS:
-    case BIWKV_OPT_WIDE_INDEX: {
+    case BIWKV_OPT_WIDE_INDEX:
+    case BIWKV_OPT_XCD_LOCAL: {
       if (value != 0 && value != 1) return BIWKV_ERR_PARAM;
-      std::atomic<int>& opt = option == BIWKV_OPT_TWO_PASS ? g_two_pass : g_wide_index;
+      std::atomic<int>& opt = option == BIWKV_OPT_TWO_PASS    ? g_two_pass
+                              : option == BIWKV_OPT_WIDE_INDEX ? g_wide_index
+                                                               : g_xcd_local;
       const int old = opt.exchange(static_cast<int>(value));
       if (previous) *previous = old;
       return BIWKV_OK;

@@ -43,10 +43,14 @@ int get_bwd_scratch(int dev, void* stream, long long floats, float** out);
 // Workgroups of `kernel` (with `block` threads) that fit on device `dev` at once. Caller holds g_mu.
 int resident_capacity(int dev, const void* kernel, int block, int* cap);
 
+// XCDs of device `dev` (workgroups are handed to them round robin). Caller holds g_mu.
+int device_xcds(int dev, int* n);
+
 // Options (biwkv_set_option).
 extern std::atomic<unsigned> g_spin_limit;
 extern std::atomic<int> g_two_pass;
 extern std::atomic<int> g_wide_index;
+extern std::atomic<int> g_xcd_local;
 
 // Scratch that the caller provides instead of the per-stream buffers: a counter block followed by
 // `n_words` 64-bit words (the allocation-free entry's static array).

@@ -168,6 +168,9 @@ struct RowParams {
   float4* carries;               // two passes: [row][chunk][dir][TILE] (q, l, mu) exclusive carries
   int H, W, shift, g1, g2, g3, g4;  // Q-Shift (fused entry only)
   int bidir;  // fused: the bidirectional shift along a sparse token sequence (the host sets W = 1)
+  // single pass: rows [0, xcd_rows) run every chunk on one XCD and exchange through its L2
+  // (blocks go to the n_xcd XCDs round robin); 0 keeps the plain order
+  int xcd_rows, n_xcd;
 };
 
 // Counts a workgroup out of a single-pass launch once none of its wavefronts reads the epoch or a
@@ -206,8 +209,19 @@ __device__ __forceinline__ RowLane row_lane(const RowParams& p, unsigned unit) {
   ln.c = tid % TILE;
   ln.g = tid / TILE;
   // integer division runs on the vector unit: read the (uniform) results back into scalars
-  ln.row = __builtin_amdgcn_readfirstlane(unit / static_cast<unsigned>(p.n_chunks));
-  ln.chunk = static_cast<int>(unit) - ln.row * p.n_chunks;
+  const unsigned nc = static_cast<unsigned>(p.n_chunks);
+  if (unit < static_cast<unsigned>(p.xcd_rows) * nc) {
+    // block `unit` runs on XCD unit % n_xcd: XCD x takes rows x, x + n_xcd, ... whole, in order
+    const unsigned nx = static_cast<unsigned>(p.n_xcd);
+    const unsigned s = __builtin_amdgcn_readfirstlane(unit / nx);
+    const unsigned x = unit - s * nx;
+    const unsigned rg = __builtin_amdgcn_readfirstlane(s / nc);
+    ln.row = static_cast<int>(rg * nx + x);
+    ln.chunk = static_cast<int>(s - rg * nc);
+  } else {
+    ln.row = __builtin_amdgcn_readfirstlane(unit / nc);
+    ln.chunk = static_cast<int>(unit) - ln.row * p.n_chunks;
+  }
   const int bi = __builtin_amdgcn_readfirstlane(ln.row / p.n_tiles);
   const int tile = ln.row - bi * p.n_tiles;
   ln.b = bi;
@@ -813,12 +827,31 @@ __device__ __forceinline__ bool row_body(const RowParams& p, const RowParams* ar
     unsigned epoch = 0;
     unsigned long long* rs = p.slots + row_base * kSlotWords;
     auto slot = [&](int ck, int dir) { return rs + (static_cast<size_t>(ck * 2 + dir) * TILE + tc) * kSlotWords; };
+    // rows whose chunks all run on one XCD exchange through its L2 (byte offsets into the slot
+    // array, which a single pass keeps far below 4 GiB)
+    const bool local = ln.row < p.xcd_rows;
+    const long long slot_bytes = static_cast<long long>(p.total) * 2 * TILE * kSlotWords * 8;
+    const __amdgpu_buffer_rsrc_t srs =
+        make_rsrc(p.slots, static_cast<uint32_t>(slot_bytes < 0xFFFFFFFFll ? slot_bytes : 0xFFFFFFFFll));
+    auto soff = [&](const unsigned long long* sp) { return static_cast<uint32_t>((sp - p.slots) * 8); };
+    auto put = [&](unsigned long long* sp, const A& a) {
+      if (local)
+        slot_store_l2(srs, soff(sp), a, epoch);
+      else
+        slot_store(sp, a, epoch);
+    };
+    auto get = [&](const unsigned long long* sp, unsigned long long* w) {
+      if (local)
+        slot_load_l2<A>(srs, soff(sp), w);
+      else
+        slot_load<A>(sp, w);
+    };
     if constexpr (MODE == kSinglePass) {
       epoch = __builtin_amdgcn_readfirstlane(*sh_epoch);  // set before the first barrier
       // the chunk's own sums, anchored as the totals above
       if (!published) {
-        if (tg == GROUPS - 1) slot_store(slot(chunk, kFwd), f, epoch);
-        if (!CAUSAL && tg == 0) slot_store(slot(chunk, kBwd), bk, epoch);
+        if (tg == GROUPS - 1) put(slot(chunk, kFwd), f);
+        if (!CAUSAL && tg == 0) put(slot(chunk, kBwd), bk);
       }
     }
     // Entries: forward sums of chunks 0 .. chunk-1, then backward sums of chunks chunk+1 ..
@@ -838,7 +871,7 @@ __device__ __forceinline__ bool row_body(const RowParams& p, const RowParams* ar
 #pragma unroll
         for (int j = 0; j < EB; ++j) {
           const int e = e0 + j * GROUPS;
-          if (e < ne) slot_load<A>(slot(e < nf ? e : e + 1, e < nf ? kFwd : kBwd), wv[j]);
+          if (e < ne) get(slot(e < nf ? e : e + 1, e < nf ? kFwd : kBwd), wv[j]);
         }
       }
 #pragma unroll
@@ -861,17 +894,17 @@ __device__ __forceinline__ bool row_body(const RowParams& p, const RowParams* ar
               // and a second poll's registers cost it spills and waits
               for (unsigned spins = 0; spins < p.spin_limit && !ready; ++spins) {
                 __builtin_amdgcn_s_sleep(2);
-                slot_load<A>(sp, wv[j]);
+                get(sp, wv[j]);
                 ready = slot_ready<A>(wv[j], epoch);
               }
             } else if (!ready) {
               // Two polls in flight, issued a short sleep apart: a slot published just after one
               // poll was served is seen by the next one instead of a full round trip later.
               unsigned long long w2[kSlotUsed<A>];
-              slot_load<A>(sp, w2);
+              get(sp, w2);
               for (unsigned spins = 0; spins < p.spin_limit; spins += 2) {
                 __builtin_amdgcn_s_sleep(2);
-                slot_load<A>(sp, wv[j]);
+                get(sp, wv[j]);
                 if (slot_ready<A>(w2, epoch)) {  // the older poll
 #pragma unroll
                   for (int x = 0; x < kSlotUsed<A>; ++x) wv[j][x] = w2[x];
@@ -879,7 +912,7 @@ __device__ __forceinline__ bool row_body(const RowParams& p, const RowParams* ar
                   break;
                 }
                 __builtin_amdgcn_s_sleep(2);
-                slot_load<A>(sp, w2);
+                get(sp, w2);
                 if (slot_ready<A>(wv[j], epoch)) {
                   ready = true;
                   break;

@@ -119,6 +119,16 @@ int launch_row(const BiwkvParams& bp, int64_t B, int dev, void* stream, const Fi
   if (rp.n_chunks > 1) {
     // single pass: three tagged 64-bit words per (chunk, direction, channel)
     const long long words = total * 2 * TILE * kSlotWords;
+    if (g_xcd_local.load()) {
+      int nx = 1;
+      rc = device_xcds(dev, &nx);
+      if (rc) return rc;
+      const long long rows = total / rp.n_chunks;
+      if (nx > 1) {
+        rp.n_xcd = nx;
+        rp.xcd_rows = static_cast<int>(rows / nx * nx);
+      }
+    }
     if (fixed) {
       if (words > fixed->n_words) return BIWKV_ERR_SCRATCH;
       rp.ctr = fixed->ctr;

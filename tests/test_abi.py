@@ -122,6 +122,11 @@ def test_options_validate_and_report_previous(L):
         assert prev.value == 0
         assert L.biwkv_set_option(_code(name), 0, ctypes.byref(prev)) == 0
         assert prev.value == 1
+    assert L.biwkv_set_option(_code("BIWKV_OPT_XCD_LOCAL"), 2, None) == bad
+    assert L.biwkv_set_option(_code("BIWKV_OPT_XCD_LOCAL"), 0, ctypes.byref(prev)) == 0
+    assert prev.value == 1
+    assert L.biwkv_set_option(_code("BIWKV_OPT_XCD_LOCAL"), 1, ctypes.byref(prev)) == 0
+    assert prev.value == 0
     with lib.option(lib.OPT_TWO_PASS, 1):
         assert lib.set_option(lib.OPT_TWO_PASS, 1) == 1
     assert lib.set_option(lib.OPT_TWO_PASS, 0) == 0

@@ -2,6 +2,8 @@
 
 * The two-pass form (chunk totals, per-chunk carries, then outputs; OPT_TWO_PASS = 1, which also
   applies to rows of one chunk) against the oracle, and bitwise reproducible.
+* The one-launch exchange through each XCD's L2 (OPT_XCD_LOCAL = 1, the default) against the plain
+  block order, bit for bit.
 * The one-launch exchange with a poll limit of 0 (OPT_SPIN_LIMIT = 0): every workgroup recomputes
   every peer chunk's sums from k and v (the slow path taken when a peer is not resident), for
   every entry point built on the tile kernel; the fault word then reports the slow path.
@@ -156,6 +158,32 @@ def test_recompute_every_peer(name, B, H, W, C, dtype):
     y_ref, s_ref = _oracle(name, wl, r)
     err = r3(y, y_ref, s_ref)
     print(f"[parity] recompute {name} {wl.name}: R3 = {err:.3e}", flush=True)
+    assert err <= 1e-4
+
+
+# rows of several chunks, 11 and 30 of them: the first 8 and 24 run each row on one XCD and
+# exchange through its L2, the rest keep the plain order
+XCD_ROWS = [("biwkv", 1, 1, 2500, 704, "f32"), ("fused", 3, 50, 60, 640, "bf16"), ("causal", 3, 1, 3000, 640, "bf16"),
+            ("gated", 1, 1, 2100, 704, "f32"), ("bidir", 3, 1, 2100, 640, "bf16")]
+
+
+@pytest.mark.parametrize("name,B,H,W,C,dtype", XCD_ROWS)
+def test_xcd_local_exchange_matches_plain_order(name, B, H, W, C, dtype):
+    """The one-launch exchange through each XCD's L2 gives the same bits as the plain block order
+    (the fold order is fixed), and both match the oracle."""
+    L = _lib()
+    wl = _make(name, B, H, W, C, dtype, seed=500 + H * W + C)
+    r = _gate(wl) if name == "gated" else None
+    print(f"[case] XCD-local exchange {name} {wl.name}", flush=True)
+    with L.option(L.OPT_XCD_LOCAL, 1):
+        y1, f1 = _run(name, wl, r)
+    with L.option(L.OPT_XCD_LOCAL, 0):
+        y0, f0 = _run(name, wl, r)
+    assert f1 == 0 and f0 == 0
+    np.testing.assert_array_equal(y1, y0)
+    y_ref, s_ref = _oracle(name, wl, r)
+    err = r3(y1, y_ref, s_ref)
+    print(f"[parity] XCD-local exchange {name} {wl.name}: R3 = {err:.3e}", flush=True)
     assert err <= 1e-4
 
 
