@@ -20,8 +20,12 @@ LIB = os.path.join(PKG, "libbiwkv.so")
 CEILING_SRC = os.path.join(CSRC, "hbm_ceiling.hip")
 CEILING_LIB = os.path.join(PKG, "libhbmceiling.so")
 ARCH = "gfx950"
+# -amdgpu-atomic-optimizer-strategy=None: the library's atomics are single-lane counters; the
+# optimizer's wave-aggregated form reads an atomic's result right after issuing it, which would
+# make the tile kernel's retirement count wait a full round trip before its sweeps.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
 
 
 def _hipcc() -> str:

@@ -175,10 +175,15 @@ struct RowParams {
 
 // Counts a workgroup out of a single-pass launch once none of its wavefronts reads the epoch or a
 // slot again; the last one resets the count and moves the epoch on for the next launch on the
-// stream. Nothing else waits for it, so only the calling wavefront sees the round trip.
-__device__ __forceinline__ void row_retire(const RowParams& p) {
-  const unsigned fin = __hip_atomic_fetch_add(&p.ctr->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (fin + 1u == p.total) {
+// stream. The count is issued before the sweeps and its result looked at after them
+// (row_retire_end), so its round trip hides behind the sweeps instead of delaying the calling
+// wavefront's.
+__device__ __forceinline__ unsigned row_retire_begin(const RowParams& p) {
+  return __hip_atomic_fetch_add(&p.ctr->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+constexpr unsigned kNotRetiring = ~0u;
+__device__ __forceinline__ void row_retire_end(const RowParams& p, unsigned fin) {
+  if (fin != kNotRetiring && fin + 1u == p.total) {
     __hip_atomic_store(&p.ctr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_fetch_add(&p.ctr->epoch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -648,7 +653,7 @@ using RowStore = std::conditional_t<PAIR, RowKVPair<L>, RowKV<DT, L>>;
 template <int DT, int TILE, int L, int NT, bool FUSED, bool PAIR, bool WIDE, bool CAUSAL, bool GATED, int MODE>
 __device__ __forceinline__ bool row_body(const RowParams& p, const RowParams* args, const RowLane& ln,
                                          RowStore<DT, TILE, L, PAIR>& kv, float* lds,
-                                         const unsigned* sh_epoch, bool published) {
+                                         const unsigned* sh_epoch, bool published, unsigned& fin) {
   constexpr int GROUPS = NT / TILE;
   constexpr int CT = GROUPS * L;  // tokens per chunk
   constexpr int SB = 8;  // tokens per sub-block of the sweeps
@@ -965,7 +970,7 @@ __device__ __forceinline__ bool row_body(const RowParams& p, const RowParams* ar
   X = acc_get<A>(xy, RS, wi);
   Y = acc_get<A>(xy + 4 * RS, RS, wi);
   // every wavefront is past its last read of the epoch and of the slots
-  if (MODE == kSinglePass && p.n_chunks > 1 && tid == 0) row_retire(p);
+  if (MODE == kSinglePass && p.n_chunks > 1 && tid == 0) fin = row_retire_begin(p);
   kv.fence();
 
   // ---- phase C: sweep each sub-block forward, then backward, writing Eq. (7) ----
@@ -1290,7 +1295,9 @@ __device__ __noinline__ void row_body_wide(const RowParams* args, float* lds, un
   const RowLane ln = row_lane<TILE, L, NT>(p, unit);
   RowStore<DT, TILE, L, PAIR> kv;
   row_load<DT, TILE, L, NT, FUSED, PAIR, POL>(p, ln, kv);
-  row_body<DT, TILE, L, NT, FUSED, PAIR, true, CAUSAL, GATED, MODE>(p, args, ln, kv, lds, sh_epoch, published);
+  unsigned fin = kNotRetiring;
+  row_body<DT, TILE, L, NT, FUSED, PAIR, true, CAUSAL, GATED, MODE>(p, args, ln, kv, lds, sh_epoch, published, fin);
+  row_retire_end(p, fin);
 }
 
 // Cache policy of a launch's k, v loads: the sums pass of two keeps the default policy, so the
@@ -1333,8 +1340,10 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4)))
   } else {
     RowStore<DT, TILE, L, PAIR> kv;
     row_load<DT, TILE, L, NT, FUSED, PAIR, POL>(p, ln, kv);
-    if (!row_body<DT, TILE, L, NT, FUSED, PAIR, false, CAUSAL, GATED, MODE>(p, args, ln, kv, lds, &sh_epoch, false))
+    unsigned fin = kNotRetiring;
+    if (!row_body<DT, TILE, L, NT, FUSED, PAIR, false, CAUSAL, GATED, MODE>(p, args, ln, kv, lds, &sh_epoch, false, fin))
       row_body_wide<DT, TILE, L, NT, FUSED, PAIR, CAUSAL, GATED, MODE, POL>(args, lds, unit, &sh_epoch, true);
+    row_retire_end(p, fin);
   }
 }
 
