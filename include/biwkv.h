@@ -31,14 +31,15 @@
  *     those calls must not be made under HIP graph capture unless an earlier call on the stream
  *     already sized the scratch. Replaying a captured call is safe: launches are told apart by a
  *     device-side epoch, not by arguments.
- *   - A row split over several workgroups is combined either in one launch, where the chunks
- *     exchange their sums while resident (used when every workgroup of the launch fits on the
- *     device at once), or in the two-pass form: 128-token chunks' sums, a per-row scan of them
- *     into each chunk's carries, then the outputs (three launches, nothing waits). In one launch a
- *     workgroup
- *     waits a bounded time for a peer chunk's sums and then recomputes them from that chunk's k
- *     and v, so results never depend on the peers being resident (for example when other work
- *     occupies the device); biwkv_stream_fault_flags reports that this happened.
+ *   - A row split over several workgroups is combined either in one launch, where the chunks of
+ *     a row exchange their sums while resident (used when every workgroup of the launch fits on
+ *     the device at once, or when a row's chunks take at most a quarter of the workgroups that
+ *     fit: later rows then start as earlier ones finish), or in the two-pass form: 128-token
+ *     chunks' sums, a per-row scan of them into each chunk's carries, then the outputs (three
+ *     launches, nothing waits). In one launch a workgroup waits a bounded time for a peer chunk's
+ *     sums and then recomputes them from that chunk's k and v, so results never depend on the
+ *     peers being resident (for example when other work occupies the device);
+ *     biwkv_stream_fault_flags reports that this happened.
  *   - All argument validation happens on the host before any HIP call. A problem with zero
  *     elements returns BIWKV_OK without enqueuing anything. Nothing is printed; no C++ exception
  *     crosses this interface.
@@ -74,8 +75,10 @@ extern "C" {
 /* Options (biwkv_set_option). Process-wide; they apply to calls made after they are set. */
 #define BIWKV_OPT_SPIN_LIMIT 1 /* polls of a peer chunk's sums before recomputing them (default 4096;
                                   0: recompute every peer's sums without waiting)             */
-#define BIWKV_OPT_TWO_PASS 2   /* 0 (default): one launch when all workgroups fit at once;
-                                  1: every row takes the two-pass form                         */
+#define BIWKV_OPT_TWO_PASS 2   /* 0 (default): one launch when all workgroups fit at once or
+                                  a row's chunks take at most a quarter of the resident
+                                  workgroups; 1: every row takes the two-pass form; 2: one
+                                  launch whenever a row's chunks fit at once                   */
 #define BIWKV_OPT_WIDE_INDEX 3 /* 0 (default): Q-Shift gathers use 32-bit index arithmetic below
                                   2^31 items; 1: always the 64-bit form                       */
 #define BIWKV_OPT_XCD_LOCAL 4  /* 1 (default): a one-launch row runs all its chunks on one XCD

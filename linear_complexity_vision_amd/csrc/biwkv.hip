@@ -666,7 +666,7 @@ int biwkv_set_option(int option, int64_t value, int64_t* previous) {
     case BIWKV_OPT_TWO_PASS:
     case BIWKV_OPT_WIDE_INDEX:
     case BIWKV_OPT_XCD_LOCAL: {
-      if (value != 0 && value != 1) return BIWKV_ERR_PARAM;
+      if (value != 0 && value != 1 && !(option == BIWKV_OPT_TWO_PASS && value == 2)) return BIWKV_ERR_PARAM;
       std::atomic<int>& opt = option == BIWKV_OPT_TWO_PASS    ? g_two_pass
                               : option == BIWKV_OPT_WIDE_INDEX ? g_wide_index
                                                                : g_xcd_local;

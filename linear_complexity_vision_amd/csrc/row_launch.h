@@ -113,8 +113,16 @@ int launch_row(const BiwkvParams& bp, int64_t B, int dev, void* stream, const Fi
   int cap = 0;
   rc = resident_capacity(dev, kfn, NT, &cap);
   if (rc) return rc;
+  // One launch needs every chunk of a row resident at once, not the whole grid: a chunk waits only
+  // on the chunks of its own row, and blocks start in order, so a later row's chunks only wait for
+  // slots that earlier rows free. Beyond one round, the chunks of a row that has started but not
+  // yet got all its slots hold theirs idle; limiting a row to a quarter of the resident slots
+  // bounds that loss, and longer rows take the two-pass form. BIWKV_OPT_TWO_PASS = 2 takes one
+  // launch whenever a row fits at all.
   const int opt = g_two_pass.load();
-  if (opt == 1 || (rp.n_chunks > 1 && total > cap))
+  const bool one_launch = rp.n_chunks == 1 || total <= cap ||
+                          (opt == 2 ? rp.n_chunks <= cap : rp.n_chunks <= cap / 4);
+  if (opt == 1 || !one_launch)
     return launch_two_pass<DT, TILE, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream, fixed);
   if (rp.n_chunks > 1) {
     // single pass: three tagged 64-bit words per (chunk, direction, channel)

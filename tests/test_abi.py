@@ -110,7 +110,8 @@ def test_options_validate_and_report_previous(L):
     assert L.biwkv_set_option(99, 1, None) == bad
     assert L.biwkv_set_option(_code("BIWKV_OPT_SPIN_LIMIT"), -1, None) == bad
     assert L.biwkv_set_option(_code("BIWKV_OPT_SPIN_LIMIT"), 2**32, None) == bad
-    assert L.biwkv_set_option(_code("BIWKV_OPT_TWO_PASS"), 2, None) == bad
+    assert L.biwkv_set_option(_code("BIWKV_OPT_TWO_PASS"), 3, None) == bad
+    assert L.biwkv_set_option(_code("BIWKV_OPT_WIDE_INDEX"), 2, None) == bad
     assert L.biwkv_set_option(_code("BIWKV_OPT_WIDE_INDEX"), -1, None) == bad
     # defaults, and the previous value comes back
     assert L.biwkv_set_option(_code("BIWKV_OPT_SPIN_LIMIT"), 7, ctypes.byref(prev)) == 0

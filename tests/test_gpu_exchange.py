@@ -187,6 +187,27 @@ def test_xcd_local_exchange_matches_plain_order(name, B, H, W, C, dtype):
     assert err <= 1e-4
 
 
+@pytest.mark.parametrize("name,dtype", [("biwkv", "f32"), ("biwkv", "bf16"), ("causal", "f32"), ("gated", "f32")])
+def test_one_launch_over_several_residency_rounds(name, dtype):
+    """More workgroups than fit at once, with rows of 18 chunks: later rows start as earlier ones
+    finish, and a row straddles the first round's end. No wait runs out (the fault word stays 0)
+    and the outputs match the oracle; OPT_TWO_PASS = 2 and the default agree bit for bit."""
+    L = _lib()
+    T = 9000 if dtype == "f32" else 18000
+    wl = _make(name, 2, 1, T, 1024, dtype, seed=600 + T)
+    r = _gate(wl) if name == "gated" else None
+    print(f"[case] one launch over several rounds {name} {wl.name}", flush=True)
+    y, flags = _run(name, wl, r)
+    with L.option(L.OPT_TWO_PASS, 2):
+        y2, flags2 = _run(name, wl, r)
+    assert flags == 0 and flags2 == 0
+    np.testing.assert_array_equal(y, y2)
+    y_ref, s_ref = _oracle(name, wl, r)
+    err = r3(y, y_ref, s_ref)
+    print(f"[parity] one launch over several rounds {name} {wl.name}: R3 = {err:.3e}", flush=True)
+    assert err <= 1e-4
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_two_pass_rows_beyond_512_chunks(dtype):
     """A row of more than 64 * 8 chunks of 128 tokens: the carry kernel reads its totals from

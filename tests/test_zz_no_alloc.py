@@ -52,8 +52,11 @@ def test_noalloc_matches_forward_on_two_calls_large_then_small():
 
 def test_noalloc_two_launch_rows_and_single_chunk_rows():
     import linear_complexity_vision_amd as L
-    print("[case] noalloc: config 5 (two-pass form), then single-chunk rows", flush=True)
+    print("[case] noalloc: config 5 (one launch over 1.5 residency rounds, then the two-pass form), "
+          "then single-chunk rows", flush=True)
     _check(L, workloads.make(5))
+    with L.option(L.OPT_TWO_PASS, 1):
+        _check(L, workloads.make(5))
     _check(L, workloads.make_random(92, 3, 300, 100, dtype="f32", w_range=5.0))
     with L.option(L.OPT_TWO_PASS, 1):
         _check(L, workloads.make_random(93, 2, 3000, 128, dtype="bf16", w_range=5.0))
