@@ -54,6 +54,7 @@ thread_local int t_last_hip_error = 0;
 std::map<std::pair<int, void*>, StreamScratch*> g_scratch;
 std::map<std::pair<int, const void*>, int> g_capacity;  // (device, kernel) -> resident workgroups
 std::map<int, int> g_xcds;                                // device -> XCDs
+std::map<int, int> g_cus;                                 // device -> compute units
 
 // Grows a zero-filled scratch buffer in stream order: the new buffer is allocated and cleared on
 // `st`, and the outgrown one is freed on `st` behind every launch already queued that uses it.
@@ -169,6 +170,21 @@ int resident_capacity(int dev, const void* kernel, int block, int* cap) {
   if (e != hipSuccess) return hip_fail(e);
   *cap = per_cu * cus;
   g_capacity[key] = *cap;
+  return BIWKV_OK;
+}
+
+int device_cus(int dev, int* n) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  auto it = g_cus.find(dev);
+  if (it != g_cus.end()) {
+    *n = it->second;
+    return BIWKV_OK;
+  }
+  int x = 0;
+  const hipError_t e = hipDeviceGetAttribute(&x, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e);
+  *n = x > 0 ? x : 1;
+  g_cus[dev] = *n;
   return BIWKV_OK;
 }
 

@@ -46,6 +46,9 @@ int resident_capacity(int dev, const void* kernel, int block, int* cap);
 // XCDs of device `dev` (workgroups are handed to them round robin). Caller holds g_mu.
 int device_xcds(int dev, int* n);
 
+// Compute units of device `dev`. Takes g_mu itself.
+int device_cus(int dev, int* n);
+
 // Options (biwkv_set_option).
 extern std::atomic<unsigned> g_spin_limit;
 extern std::atomic<int> g_two_pass;

@@ -157,21 +157,41 @@ int launch_row(const BiwkvParams& bp, int64_t B, int dev, void* stream, const Fi
 }
 
 // Tile shapes: 64 channels per tile (one 128-byte line of bf16 k, two of fp32), 64 registers of
-// k and v per lane, and chunks no longer than the sequence needs. Rows longer than one chunk of
-// 1024 tokens use 512-thread workgroups (two per CU): the workgroup a CU received first gets its
-// data first and computes and writes while the other one still reads, so reads and writes
-// overlap. fp32 rows keep 1024 threads: at 32 tokens per lane their 512-thread chunks are short
-// and the exchange between them dominates.
+// k and v per lane, and chunks no longer than the sequence needs.
+//  - Rows that one round of 1024-thread workgroups covers (at most one per CU) take one chunk of
+//    up to 1024 tokens per row in 1024 threads (16 wavefronts per CU).
+//  - More rows, and rows longer than 1024 tokens, take 512-thread workgroups, two per CU: the one
+//    a CU received first gets its data first and computes and writes while the other one still
+//    reads, so reads and writes overlap instead of alternating round by round. bf16 rows up to
+//    896 tokens split into chunks of 448 (7 sub-blocks per lane); longer ones into 512.
+//  - fp32 rows longer than 256 tokens keep 1024 threads: at 32 tokens per lane their 512-thread
+//    chunks are short and the exchange between them dominates (config B1 T16384 C768: 44 against
+//    42 us).
 template <int DT, bool FUSED, bool PAIR, bool CAUSAL, bool GATED>
 int try_row_shape(const BiwkvParams& bp, int64_t B, int dev, void* stream, const FixedScratch* fixed) {
   const long long T = bp.T;
+  int cus = 0;
+  const int rc = device_cus(dev, &cus);
+  if (rc) return rc;
+  const bool one_round = B * ((bp.C + 63) / 64) <= cus;  // rows
   if constexpr (DT == BIWKV_BF16) {
-    if (T <= 256) return launch_row<DT, 64, 16, 1024, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream, fixed);
-    if (T <= 512) return launch_row<DT, 64, 32, 1024, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream, fixed);
-    if (T <= 1024) return launch_row<DT, 64, 64, 1024, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream, fixed);
+    if (T <= 256) {
+      if (one_round) return launch_row<DT, 64, 16, 1024, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream, fixed);
+      return launch_row<DT, 64, 32, 512, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream, fixed);
+    }
+    if (T <= 512) {
+      if (one_round) return launch_row<DT, 64, 32, 1024, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream, fixed);
+      return launch_row<DT, 64, 64, 512, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream, fixed);
+    }
+    if (T <= 1024 && one_round)
+      return launch_row<DT, 64, 64, 1024, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream, fixed);
+    if (T <= 896) return launch_row<DT, 64, 56, 512, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream, fixed);
     return launch_row<DT, 64, 64, 512, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream, fixed);
   } else {
-    if (T <= 256) return launch_row<DT, 64, 16, 1024, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream, fixed);
+    if (T <= 256) {
+      if (one_round) return launch_row<DT, 64, 16, 1024, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream, fixed);
+      return launch_row<DT, 64, 32, 512, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream, fixed);
+    }
     return launch_row<DT, 64, 32, 1024, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream, fixed);
   }
 }

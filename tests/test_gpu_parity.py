@@ -129,6 +129,23 @@ EDGE_SHAPES = [(1, 1, 4), (2, 2, 6), (1, 3, 2), (1, 127, 64), (1, 128, 64), (1, 
                # several chunks per row, ragged last chunk and ragged last tile
                (1, 1025, 64), (2, 2047, 66), (1, 3000, 130), (1, 1500, 3), (1, 5121, 32)]
 
+# more rows than one round of one workgroup per CU: the 512-thread shapes (one chunk up to 256 /
+# 512 tokens, then chunks of 448 tokens up to 896 and of 512 beyond), ragged last tile
+MANY_ROW_SHAPES = [(5, 100, 4070), (5, 256, 4096), (5, 300, 4070), (3, 449, 5000), (5, 600, 4096),
+                   (3, 896, 5000), (3, 897, 4100)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("B,T,C", MANY_ROW_SHAPES)
+def test_biwkv_many_row_shapes(B, T, C, dtype):
+    wl = workloads.make_random(11 + T + C, B, T, C, dtype=dtype, w_range=8.0, k_std=3.0, u_std=2.0)
+    print(f"[case] biwkv_forward many rows {wl.name}", flush=True)
+    y = _run_biwkv(wl)
+    y_ref, s_ref = oracle.biwkv_rnn(f64(wl.k), f64(wl.v), f64(wl.w), f64(wl.u), with_scale=True)
+    err = r3(y, y_ref, s_ref)
+    _report(wl.name, err, 1e-4)
+    assert err <= 1e-4
+
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("B,T,C", EDGE_SHAPES)
