@@ -507,13 +507,36 @@ def _counter_means(path: str, counter: str, kernel: str) -> float:
     return sum(sel) / len(sel)
 
 
-def _counter_call_sum(path: str, counter: str, kernel: str) -> float:
-    """Per call of an entry made of one or more distinct kernels (same grid) whose names contain
-    `kernel`: the sum over those kernels of each one's mean per dispatch, at the largest grid
+# tile-kernel template flags (FUSED, CAUSAL, GATED) of each forward entry: a run of one entry also
+# times the plain forward beside it, so the kernels are told apart by their flags
+ROW_FLAGS = {"biwkv": (False, False, False), "fused": (True, False, False), "bidir": (True, False, False),
+             "causal": (False, True, False), "gated": (False, False, True)}
+
+
+def _row_flags(name: str):
+    """(FUSED, CAUSAL, GATED) of a biwkv_row_kernel<DT, TILE, L, NT, FUSED, PAIR, CAUSAL, GATED,
+    MODE> name, or None for any other kernel."""
+    i = name.find("biwkv_row_kernel<")
+    if i < 0:
+        return None
+    args = [a.strip() for a in name[i + len("biwkv_row_kernel<"):].split(">", 1)[0].split(",")]
+    return args[4] == "true", args[6] == "true", args[7] == "true"
+
+
+def kernel_of_entry(name: str, entry: str) -> bool:
+    """Whether a kernel (by its demangled name) belongs to `entry`."""
+    if entry in ROW_FLAGS:
+        return _row_flags(name) == ROW_FLAGS[entry]
+    return KERNEL_NAMES[entry] in name
+
+
+def _counter_call_sum(path: str, counter: str, entry: str) -> float:
+    """Per call of an entry made of one or more distinct kernels (same grid) that belong to
+    `entry`: the sum over those kernels of each one's mean per dispatch, at the largest grid
     (a two-pass forward is a sums launch and an output launch)."""
-    rows = [r for r in _counter_rows(path, counter) if kernel in r[0]]
+    rows = [r for r in _counter_rows(path, counter) if kernel_of_entry(r[0], entry)]
     if not rows:
-        raise SystemExit(f"no {counter} values for {kernel} under {path}")
+        raise SystemExit(f"no {counter} values for {entry} under {path}")
     top = max(r[2] for r in rows)
     by_name = {}
     for name, _, grid, val in rows:
@@ -541,8 +564,8 @@ def record_counters(kf: str, kw: str, cf: str, cw: str, config: int, entry: str)
         fetch = _counter_per_call(kf, "FETCH_SIZE", KERNEL_NAMES[entry], CALL_MARKER[entry])
         write = _counter_per_call(kw, "WRITE_SIZE", KERNEL_NAMES[entry], CALL_MARKER[entry])
     else:
-        fetch = _counter_call_sum(kf, "FETCH_SIZE", KERNEL_NAMES[entry])
-        write = _counter_call_sum(kw, "WRITE_SIZE", KERNEL_NAMES[entry])
+        fetch = _counter_call_sum(kf, "FETCH_SIZE", entry)
+        write = _counter_call_sum(kw, "WRITE_SIZE", entry)
     cal_fetch = _counter_means(cf, "FETCH_SIZE", COPY_KERNEL)
     cal_write = _counter_means(cw, "WRITE_SIZE", COPY_KERNEL)
     f_scale = CALIBRATION_BYTES / cal_fetch

@@ -94,3 +94,20 @@ def test_more_than_one_gpu_is_refused():
 def test_kernel_source_hash_is_stable():
     assert bench.kernel_source_hash() == bench.kernel_source_hash()
     assert len(bench.kernel_source_hash()) == 16
+
+
+def test_kernel_of_entry_tells_the_tile_kernel_variants_apart():
+    """A run of the fused entry also times the plain forward: counters must pick the fused
+    kernel's dispatches only (by the FUSED, CAUSAL, GATED template flags)."""
+    ns = "void (anonymous namespace)::biwkv_row_kernel<1, 64, 64, 512, {f}, true, {c}, {g}, 0>((anonymous namespace)::RowParams)"
+    fused = ns.format(f="true", c="false", g="false")
+    plain = ns.format(f="false", c="false", g="false")
+    causal = ns.format(f="false", c="true", g="false")
+    gated = ns.format(f="false", c="false", g="true")
+    assert bench.kernel_of_entry(fused, "fused") and not bench.kernel_of_entry(plain, "fused")
+    assert bench.kernel_of_entry(plain, "biwkv") and not bench.kernel_of_entry(fused, "biwkv")
+    assert bench.kernel_of_entry(fused, "bidir")
+    assert bench.kernel_of_entry(causal, "causal") and not bench.kernel_of_entry(causal, "biwkv")
+    assert bench.kernel_of_entry(gated, "gated") and not bench.kernel_of_entry(gated, "fused")
+    assert bench.kernel_of_entry("void (anonymous namespace)::qshift_kernel<4, false>(unsigned int const*)", "qshift")
+    assert not bench.kernel_of_entry("void (anonymous namespace)::qshift_kernel<4, false>(x)", "biwkv")
