@@ -132,7 +132,8 @@ int launch_row(const BiwkvParams& bp, int64_t B, int dev, void* stream, const Fi
       rc = device_xcds(dev, &nx);
       if (rc) return rc;
       const long long rows = total / rp.n_chunks;
-      if (nx > 1) {
+      // a row kept on one XCD needs all its chunks resident there, on 1 / nx of the device
+      if (nx > 1 && rp.n_chunks <= cap / nx) {
         rp.n_xcd = nx;
         rp.xcd_rows = static_cast<int>(rows / nx * nx);
       }

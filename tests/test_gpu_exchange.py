@@ -208,6 +208,21 @@ def test_one_launch_over_several_residency_rounds(name, dtype):
     assert err <= 1e-4
 
 
+def test_rows_longer_than_one_xcd_holds_keep_the_plain_order():
+    """Rows of 40 chunks in 1024-thread workgroups: they fit the device at once (one launch over
+    several rounds) but not one XCD's share of it, so they keep the plain block order. No wait may
+    run out (the fault word stays 0), and the outputs match the oracle."""
+    L = _lib()
+    wl = _make("biwkv", 1, 1, 20480, 1024, "f32", seed=640)
+    print(f"[case] rows of 40 chunks, one launch {wl.name}", flush=True)
+    y, flags = _run("biwkv", wl)
+    assert flags == 0
+    y_ref, s_ref = _oracle("biwkv", wl)
+    err = r3(y, y_ref, s_ref)
+    print(f"[parity] rows of 40 chunks: R3 = {err:.3e}", flush=True)
+    assert err <= 1e-4
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_two_pass_rows_beyond_512_chunks(dtype):
     """A row of more than 64 * 8 chunks of 128 tokens: the carry kernel reads its totals from
