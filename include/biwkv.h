@@ -24,8 +24,9 @@
  *     they validate on the host, enqueue, and return. No call synchronises.
  *   - The caller owns every buffer. The library keeps no pointer to caller memory after the
  *     enqueued work completes. Bi-WKV calls whose sequence is split over several workgroups
- *     (T above 1024 for bf16, above 512 for fp32) use library-owned scratch (chunk sums and a
- *     small counter block) kept per (device, stream); it is allocated in stream order
+ *     (fp32: T above 512; bf16: T above 1024, or above 512 when B * ceil(C / 64) exceeds the
+ *     device's compute units) use library-owned scratch (chunk sums and a small counter block)
+ *     kept per (device, stream); it is allocated in stream order
  *     (hipMallocAsync) on the first such call on a stream, grown when a larger problem arrives
  *     (the outgrown buffer is freed in stream order), and released by biwkv_release_scratch. So
  *     those calls must not be made under HIP graph capture unless an earlier call on the stream
@@ -108,9 +109,10 @@ int biwkv_forward(const void* k, const void* v, const float* w, const float* u, 
  * routine (the array's address is looked up once per device, on the first call there). Every
  * call on a device shares that array, and it keeps the last call's contents: calls that overlap
  * on one device (several streams or threads at once) race and must not be made. A row of several
- * chunks needs 3 KiB per chunk in one launch (B * ceil(C / 64) * ceil(T / 512) chunks for T above
- * 1024 with bf16, above 512 with fp32) and 4 KiB per 128-token chunk in the two-pass form; a
- * problem that needs more than 8 MiB returns BIWKV_ERR_SCRATCH before anything is enqueued.
+ * chunks needs 3 KiB per chunk in one launch (B * ceil(C / 64) * ceil(T / 512) chunks of 512
+ * tokens in general; bf16 rows of up to 896 tokens split into chunks of 448) and 4 KiB per
+ * 128-token chunk in the two-pass form; a problem that needs more than 8 MiB returns
+ * BIWKV_ERR_SCRATCH before anything is enqueued.
  */
 int biwkv_forward_noalloc(const void* k, const void* v, const float* w, const float* u, float* out,
                           int64_t B, int64_t T, int64_t C, int dtype, void* stream);

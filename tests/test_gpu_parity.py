@@ -262,24 +262,45 @@ def test_determinism_and_reuse_across_shapes():
     assert L.stream_fault_flags() == 0
 
 
-def test_graph_replay_matches_eager():
+def _noalloc_into(L, k, v, w, u, out):
+    import torch
+    B, T, C = k.shape
+    dt = L.BF16 if k.dtype == torch.bfloat16 else L.F32
+    rc = L.load_library().biwkv_forward_noalloc(k.data_ptr(), v.data_ptr(), w.data_ptr(), u.data_ptr(),
+                                                out.data_ptr(), B, T, C, dt,
+                                                torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+
+
+# (C, entry): 4 rows in the plain block order; 16 rows kept on one XCD each; the allocation-free
+# entry (static scratch, meant for callers under capture)
+@pytest.mark.parametrize("C,entry", [(128, "forward"), (512, "forward"), (512, "noalloc")])
+def test_graph_replay_matches_eager(C, entry):
     """A captured call replays correctly, with eager calls on the same scratch between replays: the
     chunk exchange tells launches apart by a device-side epoch, not by kernel arguments."""
     import torch
     L = _lib()
-    wl = workloads.make_random(21, 2, 3000, 128, dtype="bf16")  # three chunks per row
+    wl = workloads.make_random(21, 2, 3000, C, dtype="bf16")  # three chunks per row
     k, v, w, u = to_device_kv(wl)
     s = torch.cuda.Stream()
-    print("[case] graph replay", flush=True)
+    print(f"[case] graph replay C={C} {entry}", flush=True)
+
+    def call(out):
+        if entry == "noalloc":
+            _noalloc_into(L, k, v, w, u, out)
+        else:
+            L.biwkv_forward(k, v, w, u, out=out)
+
     with torch.cuda.stream(s):
         ref = L.biwkv_forward(k, v, w, u)  # allocates this stream's scratch outside the capture
         out = torch.empty_like(ref)
-        L.biwkv_forward(k, v, w, u, out=out)
+        call(out)
     torch.cuda.synchronize()
     ref_np = ref.cpu().numpy()
+    np.testing.assert_array_equal(out.cpu().numpy(), ref_np)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
-        L.biwkv_forward(k, v, w, u, out=out)
+        call(out)
     torch.cuda.synchronize()
     for _ in range(4):
         out.zero_()
@@ -288,11 +309,13 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         np.testing.assert_array_equal(out.cpu().numpy(), ref_np)
         with torch.cuda.stream(s):
-            eager = L.biwkv_forward(k, v, w, u)
+            eager = torch.empty_like(ref)
+            call(eager)
         torch.cuda.synchronize()
         np.testing.assert_array_equal(eager.cpu().numpy(), ref_np)
-    with torch.cuda.stream(s):
-        assert L.stream_fault_flags() == 0
+    if entry != "noalloc":
+        with torch.cuda.stream(s):
+            assert L.stream_fault_flags() == 0
 
 
 def test_side_streams_are_independent():
