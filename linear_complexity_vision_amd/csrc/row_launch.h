@@ -164,7 +164,9 @@ int launch_row(const BiwkvParams& bp, int64_t B, int dev, void* stream, const Fi
 //  - More rows, and rows longer than 1024 tokens, take 512-thread workgroups, two per CU: the one
 //    a CU received first gets its data first and computes and writes while the other one still
 //    reads, so reads and writes overlap instead of alternating round by round. bf16 rows up to
-//    896 tokens split into chunks of 448 (7 sub-blocks per lane); longer ones into 512.
+//    896 tokens split into chunks of 448 (7 sub-blocks per lane); longer ones into 512. fp32 rows
+//    up to 256 tokens take 32-channel tiles in 256 threads instead, four workgroups per CU (384
+//    rows of 196 tokens: 14.6 against 16.3 us), with the same per-channel arithmetic.
 //  - fp32 rows longer than 256 tokens keep 1024 threads: at 32 tokens per lane their 512-thread
 //    chunks are short and the exchange between them dominates (config B1 T16384 C768: 44 against
 //    42 us).
@@ -191,7 +193,9 @@ int try_row_shape(const BiwkvParams& bp, int64_t B, int dev, void* stream, const
   } else {
     if (T <= 256) {
       if (one_round) return launch_row<DT, 64, 16, 1024, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream, fixed);
-      return launch_row<DT, 64, 32, 512, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream, fixed);
+      // 32-channel tiles (one 128-byte fp32 line per token) in 256 threads: twice the workgroups,
+      // four per CU, so the rows spread evenly over the CUs
+      return launch_row<DT, 32, 32, 256, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream, fixed);
     }
     return launch_row<DT, 64, 32, 1024, FUSED, PAIR, CAUSAL, GATED>(bp, B, dev, stream, fixed);
   }

@@ -24,7 +24,7 @@ def _run(wl):
     return y.cpu().numpy()
 
 
-@pytest.mark.parametrize("index", [1, 3, 4, 5])
+@pytest.mark.parametrize("index", [1, 2, 3, 4, 5])
 def test_causal_workload_shapes(index):
     """The Bi-WKV workloads' shapes and value distributions, through the causal entry."""
     wl = workloads.make(index)

@@ -37,7 +37,7 @@ def _run(wl, r):
     return y.cpu().numpy()
 
 
-@pytest.mark.parametrize("index", [1, 3, 4, 5])
+@pytest.mark.parametrize("index", [1, 2, 3, 4, 5])
 def test_gated_workload_shapes(index):
     wl = workloads.make(index)
     r = _gate_input(wl, 500 + index)
