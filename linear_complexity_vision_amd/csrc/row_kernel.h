@@ -396,7 +396,8 @@ constexpr int kRowPad = TILE + (NT / TILE < 64 ? 64 / (NT / TILE) : 1);
 template <int TILE, int NT>
 constexpr int kRowLdsFloats = kRowSweepFloats<NT> + 8 * (NT / TILE) * kRowPad<TILE, NT> + TILE;
 
-// Single-exponent sums for the backward's scans (an empty one has the finite exponent kEmptyM).
+// Single-exponent sums with a finite empty exponent (kEmptyM), so that adding them needs no
+// branch: the fast form's addition, also used by the backward's scans.
 __device__ __forceinline__ Agg row_empty() { return Agg{kEmptyM, 0.f, 0.f}; }
 __device__ __forceinline__ Agg agg_add_f(Agg a, Agg b) {
   const float m = fmaxf(a.m, b.m);
@@ -404,11 +405,7 @@ __device__ __forceinline__ Agg agg_add_f(Agg a, Agg b) {
   return Agg{m, fmaf(a.F, sa, b.F * sb), fmaf(a.G, sa, b.G * sb)};
 }
 
-// Aggregates moved between the W consecutive lanes that hold one channel's groups (W is a power
-// of two up to 64). from_below<W, d> gives a lane the value of the lane d below it and
-// from_above<W, d> that of the lane d above; the callers only use results from inside the
-// segment. Segments of up to 16 lanes lie inside one DPP row, so these are row shifts (plain
-// VALU moves); wider segments go through the LDS crossbar (ds_bpermute).
+// One DPP move of a float across the lanes of a row (CTRL: the DPP control word).
 template <int CTRL>
 __device__ __forceinline__ float dpp_move(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, 0xf, 0xf, false));
