@@ -92,9 +92,10 @@ extern "C" {
  *   w, u : [C] float32, device memory (decay, divided by T inside; bonus).
  *   out  : [B, T, C] float32, device memory; must not overlap k, v, w or u.
  * Errors: BIWKV_ERR_NULL, _SHAPE (B, T, C < 0 or B*T*C*4 bytes overflow), _DTYPE, _ALIAS, _ALIGN,
- * _NO_DEVICE, _HIP, and _UNSUPPORTED when one chunk of a row spans 2^31 bytes of out: chunks are
- * 512 tokens (bf16, T > 1024) or 512 (fp32, T > 512), so C * 512 * 4 must stay below 2^31
- * (C < 1048576). Any T up to 2^31 - 1 is addressed.
+ * _NO_DEVICE, _HIP, and _UNSUPPORTED when one chunk of a row spans 2^31 bytes of out: a chunk is
+ * the whole row only while B * ceil(C / 64) is at most the device's compute units (so C is small),
+ * and at most 512 tokens otherwise, so C * 512 * 4 must stay below 2^31 (C < 1048576). Any T up
+ * to 2^31 - 1 is addressed.
  */
 int biwkv_forward(const void* k, const void* v, const float* w, const float* u, float* out,
                   int64_t B, int64_t T, int64_t C, int dtype, void* stream);
