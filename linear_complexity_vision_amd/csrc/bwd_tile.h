@@ -2,6 +2,7 @@
 // the tile kernel's work split.
 #pragma once
 
+#include "backward.h"
 #include "row_kernel.h"
 
 namespace {
@@ -70,6 +71,15 @@ struct BwdTileParams {
   int C;
   int n_tiles;   // channel tiles per batch item
   int n_chunks;  // chunks per row
+  // single launch (bwd_one_kernel): the exchange between the chunks of a row
+  Counters* ctr;              // epoch block (n_chunks > 1)
+  unsigned long long* slots;  // [round][row][chunk][dir][64] tagged (m, F, G) words
+  unsigned* row_fail;         // per row: the launch's tag when a wait of that row ran out
+  unsigned total;             // workgroups of the launch
+  unsigned spin_limit;        // polls of a peer's slot before the row is handed to the fallback
+  // single launch: rows [0, xcd_rows) run every chunk on one XCD and exchange through its L2
+  // (blocks go to the n_xcd XCDs round robin); 0 keeps the plain order
+  int xcd_rows, n_xcd;
 };
 
 // Makes register values opaque to the compiler (no instruction), so that values derived from them
@@ -94,9 +104,10 @@ struct BtKV<BIWKV_BF16, L> {
 #pragma unroll
     for (int i = 0; i < L; ++i) asm volatile("" : "+v"(r[i]));
   }
+  template <int POL>
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t km, __amdgpu_buffer_rsrc_t vm, uint32_t off, int i) {
-    const uint32_t kx = __builtin_amdgcn_raw_buffer_load_b16(km, off, 0, kBtLoadPolicy);
-    const uint32_t vx = __builtin_amdgcn_raw_buffer_load_b16(vm, off, 0, kBtLoadPolicy);
+    const uint32_t kx = __builtin_amdgcn_raw_buffer_load_b16(km, off, 0, POL);
+    const uint32_t vx = __builtin_amdgcn_raw_buffer_load_b16(vm, off, 0, POL);
     r[i] = kx | (vx << 16);
   }
   __device__ __forceinline__ void empty(int i) { r[i] = (r[i] & 0xffff0000u) | 0xff80u; }  // k = -inf
@@ -110,9 +121,10 @@ struct BtKV<BIWKV_F32, L> {
     bt_fence(kk);
     bt_fence(vv);
   }
+  template <int POL>
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t km, __amdgpu_buffer_rsrc_t vm, uint32_t off, int i) {
-    kk[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(km, off, 0, kBtLoadPolicy));
-    vv[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vm, off, 0, kBtLoadPolicy));
+    kk[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(km, off, 0, POL));
+    vv[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vm, off, 0, POL));
   }
   __device__ __forceinline__ void empty(int i) { kk[i] = kNegInf; }
 };
@@ -170,8 +182,19 @@ __device__ __forceinline__ BtLane bt_lane(const BwdTileParams& p, unsigned unit)
   const int tid = threadIdx.x;
   ln.c = tid % kBtTile;
   ln.g = tid / kBtTile;
-  ln.row = __builtin_amdgcn_readfirstlane(unit / static_cast<unsigned>(p.n_chunks));
-  ln.chunk = static_cast<int>(unit) - ln.row * p.n_chunks;
+  const unsigned nc = static_cast<unsigned>(p.n_chunks);
+  if (unit < static_cast<unsigned>(p.xcd_rows) * nc) {
+    // block `unit` runs on XCD unit % n_xcd: XCD x takes rows x, x + n_xcd, ... whole, in order
+    const unsigned nx = static_cast<unsigned>(p.n_xcd);
+    const unsigned s = __builtin_amdgcn_readfirstlane(unit / nx);
+    const unsigned x = unit - s * nx;
+    const unsigned rg = __builtin_amdgcn_readfirstlane(s / nc);
+    ln.row = static_cast<int>(rg * nx + x);
+    ln.chunk = static_cast<int>(s - rg * nc);
+  } else {
+    ln.row = __builtin_amdgcn_readfirstlane(unit / nc);
+    ln.chunk = static_cast<int>(unit) - ln.row * p.n_chunks;
+  }
   ln.bi = __builtin_amdgcn_readfirstlane(ln.row / p.n_tiles);
   const int tile = ln.row - ln.bi * p.n_tiles;
   ln.ch = tile * kBtTile + ln.c;
@@ -187,7 +210,7 @@ __device__ __forceinline__ BtLane bt_lane(const BwdTileParams& p, unsigned unit)
 // rest of the batch item (a uniform base, so scalar registers) and the lane's channel offset, so
 // one vector register addresses every token; tokens past the row read 0 and are then marked empty
 // (k = -inf), masked channels read 0. The host keeps a batch item below 2^31 bytes.
-template <int DT, int N>
+template <int DT, int N, int POL = kBtLoadPolicy>
 __device__ __forceinline__ void bt_load(const BwdTileParams& p, int bi, long long t0, int ch, bool on,
                                         BtKV<DT, N>& kv, float* gg) {
   constexpr int ES = DT == BIWKV_F32 ? 4 : 2;
@@ -208,12 +231,12 @@ __device__ __forceinline__ void bt_load(const BwdTileParams& p, int bi, long lon
     const int a = (t0u + i) * rb;  // below 2^31: T < 2^31 / (4 C) and the row's padding
     const int left = avail - a;
     const uint32_t n = static_cast<uint32_t>(left > 0 ? left : 0);
-    kv.load(make_rsrc(kb + a, n), make_rsrc(vb + a, n), off, i);
+    kv.template load<POL>(make_rsrc(kb + a, n), make_rsrc(vb + a, n), off, i);
     if (gg) {
       const int ag = (t0u + i) * rg;
       const int lg = availg - ag;
       gg[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-          make_rsrc(gb + ag, static_cast<uint32_t>(lg > 0 ? lg : 0)), offg, 0, kBtLoadPolicy));
+          make_rsrc(gb + ag, static_cast<uint32_t>(lg > 0 ? lg : 0)), offg, 0, POL));
     }
   }
   if (t0u + N > p.T) {  // uniform: only wavefronts at the end of a row
@@ -228,7 +251,7 @@ __device__ __forceinline__ void bt_load(const BwdTileParams& p, int bi, long lon
 // the forward tile kernel does (RowKVPair: prepare(q) then gives each lane its own channel). Half
 // the load instructions of 16-bit loads, and each lands in its final register. Tokens past the
 // row are marked empty.
-template <int N>
+template <int N, int POL = kBtLoadPolicy>
 __device__ __forceinline__ void bt_load_pairs(const BwdTileParams& p, int bi, long long t0, int ch, bool on,
                                               RowKVPair<N>& kv, float* gg) {
   const long long plane = p.T * p.C;
@@ -246,8 +269,8 @@ __device__ __forceinline__ void bt_load_pairs(const BwdTileParams& p, int bi, lo
     const int a = (t0u + 2 * m) * rb;  // below 2^31 (host check)
     const int left = avail - a;
     const uint32_t n = static_cast<uint32_t>(left > 0 ? left : 0);
-    kv.kk[m] = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(kb + a, n), off, 0, kBtLoadPolicy);
-    kv.vv[m] = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(vb + a, n), off, 0, kBtLoadPolicy);
+    kv.kk[m] = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(kb + a, n), off, 0, POL);
+    kv.vv[m] = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(vb + a, n), off, 0, POL);
   }
   if (gg) {  // the upstream gradient: fp32, each lane its own channel
     const char* gb = reinterpret_cast<const char*>(
@@ -259,7 +282,7 @@ __device__ __forceinline__ void bt_load_pairs(const BwdTileParams& p, int bi, lo
       const int ag = (t0u + i) * rg;
       const int lg = availg - ag;
       gg[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-          make_rsrc(gb + ag, static_cast<uint32_t>(lg > 0 ? lg : 0)), offg, 0, kBtLoadPolicy));
+          make_rsrc(gb + ag, static_cast<uint32_t>(lg > 0 ? lg : 0)), offg, 0, POL));
     }
   }
   if (t0u + N > p.T) kv.pad(static_cast<int>(p.T - t0u), odd);  // only wavefronts at a row's end
@@ -368,17 +391,241 @@ __device__ __forceinline__ void bt_carries(Agg f, Agg b, Agg& X, Agg& Y, BtShare
 }
 
 // ---------------------------------------------------------------------------------------------
+// Single launch: the chunks of a row exchange their sums through slots, one round at a time.
+// A chunk's sum is published as three tagged 64-bit words (m, F, G), each carrying the launch's
+// tag in its upper half, so a reader accepts a slot without a fence once every tag matches. (The
+// round-2 sums are signed, so the forward's (log-weight, mean) pair does not apply.)
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ void bt_slot_put(unsigned long long* s, Agg a, unsigned tag) {
+  const unsigned long long t = static_cast<unsigned long long>(tag) << 32;
+  __hip_atomic_store(s, t | __float_as_uint(a.m), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(s + 1, t | __float_as_uint(a.F), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(s + 2, t | __float_as_uint(a.G), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void bt_slot_get(const unsigned long long* s, unsigned long long (&w)[3]) {
+#pragma unroll
+  for (int i = 0; i < 3; ++i) w[i] = __hip_atomic_load(s + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool bt_slot_ready(const unsigned long long (&w)[3], unsigned tag) {
+  return static_cast<unsigned>(w[0] >> 32) == tag && static_cast<unsigned>(w[1] >> 32) == tag &&
+         static_cast<unsigned>(w[2] >> 32) == tag;
+}
+// The same words through the L2 of the workgroup's own XCD, for rows whose chunks all run on one
+// XCD: plain stores and non-temporal loads, which the CU's L1 does not keep (as the forward tile
+// kernel's slot_store_l2 / slot_load_l2). `rs` spans the slot array, `off` is the byte offset.
+__device__ __forceinline__ void bt_slot_put_l2(__amdgpu_buffer_rsrc_t rs, uint32_t off, Agg a, unsigned tag) {
+  const unsigned long long t = static_cast<unsigned long long>(tag) << 32;
+  slot_word_l2(rs, off, t | __float_as_uint(a.m));
+  slot_word_l2(rs, off + 8u, t | __float_as_uint(a.F));
+  slot_word_l2(rs, off + 16u, t | __float_as_uint(a.G));
+}
+__device__ __forceinline__ void bt_slot_get_l2(__amdgpu_buffer_rsrc_t rs, uint32_t off, unsigned long long (&w)[3]) {
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const slot_u2 x = __builtin_amdgcn_raw_buffer_load_b64(rs, off + 8u * i, 0, kSlotL2Load);
+    w[i] = static_cast<unsigned long long>(x.x) | (static_cast<unsigned long long>(x.y) << 32);
+  }
+}
+__device__ __forceinline__ Agg bt_slot_value(const unsigned long long (&w)[3]) {
+  return Agg{__uint_as_float(static_cast<unsigned>(w[0])), __uint_as_float(static_cast<unsigned>(w[1])),
+             __uint_as_float(static_cast<unsigned>(w[2]))};
+}
+
+// Counts a workgroup out of a single launch once none of its wavefronts reads a slot again; the
+// last one resets the count and moves the epoch on for the next launch on the stream (whose tags
+// then differ from every slot written so far).
+__device__ __forceinline__ unsigned bt_retire_begin(const BwdTileParams& p) {
+  return __hip_atomic_fetch_add(&p.ctr->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void bt_retire_end(const BwdTileParams& p, unsigned fin) {
+  if (fin != kNotRetiring && fin + 1u == p.total) {
+    __hip_atomic_store(&p.ctr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(&p.ctr->epoch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Carries of the lanes from their sums in a single launch (round rnd of the row's exchange). In
+// and out as bt_carries. The first wavefront scans each channel's groups from empty (the lanes'
+// carries inside the chunk) and publishes the chunk's sums (forward at its last slot, backward at
+// its first token); then every wavefront takes a share of the row's other chunks (wavefront g
+// folds entries g, g + GROUPS, ... in order: the forward sums of the earlier chunks, then the
+// backward sums of the later ones), the shares are folded in wavefront order, and each lane's
+// carry is the chunk's carry moved to the lane plus its carry inside the chunk. The result does
+// not depend on arrival order. Returns true (for the whole workgroup) when a wait ran out; X and Y
+// are then not formed.
+template <int NT, int L, bool ANCHORED>
+__device__ bool bt_exchange(Agg f, Agg b, Agg& X, Agg& Y, BtShared<NT>* sh, const BwdTileParams& p,
+                            const BtLane& ln, int rnd, const unsigned* sh_tag) {
+  constexpr int GROUPS = NT / kBtTile;
+  constexpr int PAD = kBtTile + 1;
+  constexpr int RS = GROUPS * PAD;
+  constexpr int CT = GROUPS * L;
+  float* red = sh->red;
+  float* xy = sh->xy;
+  float* part = &sh->sw[0][0][0];  // [GROUPS][6][64]: the wavefronts' shares (the sweep records
+                                   // of the wide form are not live here)
+  const int wi = ln.g * PAD + ln.c;
+  red[0 * RS + wi] = f.m;
+  red[1 * RS + wi] = f.F;
+  red[2 * RS + wi] = f.G;
+  red[3 * RS + wi] = b.m;
+  red[4 * RS + wi] = b.F;
+  red[5 * RS + wi] = b.G;
+  __syncthreads();
+  const unsigned tag = __builtin_amdgcn_readfirstlane(*sh_tag);  // written before the first barrier
+  const int c = ln.c;
+  const float Dt = ANCHORED ? ln.D : 0.f;  // lane (c, g) holds channel c of the tile
+  const float step = static_cast<float>(L);
+  const int nch = p.n_chunks, chunk = ln.chunk;
+  unsigned long long* rs =
+      p.slots + ((static_cast<size_t>(rnd) * p.total + static_cast<size_t>(ln.row) * nch) * 2 * kBtTile) * 3;
+  auto slot = [&](int ck, int dir) { return rs + (static_cast<size_t>(ck * 2 + dir) * kBtTile + c) * 3; };
+  // rows whose chunks all run on one XCD exchange through its L2 (byte offsets into the slot
+  // array, which the host keeps below 4 GiB for them)
+  const bool local = ln.row < p.xcd_rows;
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(p.slots, 0xFFFFFFFFu);
+  auto soff = [&](const unsigned long long* sp) { return static_cast<uint32_t>((sp - p.slots) * 8); };
+  auto put = [&](unsigned long long* sp, const Agg& a) {
+    if (local)
+      bt_slot_put_l2(srs, soff(sp), a, tag);
+    else
+      bt_slot_put(sp, a, tag);
+  };
+  auto get = [&](const unsigned long long* sp, unsigned long long (&w)[3]) {
+    if (local)
+      bt_slot_get_l2(srs, soff(sp), w);
+    else
+      bt_slot_get(sp, w);
+  };
+  if (ln.g == 0) {
+    Agg x = row_empty(), y = row_empty();
+#pragma unroll
+    for (int gi = 0; gi < GROUPS; ++gi) {
+      const int o = gi * PAD + c;
+      xy[0 * RS + o] = x.m;
+      xy[1 * RS + o] = x.F;
+      xy[2 * RS + o] = x.G;
+      x = agg_add_f(agg_shift(x, step, Dt), Agg{red[0 * RS + o], red[1 * RS + o], red[2 * RS + o]});
+    }
+#pragma unroll
+    for (int gi = GROUPS - 1; gi >= 0; --gi) {
+      const int o = gi * PAD + c;
+      xy[3 * RS + o] = y.m;
+      xy[4 * RS + o] = y.F;
+      xy[5 * RS + o] = y.G;
+      y = agg_add_f(Agg{red[3 * RS + o], red[4 * RS + o], red[5 * RS + o]}, agg_shift(y, step, Dt));
+    }
+    if (nch > 1) {
+      put(slot(chunk, kFwd), x);
+      put(slot(chunk, kBwd), y);
+    }
+  }
+  // this wavefront's share of the other chunks' sums, moved to the chunk's carry anchors (just
+  // before its first token, just after its last slot)
+  Agg pf = row_empty(), pb = row_empty();
+  bool timed_out = false;
+  const int nf = chunk, ne = nch - 1;
+  // A lane polls up to EB entries together: every poll round reissues the loads of the entries
+  // not yet seen, so a batch costs one round trip after its last peer publishes.
+  constexpr int EB = 2;
+  for (int e0 = ln.g; e0 < ne; e0 += EB * GROUPS) {
+    unsigned long long w[EB][3];
+    bool ok[EB];
+    auto entry = [&](int j) {
+      const int e = e0 + j * GROUPS;
+      return slot(e < nf ? e : e + 1, e < nf ? kFwd : kBwd);
+    };
+#pragma unroll
+    for (int j = 0; j < EB; ++j) {
+      ok[j] = e0 + j * GROUPS >= ne;  // no entry: nothing to wait for
+      if (!ok[j] && p.spin_limit != 0) get(entry(j), w[j]);
+    }
+    bool all = true;
+#pragma unroll
+    for (int j = 0; j < EB; ++j) {
+      ok[j] = ok[j] || (p.spin_limit != 0 && bt_slot_ready(w[j], tag));
+      all = all && ok[j];
+    }
+    for (unsigned spins = 1; !all && spins < p.spin_limit; ++spins) {
+      __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+      for (int j = 0; j < EB; ++j)
+        if (!ok[j]) get(entry(j), w[j]);
+      all = true;
+#pragma unroll
+      for (int j = 0; j < EB; ++j) {
+        ok[j] = ok[j] || bt_slot_ready(w[j], tag);
+        all = all && ok[j];
+      }
+    }
+    if (!all) timed_out = true;
+#pragma unroll
+    for (int j = 0; j < EB; ++j) {
+      const int e = e0 + j * GROUPS;
+      if (e >= ne || !ok[j]) continue;
+      const bool fwd = e < nf;
+      const int ck = fwd ? e : e + 1;
+      const float dist = static_cast<float>(fwd ? (chunk - 1 - ck) : (ck - chunk - 1)) * CT;
+      const Agg a = agg_shift(bt_slot_value(w[j]), dist, Dt);
+      if (fwd)
+        pf = agg_add_f(pf, a);
+      else
+        pb = agg_add_f(pb, a);
+    }
+  }
+  {
+    float* q = part + ln.g * 6 * kBtTile + c;
+    q[0 * kBtTile] = pf.m;
+    q[1 * kBtTile] = pf.F;
+    q[2 * kBtTile] = pf.G;
+    q[3 * kBtTile] = pb.m;
+    q[4 * kBtTile] = pb.F;
+    q[5 * kBtTile] = pb.G;
+  }
+  if (block_any(timed_out)) return true;
+  if (ln.g == 0) {
+    Agg cf = row_empty(), cb = row_empty();
+#pragma unroll
+    for (int gi = 0; gi < GROUPS; ++gi) {
+      const float* q = part + gi * 6 * kBtTile + c;
+      cf = agg_add_f(cf, Agg{q[0 * kBtTile], q[1 * kBtTile], q[2 * kBtTile]});
+      cb = agg_add_f(cb, Agg{q[3 * kBtTile], q[4 * kBtTile], q[5 * kBtTile]});
+    }
+#pragma unroll
+    for (int gi = 0; gi < GROUPS; ++gi) {
+      const int o = gi * PAD + c;
+      const Agg x = agg_add_f(agg_shift(cf, static_cast<float>(gi) * step, Dt),
+                              Agg{xy[0 * RS + o], xy[1 * RS + o], xy[2 * RS + o]});
+      const Agg y = agg_add_f(Agg{xy[3 * RS + o], xy[4 * RS + o], xy[5 * RS + o]},
+                              agg_shift(cb, static_cast<float>(GROUPS - 1 - gi) * step, Dt));
+      xy[0 * RS + o] = x.m;
+      xy[1 * RS + o] = x.F;
+      xy[2 * RS + o] = x.G;
+      xy[3 * RS + o] = y.m;
+      xy[4 * RS + o] = y.F;
+      xy[5 * RS + o] = y.G;
+    }
+  }
+  __syncthreads();
+  X = Agg{xy[0 * RS + wi], xy[1 * RS + wi], xy[2 * RS + wi]};
+  Y = Agg{xy[3 * RS + wi], xy[4 * RS + wi], xy[5 * RS + wi]};
+  return false;
+}
+
+// ---------------------------------------------------------------------------------------------
 // Wide form (any w, u): position-free sums, running maxima. Returns the lane's (dw, du) terms.
 // Out of line: it needs more registers than the fast form, and keeping it apart gives it its own
 // allocation. It reads the parameters through the kernel's argument pointer.
 // ---------------------------------------------------------------------------------------------
 template <int DT, int L, int NT, int STAGE>
-__device__ __noinline__ float2 bt_body_wide(const BwdTileParams* args, BtShared<NT>* sh) {
+__device__ __noinline__ float4 bt_body_wide(const BwdTileParams* args, BtShared<NT>* sh, const unsigned* sh_tag,
+                                            unsigned unit) {
   constexpr int SB = kBtSB;
   constexpr int NSB = L / SB;
   constexpr int MODE = STAGE == 0 ? kBtLocal : kBtConsume;  // when a round's carries are formed
+  const float4 failed = make_float4(0.f, 0.f, 1.f, 0.f);  // STAGE 4: a wait ran out
   const BwdTileParams p = *args;
-  const BtLane lnv = bt_lane<L, NT>(p, blockIdx.x);
+  const BtLane lnv = bt_lane<L, NT>(p, unit);
   const int tid = threadIdx.x;
   const bool on = lnv.on;
   const long long s_g = lnv.s_g;
@@ -386,7 +633,8 @@ __device__ __noinline__ float2 bt_body_wide(const BwdTileParams* args, BtShared<
   auto& sw = sh->sw;
   BtKV<DT, L> kv;
   float gg[L];
-  bt_load<DT, L>(p, lnv.bi, lnv.s_g, lnv.ch, lnv.on, kv, gg);
+  // a single launch reads k, v and g once: streaming loads
+  bt_load<DT, L, STAGE == 4 ? kStream : kBtLoadPolicy>(p, lnv.bi, lnv.s_g, lnv.ch, lnv.on, kv, gg);
   // token position times D, exact for t < 2^24
   float Dp = D;  // the copy positions are formed from, made opaque between phases
   auto tD = [&](int i) { return static_cast<float>(s_g + i) * Dp; };
@@ -421,9 +669,13 @@ __device__ __noinline__ float2 bt_body_wide(const BwdTileParams* args, BtShared<
     Agg Xc, Yc;
     if constexpr (STAGE == 1) {
       bt_carries<NT, L, false, kBtProduce>(lane_f, run, Xc, Yc, sh, p.sums1, p, lnv);
-      return make_float2(0.f, 0.f);
+      return make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    bt_carries<NT, L, false, MODE>(lane_f, run, Xc, Yc, sh, p.carry1, p, lnv);
+    if constexpr (STAGE == 4) {
+      if (bt_exchange<NT, L, false>(lane_f, run, Xc, Yc, sh, p, lnv, 0, sh_tag)) return failed;
+    } else {
+      bt_carries<NT, L, false, MODE>(lane_f, run, Xc, Yc, sh, p.carry1, p, lnv);
+    }
     lane_f = Xc;
     // from here cap1[q] is the suffix-form sum of every token after sub-block q
 #pragma unroll
@@ -511,9 +763,13 @@ __device__ __noinline__ float2 bt_body_wide(const BwdTileParams* args, BtShared<
     Agg Y2;
     if constexpr (STAGE == 2) {
       bt_carries<NT, L, false, kBtProduce>(lane2, run, X2, Y2, sh, p.sums2, p, lnv);
-      return make_float2(0.f, 0.f);
+      return make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    bt_carries<NT, L, false, MODE>(lane2, run, X2, Y2, sh, p.carry2, p, lnv);
+    if constexpr (STAGE == 4) {
+      if (bt_exchange<NT, L, false>(lane2, run, X2, Y2, sh, p, lnv, 1, sh_tag)) return failed;
+    } else {
+      bt_carries<NT, L, false, MODE>(lane2, run, X2, Y2, sh, p.carry2, p, lnv);
+    }
 #pragma unroll
     for (int q = 0; q < NSB; ++q) cap2[q] = agg_add_f(Y2, cap2[q]);
   }
@@ -601,7 +857,7 @@ __device__ __noinline__ float2 bt_body_wide(const BwdTileParams* args, BtShared<
   if (e1 > kEmptyM) dw += dw1 * fast_exp2(e1 + 2.f * D);
   if (e2 > kEmptyM) dw += dw2 * fast_exp2(e2 + 2.f * D);
 
-  return make_float2(dw, du);
+  return make_float4(dw, du, 0.f, 0.f);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -617,8 +873,9 @@ constexpr float kBtFastRange = 24.f;
 
 // Whether a channel needs the wide form. Every kernel of a backward call takes the same vote over
 // the 64 channels of a tile, so all stages of a row use the same form.
+template <int L>
 __device__ __forceinline__ bool bt_wide_lane(float D, float U) {
-  return fabsf(D) * static_cast<float>(kBwdLane - 1) > kBtFastRange || fabsf(U) > kBonusRange;
+  return fabsf(D) * static_cast<float>(L - 1) > kBtFastRange || fabsf(U) > kBonusRange;
 }
 
 template <int DT, int L, int NT, int STAGE, bool PAIR>
@@ -829,6 +1086,263 @@ __device__ __forceinline__ float2 bt_body_fast(const BwdTileParams& p, const BtL
   return make_float2(dw, du);
 }
 
+// The upstream gradient of N consecutive tokens from t0 (the same for every lane) of batch item
+// bi, channel ch; tokens past the row and masked channels read 0.
+template <int N, int POL>
+__device__ __forceinline__ void bt_load_g(const BwdTileParams& p, int bi, long long t0, int ch, bool on,
+                                          float (&gg)[N]) {
+  const long long plane = p.T * p.C;
+  const char* gb = reinterpret_cast<const char*>(
+      uniform_u64(reinterpret_cast<unsigned long long>(p.g) + static_cast<unsigned long long>(bi) * plane * 4));
+  const int t0u = __builtin_amdgcn_readfirstlane(static_cast<int>(t0));
+  const int rg = p.C * 4, availg = static_cast<int>(plane * 4);
+  const uint32_t offg = on ? static_cast<uint32_t>(ch) * 4 : kOutOfRange;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int ag = (t0u + i) * rg;  // below 2^31 (host check)
+    const int lg = availg - ag;
+    gg[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+        make_rsrc(gb + ag, static_cast<uint32_t>(lg > 0 ? lg : 0)), offg, 0, POL));
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Single launch, fast form. The lane keeps its tokens' k and v in registers, and from round 1 on
+// g / D at each token. Round 1 (lane sums, exchange, sweep) gives y and 1 / D at each
+// sub-block's tokens, which turn at once into that sub-block's round-2 terms (q, r) = (g, g y) / D;
+// the round-2 lane sums are formed like the forward tile kernel's (each sub-block against its own
+// largest term, the running sum rescaled when a larger one arrives). After the round-2 exchange
+// the round-2 sweep forms the round-1 sweep of each sub-block again (the same arithmetic on the
+// same values, for y and the states of dw) and writes dv, dk and the dw terms. Returns (dw terms,
+// du terms, failed, -); failed when a wait of either exchange ran out.
+// ---------------------------------------------------------------------------------------------
+template <int DT, int L, int NT, bool PAIR>
+__device__ __forceinline__ float4 bt_body_one(const BwdTileParams& p, const BtLane& ln, BtShared<NT>* sh,
+                                              const unsigned* sh_tag, unsigned& fin) {
+  constexpr int SB = kBtSB;
+  constexpr int NSB = L / SB;
+  const float4 failed = make_float4(0.f, 0.f, 1.f, 0.f);
+  const float D = ln.D, U = ln.U;
+  const float lam = fast_exp2(-D);
+  const float lsb = fast_exp2(-static_cast<float>(SB) * D);  // lam^SB
+  const float span = fmaxf(-D, 0.f) * static_cast<float>(L - 1);  // largest growth inside a lane
+  const float eU = fast_exp2(U);
+  std::conditional_t<PAIR, RowKVPair<L>, BtKV<DT, L>> kv;
+  if constexpr (PAIR) {
+    bt_load_pairs<L, kStream>(p, ln.bi, ln.s_g, ln.ch, ln.on, kv, nullptr);
+#pragma unroll
+    for (int q = 0; q < L / 8; ++q) kv.prepare(q);
+  } else {
+    bt_load<DT, L, kStream>(p, ln.bi, ln.s_g, ln.ch, ln.on, kv, nullptr);
+  }
+  auto kl = [&](int i) { return kv.k(i) * kLog2e; };  // -inf in empty slots
+
+  // ---- round 1 lane sums (against 2^{kmax + span}) and the caps, as in bt_body_fast ----
+  float kmax = kNegInf;
+#pragma unroll
+  for (int i = 0; i < L; ++i) kmax = fmaxf(kmax, kl(i));
+  float capF[NSB], capG[NSB];
+  Agg X, Y;
+  // g streams in one sub-block ahead of the round-1 sweep (the first during the exchange); loading
+  // all of a lane's g with its k and v measured slower (120 against 110 us at B=4, T=4096,
+  // C=1024)
+  float gq[SB];
+  {
+    const float ref = kmax == kNegInf ? 0.f : kmax + span;
+    float pp[L];
+#pragma unroll
+    for (int i = 0; i < L; ++i) pp[i] = fast_exp2(kl(i) - ref);
+    float fF = 0.f, fG = 0.f, cF = 0.f, cG = 0.f;
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      fF = fmaf(fF, lam, pp[i] * kv.v(i));
+      fG = fmaf(fG, lam, pp[i]);
+    }
+#pragma unroll
+    for (int q = NSB - 1; q >= 0; --q) {
+      capF[q] = cF;
+      capG[q] = cG;
+#pragma unroll
+      for (int i = (q + 1) * SB - 1; i >= q * SB; --i) {
+        cF = fmaf(cF, lam, pp[i] * kv.v(i));
+        cG = fmaf(cG, lam, pp[i]);
+      }
+    }
+    const float m = kmax == kNegInf ? kEmptyM : ref;
+    bt_load_g<SB, kStream>(p, ln.bi, ln.s_g, ln.ch, ln.on, gq);
+    if (bt_exchange<NT, L, true>(Agg{m, fF, fG}, Agg{m, cF, cG}, X, Y, sh, p, ln, 0, sh_tag)) return failed;
+  }
+  kv.fence();
+
+  // ---- the round-1 sweep of one sub-block: y and 1 / D at its tokens, against 2^M; also the
+  //      terms, the forward states before each token and the backward states after it ----
+  const float top = fmaxf(fmaxf(kmax, X.m), Y.m);
+  const float M = top + span;
+  const float sig = fast_exp2(kmax - top);  // the caps' scale against 2^M
+  const float sx = fast_exp2(X.m - M), sy = fast_exp2(Y.m - M);
+  const float YF = Y.F * sy, YG = Y.G * sy;
+  auto sweep1 = [&](int q, float& A, float& Cs, float (&ph)[SB], float (&ra)[SB], float (&rc)[SB],
+                    float (&yv)[SB], float (&rdv)[SB], float (&bs)[SB], float (&ds)[SB]) {
+#pragma unroll
+    for (int i = 0; i < SB; ++i) {
+      const int j = q * SB + i;
+      ph[i] = fast_exp2(kl(j) - M);
+      ra[i] = A;
+      rc[i] = Cs;
+      A = fmaf(A, lam, ph[i] * kv.v(j));
+      Cs = fmaf(Cs, lam, ph[i]);
+    }
+    // backward states entering from the right: the lane's later sub-blocks and later tokens
+    const float lr = fast_exp2(-static_cast<float>(L - (q + 1) * SB) * D);
+    float Bs = fmaf(YF, lr, sig * capF[q]), Ds = fmaf(YG, lr, sig * capG[q]);
+#pragma unroll
+    for (int i = SB - 1; i >= 0; --i) {
+      const int j = q * SB + i;
+      const float vj = kv.v(j);
+      const float e = ph[i] * eU;
+      const float num = ra[i] + fmaf(e, vj, Bs);
+      const float den = rc[i] + Ds + e;
+      const bool live = kv.k(j) != kNegInf;
+      const float r = fast_rcp(den);
+      yv[i] = live ? num * r : 0.f;
+      rdv[i] = live ? r : 0.f;
+      bs[i] = Bs;
+      ds[i] = Ds;
+      Bs = fmaf(Bs, lam, ph[i] * vj);
+      Ds = fmaf(Ds, lam, ph[i]);
+    }
+  };
+
+  // ---- round 1 sweep with the round-2 lane sums of (q, r) and the du terms. A sub-block's terms
+  //      are g (rd / rmax) 2^{-span} against 2^{mq + span}, mq = log2(rmax) - M (rmax: its
+  //      largest 1 / D) ----
+  const float e_span = fast_exp2(-span);
+  float du = 0.f;
+  float mrun = kNegInf;  // (fQ, fR) are against 2^{mrun + span}
+  float fQ = 0.f, fR = 0.f;
+  float bQ[NSB], bR[NSB], bm[NSB];  // each sub-block's backward sums, anchored at its first token
+  float gr[L];                      // g / D at each token, against 2^{-M}
+  {
+    float A = X.F * sx, Cs = X.G * sx;
+#pragma unroll
+    for (int q = 0; q < NSB; ++q) {
+      float gn[SB];
+      if (q + 1 < NSB) bt_load_g<SB, kStream>(p, ln.bi, ln.s_g + (q + 1) * SB, ln.ch, ln.on, gn);
+      float ph[SB], ra[SB], rc[SB], yv[SB], rdv[SB], bs[SB], ds[SB];
+      sweep1(q, A, Cs, ph, ra, rc, yv, rdv, bs, ds);
+      float rmx = 0.f;
+#pragma unroll
+      for (int i = 0; i < SB; ++i) {
+        const int j = q * SB + i;
+        // e^{u+k} (q v - r) = p_tt g (v - y), with p_tt = e / den
+        du = fmaf(ph[i] * eU * rdv[i] * gq[i], kv.v(j) - yv[i], du);
+        rmx = fmaxf(rmx, rdv[i]);
+        gr[j] = rdv[i] * gq[i];
+      }
+      const float mq = rmx > 0.f ? fast_log2(rmx) - M : kNegInf;
+      const float qs = rmx > 0.f ? fast_rcp(rmx) * e_span : 0.f;
+      float qq[SB];
+#pragma unroll
+      for (int i = 0; i < SB; ++i) qq[i] = gr[q * SB + i] * qs;
+      float sQ = 0.f, sR = 0.f;
+#pragma unroll
+      for (int i = 0; i < SB; ++i) {
+        sQ = fmaf(sQ, lam, qq[i]);
+        sR = fmaf(sR, lam, qq[i] * yv[i]);
+      }
+      float cQ = 0.f, cR = 0.f;
+#pragma unroll
+      for (int i = SB - 1; i >= 0; --i) {
+        cQ = fmaf(cQ, lam, qq[i]);
+        cR = fmaf(cR, lam, qq[i] * yv[i]);
+      }
+      bQ[q] = cQ;
+      bR[q] = cR;
+      bm[q] = mq;
+      // move the running sums SB tokens on and add this sub-block at the larger exponent
+      const float mn = fmaxf(mrun, mq);
+      const float mr = mn == kNegInf ? 0.f : mn;
+      const float sr = fast_exp2(mrun - mr) * lsb, sq = fast_exp2(mq - mr);
+      fQ = fmaf(fQ, sr, sQ * sq);
+      fR = fmaf(fR, sr, sR * sq);
+      mrun = mn;
+      if (q + 1 < NSB) {
+#pragma unroll
+        for (int i = 0; i < SB; ++i) gq[i] = gn[i];
+      }
+      __builtin_amdgcn_sched_barrier(0);  // one sub-block at a time (bounded live values)
+    }
+  }
+  const float qmax = mrun;  // -inf when the lane holds no token
+  float capQ[NSB], capR[NSB];
+  Agg X2, Y2;
+  {
+    const float mr = mrun == kNegInf ? 0.f : mrun;
+    float cQ = 0.f, cR = 0.f;
+#pragma unroll
+    for (int q = NSB - 1; q >= 0; --q) {
+      capQ[q] = cQ;
+      capR[q] = cR;
+      const float sq = fast_exp2(bm[q] - mr);
+      cQ = fmaf(cQ, lsb, bQ[q] * sq);
+      cR = fmaf(cR, lsb, bR[q] * sq);
+    }
+    const float m = qmax == kNegInf ? kEmptyM : qmax + span;
+    if (bt_exchange<NT, L, true>(Agg{m, fQ, fR}, Agg{m, cQ, cR}, X2, Y2, sh, p, ln, 1, sh_tag)) return failed;
+  }
+  // every wavefront is past its last read of a slot
+  if (threadIdx.x == 0 && p.n_chunks > 1) fin = bt_retire_begin(p);
+  kv.fence();
+  bt_fence(gr);
+
+  // ---- round 2 sweep: dv, dk and the dw terms, against 2^M (round 1) and 2^Mq (round 2) ----
+  const float topq = fmaxf(fmaxf(qmax, X2.m), Y2.m);
+  const float Mq = topq + span;
+  const float sigq = fast_exp2(qmax - topq);
+  const float sqx = fast_exp2(X2.m - Mq), sqy = fast_exp2(Y2.m - Mq);
+  const float S3 = fast_exp2(-M - Mq);  // q_t against 2^Mq is g_t rd_t 2^{-M - Mq}
+  const float YQ = Y2.F * sqy, YR = Y2.G * sqy;
+  float dwacc = 0.f;  // sum over tokens of b Qpre - d Rpre + a Qsuf - c Rsuf, against 2^{M + Mq}
+  {
+    float A = X.F * sx, Cs = X.G * sx, QA = X2.F * sqx, QR = X2.G * sqx;
+#pragma unroll
+    for (int q = 0; q < NSB; ++q) {
+      float ph[SB], ra[SB], rc[SB], yv[SB], rdv[SB], bs[SB], ds[SB];
+      sweep1(q, A, Cs, ph, ra, rc, yv, rdv, bs, ds);
+      float qh[SB], rqa[SB], rqr[SB];  // q against 2^Mq, and the round-2 forward states
+#pragma unroll
+      for (int i = 0; i < SB; ++i) {
+        qh[i] = gr[q * SB + i] * S3;
+        rqa[i] = QA;
+        rqr[i] = QR;
+        QA = fmaf(QA, lam, qh[i]);
+        QR = fmaf(QR, lam, qh[i] * yv[i]);
+      }
+      const float lr = fast_exp2(-static_cast<float>(L - (q + 1) * SB) * D);
+      float QB = fmaf(YQ, lr, sigq * capQ[q]), QRB = fmaf(YR, lr, sigq * capR[q]);
+#pragma unroll
+      for (int i = SB - 1; i >= 0; --i) {
+        const int j = q * SB + i;
+        const long long tt = ln.s_g + j;
+        dwacc = fmaf(bs[i], rqa[i], fmaf(-ds[i], rqr[i], fmaf(ra[i], QB, fmaf(-rc[i], QRB, dwacc))));
+        // e^{k} (Qpre + Qsuf + e^u q) and the same over r
+        const float vj = kv.v(j);
+        const float K = fast_exp2(kl(j) + Mq);
+        const float self = qh[i] * eU;
+        const float dvj = K * (rqa[i] + QB + self);
+        const float rj = K * (rqr[i] + QRB + self * yv[i]);
+        bt_store(p, ln.bi, tt, ln.ch, ln.on, dvj, fmaf(vj, dvj, -rj));
+        QB = fmaf(QB, lam, qh[i]);
+        QRB = fmaf(QRB, lam, qh[i] * yv[i]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // a lane with no token (the end of a row) has no dw terms (see bt_body_fast)
+  const float dw = kmax != kNegInf && dwacc != 0.f ? dwacc * fast_exp2(M + Mq) : 0.f;
+  return make_float4(dw, du, 0.f, 0.f);
+}
+
 // ---------------------------------------------------------------------------------------------
 // Stage 1 of a multi-chunk row: the round-1 sums of every chunk. A lane holds one channel of one
 // chunk (64 tokens, like a lane of the forward tile kernel), so the chunk's sums are the lane's
@@ -897,7 +1411,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(PAIR ? 
   const float U = on ? p.u[ch] * kLog2e : 0.f;
   // the tile kernel's vote (a wavefront holds the tile's 64 channels)
   const bool wide =
-      __ballot(bt_wide_lane(D, U)) != 0ull;
+      __ballot(bt_wide_lane<kBwdLane>(D, U)) != 0ull;
   if (chunk >= p.n_chunks) return;  // (after the vote: every lane of the wavefront took part)
   const long long t0 = static_cast<long long>(chunk) * CT;
   float* o = p.sums1 + ((static_cast<size_t>(row) * p.n_chunks + chunk) * 2 * kBtTile + c) * 3;
@@ -964,23 +1478,24 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(PAIR ? 
 // ---------------------------------------------------------------------------------------------
 constexpr int kCarryGroups = 16;
 
-template <int CT>
-__global__ void __launch_bounds__(64 * kCarryGroups)
-    bwd_carry_kernel(BwdTileParams p, const float* __restrict__ sums, float* __restrict__ carry) {
-  __shared__ float gs[kCarryGroups][6][kBtTile];  // group sums
-  __shared__ float gc[kCarryGroups][6][kBtTile];  // group carries
+// The carries of one row (`row`) by a workgroup of 64 x GR threads (thread (c, grp)), with LDS for
+// the group sums gs and group carries gc. VL: the tile kernel's lane length, whose vote decides
+// the form.
+template <int CT, int GR, int VL>
+__device__ __forceinline__ void bt_row_carries(const BwdTileParams& p, const float* __restrict__ sums,
+                                               float* __restrict__ carry, int row, float (*gs)[6][kBtTile],
+                                               float (*gc)[6][kBtTile]) {
   const int c = threadIdx.x % kBtTile, grp = threadIdx.x / kBtTile;
-  const int row = blockIdx.x;
   const int bi = row / p.n_tiles;
   const int ch = (row - bi * p.n_tiles) * kBtTile + c;
   const bool on = ch < p.C;
   const float Dc = on ? (p.w[ch] / static_cast<float>(p.T)) * kLog2e : 0.f;
   const float Uc = on ? p.u[ch] * kLog2e : 0.f;
-  const bool wide = __ballot(bt_wide_lane(Dc, Uc)) != 0ull;
+  const bool wide = __ballot(bt_wide_lane<VL>(Dc, Uc)) != 0ull;
   const float D = wide ? 0.f : Dc;  // exponent shift per token (none for position-free sums)
   const float step = static_cast<float>(CT);
   const int nch = p.n_chunks;
-  const int per = (nch + kCarryGroups - 1) / kCarryGroups;
+  const int per = (nch + GR - 1) / GR;
   const int j0 = grp * per, j1 = j0 + per < nch ? j0 + per : nch;
   const size_t base = static_cast<size_t>(row) * nch * 2 * kBtTile * 3 + static_cast<size_t>(c) * 3;
   auto at = [&](int j, int dir) { return base + static_cast<size_t>(j * 2 + dir) * kBtTile * 3; };
@@ -1001,7 +1516,7 @@ __global__ void __launch_bounds__(64 * kCarryGroups)
   __syncthreads();
   if (grp == 0) {
     Agg x = row_empty();
-    for (int k = 0; k < kCarryGroups; ++k) {
+    for (int k = 0; k < GR; ++k) {
       const int a0 = k * per, a1 = a0 + per < nch ? a0 + per : nch;
       const int len = a1 > a0 ? a1 - a0 : 0;
       gc[k][0][c] = x.m;
@@ -1010,7 +1525,7 @@ __global__ void __launch_bounds__(64 * kCarryGroups)
       x = agg_add_f(agg_shift(x, step * len, D), Agg{gs[k][0][c], gs[k][1][c], gs[k][2][c]});
     }
     Agg y = row_empty();
-    for (int k = kCarryGroups - 1; k >= 0; --k) {
+    for (int k = GR - 1; k >= 0; --k) {
       const int a0 = k * per, a1 = a0 + per < nch ? a0 + per : nch;
       const int len = a1 > a0 ? a1 - a0 : 0;
       gc[k][3][c] = y.m;
@@ -1040,27 +1555,35 @@ __global__ void __launch_bounds__(64 * kCarryGroups)
   }
 }
 
-// STAGE 0: a row of one chunk, the whole backward. STAGE 1, 2, 3: the three launches of a longer
-// row (see the top of this file).
+template <int CT>
+__global__ void __launch_bounds__(64 * kCarryGroups)
+    bwd_carry_kernel(BwdTileParams p, const float* __restrict__ sums, float* __restrict__ carry) {
+  __shared__ float gs[kCarryGroups][6][kBtTile];  // group sums
+  __shared__ float gc[kCarryGroups][6][kBtTile];  // group carries
+  bt_row_carries<CT, kCarryGroups, kBwdLane>(p, sums, carry, blockIdx.x, gs, gc);
+}
+
+// One workgroup's share of a backward launch: the chunk `unit` (row-major over (row, chunk)) in
+// STAGE 0 (a row of one chunk, the whole backward) or STAGE 1, 2, 3 (the three launches of a
+// longer row, see the top of this file), with the dw and du terms of STAGE 0 and 3 folded per
+// channel over the groups, in order, and written to pw, pu.
 // PAIR: bf16 k and v as 32-bit channel pairs (bt_load_pairs).
-template <int DT, int L, int NT, int WPE, int STAGE, bool PAIR>
-__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE)))
-    bwd_tile_kernel(BwdTileParams p) {
+template <int DT, int L, int NT, int STAGE, bool PAIR>
+__device__ __forceinline__ void bt_stage(const BwdTileParams& p, unsigned unit, BtShared<NT>& sh) {
   static_assert(!PAIR || (DT == BIWKV_BF16 && L % 8 == 0), "pairs are bf16 channel pairs");
   static_assert(L % kBtSB == 0 && NT % kBtTile == 0 && NT <= 1024, "bad backward tile shape");
   static_assert(((NT / kBtTile) & (NT / kBtTile - 1)) == 0, "a channel's groups share a wavefront");
-  __shared__ BtShared<NT> sh;
-  const BtLane ln = bt_lane<L, NT>(p, blockIdx.x);
+  const BtLane ln = bt_lane<L, NT>(p, unit);
   if (ln.g == 0) sh.dch[ln.c] = ln.D;  // read by the scans, after their first barrier
   // The whole workgroup takes the wide form when any of its channels needs it; every wavefront
   // holds all 64 channels, so a wavefront vote is the workgroup's vote (and every chunk of the
   // row, in every stage, votes the same way).
-  static_assert(L == kBwdLane, "the fast / wide vote assumes this lane length");
-  const bool wide_lane = bt_wide_lane(ln.D, ln.U);
+  const bool wide_lane = bt_wide_lane<L>(ln.D, ln.U);
   float2 r;
   if (__ballot(wide_lane) != 0ull) {
     const auto* args = (const BwdTileParams*)(__builtin_amdgcn_kernarg_segment_ptr());
-    r = bt_body_wide<DT, L, NT, STAGE>(args, &sh);
+    const float4 rw = bt_body_wide<DT, L, NT, STAGE>(args, &sh, nullptr, unit);
+    r = make_float2(rw.x, rw.y);
   } else {
     r = bt_body_fast<DT, L, NT, STAGE, PAIR>(p, ln, &sh);
   }
@@ -1081,6 +1604,154 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE)))
       p.pu[at] = b;
     }
   }
+}
+
+template <int DT, int L, int NT, int WPE, int STAGE, bool PAIR>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE)))
+    bwd_tile_kernel(BwdTileParams p) {
+  __shared__ BtShared<NT> sh;
+  bt_stage<DT, L, NT, STAGE, PAIR>(p, blockIdx.x, sh);
+}
+
+// ---------------------------------------------------------------------------------------------
+// The backward in one launch (rows of several chunks whose chunks are resident together; blocks
+// start in order, so a row's chunks only wait for slots that earlier rows free): both rounds'
+// chunk sums go through the slot exchange (bt_exchange). A workgroup whose wait runs out stores
+// nothing and marks its row in row_fail with the launch's tag; bwd_one_reduce_kernel then computes
+// that row again on its own, so no result depends on the chunks being resident together.
+// ---------------------------------------------------------------------------------------------
+template <int DT, int L, int NT, bool PAIR>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4)))
+    bwd_one_kernel(BwdTileParams p) {
+  static_assert(!PAIR || (DT == BIWKV_BF16 && L % 8 == 0), "pairs are bf16 channel pairs");
+  static_assert(L % kBtSB == 0 && NT % kBtTile == 0 && NT <= 1024, "bad backward tile shape");
+  static_assert(((NT / kBtTile) & (NT / kBtTile - 1)) == 0, "a channel's groups share a wavefront");
+  __shared__ BtShared<NT> sh;
+  __shared__ unsigned sh_tag;
+  const int tid = threadIdx.x;
+  // slots are tagged with the launch's epoch + 1 (never 0, so zeroed slots never match); the tag
+  // is read after the exchange's first barrier
+  if (tid == 0)
+    sh_tag = p.n_chunks > 1 ? __hip_atomic_load(&p.ctr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u : 1u;
+  const BtLane ln = bt_lane<L, NT>(p, blockIdx.x);
+  if (ln.g == 0) sh.dch[ln.c] = ln.D;
+  const bool wide_lane = bt_wide_lane<L>(ln.D, ln.U);
+  unsigned fin = kNotRetiring;
+  float4 r;
+  if (__ballot(wide_lane) != 0ull) {
+    const auto* args = (const BwdTileParams*)(__builtin_amdgcn_kernarg_segment_ptr());
+    r = bt_body_wide<DT, L, NT, 4>(args, &sh, &sh_tag, blockIdx.x);
+  } else {
+    r = bt_body_one<DT, L, NT, PAIR>(p, ln, &sh, &sh_tag, fin);
+  }
+  if (r.z != 0.f) {  // uniform: a wait ran out
+    if (tid == 0) {
+      p.row_fail[ln.row] = sh_tag;
+      __hip_atomic_fetch_or(&p.ctr->fault, kFaultSpin, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  } else {
+    sh.fold[0][ln.g][ln.c] = r.x;
+    sh.fold[1][ln.g][ln.c] = r.y;
+    __syncthreads();
+    if (ln.g == 0 && ln.on) {
+      float a = 0.f, b = 0.f;
+#pragma unroll
+      for (int i = 0; i < NT / kBtTile; ++i) {
+        a += sh.fold[0][i][ln.c];
+        b += sh.fold[1][i][ln.c];
+      }
+      const long long at = (static_cast<long long>(ln.bi) * p.n_chunks + ln.chunk) * p.C + ln.ch;
+      p.pw[at] = a;
+      p.pu[at] = b;
+    }
+  }
+  if (p.n_chunks > 1 && tid == 0) {
+    if (fin == kNotRetiring) fin = bt_retire_begin(p);
+    bt_retire_end(p, fin);
+  }
+}
+
+// A row of the last bwd_one_kernel launch whose waits ran out, computed again by one workgroup
+// alone: the three stages of the multi-launch form over the row's chunks in order (chunk sums,
+// carries, round 1 and the round-2 sums, carries, both rounds), so it needs no other workgroup.
+template <int DT, int L, int NT, bool PAIR>
+__device__ void bt_row_fallback(const BwdTileParams& p, int row, BtShared<NT>& sh) {
+  constexpr int CT = (NT / kBtTile) * L;
+  constexpr int GR = NT / kBtTile;
+  static_assert(sizeof(sh.sw) >= 2 * GR * 6 * kBtTile * sizeof(float), "carry scratch");
+  float(*gs)[6][kBtTile] = reinterpret_cast<float(*)[6][kBtTile]>(&sh.sw[0][0][0]);
+  float(*gc)[6][kBtTile] = gs + GR;
+  const unsigned u0 = static_cast<unsigned>(row) * static_cast<unsigned>(p.n_chunks);
+  for (int ck = 0; ck < p.n_chunks; ++ck) {
+    bt_stage<DT, L, NT, 1, PAIR>(p, u0 + ck, sh);
+    __syncthreads();
+  }
+  bt_row_carries<CT, GR, L>(p, p.sums1, p.carry1, row, gs, gc);
+  __syncthreads();
+  for (int ck = 0; ck < p.n_chunks; ++ck) {
+    bt_stage<DT, L, NT, 2, PAIR>(p, u0 + ck, sh);
+    __syncthreads();
+  }
+  bt_row_carries<CT, GR, L>(p, p.sums2, p.carry2, row, gs, gc);
+  __syncthreads();
+  for (int ck = 0; ck < p.n_chunks; ++ck) {
+    bt_stage<DT, L, NT, 3, PAIR>(p, u0 + ck, sh);
+    __syncthreads();
+  }
+}
+
+// The last kernel of a single-launch call, one workgroup per 64-channel tile: first the rows of
+// that tile whose waits ran out in the bwd_one_kernel launch before it (row_fail holds that
+// launch's tag, which is the epoch now), each computed again by bt_row_fallback; then dw and du of
+// the tile's channels, the per-chunk terms folded in batch and chunk order (thread (c, grp) sums
+// a contiguous segment of them, the segments are added in order). p addresses chunks in plain row
+// order (xcd_rows = 0).
+template <int DT, int L, int NT, bool PAIR>
+__global__ void __launch_bounds__(NT) bwd_one_reduce_kernel(BwdTileParams p, BwdParams rp) {
+  constexpr int GR = NT / kBtTile;
+  __shared__ BtShared<NT> sh;
+  const int tile = blockIdx.x;
+  if (p.n_chunks > 1) {
+    const unsigned tag = __hip_atomic_load(&p.ctr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // lane j of every wavefront reads the flag of batch item b0 + j (all in flight at once); the
+    // vote is the same in every wavefront, so the fallback's barriers are met by all of them
+    for (int b0 = 0; b0 < rp.B; b0 += 64) {
+      const int bi = b0 + static_cast<int>(threadIdx.x % 64);
+      const bool hit = bi < rp.B && p.row_fail[bi * p.n_tiles + tile] == tag;
+      unsigned long long m = __ballot(hit);
+      while (m != 0ull) {
+        const int j = __builtin_ctzll(m);
+        m &= m - 1ull;
+        bt_row_fallback<DT, L, NT, PAIR>(p, (b0 + j) * p.n_tiles + tile, sh);
+      }
+    }
+  }
+  const int c = threadIdx.x % kBtTile, grp = threadIdx.x / kBtTile;
+  const int ch = tile * kBtTile + c;
+  const long long n = static_cast<long long>(rp.B) * rp.n_wg;
+  const long long per = (n + GR - 1) / GR;
+  const long long r0 = grp * per, r1 = r0 + per < n ? r0 + per : n;
+  float sw = 0.f, su = 0.f;
+  if (ch < rp.C) {
+#pragma unroll 8
+    for (long long r = r0; r < r1; ++r) {
+      sw += rp.s.pw[r * rp.C + ch];
+      su += rp.s.pu[r * rp.C + ch];
+    }
+  }
+  sh.fold[0][grp][c] = sw;
+  sh.fold[1][grp][c] = su;
+  __syncthreads();
+  if (grp != 0 || ch >= rp.C) return;
+  sw = 0.f;
+  su = 0.f;
+  for (int i = 0; i < GR; ++i) {
+    sw += sh.fold[0][i][c];
+    su += sh.fold[1][i][c];
+  }
+  const float D = bwd_decay(rp, ch);
+  rp.dw[ch] = -(fast_exp2(-D) / static_cast<float>(rp.T)) * sw;
+  rp.du[ch] = su;
 }
 
 }  // namespace
