@@ -454,7 +454,7 @@ __device__ __forceinline__ void bt_retire_end(const BwdTileParams& p, unsigned f
 // not depend on arrival order. Returns true (for the whole workgroup) when a wait ran out; X and Y
 // are then not formed.
 template <int NT, int L, bool ANCHORED>
-__device__ bool bt_exchange(Agg f, Agg b, Agg& X, Agg& Y, BtShared<NT>* sh, const BwdTileParams& p,
+__device__ __forceinline__ bool bt_exchange(Agg f, Agg b, Agg& X, Agg& Y, BtShared<NT>* sh, const BwdTileParams& p,
                             const BtLane& ln, int rnd, const unsigned* sh_tag) {
   constexpr int GROUPS = NT / kBtTile;
   constexpr int PAD = kBtTile + 1;
@@ -485,7 +485,7 @@ __device__ bool bt_exchange(Agg f, Agg b, Agg& X, Agg& Y, BtShared<NT>* sh, cons
   const bool local = ln.row < p.xcd_rows;
   const __amdgpu_buffer_rsrc_t srs = make_rsrc(p.slots, 0xFFFFFFFFu);
   auto soff = [&](const unsigned long long* sp) { return static_cast<uint32_t>((sp - p.slots) * 8); };
-  auto put = [&](unsigned long long* sp, const Agg& a) {
+  auto put = [&](unsigned long long* sp, Agg a) {
     if (local)
       bt_slot_put_l2(srs, soff(sp), a, tag);
     else
