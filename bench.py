@@ -59,8 +59,9 @@ KERNEL_NAMES = {"fused": "biwkv_row_kernel", "biwkv": "biwkv_row_kernel", "causa
                 "gated": "biwkv_row_kernel", "qshift": "qshift_kernel", "mix": "qshift_mix_kernel",
                 "backward": "bwd_", "bidir": "biwkv_row_kernel"}
 # entries made of several kernels: their counters are summed over every kernel of a call, and the
-# calls are counted by a kernel that runs once per call
-CALL_MARKER = {"backward": "bwd_reduce_kernel"}
+# calls are counted by a kernel that runs once per call (the backward's last kernel, the dw / du
+# fold: bwd_reduce_kernel after the multi-launch form, bwd_one_reduce_kernel after one launch)
+CALL_MARKER = {"backward": "reduce_kernel"}
 N_MIX = 3  # mixing vectors of the mix entry (the R, K and V projection inputs)
 
 

@@ -75,16 +75,19 @@ extern "C" {
 
 /* Options (biwkv_set_option). Process-wide; they apply to calls made after they are set. */
 #define BIWKV_OPT_SPIN_LIMIT 1 /* polls of a peer chunk's sums before recomputing them (default 4096;
-                                  0: recompute every peer's sums without waiting)             */
+                                  0: recompute every peer's sums without waiting; the backward
+                                  then hands every row of several chunks to its fallback)    */
 #define BIWKV_OPT_TWO_PASS 2   /* 0 (default): one launch when all workgroups fit at once or
                                   a row's chunks take at most a quarter of the resident
-                                  workgroups; 1: every row takes the two-pass form; 2: one
-                                  launch whenever a row's chunks fit at once                   */
+                                  workgroups; 1: every row takes the two-pass form (the
+                                  backward: its multi-launch form); 2: one launch whenever a
+                                  row's chunks fit at once (forward entries)                  */
 #define BIWKV_OPT_WIDE_INDEX 3 /* 0 (default): Q-Shift gathers use 32-bit index arithmetic below
                                   2^31 items; 1: always the 64-bit form                       */
-#define BIWKV_OPT_XCD_LOCAL 4  /* 1 (default): a one-launch row runs all its chunks on one XCD
-                                  and exchanges their sums through that XCD's L2; 0: plain
-                                  block order, sums through the device-coherent level         */
+#define BIWKV_OPT_XCD_LOCAL 4  /* 1 (default): a one-launch row (forward or backward) runs all
+                                  its chunks on one XCD and exchanges their sums through that
+                                  XCD's L2; 0: plain block order, sums through the
+                                  device-coherent level                                       */
 
 /*
  * Bi-WKV forward, Eq. (5) of the Vision-RWKV article.
@@ -126,9 +129,20 @@ int biwkv_forward_noalloc(const void* k, const void* v, const float* w, const fl
  *   dw, du : [C] float32, device memory (dL/dw, dL/du summed over the batch; written).
  *   k, v, w, u, B, T, C, dtype: as for biwkv_forward; g: [B, T, C] float32, device memory.
  * Outputs must not overlap each other or any input. The pass recomputes the forward sums, so it
- * needs no forward state. A row of up to 64 tokens runs in one launch; a longer row in five
- * that pass per-chunk sums and carries (64-token chunks) through library-owned scratch per
- * (device, stream) of 4 * (2 * B * ceil(T / 64) * C + 4 * 384 * B * ceil(C / 64) * ceil(T / 64)) bytes,
+ * needs no forward state. Launch forms:
+ *  - a row of up to 64 tokens: one launch, no scratch but the dw / du terms;
+ *  - a longer row whose 128-token chunks take at most a quarter of the workgroups resident on the
+ *    device (B * ceil(C / 64) rows of ceil(T / 128) chunks; T up to 16384 on MI355X): one launch
+ *    in which the chunks of a row exchange both rounds' sums while they run (96 bytes per chunk
+ *    and tile channel of tagged sums), then one more kernel for dw and du. A workgroup whose
+ *    bounded wait for a peer runs out (BIWKV_OPT_SPIN_LIMIT) stores nothing and marks its row;
+ *    that last kernel then computes every marked row again with one workgroup that needs no
+ *    other, so no result depends on the chunks being resident together, and
+ *    biwkv_stream_fault_flags reports that it happened;
+ *  - otherwise (or with BIWKV_OPT_TWO_PASS = 1) five launches that pass per-chunk sums and carries
+ *    (64-token chunks) from one to the next.
+ * Scratch is library-owned per (device, stream): the tagged sums, and 4 * (2 * B * n * C +
+ * 4 * 384 * B * ceil(C / 64) * n) bytes of dw / du terms and chunk sums (n chunks per row),
  * allocated on the first call and grown when a larger problem arrives (so the first call on a
  * stream must not be made under graph capture). dw and du are folded in a fixed order: results
  * are bitwise reproducible. With B * T == 0 (and C > 0), dw and du are set to 0.
@@ -251,7 +265,8 @@ int biwkv_release_scratch(void* stream);
 
 /*
  * Sets process-wide option `option` (BIWKV_OPT_*) to `value`; the previous value is written to
- * *previous unless it is NULL. BIWKV_OPT_SPIN_LIMIT takes 0 .. 2^32 - 1, the others 0 or 1.
+ * *previous unless it is NULL. BIWKV_OPT_SPIN_LIMIT takes 0 .. 2^32 - 1, BIWKV_OPT_TWO_PASS 0, 1
+ * or 2, the others 0 or 1.
  * Calls already enqueued are not affected. Returns BIWKV_OK or BIWKV_ERR_PARAM (unknown option or
  * value out of range; nothing changed).
  */

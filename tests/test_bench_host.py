@@ -83,6 +83,22 @@ def test_counter_per_call_sums_the_kernels_of_a_call(tmp_path):
     assert bench._counter_per_call(str(tmp_path), "FETCH_SIZE", "bwd_", "bwd_reduce_kernel") == pytest.approx(604.0)
 
 
+def test_backward_call_marker_counts_both_forms(tmp_path):
+    """The backward's once-per-call kernel is its dw / du fold, named differently after the one-launch
+    and the multi-launch form; the marker counts either, once per call."""
+    rows = []
+    for call, names in enumerate([[("bwd_one_kernel", 500), ("bwd_one_reduce_kernel", 6)],
+                                  [("bwd_chunk_sums_kernel", 100), ("bwd_tile_kernel<3>", 300),
+                                   ("bwd_reduce_kernel", 4)]]):
+        for i, (name, val) in enumerate(names):
+            rows.append({"Dispatch_Id": 10 * call + i, "Kernel_Name": name, "Grid_Size": 1,
+                         "Counter_Name": "FETCH_SIZE", "Counter_Value": val})
+    _write_counters(str(tmp_path), rows)
+    got = bench._counter_per_call(str(tmp_path), "FETCH_SIZE", bench.KERNEL_NAMES["backward"],
+                                  bench.CALL_MARKER["backward"])
+    assert got == pytest.approx((506 + 404) / 2)
+
+
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
                        cwd=ROOT, timeout=120)
