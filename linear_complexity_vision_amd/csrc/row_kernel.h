@@ -207,7 +207,7 @@ struct RowLane {
 };
 
 template <int TILE, int L, int NT>
-__device__ __forceinline__ RowLane row_lane(const RowParams& p, unsigned unit) {
+__device__ __forceinline__ RowLane row_lane_index(const RowParams& p, unsigned unit) {
   constexpr int CT = (NT / TILE) * L;  // tokens per chunk
   RowLane ln;
   const int tid = threadIdx.x;
@@ -235,13 +235,22 @@ __device__ __forceinline__ RowLane row_lane(const RowParams& p, unsigned unit) {
   ln.s_g = static_cast<long long>(ln.chunk) * CT + static_cast<long long>(ln.g) * L;
   const long long rem = p.T - ln.s_g;
   ln.n_g = rem <= 0 ? 0 : (rem < L ? static_cast<int>(rem) : L);
-  const float wc = ln.on ? p.w[ln.ch] : 0.f;
-  const float uc = ln.on ? p.u[ln.ch] : 0.f;
-  ln.D = (wc / static_cast<float>(p.T)) * kLog2e;
+  return ln;
+}
+
+// The lane's per-channel constants from its w and u (0 for a masked lane).
+__device__ __forceinline__ void row_lane_params(RowLane& ln, long long T, float wc, float uc) {
+  ln.D = (wc / static_cast<float>(T)) * kLog2e;
   ln.lam = fast_exp2(-ln.D);
   ln.U = uc * kLog2e;
   ln.grow = fmaxf(-ln.D, 0.f);
   ln.eU = fast_exp2(ln.U);
+}
+
+template <int TILE, int L, int NT>
+__device__ __forceinline__ RowLane row_lane(const RowParams& p, unsigned unit) {
+  RowLane ln = row_lane_index<TILE, L, NT>(p, unit);
+  row_lane_params(ln, p.T, ln.on ? p.w[ln.ch] : 0.f, ln.on ? p.u[ln.ch] : 0.f);
   return ln;
 }
 
@@ -294,26 +303,27 @@ __device__ __forceinline__ void row_load(const RowParams& p, const RowLane& ln, 
   const uint32_t lane_byte = static_cast<uint32_t>(ln.ch - odd) * ES;
   constexpr int CT = (NT / TILE) * L;
   if constexpr (!FUSED) {
-    // The token offset of word m is uniform, so it moves the resource base (scalar work) and the
-    // lane keeps one vector offset. Tokens past the row fall past the shortened resource and
+    // One resource per array from the chunk's start to the end of the batch item; word m adds its
+    // token offset to the lane's vector offset (one add, no scalar work per word: sixteen
+    // wavefronts of a CU share one scalar unit). Tokens past the row fall past the resource and
     // read 0, and so does every slot of a masked lane.
     const long long c0 = static_cast<long long>(ln.chunk) * CT * row_bytes;  // chunk start
     // offsets below 2^31 (the host checks CT * C * 4)
     const uint32_t lane_off =
         ln.on ? static_cast<uint32_t>(ln.g * L + odd) * row_bytes + lane_byte : kOutOfRange;
+    const uint32_t n = row_span(item, c0);
+    const __amdgpu_buffer_rsrc_t km = make_rsrc(kb + c0, n);
+    const __amdgpu_buffer_rsrc_t vm = make_rsrc(vb + c0, n);
 #pragma unroll
     for (int m = 0; m < NW; ++m) {
-      const long long adv = c0 + static_cast<long long>(m * STEP) * row_bytes;
-      const uint32_t n = row_span(item, adv);
-      const __amdgpu_buffer_rsrc_t km = make_rsrc(kb + adv, n);
-      const __amdgpu_buffer_rsrc_t vm = make_rsrc(vb + adv, n);
-      row_load_word<DT, PAIR, POL>(kv, m, km, vm, lane_off);
+      row_load_word<DT, PAIR, POL>(kv, m, km, vm, lane_off + static_cast<uint32_t>(m * STEP) * row_bytes);
+      __builtin_amdgcn_sched_barrier(0);  // each word's offset formed just before its loads
     }
   } else {
     // Q-Shift: the lane reads its own channel at token t + delta, where delta is fixed by the
-    // channel's quarter (right: -s, left: +s, down: -s W, up: +s W, rest: 0). Word m's resource
-    // starts SH = s W tokens before the word's token, so every lane offset is non-negative and
-    // constant; sources past the end of the batch item fall past the resource and read 0. The
+    // channel's quarter (right: -s, left: +s, down: -s W, up: +s W, rest: 0). The resources start
+    // SH = s W tokens before the chunk, so every lane offset is non-negative; word m adds its token
+    // offset, and sources past the end of the batch item fall past the resource and read 0. The
     // other zero-filled sources (a column outside the quarter's band, or a row above the grid for
     // "down") are cleared words of a per-lane mask, set once. The bidirectional shift of a sparse
     // sequence (W = 1) moves the right and down groups by -s and the left and up groups by +s, with
@@ -362,17 +372,17 @@ __device__ __forceinline__ void row_load(const RowParams& p, const RowLane& ln, 
     // offsets below 2^31 (the host checks (CT + 2 s W) * C * 4)
     const uint32_t lane_off = static_cast<uint32_t>(ln.g * L + odd + delta + SH) * row_bytes + lane_byte;
     const long long c0 = (static_cast<long long>(ln.chunk) * CT - SH) * row_bytes;  // may be negative
+    const uint32_t n = row_span(item, c0);
+    const __amdgpu_buffer_rsrc_t km = make_rsrc(kb + c0, n);
+    const __amdgpu_buffer_rsrc_t vm = make_rsrc(vb + c0, n);
 #pragma unroll
     for (int m = 0; m < NW; ++m) {
-      const long long adv = c0 + static_cast<long long>(m * STEP) * row_bytes;
-      const uint32_t n = row_span(item, adv);
-      const __amdgpu_buffer_rsrc_t km = make_rsrc(kb + adv, n);
-      const __amdgpu_buffer_rsrc_t vm = make_rsrc(vb + adv, n);
       // all ones when word m is valid (bit m of the mask, sign-extended)
       const uint32_t keep =
           static_cast<uint32_t>(static_cast<std::make_signed_t<Mask>>(valid << (MB - 1 - m)) >> (MB - 1));
-      const uint32_t off = (lane_off & keep) | (kOutOfRange & ~keep);
+      const uint32_t off = ((lane_off + static_cast<uint32_t>(m * STEP) * row_bytes) & keep) | (kOutOfRange & ~keep);
       row_load_word<DT, PAIR, POL>(kv, m, km, vm, off);
+      __builtin_amdgcn_sched_barrier(0);  // each word's offset formed just before its loads
     }
   }
   // all loads in flight before anything consumes them
@@ -650,7 +660,7 @@ using RowStore = std::conditional_t<PAIR, RowKVPair<L>, RowKV<DT, L>>;
 template <int DT, int TILE, int L, int NT, bool FUSED, bool PAIR, bool WIDE, bool CAUSAL, bool GATED, int MODE>
 __device__ __forceinline__ bool row_body(const RowParams& p, const RowParams* args, const RowLane& ln,
                                          RowStore<DT, TILE, L, PAIR>& kv, float* lds,
-                                         const unsigned* sh_epoch, bool published, unsigned& fin) {
+                                         unsigned epoch_raw, bool published, unsigned& fin) {
   constexpr int GROUPS = NT / TILE;
   constexpr int CT = GROUPS * L;  // tokens per chunk
   constexpr int SB = 8;  // tokens per sub-block of the sweeps
@@ -849,7 +859,9 @@ __device__ __forceinline__ bool row_body(const RowParams& p, const RowParams* ar
         slot_load<A>(sp, w);
     };
     if constexpr (MODE == kSinglePass) {
-      epoch = __builtin_amdgcn_readfirstlane(*sh_epoch);  // set before the first barrier
+      // the slots' tag: the launch's epoch + 1 (never 0, so zeroed slots never match, whatever the
+      // counter block started at)
+      epoch = __builtin_amdgcn_readfirstlane(epoch_raw) + 1u;
       // the chunk's own sums, anchored as the totals above
       if (!published) {
         if (tg == GROUPS - 1) put(slot(chunk, kFwd), f);
@@ -1280,20 +1292,34 @@ __global__ void __launch_bounds__(64 * kCarryChans) row_carry_kernel(CarryParams
   }
 }
 
+// The epoch counter of a single pass, read through the scalar cache (the load waits in its own
+// asm block, on the scalar counter only, so vector loads issued before it stay in flight). The
+// cache holds no stale copy: caches are invalidated when a launch starts, and no workgroup moves
+// the counter before every workgroup of the launch has read it.
+template <int MODE>
+__device__ __forceinline__ unsigned row_epoch(const RowParams& p) {
+  unsigned e = 0u;
+  if (MODE == kSinglePass && p.n_chunks > 1) {
+    const unsigned long long ep = uniform_u64(reinterpret_cast<unsigned long long>(&p.ctr->epoch));
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(e) : "s"(ep) : "memory");
+  }
+  return e;
+}
+
 // The wide form is rare (extreme w or u) and needs more registers than the fast form: keeping it
 // out of line gives it its own register allocation, so its spills never touch the fast form. It
 // reads the parameters from the kernel's argument segment (a pointer, so the kernel keeps them in
 // scalar registers instead of building a private copy). It also takes over a fast-form chunk of a
 // single pass whose wait ran out (`published`: that chunk's slot is already out).
 template <int DT, int TILE, int L, int NT, bool FUSED, bool PAIR, bool CAUSAL, bool GATED, int MODE, int POL>
-__device__ __noinline__ void row_body_wide(const RowParams* args, float* lds, unsigned unit,
-                                           const unsigned* sh_epoch, bool published) {
+__device__ __noinline__ void row_body_wide(const RowParams* args, float* lds, unsigned unit, bool published) {
   const RowParams p = *args;
+  const unsigned ep = row_epoch<MODE>(p);
   const RowLane ln = row_lane<TILE, L, NT>(p, unit);
   RowStore<DT, TILE, L, PAIR> kv;
   row_load<DT, TILE, L, NT, FUSED, PAIR, POL>(p, ln, kv);
   unsigned fin = kNotRetiring;
-  row_body<DT, TILE, L, NT, FUSED, PAIR, true, CAUSAL, GATED, MODE>(p, args, ln, kv, lds, sh_epoch, published, fin);
+  row_body<DT, TILE, L, NT, FUSED, PAIR, true, CAUSAL, GATED, MODE>(p, args, ln, kv, lds, ep, published, fin);
   row_retire_end(p, fin);
 }
 
@@ -1314,33 +1340,57 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4)))
   static_assert(NT % 256 == 0 && NT <= 1024 && NT >= 2 * TILE, "bad row-kernel workgroup size");
   constexpr int POL = kRowLoadPolicy<MODE>;
   __shared__ float lds[kRowLdsFloats<TILE, NT>];
-  __shared__ unsigned sh_epoch;
-  const int tid = threadIdx.x;
   const unsigned unit = blockIdx.x;
-  // a single pass exchanges through slots tagged with the launch's epoch + 1 (never 0, so zeroed
-  // slots never match, whatever the counter block started at); the tag is only needed once the
-  // scan (and its barriers) is done
-  if (MODE == kSinglePass && p.n_chunks > 1 && tid == 0)
-    sh_epoch = __hip_atomic_load(&p.ctr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-  const RowLane ln = row_lane<TILE, L, NT>(p, unit);
+  // the kernel's only argument is p, at the start of the argument segment (the argument segment
+  // pointer exists only here, in the kernel: out-of-line functions get it passed down)
+  const auto* args = (const RowParams*)(__builtin_amdgcn_kernarg_segment_ptr());
+  RowLane ln = row_lane_index<TILE, L, NT>(p, unit);
+  RowStore<DT, TILE, L, PAIR> kv;
+  unsigned ep = 0;
+  // Single passes over 32-bit words issue every vector load before anything waits: w and u
+  // (range-checked: a masked lane reads 0), then the chunk's k and v in the fast form's layout;
+  // the form is chosen once w and u have arrived, and the wide form loads the chunk again itself.
+  // Elsewhere (16-bit loads, two passes) the early loads cost the fast form registers: the form is
+  // chosen first.
+  constexpr bool kEarly = MODE == kSinglePass && (PAIR || DT == BIWKV_F32);
+  if constexpr (kEarly) {
+    const uint32_t coff = ln.on ? static_cast<uint32_t>(ln.ch) * 4u : kOutOfRange;
+    const uint32_t cbytes = static_cast<uint32_t>(p.C) * 4u;
+    const uint32_t wbits = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(p.w, cbytes), coff, 0, 0);
+    const uint32_t ubits = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(p.u, cbytes), coff, 0, 0);
+    row_load<DT, TILE, L, NT, FUSED, PAIR, POL>(p, ln, kv);
+    ep = row_epoch<MODE>(p);
+    row_lane_params(ln, p.T, __uint_as_float(wbits), __uint_as_float(ubits));
+  } else {
+    ep = row_epoch<MODE>(p);
+    row_lane_params(ln, p.T, ln.on ? p.w[ln.ch] : 0.f, ln.on ? p.u[ln.ch] : 0.f);
+  }
   // The whole workgroup takes the wide form when any of its channels needs it: decay or growth
   // across one lane beyond kFastRange, a bonus beyond kBonusRange, or decay across the row beyond
   // kExactRange (the sums' exponents then need exact token counts). Every wavefront holds all TILE
   // channels, so a wavefront vote is the workgroup's vote, and every chunk of a row votes alike.
   const bool wide_lane = fabsf(ln.D) * static_cast<float>(L - 1) > kFastRange || ln.U > kBonusRange ||
                          ln.U < -kBonusRange || fabsf(ln.D) * static_cast<float>(p.T) > kExactRange;
-  // the kernel's only argument is p, at the start of the argument segment (the argument segment
-  // pointer exists only here, in the kernel: out-of-line functions get it passed down)
-  const auto* args = (const RowParams*)(__builtin_amdgcn_kernarg_segment_ptr());
-  if (__ballot(wide_lane) != 0ull) {
-    row_body_wide<DT, TILE, L, NT, FUSED, PAIR, CAUSAL, GATED, MODE, POL>(args, lds, unit, &sh_epoch, false);
-  } else {
-    RowStore<DT, TILE, L, PAIR> kv;
-    row_load<DT, TILE, L, NT, FUSED, PAIR, POL>(p, ln, kv);
+  const bool fast = __ballot(wide_lane) == 0ull;
+  if constexpr (kEarly) {
+    // one call site of the wide form: from the start, or for a fast chunk whose wait ran out (its
+    // slot already published)
     unsigned fin = kNotRetiring;
-    if (!row_body<DT, TILE, L, NT, FUSED, PAIR, false, CAUSAL, GATED, MODE>(p, args, ln, kv, lds, &sh_epoch, false, fin))
-      row_body_wide<DT, TILE, L, NT, FUSED, PAIR, CAUSAL, GATED, MODE, POL>(args, lds, unit, &sh_epoch, true);
-    row_retire_end(p, fin);
+    if (fast && row_body<DT, TILE, L, NT, FUSED, PAIR, false, CAUSAL, GATED, MODE>(p, args, ln, kv, lds, ep, false, fin)) {
+      row_retire_end(p, fin);
+      return;
+    }
+    row_body_wide<DT, TILE, L, NT, FUSED, PAIR, CAUSAL, GATED, MODE, POL>(args, lds, unit, fast);
+  } else {
+    if (!fast) {
+      row_body_wide<DT, TILE, L, NT, FUSED, PAIR, CAUSAL, GATED, MODE, POL>(args, lds, unit, false);
+    } else {
+      row_load<DT, TILE, L, NT, FUSED, PAIR, POL>(p, ln, kv);
+      unsigned fin = kNotRetiring;
+      if (!row_body<DT, TILE, L, NT, FUSED, PAIR, false, CAUSAL, GATED, MODE>(p, args, ln, kv, lds, ep, false, fin))
+        row_body_wide<DT, TILE, L, NT, FUSED, PAIR, CAUSAL, GATED, MODE, POL>(args, lds, unit, true);
+      row_retire_end(p, fin);
+    }
   }
 }
 
