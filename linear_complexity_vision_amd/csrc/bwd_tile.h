@@ -176,7 +176,7 @@ struct BtLane {
 };
 
 template <int L, int NT>
-__device__ __forceinline__ BtLane bt_lane(const BwdTileParams& p, unsigned unit) {
+__device__ __forceinline__ BtLane bt_lane_index(const BwdTileParams& p, unsigned unit) {
   constexpr int CT = (NT / kBtTile) * L;
   BtLane ln;
   const int tid = threadIdx.x;
@@ -200,8 +200,19 @@ __device__ __forceinline__ BtLane bt_lane(const BwdTileParams& p, unsigned unit)
   ln.ch = tile * kBtTile + ln.c;
   ln.on = ln.ch < p.C;
   ln.s_g = static_cast<long long>(ln.chunk) * CT + static_cast<long long>(ln.g) * L;
-  ln.D = ln.on ? (p.w[ln.ch] / static_cast<float>(p.T)) * kLog2e : 0.f;
-  ln.U = ln.on ? p.u[ln.ch] * kLog2e : 0.f;
+  return ln;
+}
+
+// The lane's D and U from its w and u (a masked lane passes 0: D = U = 0).
+__device__ __forceinline__ void bt_lane_params(BtLane& ln, long long T, float wc, float uc) {
+  ln.D = (wc / static_cast<float>(T)) * kLog2e;
+  ln.U = uc * kLog2e;
+}
+
+template <int L, int NT>
+__device__ __forceinline__ BtLane bt_lane(const BwdTileParams& p, unsigned unit) {
+  BtLane ln = bt_lane_index<L, NT>(p, unit);
+  bt_lane_params(ln, p.T, ln.on ? p.w[ln.ch] : 0.f, ln.on ? p.u[ln.ch] : 0.f);
   return ln;
 }
 
@@ -1116,9 +1127,21 @@ __device__ __forceinline__ void bt_load_g(const BwdTileParams& p, int bi, long l
 // same values, for y and the states of dw) and writes dv, dk and the dw terms. Returns (dw terms,
 // du terms, failed, -); failed when a wait of either exchange ran out.
 // ---------------------------------------------------------------------------------------------
+template <int DT, int L, bool PAIR>
+using BtOneKV = std::conditional_t<PAIR, RowKVPair<L>, BtKV<DT, L>>;
+
+// Issues the loads of the chunk's k and v for bt_body_one (nothing waits here).
+template <int DT, int L, bool PAIR>
+__device__ __forceinline__ void bt_one_load(const BwdTileParams& p, const BtLane& ln, BtOneKV<DT, L, PAIR>& kv) {
+  if constexpr (PAIR)
+    bt_load_pairs<L, kStream>(p, ln.bi, ln.s_g, ln.ch, ln.on, kv, nullptr);
+  else
+    bt_load<DT, L, kStream>(p, ln.bi, ln.s_g, ln.ch, ln.on, kv, nullptr);
+}
+
 template <int DT, int L, int NT, bool PAIR>
-__device__ __forceinline__ float4 bt_body_one(const BwdTileParams& p, const BtLane& ln, BtShared<NT>* sh,
-                                              const unsigned* sh_tag, unsigned& fin) {
+__device__ __forceinline__ float4 bt_body_one(const BwdTileParams& p, const BtLane& ln, BtOneKV<DT, L, PAIR>& kv,
+                                              BtShared<NT>* sh, const unsigned* sh_tag, unsigned& fin) {
   constexpr int SB = kBtSB;
   constexpr int NSB = L / SB;
   const float4 failed = make_float4(0.f, 0.f, 1.f, 0.f);
@@ -1127,13 +1150,9 @@ __device__ __forceinline__ float4 bt_body_one(const BwdTileParams& p, const BtLa
   const float lsb = fast_exp2(-static_cast<float>(SB) * D);  // lam^SB
   const float span = fmaxf(-D, 0.f) * static_cast<float>(L - 1);  // largest growth inside a lane
   const float eU = fast_exp2(U);
-  std::conditional_t<PAIR, RowKVPair<L>, BtKV<DT, L>> kv;
   if constexpr (PAIR) {
-    bt_load_pairs<L, kStream>(p, ln.bi, ln.s_g, ln.ch, ln.on, kv, nullptr);
 #pragma unroll
     for (int q = 0; q < L / 8; ++q) kv.prepare(q);
-  } else {
-    bt_load<DT, L, kStream>(p, ln.bi, ln.s_g, ln.ch, ln.on, kv, nullptr);
   }
   auto kl = [&](int i) { return kv.k(i) * kLog2e; };  // -inf in empty slots
 
@@ -1629,11 +1648,27 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4)))
   __shared__ BtShared<NT> sh;
   __shared__ unsigned sh_tag;
   const int tid = threadIdx.x;
+  BtLane ln = bt_lane_index<L, NT>(p, blockIdx.x);
+  // Every vector load is issued before anything waits: w and u (range-checked: a masked lane reads
+  // 0), then the chunk's k and v in the fast form's layout; the form is chosen once w and u have
+  // arrived, and the wide form loads the chunk again itself.
+  const uint32_t coff = ln.on ? static_cast<uint32_t>(ln.ch) * 4u : kOutOfRange;
+  const uint32_t cbytes = static_cast<uint32_t>(p.C) * 4u;
+  const uint32_t wbits = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(p.w, cbytes), coff, 0, 0);
+  const uint32_t ubits = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(p.u, cbytes), coff, 0, 0);
+  BtOneKV<DT, L, PAIR> kv;
+  bt_one_load<DT, L, PAIR>(p, ln, kv);
   // slots are tagged with the launch's epoch + 1 (never 0, so zeroed slots never match); the tag
-  // is read after the exchange's first barrier
-  if (tid == 0)
-    sh_tag = p.n_chunks > 1 ? __hip_atomic_load(&p.ctr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u : 1u;
-  const BtLane ln = bt_lane<L, NT>(p, blockIdx.x);
+  // is read after the exchange's first barrier. The epoch comes through the scalar cache, which
+  // holds no stale copy (caches are invalidated when a launch starts, and the counter only moves
+  // once every workgroup of the launch has read it); the load waits on the scalar counter only.
+  unsigned ep = 0u;
+  if (p.n_chunks > 1) {
+    const unsigned long long ea = uniform_u64(reinterpret_cast<unsigned long long>(&p.ctr->epoch));
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(ep) : "s"(ea) : "memory");
+  }
+  if (tid == 0) sh_tag = p.n_chunks > 1 ? ep + 1u : 1u;
+  bt_lane_params(ln, p.T, __uint_as_float(wbits), __uint_as_float(ubits));
   if (ln.g == 0) sh.dch[ln.c] = ln.D;
   const bool wide_lane = bt_wide_lane<L>(ln.D, ln.U);
   unsigned fin = kNotRetiring;
@@ -1642,7 +1677,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4)))
     const auto* args = (const BwdTileParams*)(__builtin_amdgcn_kernarg_segment_ptr());
     r = bt_body_wide<DT, L, NT, 4>(args, &sh, &sh_tag, blockIdx.x);
   } else {
-    r = bt_body_one<DT, L, NT, PAIR>(p, ln, &sh, &sh_tag, fin);
+    r = bt_body_one<DT, L, NT, PAIR>(p, ln, kv, &sh, &sh_tag, fin);
   }
   if (r.z != 0.f) {  // uniform: a wait ran out
     if (tid == 0) {
