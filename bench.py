@@ -18,6 +18,9 @@ else computed), with the kernel's fraction of it.
 
     python bench.py --calibrate-copy      plain device copy of a known size (for counter scaling)
     python bench.py --summarize DIR       summarise rocprofv3 output (kernel stats / counters)
+    python bench.py --counters-table      the recorded HBM traffic of every entry against its algorithmic bytes
+    python bench.py --summarize-sq D1 D2 D3   instruction mix, occupancy, LDS conflicts from three
+                                          rocprofv3 --pmc passes of SQ counters
     python bench.py --record-counters KF KW CF CW [--config N --entry E]
         turn four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE of the bench, the same two of
         --calibrate-copy) into profiles/hbm_counters.json: HBM bytes per call, scaled so that the
@@ -51,9 +54,10 @@ GATE_ENTRY = {2: "biwkv", 4: "biwkv"}
 # entries whose byte mix is the forward's (k, v read once, fp32 out written): the memory ceiling
 # applies to them
 CEILING_ENTRIES = ("biwkv", "fused", "causal", "bidir")
-# grid-stride streaming variants tried for the ceiling (blocks, unroll, policy: non-temporal loads
-# and stores); the fastest is the ceiling
-CEILING_VARIANTS = [(512, 1, 3), (2048, 1, 3), (8192, 2, 3), (8192, 4, 3), (1024, 1, 1), (4096, 2, 1)]
+# grid-stride streaming variants tried for the ceiling (blocks, unroll, policy: bit 0 non-temporal
+# loads, bit 1 non-temporal stores, bit 2 8-byte pieces of k and v); the fastest is the ceiling
+CEILING_VARIANTS = [(512, 1, 3), (2048, 1, 3), (8192, 2, 3), (8192, 4, 3), (1024, 1, 1), (4096, 2, 1),
+                    (8192, 1, 7), (16384, 1, 7), (4096, 2, 7), (8192, 2, 7)]
 COPY_KERNEL = "copy"  # substring of the device copy kernel's name in the counter output
 KERNEL_NAMES = {"fused": "biwkv_row_kernel", "biwkv": "biwkv_row_kernel", "causal": "biwkv_row_kernel",
                 "gated": "biwkv_row_kernel", "qshift": "qshift_kernel", "mix": "qshift_mix_kernel",
@@ -589,6 +593,64 @@ def record_counters(kf: str, kw: str, cf: str, cw: str, config: int, entry: str)
     print(json.dumps(rec["entries"][counter_key(config, entry)]))
 
 
+def counters_table() -> None:
+    """One line per recorded entry of profiles/hbm_counters.json: FETCH_SIZE and WRITE_SIZE per
+    call, the scaled HBM bytes, the algorithmic bytes of the call and their ratio."""
+    import workloads
+
+    rec = json.load(open(COUNTERS_FILE))
+    print(f"kernel sources sha256[:16]: {rec.get('kernel_source_sha256_16')}")
+    cal = rec["calibration"]
+    print(f"calibration: FETCH_SIZE {cal['fetch_kib']:.1f} KiB -> {cal['fetch_bytes_per_unit']:.2f} B per unit; "
+          f"WRITE_SIZE {cal['write_kib']:.1f} KiB -> {cal['write_bytes_per_unit']:.2f} B per unit")
+    for key, e in rec["entries"].items():
+        config, entry = int(key.split(":")[0][len("config"):]), key.split(":")[1]
+        wl = workloads.make_mae(2) if entry == "bidir" else workloads.make(config)
+        kvb = 4 if entry in ("qshift", "mix") else (2 if wl.dtype == "bf16" else 4)
+        ab = alg_bytes(entry, wl.B, wl.H, wl.W, wl.C, kvb, wl.shift, wl.gamma)
+        shape = f"B{wl.B}_{'N' if entry == 'bidir' else 'T'}{wl.H * wl.W}_C{wl.C}_{'bf16' if kvb == 2 else 'f32'}"
+        hbm = e["hbm_bytes_per_call"]
+        print(f"config {config} {entry:9s} {shape:26s} FETCH {e['fetch_kib_per_call']:12.1f} KiB  WRITE "
+              f"{e['write_kib_per_call']:12.1f} KiB  HBM {hbm / 1e6:9.2f} MB  algorithmic {ab / 1e6:9.2f} MB  "
+              f"ratio {hbm / ab:.3f}")
+
+
+def summarize_sq(d1: str, d2: str, d3: str) -> None:
+    """Per-kernel instruction mix, occupancy and LDS conflicts from three rocprofv3 --pmc passes
+    (d1: SQ_WAVES SQ_INSTS_VALU SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_SALU SQ_INSTS_LDS SQ_INSTS_VMEM_RD
+    SQ_INSTS_VMEM_WR SQ_INSTS_SMEM; d2: SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_ACTIVE_INST_VALU; d3:
+    SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE). Counters are summed over the shader engines of a
+    dispatch and averaged over the dispatches of a kernel name. Per-wave counts = SQ_INSTS_* /
+    SQ_WAVES; resident waves per SIMD = 4 SQ_WAVE_CYCLES / (SQ_BUSY_CYCLES x 8 CUs x 4 SIMDs);
+    VALU-active share = 4 SQ_ACTIVE_INST_VALU / (SQ_BUSY_CYCLES x 32 SIMDs per SE)."""
+    means: dict = {}
+    for d in (d1, d2, d3):
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            acc: dict = {}
+            for row in csv.DictReader(open(f)):
+                key = (row.get("Kernel_Name", "?"), row.get("Counter_Name"))
+                acc.setdefault(key, []).append(float(row.get("Counter_Value", "nan")))
+            for (kname, cname), vals in acc.items():
+                means.setdefault(kname, {})[cname] = sum(vals) / len(vals)
+    for kname in sorted(means):
+        m = means[kname]
+        # the library's and the runtime's helper kernels (copies, fills, counter set-up) are skipped
+        if "SQ_WAVES" not in m or m["SQ_WAVES"] <= 0 or any(x in kname for x in ("rocclr", "fill_", "init_counters")):
+            continue
+        w = m["SQ_WAVES"]
+        print(kname.replace("void ", "").replace("(anonymous namespace)::", "").split("(")[0][:100])
+        print(f"  waves {w:.0f}; per wave: VALU {m.get('SQ_INSTS_VALU', 0) / w:.0f} (transcendental "
+              f"{m.get('SQ_INSTS_VALU_TRANS_F32', 0) / w:.0f}), SALU {m.get('SQ_INSTS_SALU', 0) / w:.0f}, "
+              f"LDS {m.get('SQ_INSTS_LDS', 0) / w:.1f}, vector loads {m.get('SQ_INSTS_VMEM_RD', 0) / w:.1f}, "
+              f"vector stores {m.get('SQ_INSTS_VMEM_WR', 0) / w:.1f}, scalar loads {m.get('SQ_INSTS_SMEM', 0) / w:.1f}")
+        busy = m.get("SQ_BUSY_CYCLES", 0)
+        if busy > 0:
+            print(f"  busy {busy:.0f} cycles (summed over SEs); resident waves per SIMD "
+                  f"{4 * m.get('SQ_WAVE_CYCLES', 0) / (busy * 8 * 4):.2f}; VALU-active share "
+                  f"{4 * m.get('SQ_ACTIVE_INST_VALU', 0) / (busy * 32):.2f}; LDS bank-conflict cycles "
+                  f"{m.get('SQ_LDS_BANK_CONFLICT', 0):.0f} of {m.get('SQ_LDS_IDX_ACTIVE', 0):.0f} LDS-active")
+
+
 def summarize(path: str) -> None:
     """Summarise rocprofv3 CSV output under `path`: per-kernel durations or counter values."""
     stats = glob.glob(os.path.join(path, "**", "*kernel_stats.csv"), recursive=True)
@@ -624,9 +686,17 @@ def main() -> int:
                     help="every row through the two-pass form (BIWKV_OPT_TWO_PASS = 1), for comparison")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize", metavar="DIR")
+    ap.add_argument("--summarize-sq", nargs=3, metavar=("D1", "D2", "D3"))
+    ap.add_argument("--counters-table", action="store_true")
     ap.add_argument("--record-counters", nargs=4, metavar=("KF", "KW", "CF", "CW"))
     args = ap.parse_args()
 
+    if args.counters_table:
+        counters_table()
+        return
+    if args.summarize_sq:
+        summarize_sq(*args.summarize_sq)
+        return
     if args.summarize:
         summarize(args.summarize)
         return 0

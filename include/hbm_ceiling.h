@@ -27,10 +27,11 @@ extern "C" {
  * Streams n elements: mode 0 reads k and v (dtype HBM_BF16 or HBM_F32, [n]) and writes
  * out[i] = k[i] + v[i] (fp32, [n]); mode 1 only reads k and v; mode 2 only writes out.
  *   k, v, out : device pointers, 16-byte aligned; the caller owns them; out must not overlap.
- *   n         : a multiple of 8 (bf16) or 4 (fp32).
- *   blocks    : 256-thread workgroups of the grid-stride loop (0: one 16-byte piece per thread).
+ *   n         : a multiple of 8 (bf16) or 4 (fp32); with policy bit 2, of 4 (bf16) or 2 (fp32).
+ *   blocks    : 256-thread workgroups of the grid-stride loop (0: one piece per thread).
  *   unroll    : 1, 2, 4 or 8 pieces per thread per loop trip, all loads issued before any store.
- *   policy    : bit 0 non-temporal loads, bit 1 non-temporal stores.
+ *   policy    : bit 0 non-temporal loads, bit 1 non-temporal stores, bit 2 8-byte pieces of k
+ *               and v per thread (4 bf16 or 2 fp32 elements) instead of 16-byte ones.
  *   stream    : hipStream_t as void* (NULL: the null stream). Asynchronous; nothing allocated.
  * Returns HBM_OK, HBM_ERR_ARG (nothing launched) or HBM_ERR_HIP.
  */

@@ -157,8 +157,10 @@ def test_ceiling_library_exports_and_validates():
     assert f(K16, V16, O16, 64, 5, 0, 0, 1, 3, None) == -1          # dtype
     assert f(K16, V16, O16, 64, 1, 3, 0, 1, 3, None) == -1          # mode
     assert f(K16, V16, O16, 64, 1, 0, 0, 3, 3, None) == -1          # unroll
-    assert f(K16, V16, O16, 64, 1, 0, 0, 1, 4, None) == -1          # policy
+    assert f(K16, V16, O16, 64, 1, 0, 0, 1, 8, None) == -1          # policy
     assert f(K16, V16, O16, 12, 1, 0, 0, 1, 3, None) == -1          # not whole 16-byte pieces
+    assert f(K16, V16, O16, 6, 1, 0, 0, 1, 7, None) == -1           # not whole 8-byte pieces
+    assert f(K16, V16, O16, 5, 0, 0, 0, 1, 7, None) == -1           # fp32: not whole 8-byte pieces
     assert f(K16 + 4, V16, O16, 64, 1, 0, 0, 1, 3, None) == -1      # misaligned
     assert f(None, V16, O16, 64, 1, 0, 0, 1, 3, None) == -1         # NULL
 

@@ -127,3 +127,31 @@ def test_kernel_of_entry_tells_the_tile_kernel_variants_apart():
     assert bench.kernel_of_entry(gated, "gated") and not bench.kernel_of_entry(gated, "fused")
     assert bench.kernel_of_entry("void (anonymous namespace)::qshift_kernel<4, false>(unsigned int const*)", "qshift")
     assert not bench.kernel_of_entry("void (anonymous namespace)::qshift_kernel<4, false>(x)", "biwkv")
+
+
+def test_summarize_sq_derives_per_wave_figures(tmp_path, capsys):
+    # three passes, two dispatches of one kernel: means per counter, then the stated formulas
+    rows = {
+        "p1": {"SQ_WAVES": (100, 100), "SQ_INSTS_VALU": (2000, 2200), "SQ_INSTS_VALU_TRANS_F32": (300, 300),
+               "SQ_INSTS_SALU": (500, 500), "SQ_INSTS_LDS": (10, 10), "SQ_INSTS_VMEM_RD": (640, 640),
+               "SQ_INSTS_VMEM_WR": (320, 320), "SQ_INSTS_SMEM": (70, 70)},
+        "p2": {"SQ_WAVE_CYCLES": (1000, 1000), "SQ_BUSY_CYCLES": (50, 50), "SQ_ACTIVE_INST_VALU": (200, 200)},
+        "p3": {"SQ_LDS_BANK_CONFLICT": (7, 9), "SQ_LDS_IDX_ACTIVE": (100, 100)},
+    }
+    dirs = []
+    for name, ctrs in rows.items():
+        d = tmp_path / name
+        d.mkdir()
+        with open(d / "run_counter_collection.csv", "w", newline="") as f:
+            w = csv.writer(f)
+            w.writerow(["Kernel_Name", "Counter_Name", "Counter_Value"])
+            for cname, vals in ctrs.items():
+                for v in vals:
+                    w.writerow(["my_kernel(int)", cname, v])
+        dirs.append(str(d))
+    bench.summarize_sq(*dirs)
+    out = capsys.readouterr().out
+    assert "my_kernel" in out
+    assert "per wave: VALU 21 (transcendental 3), SALU 5, LDS 0.1, vector loads 6.4" in out
+    # 4 * 1000 / (50 * 32) = 2.50 waves per SIMD; 4 * 200 / (50 * 32) = 0.50 VALU-active
+    assert "resident waves per SIMD 2.50; VALU-active share 0.50; LDS bank-conflict cycles 8 of 100" in out
