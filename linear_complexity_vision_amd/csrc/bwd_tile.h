@@ -1709,8 +1709,11 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4)))
 // A row of the last bwd_one_kernel launch whose waits ran out, computed again by one workgroup
 // alone: the three stages of the multi-launch form over the row's chunks in order (chunk sums,
 // carries, round 1 and the round-2 sums, carries, both rounds), so it needs no other workgroup.
+// Inlined into the kernel that calls it: bt_stage's wide form reads the parameters through the
+// kernel's argument segment pointer, which only a kernel body has (an out-of-line function sees a
+// null pointer there).
 template <int DT, int L, int NT, bool PAIR>
-__device__ void bt_row_fallback(const BwdTileParams& p, int row, BtShared<NT>& sh) {
+__device__ __forceinline__ void bt_row_fallback(const BwdTileParams& p, int row, BtShared<NT>& sh) {
   constexpr int CT = (NT / kBtTile) * L;
   constexpr int GR = NT / kBtTile;
   static_assert(sizeof(sh.sw) >= 2 * GR * 6 * kBtTile * sizeof(float), "carry scratch");
@@ -1744,35 +1747,86 @@ __device__ void bt_row_fallback(const BwdTileParams& p, int row, BtShared<NT>& s
 template <int DT, int L, int NT, bool PAIR>
 __global__ void __launch_bounds__(NT) bwd_one_reduce_kernel(BwdTileParams p, BwdParams rp) {
   constexpr int GR = NT / kBtTile;
+  constexpr int kHeld = 32;  // partial sums of a lane held in registers (more are read in a loop)
   __shared__ BtShared<NT> sh;
   const int tile = blockIdx.x;
-  if (p.n_chunks > 1) {
-    const unsigned tag = __hip_atomic_load(&p.ctr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // lane j of every wavefront reads the flag of batch item b0 + j (all in flight at once); the
-    // vote is the same in every wavefront, so the fallback's barriers are met by all of them
+  const int c = threadIdx.x % kBtTile, grp = threadIdx.x / kBtTile;
+  const int ch = tile * kBtTile + c;
+  const int chc = ch < rp.C ? ch : rp.C - 1;  // a masked lane reads a valid term and ignores it
+  const long long n = static_cast<long long>(rp.B) * rp.n_wg;
+  const long long per = (n + GR - 1) / GR;
+  const long long r0 = grp * per, r1 = r0 + per < n ? r0 + per : n;
+  // This lane's dw and du terms, the row flags of the first 64 batch items and the launch's tag
+  // are all requested before anything waits (one round trip): the terms are read unconditionally
+  // at clamped rows, the tag through the scalar cache (its wait is on the scalar counter only).
+  // The terms are read non-temporally, so the CU's L1 keeps no copy that a second read could find
+  // stale after this workgroup computed a row again below.
+  float hw[kHeld], hu[kHeld];
+  const bool held = per <= kHeld;
+  if (held) {
+#pragma unroll
+    for (int i = 0; i < kHeld; ++i) {
+      const long long r = r0 + i < n ? r0 + i : n - 1;
+      hw[i] = __builtin_nontemporal_load(rp.s.pw + r * rp.C + chc);
+      hu[i] = __builtin_nontemporal_load(rp.s.pu + r * rp.C + chc);
+    }
+  }
+  const bool many = p.n_chunks > 1;
+  const int lane = static_cast<int>(threadIdx.x % 64);
+  const int b0c = lane < rp.B ? lane : rp.B - 1;
+  const unsigned flag0 = many ? p.row_fail[b0c * p.n_tiles + tile] : 0u;
+  unsigned tag = 0u;
+  if (many) {
+    const unsigned long long ea = uniform_u64(reinterpret_cast<unsigned long long>(&p.ctr->epoch));
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(tag) : "s"(ea) : "memory");
+  }
+  // the terms in a fixed order (the same additions whether held or read in the loop)
+  auto fold = [&](float& sw, float& su, bool use_held) {
+    sw = 0.f;
+    su = 0.f;
+    if (use_held) {
+#pragma unroll
+      for (int i = 0; i < kHeld; ++i) {
+        if (r0 + i < r1) {
+          sw += hw[i];
+          su += hu[i];
+        }
+      }
+    } else {
+#pragma unroll 8
+      for (long long r = r0; r < r1; ++r) {
+        sw += __builtin_nontemporal_load(rp.s.pw + r * rp.C + chc);
+        su += __builtin_nontemporal_load(rp.s.pu + r * rp.C + chc);
+      }
+    }
+  };
+  // Rows whose waits ran out in the bwd_one_kernel launch before this one (row_fail holds that
+  // launch's tag, which is the epoch now). Lane j of every wavefront holds the flag of batch item
+  // b0 + j; the vote is the same in every wavefront, so the fallback's barriers are met by all.
+  // The held terms are only used when no row was computed again, so they are not live across the
+  // (out-of-line) fallback.
+  auto hits = [&](int b0) {
+    const int bi = b0 + lane;
+    const unsigned f = b0 == 0 ? flag0 : (bi < rp.B ? p.row_fail[bi * p.n_tiles + tile] : 0u);
+    return __ballot(bi < rp.B && f == tag);
+  };
+  bool any = false;
+  if (many)
+    for (int b0 = 0; b0 < rp.B; b0 += 64) any = any || hits(b0) != 0ull;
+  float sw, su;
+  if (!any) {
+    fold(sw, su, held);
+  } else {
     for (int b0 = 0; b0 < rp.B; b0 += 64) {
-      const int bi = b0 + static_cast<int>(threadIdx.x % 64);
-      const bool hit = bi < rp.B && p.row_fail[bi * p.n_tiles + tile] == tag;
-      unsigned long long m = __ballot(hit);
+      unsigned long long m = hits(b0);
       while (m != 0ull) {
         const int j = __builtin_ctzll(m);
         m &= m - 1ull;
         bt_row_fallback<DT, L, NT, PAIR>(p, (b0 + j) * p.n_tiles + tile, sh);
       }
     }
-  }
-  const int c = threadIdx.x % kBtTile, grp = threadIdx.x / kBtTile;
-  const int ch = tile * kBtTile + c;
-  const long long n = static_cast<long long>(rp.B) * rp.n_wg;
-  const long long per = (n + GR - 1) / GR;
-  const long long r0 = grp * per, r1 = r0 + per < n ? r0 + per : n;
-  float sw = 0.f, su = 0.f;
-  if (ch < rp.C) {
-#pragma unroll 8
-    for (long long r = r0; r < r1; ++r) {
-      sw += rp.s.pw[r * rp.C + ch];
-      su += rp.s.pu[r * rp.C + ch];
-    }
+    __syncthreads();  // the rows' terms, written by this workgroup, are visible to it
+    fold(sw, su, false);
   }
   sh.fold[0][grp][c] = sw;
   sh.fold[1][grp][c] = su;
